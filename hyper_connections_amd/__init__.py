@@ -1,0 +1,299 @@
+"""Python binding of libdecodehp (MI355X decode hot path).
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind the C
+ABI declared in include/decodehp.h. PyTorch supplies device memory and the stream; the
+binding checks dtype, device and contiguity, allocates the workspace an entry point asks
+for, and raises DecodeHPError on a nonzero return. There is no fallback: without the
+built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .layout import pack_int4_codes, bf16_bits_to_tensor  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdecodehp.so")
+
+DHP_F16, DHP_F32, DHP_BF16 = 0, 1, 2
+DHP_OP_GEMV_ARGMAX, DHP_OP_MOE_DECODE, DHP_OP_HC_READ = 1, 2, 3
+DHP_MOE_FP16_BOUNDARY = 1
+ERRORS = {-1: "invalid argument", -2: "unsupported", -3: "misaligned", -4: "workspace",
+          -5: "no device", -6: "launch"}
+
+
+class DecodeHPError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"libdecodehp error {code} ({ERRORS.get(code, '?')}): {message}")
+        self.code = code
+
+
+class CInt4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+
+class CInt4Experts(ctypes.Structure):
+    _fields_ = [("first", CInt4), ("codes_stride", ctypes.c_int64), ("scales_stride", ctypes.c_int64),
+                ("count", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdecodehp; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with hyper_connections_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        P4, PE = ctypes.POINTER(CInt4), ctypes.POINTER(CInt4Experts)
+        L.decodehp_dequant_gemv.argtypes = [P4, vp, i32, vp, i32, vp, vp, sz, vp]
+        L.decodehp_dequant_gemm_batched.argtypes = [P4, vp, i32, vp, vp]
+        L.decodehp_moe_decode.argtypes = [vp, vp, i32, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp,
+                                          vp, sz, vp]
+        L.decodehp_hc_read.argtypes = [vp, vp, i32, i32, ctypes.c_float, P4, P4, P4, vp, vp, vp, sz, vp]
+        L.decodehp_hc_inject.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.decodehp_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.decodehp_workspace_bytes.restype = sz
+        L.decodehp_last_error.restype = ctypes.c_char_p
+        L.decodehp_version.restype = i32
+        for name in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
+                     "decodehp_hc_read", "decodehp_hc_inject"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DecodeHPError(rc, lib().decodehp_last_error().decode())
+
+
+def workspace_bytes(op: int, a: int, b: int = 0, c: int = 0) -> int:
+    return int(lib().decodehp_workspace_bytes(op, a, b, c))
+
+
+# --------------------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, name, numel=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class Int4Weight:
+    """Device INT4-affine tensor: codes uint8 [rows, cols/2], scales/biases bf16-bit int16 [rows, cols/64]."""
+
+    codes: "object"
+    scales: "object"
+    biases: "object"
+    rows: int
+    cols: int
+
+    @classmethod
+    def from_logical(cls, q, s_bits, b_bits, device="cuda"):
+        torch = _torch()
+        q = np.asarray(q)
+        rows, cols = q.shape
+        codes = torch.from_numpy(pack_int4_codes(q)).to(device)
+        scales = bf16_bits_to_tensor(s_bits).to(device)
+        biases = bf16_bits_to_tensor(b_bits).to(device)
+        return cls(codes, scales, biases, rows, cols)
+
+    def desc(self) -> CInt4:
+        torch = _torch()
+        _need(self.codes, torch.uint8, "codes", self.rows * self.cols // 2)
+        _need(self.scales, torch.int16, "scales", self.rows * self.cols // 64)
+        _need(self.biases, torch.int16, "biases", self.rows * self.cols // 64)
+        return CInt4(self.codes.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
+                     self.rows, self.cols, 64)
+
+    @property
+    def nbytes(self) -> int:
+        return self.rows * self.cols // 2 + 2 * 2 * self.rows * (self.cols // 64)
+
+
+@dataclass
+class Int4Experts:
+    """`count` same-shaped INT4 tensors stored back to back: codes [count, rows, cols/2], scales/biases
+    [count, rows, cols/64]."""
+
+    codes: "object"
+    scales: "object"
+    biases: "object"
+    count: int
+    rows: int
+    cols: int
+
+    @classmethod
+    def from_logical(cls, tensors, device="cuda"):
+        torch = _torch()
+        rows, cols = tensors[0].q.shape
+        codes = torch.from_numpy(np.stack([pack_int4_codes(t.q) for t in tensors])).to(device)
+        scales = torch.from_numpy(np.stack([np.asarray(t.s_bits, np.uint16) for t in tensors]).view(np.int16)).to(device)
+        biases = torch.from_numpy(np.stack([np.asarray(t.b_bits, np.uint16) for t in tensors]).view(np.int16)).to(device)
+        return cls(codes, scales, biases, len(tensors), rows, cols)
+
+    def desc(self) -> CInt4Experts:
+        torch = _torch()
+        _need(self.codes, torch.uint8, "expert codes", self.count * self.rows * self.cols // 2)
+        _need(self.scales, torch.int16, "expert scales", self.count * self.rows * self.cols // 64)
+        _need(self.biases, torch.int16, "expert biases", self.count * self.rows * self.cols // 64)
+        first = CInt4(self.codes.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
+                      self.rows, self.cols, 64)
+        return CInt4Experts(first, self.rows * self.cols // 2, 2 * self.rows * (self.cols // 64), self.count)
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+# --------------------------------------------------------------------------- entry points
+
+def dequant_gemv(w: Int4Weight, x, y=None, out_dtype=None, argmax=False, stream=None):
+    """y[m, n] = sum_k W[n, k] x[m, k]; x fp16 [K] or [m, K] (m <= 16). Returns y (and argmax int32 [m])."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float16
+    x2 = x.reshape(-1, w.cols)
+    m = x2.shape[0]
+    _need(x2, torch.float16, "x")
+    if y is None:
+        y = torch.empty((m, w.rows), dtype=out_dtype, device=x.device)
+    _need(y, out_dtype, "y", m * w.rows)
+    am = torch.empty(m, dtype=torch.int32, device=x.device) if argmax else None
+    ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device) if argmax else None
+    d = w.desc()
+    _check(lib().decodehp_dequant_gemv(ctypes.byref(d), x2.data_ptr(), m, y.data_ptr(),
+                                       DHP_F32 if out_dtype == torch.float32 else DHP_F16,
+                                       _ptr(am), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    yv = y.reshape(x.shape[:-1] + (w.rows,)) if x.dim() == 1 else y
+    return (yv, am) if argmax else yv
+
+
+def dequant_gemm_batched(w: Int4Weight, x, y=None, stream=None):
+    """Y = X W^T for X fp16 [m, K] (m <= 128); Y fp16 [m, N]."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, w.rows), dtype=torch.float16, device=x.device)
+    _need(y, torch.float16, "y", m * w.rows)
+    d = w.desc()
+    _check(lib().decodehp_dequant_gemm_batched(ctypes.byref(d), x.data_ptr(), m, y.data_ptr(), _stream(stream)))
+    return y
+
+
+def moe_decode(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, down: Int4Experts,
+               shared_gate: Int4Weight, shared_up: Int4Weight, shared_down: Int4Weight, top_k: int,
+               fp16_boundary=False, out=None, ids=None, weights=None, stream=None):
+    """One token through the routed MoE layer. router bf16 (int16 bits) or fp32 [E, hidden].
+
+    Returns (out fp16 [hidden], ids int32 [top_k], weights fp32 [top_k]).
+    """
+    torch = _torch()
+    hidden = gate.cols
+    _need(x, torch.float16, "x", hidden)
+    if router.dtype == torch.int16:
+        rdt = DHP_BF16
+    elif router.dtype == torch.float32:
+        rdt = DHP_F32
+    else:
+        raise TypeError("router: int16 (bf16 bits) or float32")
+    _need(router, router.dtype, "router", gate.count * hidden)
+    _need(shared_gate_row, torch.int16, "shared_gate_row", hidden)
+    dev = x.device
+    out = torch.empty(hidden, dtype=torch.float16, device=dev) if out is None else out
+    ids = torch.empty(top_k, dtype=torch.int32, device=dev) if ids is None else ids
+    weights = torch.empty(top_k, dtype=torch.float32, device=dev) if weights is None else weights
+    _need(out, torch.float16, "out", hidden)
+    _need(ids, torch.int32, "ids", top_k)
+    _need(weights, torch.float32, "weights", top_k)
+    ws = _workspace(workspace_bytes(DHP_OP_MOE_DECODE, gate.count, top_k, gate.rows), dev)
+    g, u, d = gate.desc(), up.desc(), down.desc()
+    sg, su, sd = shared_gate.desc(), shared_up.desc(), shared_down.desc()
+    _check(lib().decodehp_moe_decode(x.data_ptr(), router.data_ptr(), rdt, shared_gate_row.data_ptr(),
+                                     ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(sg),
+                                     ctypes.byref(su), ctypes.byref(sd), top_k,
+                                     DHP_MOE_FP16_BOUNDARY if fp16_boundary else 0, out.data_ptr(),
+                                     ids.data_ptr(), weights.data_ptr(), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream)))
+    return out, ids, weights
+
+
+def hc_read(raw, hc_norm, C: int, H: int, down: Int4Weight, up: Int4Weight, inject: Optional[Int4Weight],
+            eps: float = 1e-6, mixed=None, inject_w=None, stream=None):
+    """One hyper-connection read. raw fp16 [C*H]; hc_norm bf16 bits (int16) [C*H].
+
+    Returns (mixed fp16 [H], inject_w fp32 [C] or None).
+    """
+    torch = _torch()
+    _need(raw, torch.float16, "raw", C * H)
+    _need(hc_norm, torch.int16, "hc_norm", C * H)
+    dev = raw.device
+    mixed = torch.empty(H, dtype=torch.float16, device=dev) if mixed is None else mixed
+    _need(mixed, torch.float16, "mixed", H)
+    if inject is not None and inject_w is None:
+        inject_w = torch.empty(C, dtype=torch.float32, device=dev)
+    if inject_w is not None:
+        _need(inject_w, torch.float32, "inject_w", C)
+    ws = _workspace(workspace_bytes(DHP_OP_HC_READ, C, down.rows), dev)
+    dd, ud = down.desc(), up.desc()
+    idesc = inject.desc() if inject is not None else None
+    _check(lib().decodehp_hc_read(raw.data_ptr(), hc_norm.data_ptr(), C, H, eps, ctypes.byref(dd),
+                                  ctypes.byref(ud), ctypes.byref(idesc) if idesc is not None else None,
+                                  mixed.data_ptr(), _ptr(inject_w), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream)))
+    return mixed, (inject_w if inject is not None else None)
+
+
+def hc_inject(wide, out, inject_w, C: int, H: int, stream=None):
+    """wide[c*H + h] += out[h] * inject_w[c] in place (fp16 storage, fp32 math); returns wide."""
+    torch = _torch()
+    _need(wide, torch.float16, "wide", C * H)
+    _need(out, torch.float16, "out", H)
+    _need(inject_w, torch.float32, "inject_w", C)
+    _check(lib().decodehp_hc_inject(wide.data_ptr(), out.data_ptr(), inject_w.data_ptr(), C, H, _stream(stream)))
+    return wide

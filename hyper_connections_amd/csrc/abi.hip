@@ -1,0 +1,189 @@
+// libdecodehp C ABI: argument validation, error reporting and dispatch to the kernel
+// launchers. Every check here runs on the host before any HIP call, so a rejected call
+// never touches the device.
+#include "dhp_internal.hpp"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_dev_mu;
+DeviceFacts g_dev[MAX_DEVICES];
+int g_dev_state[MAX_DEVICES];  // 0 unknown, 1 ok, -1 unusable
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape and pointer checks for one INT4 tensor; `name` goes into the message.
+int check_int4(const dhp_int4* w, const char* name) {
+    if (!w) return dhp_fail(DHP_ERR_INVALID, "%s: null descriptor", name);
+    if (!w->codes || !w->scales || !w->biases)
+        return dhp_fail(DHP_ERR_INVALID, "%s: null codes/scales/biases", name);
+    if (w->rows <= 0 || w->cols <= 0)
+        return dhp_fail(DHP_ERR_INVALID, "%s: non-positive shape %d x %d", name, w->rows, w->cols);
+    if (w->group != 64) return dhp_fail(DHP_ERR_UNSUPPORTED, "%s: group %d (only 64)", name, w->group);
+    if (w->cols % 64) return dhp_fail(DHP_ERR_UNSUPPORTED, "%s: cols %d not a multiple of 64", name, w->cols);
+    if (!aligned(w->codes, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "%s: codes not 16-byte aligned", name);
+    if (!aligned(w->scales, 2) || !aligned(w->biases, 2))
+        return dhp_fail(DHP_ERR_MISALIGNED, "%s: scales/biases not 2-byte aligned", name);
+    return DHP_OK;
+}
+
+int check_experts(const dhp_int4_experts* e, const char* name) {
+    if (!e) return dhp_fail(DHP_ERR_INVALID, "%s: null descriptor", name);
+    int rc = check_int4(&e->first, name);
+    if (rc) return rc;
+    if (e->count <= 0) return dhp_fail(DHP_ERR_INVALID, "%s: count %d", name, e->count);
+    if (e->codes_stride < 0 || e->scales_stride < 0)
+        return dhp_fail(DHP_ERR_INVALID, "%s: negative stride", name);
+    if (e->codes_stride % 16) return dhp_fail(DHP_ERR_MISALIGNED, "%s: codes stride %% 16", name);
+    if (e->scales_stride % 2) return dhp_fail(DHP_ERR_MISALIGNED, "%s: scales stride %% 2", name);
+    return DHP_OK;
+}
+
+}  // namespace
+
+int dhp_fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool dhp_current_device(DeviceFacts* out) {
+    int dev = -1;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        dhp_fail(DHP_ERR_NO_DEVICE, "no HIP device");
+        return false;
+    }
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+        (void)hipGetLastError();
+        dhp_fail(DHP_ERR_NO_DEVICE, "no current HIP device");
+        return false;
+    }
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_state[dev] == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            g_dev_state[dev] = -1;
+        } else if (strncmp(p.gcnArchName, "gfx950", 6) != 0) {
+            g_dev_state[dev] = -1;
+        } else {
+            g_dev[dev].device = dev;
+            g_dev[dev].cus = p.multiProcessorCount;
+            g_dev_state[dev] = 1;
+        }
+    }
+    if (g_dev_state[dev] != 1) {
+        dhp_fail(DHP_ERR_NO_DEVICE, "device %d is not a gfx950 GPU", dev);
+        return false;
+    }
+    *out = g_dev[dev];
+    return true;
+}
+
+size_t dhp_gemv_argmax_ws(int32_t n_rows, int32_t m);
+size_t dhp_moe_ws(int32_t n_experts, int32_t top_k, int32_t inter);
+size_t dhp_hc_ws(int32_t C, int32_t R);
+
+extern "C" {
+
+const char* decodehp_last_error(void) { return g_err; }
+
+int32_t decodehp_version(void) { return (0 << 16) | 1; }
+
+size_t decodehp_workspace_bytes(int32_t op, int32_t a, int32_t b, int32_t c) {
+    switch (op) {
+        case DHP_OP_GEMV_ARGMAX: return (a > 0 && b > 0) ? dhp_gemv_argmax_ws(a, b) : 0;
+        case DHP_OP_MOE_DECODE: return (a > 0 && b > 0 && c > 0) ? dhp_moe_ws(a, b, c) : 0;
+        case DHP_OP_HC_READ: return (a > 0 && b > 0) ? dhp_hc_ws(a, b) : 0;
+        default: return 0;
+    }
+}
+
+int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, int32_t y_dtype,
+                          int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_int4(w, "w");
+    if (rc) return rc;
+    if (!x || !y) return dhp_fail(DHP_ERR_INVALID, "null x or y");
+    if (m < 1 || m > DHP_GEMV_MAX_M) return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d outside 1..%d", m, DHP_GEMV_MAX_M);
+    if (y_dtype != DHP_F16 && y_dtype != DHP_F32) return dhp_fail(DHP_ERR_UNSUPPORTED, "y_dtype %d", y_dtype);
+    if (w->cols > 16384) return dhp_fail(DHP_ERR_UNSUPPORTED, "K=%d above 16384", w->cols);
+    if (!aligned(x, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "x not 16-byte aligned");
+    if (!aligned(y, y_dtype == DHP_F32 ? 4 : 2)) return dhp_fail(DHP_ERR_MISALIGNED, "y misaligned");
+    if (argmax) {
+        if (!aligned(argmax, 4)) return dhp_fail(DHP_ERR_MISALIGNED, "argmax misaligned");
+        const size_t need = dhp_gemv_argmax_ws(w->rows, m);
+        if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+        if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    }
+    if (m != 1) return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d: the multi-row arm is not built yet", m);
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_gemv_m1(w, x, y, y_dtype == DHP_F32, argmax, ws, static_cast<hipStream_t>(stream), dev);
+}
+
+int decodehp_dequant_gemm_batched(const dhp_int4* w, const void* x, int32_t m, void* y, void* stream) {
+    g_err[0] = 0;
+    int rc = check_int4(w, "w");
+    if (rc) return rc;
+    if (!x || !y) return dhp_fail(DHP_ERR_INVALID, "null x or y");
+    if (m < 1 || m > DHP_GEMM_MAX_M) return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d outside 1..%d", m, DHP_GEMM_MAX_M);
+    if (w->rows % 16) return dhp_fail(DHP_ERR_UNSUPPORTED, "N=%d not a multiple of 16", w->rows);
+    if (w->cols > 32768) return dhp_fail(DHP_ERR_UNSUPPORTED, "K=%d above 32768", w->cols);
+    if (!aligned(x, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "x not 16-byte aligned");
+    if (!aligned(y, 2)) return dhp_fail(DHP_ERR_MISALIGNED, "y misaligned");
+    (void)stream;
+    return dhp_fail(DHP_ERR_UNSUPPORTED, "batched arm not built yet");
+}
+
+int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
+                        const void* shared_gate_row, const dhp_int4_experts* gate,
+                        const dhp_int4_experts* up, const dhp_int4_experts* down,
+                        const dhp_int4* shared_gate, const dhp_int4* shared_up,
+                        const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
+                        int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    (void)x; (void)router; (void)router_dtype; (void)shared_gate_row; (void)gate; (void)up;
+    (void)down; (void)shared_gate; (void)shared_up; (void)shared_down; (void)top_k; (void)flags;
+    (void)out; (void)ids; (void)weights; (void)ws; (void)ws_bytes; (void)stream;
+    return dhp_fail(DHP_ERR_UNSUPPORTED, "moe_decode not built yet");
+}
+
+int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H, float eps,
+                     const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject,
+                     void* mixed, float* inject_w, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    (void)raw; (void)hc_norm; (void)C; (void)H; (void)eps; (void)down; (void)up; (void)inject;
+    (void)mixed; (void)inject_w; (void)ws; (void)ws_bytes; (void)stream;
+    return dhp_fail(DHP_ERR_UNSUPPORTED, "hc_read not built yet");
+}
+
+int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32_t C, int32_t H,
+                       void* stream) {
+    g_err[0] = 0;
+    (void)wide; (void)out; (void)inject_w; (void)C; (void)H; (void)stream;
+    return dhp_fail(DHP_ERR_UNSUPPORTED, "hc_inject not built yet");
+}
+
+}  // extern "C"
+
+size_t dhp_moe_ws(int32_t n_experts, int32_t top_k, int32_t inter) {
+    (void)n_experts; (void)top_k; (void)inter;
+    return 0;
+}
+size_t dhp_hc_ws(int32_t C, int32_t R) {
+    (void)C; (void)R;
+    return 0;
+}

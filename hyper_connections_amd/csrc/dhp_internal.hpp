@@ -1,0 +1,145 @@
+// Internal declarations of libdecodehp: device helpers shared by the kernels, the
+// per-device launch facts, and the launchers each kernel file exports to abi.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "decodehp.h"
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define DHP_DEV __device__ __forceinline__
+
+// ------------------------------------------------------------------ bit helpers
+
+DHP_DEV h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+DHP_DEV uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+DHP_DEV float bf16_to_f32(uint32_t b16) { return __builtin_bit_cast(float, b16 << 16); }
+DHP_DEV float f16_to_f32(_Float16 h) { return (float)h; }
+
+// Eight INT4 codes k0..k7 of one 32-bit word (byte j holds k=2j low, k=2j+1 high) become
+// four exact fp16 pairs in the order (k0,k4) (k1,k5) (k2,k6) (k3,k7).
+//
+// A nibble OR-ed into the mantissa of fp16 1024.0 (0x6400, ulp 1) gives 1024 + q exactly;
+// a nibble sitting four bits higher gives 1024 + 16 q, and (1024 + 16 q) / 16 - 64 = q.
+// Both halves of a 32-bit word are handled at once, so one AND-OR makes two codes.
+DHP_DEV void unpack8(uint32_t w, h2 q[4]) {
+    const uint32_t MAGIC = 0x64006400u;
+    const uint32_t w8 = w >> 8;
+    const h2 c1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const h2 c64 = {(_Float16)64.0f, (_Float16)64.0f};
+    const h2 c16th = {(_Float16)0.0625f, (_Float16)0.0625f};
+    q[0] = as_h2((w & 0x000F000Fu) | MAGIC) - c1024;
+    q[1] = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | MAGIC), c16th, -c64);
+    q[2] = as_h2((w8 & 0x000F000Fu) | MAGIC) - c1024;
+    q[3] = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | MAGIC), c16th, -c64);
+}
+
+// Eight consecutive fp16 activations (as four 32-bit words, x0x1 x2x3 x4x5 x6x7) rearranged
+// into the pair order unpack8 produces: (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+DHP_DEV void permute8(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, h2 out[4]) {
+    out[0] = as_h2((d0 & 0xFFFFu) | (d2 << 16));
+    out[1] = as_h2((d0 >> 16) | (d2 & 0xFFFF0000u));
+    out[2] = as_h2((d1 & 0xFFFFu) | (d3 << 16));
+    out[3] = as_h2((d1 >> 16) | (d3 & 0xFFFF0000u));
+}
+
+// sum over 32 codes of q * x, fp32 accumulate: c holds 32 codes (16 bytes), xp the 16
+// permuted activation pairs for the same 32 positions.
+DHP_DEV float dot32_f16(const u32x4 c, const h2* xp) {
+    float d = 0.0f;
+    h2 q[4];
+    unpack8(c.x, q);
+    d = __builtin_amdgcn_fdot2(q[0], xp[0], d, false);
+    d = __builtin_amdgcn_fdot2(q[1], xp[1], d, false);
+    d = __builtin_amdgcn_fdot2(q[2], xp[2], d, false);
+    d = __builtin_amdgcn_fdot2(q[3], xp[3], d, false);
+    unpack8(c.y, q);
+    d = __builtin_amdgcn_fdot2(q[0], xp[4], d, false);
+    d = __builtin_amdgcn_fdot2(q[1], xp[5], d, false);
+    d = __builtin_amdgcn_fdot2(q[2], xp[6], d, false);
+    d = __builtin_amdgcn_fdot2(q[3], xp[7], d, false);
+    unpack8(c.z, q);
+    d = __builtin_amdgcn_fdot2(q[0], xp[8], d, false);
+    d = __builtin_amdgcn_fdot2(q[1], xp[9], d, false);
+    d = __builtin_amdgcn_fdot2(q[2], xp[10], d, false);
+    d = __builtin_amdgcn_fdot2(q[3], xp[11], d, false);
+    unpack8(c.w, q);
+    d = __builtin_amdgcn_fdot2(q[0], xp[12], d, false);
+    d = __builtin_amdgcn_fdot2(q[1], xp[13], d, false);
+    d = __builtin_amdgcn_fdot2(q[2], xp[14], d, false);
+    d = __builtin_amdgcn_fdot2(q[3], xp[15], d, false);
+    return d;
+}
+
+// Load 32 fp16 activations starting at p (16-byte aligned) into 16 permuted pairs and
+// return their fp32 sum (the factor multiplying the group bias).
+DHP_DEV float load_x32(const _Float16* p, h2* xp) {
+    const u32x4* v = reinterpret_cast<const u32x4*>(p);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 u = v[i];
+        permute8(u.x, u.y, u.z, u.w, xp + 4 * i);
+        h2 a = as_h2(u.x), b = as_h2(u.y), c = as_h2(u.z), d = as_h2(u.w);
+        s += ((float)a.x + (float)a.y) + ((float)b.x + (float)b.y) + ((float)c.x + (float)c.y) +
+             ((float)d.x + (float)d.y);
+    }
+    return s;
+}
+
+// sum over 32 codes of q * x for fp32 activations x[0..31] (contiguous k order).
+DHP_DEV float dot32_f32(const u32x4 c, const float* x) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = w[i] & 0x0F0F0F0Fu;          // k = 8i + 0, 2, 4, 6
+        const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;   // k = 8i + 1, 3, 5, 7
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            d = __builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), x[8 * i + 2 * b], d);
+            d = __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), x[8 * i + 2 * b + 1], d);
+        }
+    }
+    return d;
+}
+
+// Sum across `width` consecutive lanes (width a power of two <= 64); every lane of the
+// group receives the same total, summed in the same tree order for every group.
+template <int WIDTH>
+DHP_DEV float group_sum(float v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+DHP_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+DHP_DEV float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Argmax order: larger value first, lower index first among equal values.
+DHP_DEV bool better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+// ------------------------------------------------------------------ host side
+
+struct DeviceFacts {
+    int device;
+    int cus;
+};
+
+// Facts about the current device, cached per device. Returns false (and sets the error)
+// when there is no usable gfx950 device.
+bool dhp_current_device(DeviceFacts* out);
+int dhp_fail(int code, const char* fmt, ...);
+int dhp_launch_status(const char* what);
+
+// Launchers (validation already done by abi.hip).
+int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t* argmax,
+                   void* ws, hipStream_t s, const DeviceFacts& dev);

@@ -1,0 +1,199 @@
+/*
+ * decodehp.h -- C ABI of libdecodehp, the MI355X (gfx950) decode hot path:
+ * INT4-affine dequantizing GEMV / GEMM, routed-MoE decode, hyper-connection read/inject.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument that names tensor data is a DEVICE pointer (HIP device
+ *    memory, or memory the device can address) owned by the caller. The library never
+ *    allocates, frees or retains caller memory; it holds no pointer past the return.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*, NULL for the
+ *    default stream). The library never synchronizes. Results are valid once the caller
+ *    has synchronized with `stream`.
+ *  - Arguments are validated on the host before any HIP call. A nonzero return means
+ *    nothing was launched, except DHP_ERR_LAUNCH, which reports that the HIP runtime
+ *    rejected a launch; decodehp_last_error() then holds a message for this thread.
+ *  - Calls that overlap on one device share nothing but their arguments: two calls are
+ *    independent unless the caller passes them the same output or workspace buffer.
+ *  - Deterministic: no floating-point atomics; the same inputs give the same bits.
+ *
+ * INT4-affine weights (struct dhp_int4)
+ * -------------------------------------
+ * "src/real_forward.rs" (turbospark-runtime 0.3.0), module doc, memory model: every
+ * projection binds the weights, scales and biases of an INT4-affine tensor in place, with
+ * nothing staged per dispatch. Element (n, k) of a [rows x cols] tensor is
+ *     W[n, k] = q[n, k] * scale[n, k / 64] + bias[n, k / 64],    q in 0..15,
+ * with one bf16 scale and one bf16 bias per group of 64 consecutive k.
+ *   codes : uint8 [rows][cols/2], row-major; byte j of a row holds k = 2j in bits 0..3
+ *           and k = 2j+1 in bits 4..7. 16-byte aligned.
+ *   scales: bf16 (uint16 bit patterns) [rows][cols/64], row-major. 2-byte aligned.
+ *   biases: bf16 [rows][cols/64], row-major. 2-byte aligned.
+ *   cols % 64 == 0, group == 64.
+ */
+#ifndef DECODEHP_H
+#define DECODEHP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define DHP_OK 0
+#define DHP_ERR_INVALID (-1)     /* null pointer, non-positive or inconsistent size */
+#define DHP_ERR_UNSUPPORTED (-2) /* a shape or option outside what the kernels cover */
+#define DHP_ERR_MISALIGNED (-3)  /* a pointer below its required alignment */
+#define DHP_ERR_WORKSPACE (-4)   /* workspace missing or smaller than decodehp_workspace_bytes */
+#define DHP_ERR_NO_DEVICE (-5)   /* no HIP device, or the current device is not gfx950 */
+#define DHP_ERR_LAUNCH (-6)      /* the HIP runtime rejected a launch */
+
+/* Element types. */
+#define DHP_F16 0
+#define DHP_F32 1
+#define DHP_BF16 2
+
+/* Workspace queries (decodehp_workspace_bytes `op`). */
+#define DHP_OP_GEMV_ARGMAX 1 /* a = rows (N), b = m                       */
+#define DHP_OP_MOE_DECODE 2  /* a = n_experts, b = top_k, c = inter (rows of gate) */
+#define DHP_OP_HC_READ 3     /* a = C, b = R (low rank)                  */
+
+/* moe_decode flags. */
+#define DHP_MOE_FP16_BOUNDARY 1 /* round routed sum and gated shared output to fp16 before the add */
+
+/* Limits. */
+#define DHP_GEMV_MAX_M 16
+#define DHP_GEMM_MAX_M 128
+#define DHP_MOE_MAX_TOP_K 8
+#define DHP_HC_MAX_C 16
+
+typedef struct dhp_int4 {
+    const void* codes;  /* uint8 [rows][cols/2], 16-byte aligned */
+    const void* scales; /* bf16  [rows][cols/64] */
+    const void* biases; /* bf16  [rows][cols/64] */
+    int32_t rows;
+    int32_t cols;
+    int32_t group; /* must be 64 */
+} dhp_int4;
+
+/* A stack of same-shaped INT4 tensors (one per expert): expert e's codes start at
+ * first.codes + e * codes_stride bytes, its scales and biases at first.scales /
+ * first.biases + e * scales_stride bytes. The analog of the pages' per-layer expert
+ * offset table ("src/real_forward.rs", fields around the routed blob layout). */
+typedef struct dhp_int4_experts {
+    dhp_int4 first;
+    int64_t codes_stride;  /* bytes, multiple of 16 */
+    int64_t scales_stride; /* bytes, multiple of 2 */
+    int32_t count;
+} dhp_int4_experts;
+
+/*
+ * decodehp_dequant_gemv -- Y[r, n] = sum_k W[n, k] * X[r, k] for r < m (m <= 16).
+ * "src/real_forward.rs": module doc (dequant_int4_gemv_simd against resident INT4-affine
+ * weights) and field batched_gemv_prefill (the multi-row GEMM gives the same outputs as
+ * m separate GEMVs). The LM head of "src/families/qwen4/mod.rs" (decoder-layer
+ * pseudocode, exit) is this call over the vocabulary, with argmax.
+ *   w       : weight [N x K].
+ *   x       : fp16 [m][K], row-major, 16-byte aligned.
+ *   y       : [m][N] row-major, fp16 (y_dtype DHP_F16) or fp32 (DHP_F32); fp32 accumulate.
+ *   argmax  : nullable int32 [m]; when set, argmax[r] = lowest n with the largest fp32 value
+ *             of row r (computed before any fp16 rounding of y).
+ *   ws      : workspace of decodehp_workspace_bytes(DHP_OP_GEMV_ARGMAX, N, m, 0) bytes when
+ *             argmax is set (may be NULL otherwise). Scratch only; contents undefined after.
+ * Errors: -1 null/size, -2 K % 64, K > 16384, group != 64, m outside 1..16, y_dtype, -3 alignment,
+ *         -4 workspace, -5 device, -6 launch.
+ */
+int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, int32_t y_dtype,
+                          int32_t* argmax, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * decodehp_dequant_gemm_batched -- Y = X W^T for a chunked-prefill block of m <= 128 rows.
+ * "src/real_forward.rs", field batched_gemv_prefill: resident GEMVs run as one M-row GEMM;
+ * the same field and prefill_steel give the 64-row micro-batched form this replaces.
+ * Matrix cores (fp16 operands, fp32 accumulate): each weight is dequantized once into an
+ * fp16 operand, q*s+b rounded to fp16 (exact when the bias is -8*scale and the scale is
+ * a bf16 value in fp16's normal range).
+ *   w : weight [N x K], N % 16 == 0.   x : fp16 [m][K], 16-byte aligned.   y : fp16 [m][N].
+ * Errors: -1, -2 (K % 64, N % 16, m outside 1..128, K > 32768), -3, -5, -6.
+ */
+int decodehp_dequant_gemm_batched(const dhp_int4* w, const void* x, int32_t m, void* y,
+                                  void* stream);
+
+/*
+ * decodehp_moe_decode -- one token through a routed MoE layer with a gated shared expert.
+ * "src/families/qwen4/mod.rs", section MoE: top-k on the raw router logits, softmax over
+ * the selected set only. "src/families/qwen/state.rs", struct RealQwenState: fp32 router
+ * logits, unit router and per-expert scales, the shared expert gated by a scalar logit
+ * through a sigmoid. "src/real_forward.rs", module doc: phase 1 = gate/up GEMV and the
+ * gated-FFN activation silu(gate)*up, phase 2 = down GEMV and the weighted k-way reduce.
+ *     logits = router @ x (fp32); ids = the top_k largest, largest first, lowest expert
+ *     index first among equal fp32 logits; weights = softmax over those logits;
+ *     out = fp16( sum_j weights[j] * down_ids[j](act_ids[j]) + sigmoid(g) * down_s(act_s) ),
+ *     act_e = silu(gate_e x) * (up_e x) kept in fp32, g = shared_gate_row . x.
+ * With DHP_MOE_FP16_BOUNDARY the routed sum and the gated shared output are each rounded
+ * to fp16 before the add ("src/families/qwen4/mod.rs", section MoE, the fp16 boundary).
+ *   x               : fp16 [hidden], 16-byte aligned.
+ *   router          : [n_experts][hidden], bf16 (router_dtype DHP_BF16) or fp32 (DHP_F32),
+ *                     16-byte aligned rows.
+ *   shared_gate_row : bf16 [hidden], 16-byte aligned.
+ *   gate, up        : experts [inter x hidden];  down : experts [hidden x inter]; same count.
+ *   shared_*        : one expert of the same shapes.
+ *   top_k           : 1..8, <= n_experts.
+ *   out             : fp16 [hidden].  ids : int32 [top_k].  weights : fp32 [top_k].
+ *   ws              : decodehp_workspace_bytes(DHP_OP_MOE_DECODE, n_experts, top_k, inter).
+ * Errors: -1, -2 (hidden or inter % 64, hidden > 8192, inter > 4096, top_k, n_experts > 1024,
+ *         router_dtype, flags), -3, -4, -5, -6.
+ */
+int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
+                        const void* shared_gate_row, const dhp_int4_experts* gate,
+                        const dhp_int4_experts* up, const dhp_int4_experts* down,
+                        const dhp_int4* shared_gate, const dhp_int4* shared_up,
+                        const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
+                        int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * decodehp_hc_read -- one hyper-connection read (attn_hc / mlp_hc / the final mixer).
+ * "src/families/qwen4/mod.rs", section Hyper-connections, and "src/families/qwen4/hc.rs",
+ * encode_hyper_connection: with the residual `raw` viewed as C streams of width H,
+ *     normed    = raw / sqrt(mean over each stream of raw^2 + eps) * hc_norm  (direct scale)
+ *     lo        = silu(down(normed) / C)
+ *     mixed     = mean over streams of sigmoid(up(lo)) * normed                -> fp16 [H]
+ *     inject_w  = 2 * sigmoid(inject(normed) / C)                              -> fp32 [C]
+ * `raw` is read and never written (hc.rs doc); the caller injects separately.
+ *   raw     : fp16 [C*H], 16-byte aligned.   hc_norm : bf16 [C*H], 16-byte aligned.
+ *   down    : [R x C*H].   up : [C*H x R].   inject : [C x C*H] or NULL (final mixer).
+ *   mixed   : fp16 [H].    inject_w : fp32 [C], NULL exactly when inject is NULL.
+ *   ws      : decodehp_workspace_bytes(DHP_OP_HC_READ, C, R, 0) bytes.
+ * Errors: -1, -2 (C not a power of two in 1..16, H % 64, R % 64, C*H > 32768, R > 1024),
+ *         -3, -4, -5, -6.
+ */
+int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H, float eps,
+                     const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject,
+                     void* mixed, float* inject_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * decodehp_hc_inject -- wide[c*H + h] = fp16(wide[c*H + h] + out[h] * inject_w[c]), in place.
+ * "src/families/qwen4/mod.rs", the decoder-layer pseudocode and THE INJECTION TRAP: the
+ * sublayer output is added, scaled per stream, to the UN-normalized residual `raw`.
+ *   wide : fp16 [C*H] (raw in, hidden out), 16-byte aligned.   out : fp16 [H], 16-byte aligned.
+ *   inject_w : fp32 [C].
+ * Errors: -1, -2 (C outside 1..16, H % 8), -3, -5, -6.
+ */
+int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32_t C, int32_t H,
+                       void* stream);
+
+/* Workspace bytes an entry point needs (0 when none). Pure host arithmetic. */
+size_t decodehp_workspace_bytes(int32_t op, int32_t a, int32_t b, int32_t c);
+
+/* Message for the last nonzero return on this thread ("" if none). */
+const char* decodehp_last_error(void);
+
+/* Library ABI version, (major << 16) | minor. */
+int32_t decodehp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODEHP_H */

@@ -1,0 +1,104 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and rejects
+bad arguments with the documented codes before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hyper_connections_amd as hca
+from helpers import gpu_present
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decodehp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hca.LIB_PATH), reason="libdecodehp.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(decodehp_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
+              "decodehp_hc_read", "decodehp_hc_inject", "decodehp_workspace_bytes", "decodehp_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(hca.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version():
+    assert hca.lib().decodehp_version() >= 1
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def int4(codes=FAKE, scales=FAKE, biases=FAKE, rows=16, cols=128, group=64):
+    return hca.CInt4(codes, scales, biases, rows, cols, group)
+
+
+def gemv(w, x=FAKE, m=1, y=FAKE, dt=0, am=None, ws=None, wsb=0):
+    L = hca.lib()
+    return L.decodehp_dequant_gemv(ctypes.byref(w) if w is not None else None, x, m, y, dt, am, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(codes=0), -1), (dict(scales=0), -1), (dict(rows=0), -1), (dict(cols=-64), -1),
+    (dict(cols=96), -2), (dict(group=32), -2), (dict(cols=16448), -2),
+    (dict(codes=FAKE + 8), -3), (dict(scales=FAKE + 1), -3),
+])
+def test_gemv_rejects_bad_weights(kw, code):
+    assert gemv(int4(**kw)) == code
+    assert hca.lib().decodehp_last_error().decode()
+
+
+def test_gemv_rejects_bad_calls():
+    assert gemv(None) == -1
+    assert gemv(int4(), x=0) == -1
+    assert gemv(int4(), m=0) == -2
+    assert gemv(int4(), m=17) == -2
+    assert gemv(int4(), dt=2) == -2
+    assert gemv(int4(), x=FAKE + 2) == -3
+    assert gemv(int4(), y=FAKE + 1) == -3
+    assert gemv(int4(), am=FAKE, ws=None) == -4
+    need = hca.workspace_bytes(hca.DHP_OP_GEMV_ARGMAX, 16, 1)
+    assert need > 0
+    assert gemv(int4(), am=FAKE, ws=FAKE, wsb=need - 1) == -4
+
+
+def test_gemm_batched_rejects_bad_calls():
+    L = hca.lib()
+    f = lambda w, m=128, x=FAKE, y=FAKE: L.decodehp_dequant_gemm_batched(ctypes.byref(w), x, m, y, None)
+    assert f(int4(), m=0) == -2
+    assert f(int4(), m=129) == -2
+    assert f(int4(rows=24)) == -2
+    assert f(int4(), x=FAKE + 4) == -3
+    assert f(int4(cols=100)) == -2
+
+
+def test_error_message_is_per_call():
+    assert gemv(int4(group=32)) == -2
+    assert "group" in hca.lib().decodehp_last_error().decode()
+
+
+@pytest.mark.skipif(gpu_present(), reason="a GPU is visible; a valid call would launch")
+def test_valid_call_without_device_reports_no_device():
+    assert gemv(int4()) == -5
+    assert "device" in hca.lib().decodehp_last_error().decode()
+
+
+def test_pack_int4_codes_layout():
+    import numpy as np
+    q = np.array([[1, 2, 3, 4, 15, 0, 7, 8]], np.uint8)
+    p = hca.pack_int4_codes(q)
+    assert p.tolist() == [[0x21, 0x43, 0x0F, 0x87]]
+    with pytest.raises(ValueError):
+        hca.pack_int4_codes(np.array([[16, 0]], np.uint8))

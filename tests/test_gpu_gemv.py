@@ -1,0 +1,111 @@
+"""GPU parity: decodehp_dequant_gemv (M=1) and its argmax against the fp64 oracle.
+
+Bar: |gpu - oracle| <= 1e-3 + 1e-2 |oracle| elementwise for every fp output; argmax
+indices bit-exact (lowest index on ties).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_within_tol, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+hca = pytest.importorskip("hyper_connections_amd")
+
+
+def run_gemv(t, x, out_dtype=None, argmax=False):
+    w = hca.Int4Weight.from_logical(t.q, t.s_bits, t.b_bits)
+    xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    r = hca.dequant_gemv(w, xd, out_dtype=out_dtype or torch.float16, argmax=argmax)
+    torch.cuda.synchronize()
+    return r
+
+
+def test_gemv_workload_2560():
+    say("gemv 2560x2560 seed 0")
+    d = synth.gemv_workload(0)
+    y = run_gemv(d["w"], d["x"])
+    ref = oracle.dequant_gemv(d["w"].q, d["w"].s_bits, d["w"].b_bits, d["x"])
+    assert_within_tol(y.float().cpu().numpy(), ref, "gemv 2560")
+    assert float(np.std(ref)) > 1.0          # the outputs are not trivially small
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (17, 192), (33, 512), (100, 2560), (1000, 4096),
+                                 (37, 640), (5, 10240), (4099, 1024), (257, 3072), (16, 2048), (2, 8192)])
+def test_gemv_shapes_and_ragged_tails(n, k):
+    say(f"gemv n={n} k={k}")
+    rng = np.random.default_rng([99, n, k])
+    t = synth.int4_tensor(rng, n, k)
+    x = synth.normal_f16(rng, (k,))
+    y = run_gemv(t, x, out_dtype=torch.float32)
+    ref = oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, x)
+    assert_within_tol(y.cpu().numpy(), ref, f"gemv {n}x{k}")
+
+
+def test_gemv_fp16_and_fp32_outputs_agree():
+    say("gemv f16 vs f32 outputs")
+    d = synth.gemv_workload(1)
+    y16 = run_gemv(d["w"], d["x"])
+    y32 = run_gemv(d["w"], d["x"], out_dtype=torch.float32)
+    assert torch.equal(y16.cpu(), y32.cpu().half())
+
+
+def test_gemv_deterministic_and_guarded():
+    say("gemv determinism + guard band")
+    d = synth.gemv_workload(2)
+    w = hca.Int4Weight.from_logical(d["w"].q, d["w"].s_bits, d["w"].b_bits)
+    x = torch.from_numpy(d["x"]).cuda()
+    buf = torch.full((2560 + 512,), 1234.5, dtype=torch.float16, device="cuda")
+    y = buf[256:256 + 2560]
+    hca.dequant_gemv(w, x, y=y)
+    first = y.clone()
+    hca.dequant_gemv(w, x, y=y)
+    torch.cuda.synchronize()
+    assert torch.equal(first, y)
+    assert torch.all(buf[:256] == 1234.5) and torch.all(buf[256 + 2560:] == 1234.5)
+
+
+def test_lmhead_m1_full_vocab_with_argmax():
+    say("lm head 151936x2560 M=1 fp32 + argmax")
+    d = synth.lmhead_workload(0, m=1)
+    logits, am = run_gemv(d["w"], d["x"][0], out_dtype=torch.float32, argmax=True)
+    ref = oracle.dequant_gemv(d["w"].q, d["w"].s_bits, d["w"].b_bits, d["x"][0])
+    assert_within_tol(logits.cpu().numpy().reshape(-1), ref, "lm head logits")
+    assert int(am.cpu()[0]) == int(oracle.argmax_lowest(ref))
+    top2 = np.sort(ref)[-2:]
+    print(f"top-1/top-2 gap {top2[1] - top2[0]:.4f}")
+
+
+@pytest.mark.parametrize("where", ["before", "after"])
+def test_argmax_tie_goes_to_lowest_index(where):
+    say(f"argmax tie {where}")
+    rng = np.random.default_rng(77)
+    n, k = 40000, 2560
+    t = synth.int4_tensor(rng, n, k)
+    x = synth.normal_f16(rng, (k,))
+    ref = oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, x)
+    a = int(oracle.argmax_lowest(ref))
+    b = a // 2 if where == "before" else (a + n) // 2
+    for arr in (t.q, t.s_bits, t.b_bits):
+        arr[b] = arr[a]
+    logits, am = run_gemv(t, x, out_dtype=torch.float32, argmax=True)
+    lg = logits.cpu().numpy().reshape(-1)
+    assert lg[a] == lg[b]                         # duplicated rows give the same bits
+    assert int(am.cpu()[0]) == min(a, b)
+
+
+def test_argmax_planted_max_at_ends():
+    say("argmax planted first/last row")
+    rng = np.random.default_rng(78)
+    n, k = 5000, 512
+    t = synth.int4_tensor(rng, n, k)
+    x = np.abs(synth.normal_f16(rng, (k,)))
+    for row in (0, n - 1):
+        t2 = synth.Int4Tensor(t.q.copy(), t.s_bits.copy(), t.b_bits.copy())
+        t2.q[row] = 15                                  # all-max codes with a positive x: the largest row
+        _, am = run_gemv(t2, x, out_dtype=torch.float32, argmax=True)
+        ref = oracle.dequant_gemv(t2.q, t2.s_bits, t2.b_bits, x)
+        assert int(am.cpu()[0]) == int(oracle.argmax_lowest(ref)) == row
