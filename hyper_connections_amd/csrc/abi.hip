@@ -165,25 +165,62 @@ int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H,
                      const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject,
                      void* mixed, float* inject_w, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
-    (void)raw; (void)hc_norm; (void)C; (void)H; (void)eps; (void)down; (void)up; (void)inject;
-    (void)mixed; (void)inject_w; (void)ws; (void)ws_bytes; (void)stream;
-    return dhp_fail(DHP_ERR_UNSUPPORTED, "hc_read not built yet");
+    if (!raw || !hc_norm || !mixed) return dhp_fail(DHP_ERR_INVALID, "null raw, hc_norm or mixed");
+    if (C <= 0 || H <= 0) return dhp_fail(DHP_ERR_INVALID, "C=%d H=%d", C, H);
+    if (C > DHP_HC_MAX_C || (C & (C - 1)))
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "C=%d (a power of two up to %d)", C, DHP_HC_MAX_C);
+    if (H % 64) return dhp_fail(DHP_ERR_UNSUPPORTED, "H=%d not a multiple of 64", H);
+    const long wide = (long)C * H;
+    if (wide % 2048 || wide > 32768)
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "C*H=%ld (a multiple of 2048, at most 32768)", wide);
+    if (!(eps >= 0.0f) || eps > 1.0f) return dhp_fail(DHP_ERR_INVALID, "eps %g", (double)eps);
+    int rc = check_int4(down, "down");
+    if (rc) return rc;
+    rc = check_int4(up, "up");
+    if (rc) return rc;
+    const int R = down->rows;
+    if (down->cols != wide) return dhp_fail(DHP_ERR_INVALID, "down is %d x %d, expected R x %ld", down->rows, down->cols, wide);
+    if (R % 64 || R > 1024) return dhp_fail(DHP_ERR_UNSUPPORTED, "R=%d (a multiple of 64, at most 1024)", R);
+    if (up->rows != wide || up->cols != R)
+        return dhp_fail(DHP_ERR_INVALID, "up is %d x %d, expected %ld x %d", up->rows, up->cols, wide, R);
+    if (inject) {
+        rc = check_int4(inject, "inject");
+        if (rc) return rc;
+        if (inject->rows != C || inject->cols != wide)
+            return dhp_fail(DHP_ERR_INVALID, "inject is %d x %d, expected %d x %ld", inject->rows, inject->cols, C, wide);
+        if (!inject_w) return dhp_fail(DHP_ERR_INVALID, "inject given but inject_w is null");
+        if (!aligned(inject_w, 4)) return dhp_fail(DHP_ERR_MISALIGNED, "inject_w misaligned");
+    } else if (inject_w) {
+        return dhp_fail(DHP_ERR_INVALID, "inject_w given without an inject projection");
+    }
+    if (!aligned(raw, 16) || !aligned(hc_norm, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "raw/hc_norm not 16-byte aligned");
+    if (!aligned(mixed, 2)) return dhp_fail(DHP_ERR_MISALIGNED, "mixed misaligned");
+    const size_t need = dhp_hc_ws(C, R);
+    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_hc_read(raw, hc_norm, C, H, eps, down, up, inject, mixed, inject_w, ws,
+                          static_cast<hipStream_t>(stream));
 }
 
 int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32_t C, int32_t H,
                        void* stream) {
     g_err[0] = 0;
-    (void)wide; (void)out; (void)inject_w; (void)C; (void)H; (void)stream;
-    return dhp_fail(DHP_ERR_UNSUPPORTED, "hc_inject not built yet");
+    if (!wide || !out || !inject_w) return dhp_fail(DHP_ERR_INVALID, "null wide, out or inject_w");
+    if (C <= 0 || H <= 0) return dhp_fail(DHP_ERR_INVALID, "C=%d H=%d", C, H);
+    if (C > DHP_HC_MAX_C) return dhp_fail(DHP_ERR_UNSUPPORTED, "C=%d above %d", C, DHP_HC_MAX_C);
+    if (H % 8) return dhp_fail(DHP_ERR_UNSUPPORTED, "H=%d not a multiple of 8", H);
+    if (!aligned(wide, 16) || !aligned(out, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "wide/out not 16-byte aligned");
+    if (!aligned(inject_w, 4)) return dhp_fail(DHP_ERR_MISALIGNED, "inject_w misaligned");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_hc_inject(wide, out, inject_w, C, H, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
 
 size_t dhp_moe_ws(int32_t n_experts, int32_t top_k, int32_t inter) {
     (void)n_experts; (void)top_k; (void)inter;
-    return 0;
-}
-size_t dhp_hc_ws(int32_t C, int32_t R) {
-    (void)C; (void)R;
     return 0;
 }

@@ -143,3 +143,7 @@ int dhp_launch_status(const char* what);
 // Launchers (validation already done by abi.hip).
 int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t* argmax,
                    void* ws, hipStream_t s, const DeviceFacts& dev);
+int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, const dhp_int4* down,
+                   const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w,
+                   void* ws, hipStream_t s);
+int launch_hc_inject(void* wide, const void* out, const float* w, int C, int H, hipStream_t s);

@@ -1,0 +1,243 @@
+// Hyper-connection read (grouped RMS norm, low-rank mix, inject gate) and inject add.
+//
+// "src/families/qwen4/mod.rs" (turbospark-runtime 0.3.0), section Hyper-connections, and
+// "src/families/qwen4/hc.rs", encode_hyper_connection. The pages run one dispatch per
+// step (norm, down GEMV, scale by 1/C, SiLU, up GEMV, sigmoid, mix, inject GEMV, scale,
+// sigmoid, scale by 2). Here the read is two kernels:
+//
+//  k_hc_down : one block per output row of the down projection (R rows) and of the inject
+//              projection (C rows). Every block recomputes the C stream RMS values from the
+//              20 KB residual (an L2 hit after the first block), normalizes its own 32-wide
+//              slice in registers, and reduces one dot product over the whole C*H input:
+//              lane t owns input positions 32t..32t+31, so the block is C*H/32 lanes wide.
+//              The epilogue applies the 1/C, then SiLU (down rows) or 2*sigmoid (inject rows).
+//  k_hc_up   : 16 lanes per output position h: 16/C lanes per stream row c*H+h walk that row's
+//              R/32 code chunks against the low-rank vector staged in LDS, the row sums go
+//              through the sigmoid, multiply the recomputed normed value, and the C products
+//              are averaged.
+//
+// The normalized stream is never written to memory; only lo [R] and the C inverse RMS
+// values pass between the two kernels through the workspace.
+#include "dhp_internal.hpp"
+
+namespace {
+
+constexpr int HC_MAX_THREADS = 1024;
+
+// raw, gamma: the C*H stream; one block per projection row (down rows first, then inject rows).
+__global__ __launch_bounds__(HC_MAX_THREADS) void k_hc_down(
+    const _Float16* __restrict__ raw, const uint16_t* __restrict__ gamma, int C, int H, float eps,
+    const u32x4* __restrict__ dcodes, const uint16_t* __restrict__ dscales,
+    const uint16_t* __restrict__ dbiases, int R, const u32x4* __restrict__ icodes,
+    const uint16_t* __restrict__ iscales, const uint16_t* __restrict__ ibiases,
+    float* __restrict__ lo_out, float* __restrict__ inv_rms_out, float* __restrict__ inject_w) {
+    __shared__ float part[HC_MAX_THREADS];
+    __shared__ float inv_rms[DHP_HC_MAX_C];
+    __shared__ float wsum[HC_MAX_THREADS / 64];
+
+    const int t = threadIdx.x;            // chunk index, input positions 32t .. 32t+31
+    const int CH = (C * H) >> 5;          // == blockDim.x
+    const int G = (C * H) >> 6;
+    const int row = blockIdx.x;
+    const bool is_inject = row >= R;
+    const int r = is_inject ? row - R : row;
+
+    // this block's weight slice first, so it is in flight during the norm
+    const u32x4* codes = is_inject ? icodes : dcodes;
+    const uint16_t* sc = is_inject ? iscales : dscales;
+    const uint16_t* bi = is_inject ? ibiases : dbiases;
+    const u32x4 c = __builtin_nontemporal_load(codes + (size_t)r * CH + t);
+    const float s = bf16_to_f32(sc[(size_t)r * G + (t >> 1)]);
+    const float b = bf16_to_f32(bi[(size_t)r * G + (t >> 1)]);
+
+    // residual slice and its squares
+    float v[32];
+    {
+        const u32x4* rp = reinterpret_cast<const u32x4*>(raw + 32 * t);
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 u = rp[i];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const h2 p = as_h2(w[k]);
+                v[8 * i + 2 * k] = (float)p.x;
+                v[8 * i + 2 * k + 1] = (float)p.y;
+                ss = __builtin_fmaf(v[8 * i + 2 * k], v[8 * i + 2 * k], ss);
+                ss = __builtin_fmaf(v[8 * i + 2 * k + 1], v[8 * i + 2 * k + 1], ss);
+            }
+        }
+        part[t] = ss;
+    }
+    __syncthreads();
+    const int per = H >> 5;               // chunks per stream
+    if (t < C) {
+        float acc = 0.0f;
+        for (int i = 0; i < per; ++i) acc += part[t * per + i];
+        inv_rms[t] = 1.0f / sqrtf(acc / (float)H + eps);
+    }
+    __syncthreads();
+
+    // normalized slice (direct-scale weight), its dot with the codes, and its sum
+    const float ir = inv_rms[t / per];
+    {
+        const u32x4* gp = reinterpret_cast<const u32x4*>(gamma + 32 * t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 u = gp[i];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[8 * i + 2 * k] = v[8 * i + 2 * k] * ir * bf16_to_f32(w[k] & 0xFFFFu);
+                v[8 * i + 2 * k + 1] = v[8 * i + 2 * k + 1] * ir * bf16_to_f32(w[k] >> 16);
+            }
+        }
+    }
+    float xs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xs += v[i];
+    float acc = __builtin_fmaf(s, dot32_f32(c, v), b * xs);
+
+    acc = group_sum<64>(acc);
+    if ((t & 63) == 0) wsum[t >> 6] = acc;
+    __syncthreads();
+    if (t == 0) {
+        float tot = 0.0f;
+        const int nw = (CH + 63) >> 6;
+        for (int w = 0; w < nw; ++w) tot += wsum[w];
+        const float z = tot / (float)C;
+        if (is_inject) inject_w[r] = 2.0f * sigmoid_f(z);
+        else lo_out[r] = silu_f(z);
+        if (row == 0)
+            for (int k = 0; k < C; ++k) inv_rms_out[k] = inv_rms[k];
+    }
+}
+
+// 16 lanes per output h; LPRU = 16 / C lanes per stream row.
+template <int C>
+__global__ __launch_bounds__(256) void k_hc_up(
+    const _Float16* __restrict__ raw, const uint16_t* __restrict__ gamma, int H,
+    const u32x4* __restrict__ ucodes, const uint16_t* __restrict__ uscales,
+    const uint16_t* __restrict__ ubiases, int R, const float* __restrict__ lo,
+    const float* __restrict__ inv_rms, _Float16* __restrict__ mixed) {
+    constexpr int LPRU = 16 / C;
+    extern __shared__ float lds_lo[];     // [R] then chunk sums [R/32]
+    const int CHR = R >> 5;
+    const int G = R >> 6;
+    float* lo_sum = lds_lo + R;
+    for (int i = threadIdx.x; i < R; i += blockDim.x) lds_lo[i] = lo[i];
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < CHR; ch += blockDim.x) {
+        float s = 0.0f;
+        for (int i = 0; i < 32; ++i) s += lds_lo[32 * ch + i];
+        lo_sum[ch] = s;
+    }
+    __syncthreads();
+
+    const int lane16 = threadIdx.x & 15;
+    const int c = lane16 / LPRU;
+    const int sub = lane16 % LPRU;
+    const int h = blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4);
+    if (h >= H) return;                   // whole 16-lane groups leave together
+    const size_t urow = (size_t)c * H + h;
+    const u32x4* cr = ucodes + urow * CHR;
+    const uint16_t* sr = uscales + urow * G;
+    const uint16_t* br = ubiases + urow * G;
+    float acc = 0.0f;
+    for (int ch = sub; ch < CHR; ch += LPRU) {
+        const u32x4 cc = __builtin_nontemporal_load(cr + ch);
+        const float d = dot32_f32(cc, lds_lo + 32 * ch);
+        acc = __builtin_fmaf(bf16_to_f32(sr[ch >> 1]), d, acc);
+        acc = __builtin_fmaf(bf16_to_f32(br[ch >> 1]), lo_sum[ch], acc);
+    }
+    acc = group_sum<LPRU>(acc);
+    const float n = (float)raw[urow] * inv_rms[c] * bf16_to_f32(gamma[urow]);
+    float p = sigmoid_f(acc) * n;
+#pragma unroll
+    for (int o = LPRU; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
+    if (lane16 == 0) mixed[h] = (_Float16)(p / (float)C);
+}
+
+// wide[c*H + h] = fp16(wide + out[h] * w[c]); 8 elements per thread, H % 8 == 0.
+__global__ __launch_bounds__(256) void k_hc_inject(_Float16* __restrict__ wide,
+                                                   const _Float16* __restrict__ out,
+                                                   const float* __restrict__ w, int C, int H) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;   // 8-element chunk
+    if (i >= (C * H) >> 3) return;
+    const int e0 = i << 3;
+    const float g = w[e0 / H];
+    const int h0 = e0 % H;
+    u32x4 a = *reinterpret_cast<const u32x4*>(wide + e0);
+    const u32x4 o = *reinterpret_cast<const u32x4*>(out + h0);
+    uint32_t av[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const h2 x = as_h2(av[k]), y = as_h2(ov[k]);
+        h2 r;
+        r.x = (_Float16)__builtin_fmaf((float)y.x, g, (float)x.x);
+        r.y = (_Float16)__builtin_fmaf((float)y.y, g, (float)x.y);
+        av[k] = h2_bits(r);
+    }
+    a = u32x4{av[0], av[1], av[2], av[3]};
+    *reinterpret_cast<u32x4*>(wide + e0) = a;
+}
+
+}  // namespace
+
+size_t dhp_hc_ws(int32_t C, int32_t R) {
+    (void)C;
+    const size_t b = (size_t)(R + DHP_HC_MAX_C) * sizeof(float);
+    return (b + 255) & ~(size_t)255;
+}
+
+int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, const dhp_int4* down,
+                   const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w,
+                   void* ws, hipStream_t s) {
+    const int R = down->rows;
+    float* lo = static_cast<float*>(ws);
+    float* inv_rms = lo + R;
+    const int rows = R + (inject ? C : 0);
+    const int threads = (C * H) / 32;
+    hipLaunchKernelGGL(k_hc_down, dim3(rows), dim3(threads), 0, s,
+                       static_cast<const _Float16*>(raw), static_cast<const uint16_t*>(gamma), C, H, eps,
+                       static_cast<const u32x4*>(down->codes), static_cast<const uint16_t*>(down->scales),
+                       static_cast<const uint16_t*>(down->biases), R,
+                       inject ? static_cast<const u32x4*>(inject->codes) : nullptr,
+                       inject ? static_cast<const uint16_t*>(inject->scales) : nullptr,
+                       inject ? static_cast<const uint16_t*>(inject->biases) : nullptr, lo, inv_rms,
+                       inject_w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hc_down launch: %s", hipGetErrorString(e));
+
+    const int block = 64;                  // 4 outputs per block
+    const dim3 g((unsigned)((H + 3) / 4));
+    const size_t lds = (size_t)(R + R / 32) * sizeof(float);
+    const auto* rw = static_cast<const _Float16*>(raw);
+    const auto* gm = static_cast<const uint16_t*>(gamma);
+    const auto* uc = static_cast<const u32x4*>(up->codes);
+    const auto* us = static_cast<const uint16_t*>(up->scales);
+    const auto* ub = static_cast<const uint16_t*>(up->biases);
+    auto* mx = static_cast<_Float16*>(mixed);
+    switch (C) {
+        case 1: hipLaunchKernelGGL(k_hc_up<1>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 2: hipLaunchKernelGGL(k_hc_up<2>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 4: hipLaunchKernelGGL(k_hc_up<4>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 8: hipLaunchKernelGGL(k_hc_up<8>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 16: hipLaunchKernelGGL(k_hc_up<16>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        default: return dhp_fail(DHP_ERR_UNSUPPORTED, "C=%d", C);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hc_up launch: %s", hipGetErrorString(e));
+    return DHP_OK;
+}
+
+int launch_hc_inject(void* wide, const void* out, const float* w, int C, int H, hipStream_t s) {
+    const int chunks = (C * H) / 8;
+    hipLaunchKernelGGL(k_hc_inject, dim3((chunks + 255) / 256), dim3(256), 0, s,
+                       static_cast<_Float16*>(wide), static_cast<const _Float16*>(out), w, C, H);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hc_inject launch: %s", hipGetErrorString(e));
+    return DHP_OK;
+}

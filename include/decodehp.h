@@ -165,7 +165,8 @@ int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
  *   down    : [R x C*H].   up : [C*H x R].   inject : [C x C*H] or NULL (final mixer).
  *   mixed   : fp16 [H].    inject_w : fp32 [C], NULL exactly when inject is NULL.
  *   ws      : decodehp_workspace_bytes(DHP_OP_HC_READ, C, R, 0) bytes.
- * Errors: -1, -2 (C not a power of two in 1..16, H % 64, R % 64, C*H > 32768, R > 1024),
+ * Errors: -1, -2 (C not a power of two in 1..16, H % 64, C*H not a multiple of 2048 or
+ *         above 32768, R % 64, R > 1024),
  *         -3, -4, -5, -6.
  */
 int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H, float eps,
