@@ -155,10 +155,44 @@ int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
                         const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
                         int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
-    (void)x; (void)router; (void)router_dtype; (void)shared_gate_row; (void)gate; (void)up;
-    (void)down; (void)shared_gate; (void)shared_up; (void)shared_down; (void)top_k; (void)flags;
-    (void)out; (void)ids; (void)weights; (void)ws; (void)ws_bytes; (void)stream;
-    return dhp_fail(DHP_ERR_UNSUPPORTED, "moe_decode not built yet");
+    if (!x || !router || !shared_gate_row || !out || !ids || !weights)
+        return dhp_fail(DHP_ERR_INVALID, "null x, router, shared_gate_row, out, ids or weights");
+    int rc = check_experts(gate, "gate");
+    if (!rc) rc = check_experts(up, "up");
+    if (!rc) rc = check_experts(down, "down");
+    if (!rc) rc = check_int4(shared_gate, "shared_gate");
+    if (!rc) rc = check_int4(shared_up, "shared_up");
+    if (!rc) rc = check_int4(shared_down, "shared_down");
+    if (rc) return rc;
+    const int hidden = gate->first.cols, inter = gate->first.rows, E = gate->count;
+    if (up->first.rows != inter || up->first.cols != hidden || up->count != E)
+        return dhp_fail(DHP_ERR_INVALID, "up experts do not match gate (%d x %d x %d)", E, inter, hidden);
+    if (down->first.rows != hidden || down->first.cols != inter || down->count != E)
+        return dhp_fail(DHP_ERR_INVALID, "down experts must be %d x [%d x %d]", E, hidden, inter);
+    if (shared_gate->rows != inter || shared_gate->cols != hidden || shared_up->rows != inter ||
+        shared_up->cols != hidden || shared_down->rows != hidden || shared_down->cols != inter)
+        return dhp_fail(DHP_ERR_INVALID, "shared expert shapes must match the routed experts");
+    if (hidden % 512 || hidden > 4096)
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "hidden=%d (a multiple of 512, at most 4096)", hidden);
+    if (inter > 1024) return dhp_fail(DHP_ERR_UNSUPPORTED, "inter=%d above 1024", inter);
+    if (E > 1024) return dhp_fail(DHP_ERR_UNSUPPORTED, "n_experts=%d above 1024", E);
+    if (top_k < 1 || top_k > DHP_MOE_MAX_TOP_K || top_k > E)
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "top_k=%d (1..%d and at most n_experts=%d)", top_k, DHP_MOE_MAX_TOP_K, E);
+    if (router_dtype != DHP_BF16 && router_dtype != DHP_F32)
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "router_dtype %d (bf16 or fp32)", router_dtype);
+    if (flags & ~DHP_MOE_FP16_BOUNDARY) return dhp_fail(DHP_ERR_UNSUPPORTED, "flags 0x%x", flags);
+    if (!aligned(x, 16) || !aligned(router, 16) || !aligned(shared_gate_row, 16))
+        return dhp_fail(DHP_ERR_MISALIGNED, "x, router and shared_gate_row must be 16-byte aligned");
+    if (!aligned(out, 2) || !aligned(ids, 4) || !aligned(weights, 4))
+        return dhp_fail(DHP_ERR_MISALIGNED, "out, ids or weights misaligned");
+    const size_t need = dhp_moe_ws(E, top_k, inter);
+    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_moe(x, router, router_dtype == DHP_F32, shared_gate_row, gate, up, down, shared_gate,
+                      shared_up, shared_down, top_k, (flags & DHP_MOE_FP16_BOUNDARY) != 0, out, ids,
+                      weights, ws, static_cast<hipStream_t>(stream));
 }
 
 int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H, float eps,
@@ -220,7 +254,3 @@ int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32
 
 }  // extern "C"
 
-size_t dhp_moe_ws(int32_t n_experts, int32_t top_k, int32_t inter) {
-    (void)n_experts; (void)top_k; (void)inter;
-    return 0;
-}

@@ -1,0 +1,391 @@
+// Routed mixture-of-experts decode for one token: router GEMV, on-device top-k with softmax
+// over the selected experts, phase 1 (gate/up GEMV + silu(gate)*up), phase 2 (down GEMV +
+// weighted k-way reduce) and the sigmoid-gated shared expert.
+//
+// "src/families/qwen4/mod.rs" (turbospark-runtime 0.3.0), section MoE; "src/families/qwen/
+// state.rs", struct RealQwenState (fp32 router logits, unit router scales, gated shared
+// expert); "src/real_forward.rs", module doc (phase-1 gate_up_act and phase-2 down_reduce
+// kernels, with the router logits read back to the host for top-k between two command
+// buffers). Here nothing returns to the host: three kernels on one stream.
+//
+//  k_moe_router : one wave per router row (fp32 logits into the workspace), one wave for the
+//                 shared expert's scalar gate logit, and quarter-waves running the shared
+//                 expert's gate/up pairs, which need no routing decision.
+//  k_moe_phase1 : every block re-derives the top-k from the E logits (a handful of wave
+//                 reductions, cheaper than another launch), then its quarter-waves run one
+//                 (selected expert, row) pair each: gate and up rows against register-resident
+//                 activations, act = silu(gate) * up in fp32. Block 0 writes ids and weights.
+//  k_moe_phase2 : 16 lanes per output element walk the down rows of all selected experts and
+//                 the shared expert (K = inter) against the fp32 activations staged in LDS,
+//                 weighting each expert's partial by its softmax weight; the shared part is
+//                 scaled by sigmoid(g) and both halves meet in one fp16 rounding.
+#include "dhp_internal.hpp"
+
+#include <math.h>
+#include <limits.h>
+
+namespace {
+
+constexpr int LPR = 16;
+constexpr int MAX_E = 1024;
+
+struct MoeArgs {
+    const _Float16* x;
+    const void* router;
+    int router_f32;
+    const uint16_t* sgate_row;
+    // routed experts: first tensor and byte strides
+    const uint8_t* g_codes; const uint8_t* g_scales; const uint8_t* g_biases;
+    const uint8_t* u_codes; const uint8_t* u_scales; const uint8_t* u_biases;
+    const uint8_t* d_codes; const uint8_t* d_scales; const uint8_t* d_biases;
+    long long gu_cstride, gu_sstride;     // gate and up share strides (same shapes)
+    long long u_cstride, u_sstride;
+    long long d_cstride, d_sstride;
+    // shared expert
+    const u32x4* sg_codes; const uint16_t* sg_scales; const uint16_t* sg_biases;
+    const u32x4* su_codes; const uint16_t* su_scales; const uint16_t* su_biases;
+    const u32x4* sd_codes; const uint16_t* sd_scales; const uint16_t* sd_biases;
+    int E, hidden, inter, top_k, boundary;
+    float* logits;     // ws [E]
+    float* gate_logit; // ws [1]
+    float* act;        // ws [(top_k + 1) * inter]; slot top_k is the shared expert
+    _Float16* out;
+    int32_t* ids;
+    float* weights;
+};
+
+// gate and up dots of one expert row pair (K = hidden = 512 * CPL) for the 16-lane group
+// whose lane index is j; returns silu(gate) * up in every lane of the group.
+template <int CPL>
+DHP_DEV float gate_up_pair(const u32x4* gc, const uint16_t* gs, const uint16_t* gb,
+                           const u32x4* uc, const uint16_t* us, const uint16_t* ub, int row, int j,
+                           const h2 (*xp)[16], const float* xs) {
+    constexpr int CH = LPR * CPL;
+    constexpr int G = CH / 2;
+    u32x4 cg[CPL], cu[CPL];
+    uint32_t sg[CPL], bg[CPL], su[CPL], bu[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int ch = j + LPR * i;
+        cg[i] = __builtin_nontemporal_load(gc + (size_t)row * CH + ch);
+        cu[i] = __builtin_nontemporal_load(uc + (size_t)row * CH + ch);
+        sg[i] = gs[(size_t)row * G + (ch >> 1)];
+        bg[i] = gb[(size_t)row * G + (ch >> 1)];
+        su[i] = us[(size_t)row * G + (ch >> 1)];
+        bu[i] = ub[(size_t)row * G + (ch >> 1)];
+    }
+    float ag = 0.0f, au = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        ag = __builtin_fmaf(bf16_to_f32(sg[i]), dot32_f16(cg[i], xp[i]), ag);
+        ag = __builtin_fmaf(bf16_to_f32(bg[i]), xs[i], ag);
+        au = __builtin_fmaf(bf16_to_f32(su[i]), dot32_f16(cu[i], xp[i]), au);
+        au = __builtin_fmaf(bf16_to_f32(bu[i]), xs[i], au);
+    }
+    ag = group_sum<LPR>(ag);
+    au = group_sum<LPR>(au);
+    return silu_f(ag) * au;
+}
+
+// fp32 dot of one bf16 or fp32 row of length `hidden` with the fp16 activations, one wave.
+DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x, int hidden) {
+    const int lane = threadIdx.x & 63;
+    float acc = 0.0f;
+    if (!f32) {
+        const u32x4* r = static_cast<const u32x4*>(row);          // 8 bf16 per chunk
+        for (int c = lane; c < hidden / 8; c += 64) {
+            const u32x4 w = __builtin_nontemporal_load(r + c);
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(x + 8 * c);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            const uint32_t xx[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const h2 xh = as_h2(xx[k]);
+                acc = __builtin_fmaf(bf16_to_f32(ww[k] & 0xFFFFu), (float)xh.x, acc);
+                acc = __builtin_fmaf(bf16_to_f32(ww[k] >> 16), (float)xh.y, acc);
+            }
+        }
+    } else {
+        const f4v* r = static_cast<const f4v*>(row);               // 4 fp32 per chunk
+        for (int c = lane; c < hidden / 4; c += 64) {
+            const f4v w = __builtin_nontemporal_load(r + c);
+            const uint2 xv = *reinterpret_cast<const uint2*>(x + 4 * c);
+            const h2 x0 = as_h2(xv.x), x1 = as_h2(xv.y);
+            acc = __builtin_fmaf(w.x, (float)x0.x, acc);
+            acc = __builtin_fmaf(w.y, (float)x0.y, acc);
+            acc = __builtin_fmaf(w.z, (float)x1.x, acc);
+            acc = __builtin_fmaf(w.w, (float)x1.y, acc);
+        }
+    }
+    return group_sum<64>(acc);
+}
+
+template <int CPL>
+DHP_DEV void load_x_regs(const _Float16* x, int j, h2 (*xp)[16], float* xs) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) xs[i] = load_x32(x + (size_t)(j + LPR * i) * 32, xp[i]);
+}
+
+// Blocks [0, E): router rows. Block E: shared gate logit. Blocks after: 4 shared pairs each.
+template <int CPL>
+__global__ __launch_bounds__(64) void k_moe_router(MoeArgs a) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    if (b < a.E) {
+        const size_t rb = (size_t)a.hidden * (a.router_f32 ? 4 : 2);
+        const float v = wave_row_dot(static_cast<const uint8_t*>(a.router) + rb * b, a.router_f32, a.x, a.hidden);
+        if (lane == 0) a.logits[b] = v;
+        return;
+    }
+    if (b == a.E) {
+        const float v = wave_row_dot(a.sgate_row, 0, a.x, a.hidden);
+        if (lane == 0) a.gate_logit[0] = v;
+        return;
+    }
+    const int j = lane % LPR;
+    const int row = (b - a.E - 1) * 4 + lane / LPR;
+    if (row >= a.inter) return;           // whole 16-lane groups leave together
+    h2 xp[CPL][16];
+    float xs[CPL];
+    load_x_regs<CPL>(a.x, j, xp, xs);
+    const float v = gate_up_pair<CPL>(a.sg_codes, a.sg_scales, a.sg_biases, a.su_codes, a.su_scales,
+                                      a.su_biases, row, j, xp, xs);
+    if (j == 0) a.act[(size_t)a.top_k * a.inter + row] = v;
+}
+
+// Top-k of the E logits by one wave (values larger first, lower index first among equals).
+// Every lane returns the same ids and logits.
+DHP_DEV void wave_topk(const float* logits, int E, int k, int* ids, float* vals) {
+    const int lane = threadIdx.x & 63;
+    constexpr int PER = MAX_E / 64;
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        const float l = (e < E) ? logits[e] : -INFINITY;
+        v[i] = (l == l) ? l : -INFINITY;   // a NaN logit ranks as -inf, so ids stay valid
+    }
+    int taken = 0;                         // bit i: v[i] already selected
+    for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1) && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+        ids[r] = bi;
+        vals[r] = bv;
+        if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
+    }
+}
+
+template <int CPL>
+__global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
+    const int lane = threadIdx.x;
+    const int j = lane % LPR;
+    h2 xp[CPL][16];
+    float xs[CPL];
+    load_x_regs<CPL>(a.x, j, xp, xs);      // independent of routing: issue first
+
+    int ids[DHP_MOE_MAX_TOP_K];
+    float vals[DHP_MOE_MAX_TOP_K];
+    wave_topk(a.logits, a.E, a.top_k, ids, vals);
+
+    if (blockIdx.x == 0 && lane == 0) {
+        float w[DHP_MOE_MAX_TOP_K];
+        float sum = 0.0f;
+        for (int r = 0; r < a.top_k; ++r) {
+            w[r] = __expf(vals[r] - vals[0]);
+            sum += w[r];
+        }
+        for (int r = 0; r < a.top_k; ++r) {
+            a.ids[r] = ids[r];
+            a.weights[r] = w[r] / sum;
+        }
+    }
+
+    const int pair = blockIdx.x * 4 + lane / LPR;      // (slot, row) flattened
+    if (pair >= a.top_k * a.inter) return;
+    const int slot = pair / a.inter;
+    const int row = pair % a.inter;
+    int e = ids[0];
+#pragma unroll
+    for (int r = 1; r < DHP_MOE_MAX_TOP_K; ++r)
+        if (r == slot) e = ids[r];
+    const auto* gc = reinterpret_cast<const u32x4*>(a.g_codes + (size_t)e * a.gu_cstride);
+    const auto* gs = reinterpret_cast<const uint16_t*>(a.g_scales + (size_t)e * a.gu_sstride);
+    const auto* gb = reinterpret_cast<const uint16_t*>(a.g_biases + (size_t)e * a.gu_sstride);
+    const auto* uc = reinterpret_cast<const u32x4*>(a.u_codes + (size_t)e * a.u_cstride);
+    const auto* us = reinterpret_cast<const uint16_t*>(a.u_scales + (size_t)e * a.u_sstride);
+    const auto* ub = reinterpret_cast<const uint16_t*>(a.u_biases + (size_t)e * a.u_sstride);
+    const float v = gate_up_pair<CPL>(gc, gs, gb, uc, us, ub, row, j, xp, xs);
+    if (j == 0) a.act[(size_t)slot * a.inter + row] = v;
+}
+
+// 16 lanes per output element h, RH elements per 16-lane group; a block of 64 lanes covers
+// 4 * RH consecutive outputs. Down rows have K = inter; lane j takes chunks j, j+16, ...
+constexpr int RH = 2;
+
+__global__ __launch_bounds__(64) void k_moe_phase2(MoeArgs a) {
+    extern __shared__ float lds_act[];     // [(top_k + 1) * inter] then chunk sums
+    const int lane = threadIdx.x;
+    const int j = lane % LPR;
+    const int nslot = a.top_k + 1;
+    const int CH = a.inter >> 5;
+    const int G = a.inter >> 6;
+    const int h0 = (blockIdx.x * 4 + lane / LPR) * RH;
+
+    // stage the activations of every slot
+    const int n = nslot * a.inter;
+    float* act_sum = lds_act + n;
+    for (int i = lane * 4; i < n; i += 64 * 4)
+        *reinterpret_cast<f4v*>(lds_act + i) = *reinterpret_cast<const f4v*>(a.act + i);
+    __syncthreads();
+    for (int c = lane; c < nslot * CH; c += 64) {
+        float s = 0.0f;
+        for (int i = 0; i < 32; ++i) s += lds_act[32 * c + i];
+        act_sum[c] = s;
+    }
+    __syncthreads();
+
+    float racc[RH], sacc[RH];
+#pragma unroll
+    for (int r = 0; r < RH; ++r) { racc[r] = 0.0f; sacc[r] = 0.0f; }
+    for (int slot = 0; slot < nslot; ++slot) {
+        const bool shared = slot == a.top_k;
+        const u32x4* dc;
+        const uint16_t* ds;
+        const uint16_t* db;
+        float wgt = 1.0f;
+        if (shared) {
+            dc = a.sd_codes; ds = a.sd_scales; db = a.sd_biases;
+        } else {
+            const int e = a.ids[slot];
+            dc = reinterpret_cast<const u32x4*>(a.d_codes + (size_t)e * a.d_cstride);
+            ds = reinterpret_cast<const uint16_t*>(a.d_scales + (size_t)e * a.d_sstride);
+            db = reinterpret_cast<const uint16_t*>(a.d_biases + (size_t)e * a.d_sstride);
+            wgt = a.weights[slot];
+        }
+        const float* av = lds_act + (size_t)slot * a.inter;
+        const float* asum = act_sum + (size_t)slot * CH;
+#pragma unroll
+        for (int r = 0; r < RH; ++r) {
+            const int h = h0 + r;
+            if (h >= a.hidden) break;
+            float p = 0.0f;
+            for (int ch = j; ch < CH; ch += LPR) {
+                const u32x4 c = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
+                const float d = dot32_f32(c, av + 32 * ch);
+                p = __builtin_fmaf(bf16_to_f32(ds[(size_t)h * G + (ch >> 1)]), d, p);
+                p = __builtin_fmaf(bf16_to_f32(db[(size_t)h * G + (ch >> 1)]), asum[ch], p);
+            }
+            if (shared) sacc[r] += p;
+            else racc[r] = __builtin_fmaf(wgt, p, racc[r]);
+        }
+    }
+    const float sg = sigmoid_f(a.gate_logit[0]);
+#pragma unroll
+    for (int r = 0; r < RH; ++r) {
+        const float rr = group_sum<LPR>(racc[r]);
+        const float ss = group_sum<LPR>(sacc[r]) * sg;
+        const int h = h0 + r;
+        if (j == 0 && h < a.hidden) {
+            float o;
+            if (a.boundary) o = (float)(_Float16)rr + (float)(_Float16)ss;
+            else o = rr + ss;
+            a.out[h] = (_Float16)o;
+        }
+    }
+}
+
+template <int CPL>
+hipError_t launch_all(const MoeArgs& a, hipStream_t s) {
+    const int shared_blocks = (a.inter + 3) / 4;
+    hipLaunchKernelGGL(k_moe_router<CPL>, dim3(a.E + 1 + shared_blocks), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int pairs = a.top_k * a.inter;
+    hipLaunchKernelGGL(k_moe_phase1<CPL>, dim3((pairs + 3) / 4), dim3(64), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)(a.top_k + 1) * (a.inter + a.inter / 32) * sizeof(float);
+    const int per_block = 4 * RH;
+    hipLaunchKernelGGL(k_moe_phase2, dim3((a.hidden + per_block - 1) / per_block), dim3(64), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t dhp_moe_ws(int32_t n_experts, int32_t top_k, int32_t inter) {
+    const size_t floats = (size_t)((n_experts + 4) & ~3) + (size_t)(top_k + 1) * inter;
+    return (floats * sizeof(float) + 255) & ~(size_t)255;
+}
+
+int launch_moe(const void* x, const void* router, int router_f32, const void* sgate_row,
+               const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
+               const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
+               void* out, int32_t* ids, float* weights, void* ws, hipStream_t s) {
+    MoeArgs a;
+    a.x = static_cast<const _Float16*>(x);
+    a.router = router;
+    a.router_f32 = router_f32;
+    a.sgate_row = static_cast<const uint16_t*>(sgate_row);
+    a.g_codes = static_cast<const uint8_t*>(gate->first.codes);
+    a.g_scales = static_cast<const uint8_t*>(gate->first.scales);
+    a.g_biases = static_cast<const uint8_t*>(gate->first.biases);
+    a.u_codes = static_cast<const uint8_t*>(up->first.codes);
+    a.u_scales = static_cast<const uint8_t*>(up->first.scales);
+    a.u_biases = static_cast<const uint8_t*>(up->first.biases);
+    a.d_codes = static_cast<const uint8_t*>(down->first.codes);
+    a.d_scales = static_cast<const uint8_t*>(down->first.scales);
+    a.d_biases = static_cast<const uint8_t*>(down->first.biases);
+    a.gu_cstride = gate->codes_stride;
+    a.gu_sstride = gate->scales_stride;
+    a.u_cstride = up->codes_stride;
+    a.u_sstride = up->scales_stride;
+    a.d_cstride = down->codes_stride;
+    a.d_sstride = down->scales_stride;
+    a.sg_codes = static_cast<const u32x4*>(sg->codes);
+    a.sg_scales = static_cast<const uint16_t*>(sg->scales);
+    a.sg_biases = static_cast<const uint16_t*>(sg->biases);
+    a.su_codes = static_cast<const u32x4*>(su->codes);
+    a.su_scales = static_cast<const uint16_t*>(su->scales);
+    a.su_biases = static_cast<const uint16_t*>(su->biases);
+    a.sd_codes = static_cast<const u32x4*>(sd->codes);
+    a.sd_scales = static_cast<const uint16_t*>(sd->scales);
+    a.sd_biases = static_cast<const uint16_t*>(sd->biases);
+    a.E = gate->count;
+    a.hidden = gate->first.cols;
+    a.inter = gate->first.rows;
+    a.top_k = top_k;
+    a.boundary = boundary;
+    float* w = static_cast<float*>(ws);
+    a.logits = w;
+    a.gate_logit = w + a.E;
+    a.act = w + ((a.E + 4) & ~3);        // 16-byte aligned
+    a.out = static_cast<_Float16*>(out);
+    a.ids = ids;
+    a.weights = weights;
+
+    hipError_t e;
+    switch (a.hidden / 512) {
+        case 1: e = launch_all<1>(a, s); break;
+        case 2: e = launch_all<2>(a, s); break;
+        case 3: e = launch_all<3>(a, s); break;
+        case 4: e = launch_all<4>(a, s); break;
+        case 5: e = launch_all<5>(a, s); break;
+        case 6: e = launch_all<6>(a, s); break;
+        case 7: e = launch_all<7>(a, s); break;
+        case 8: e = launch_all<8>(a, s); break;
+        default: return dhp_fail(DHP_ERR_UNSUPPORTED, "hidden=%d", a.hidden);
+    }
+    if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "moe launch: %s", hipGetErrorString(e));
+    return DHP_OK;
+}

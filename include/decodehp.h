@@ -142,8 +142,8 @@ int decodehp_dequant_gemm_batched(const dhp_int4* w, const void* x, int32_t m, v
  *   top_k           : 1..8, <= n_experts.
  *   out             : fp16 [hidden].  ids : int32 [top_k].  weights : fp32 [top_k].
  *   ws              : decodehp_workspace_bytes(DHP_OP_MOE_DECODE, n_experts, top_k, inter).
- * Errors: -1, -2 (hidden or inter % 64, hidden > 8192, inter > 4096, top_k, n_experts > 1024,
- *         router_dtype, flags), -3, -4, -5, -6.
+ * Errors: -1, -2 (hidden % 512, hidden > 4096, inter % 64, inter > 1024, top_k,
+ *         n_experts > 1024, router_dtype, flags), -3, -4, -5, -6.
  */
 int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
                         const void* shared_gate_row, const dhp_int4_experts* gate,

@@ -102,3 +102,72 @@ def test_pack_int4_codes_layout():
     assert p.tolist() == [[0x21, 0x43, 0x0F, 0x87]]
     with pytest.raises(ValueError):
         hca.pack_int4_codes(np.array([[16, 0]], np.uint8))
+
+
+def experts(count=8, rows=64, cols=512, **kw):
+    return hca.CInt4Experts(int4(rows=rows, cols=cols, **kw), rows * cols // 2, 2 * rows * (cols // 64), count)
+
+
+def moe(top_k=2, flags=0, rdt=2, E=8, hidden=512, inter=64, ws=FAKE, wsb=1 << 20, x=FAKE, down_rows=None,
+        sh_rows=None):
+    L = hca.lib()
+    g, u = experts(E, inter, hidden), experts(E, inter, hidden)
+    d = experts(E, down_rows or hidden, inter)
+    sg, su = int4(rows=sh_rows or inter, cols=hidden), int4(rows=inter, cols=hidden)
+    sd = int4(rows=hidden, cols=inter)
+    return L.decodehp_moe_decode(x, FAKE, rdt, FAKE, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                 ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), top_k, flags, FAKE,
+                                 FAKE, FAKE, ws, wsb, None)
+
+
+def test_moe_rejects_bad_calls():
+    assert moe(x=0) == -1
+    assert moe(top_k=0) == -2
+    assert moe(top_k=9) == -2
+    assert moe(top_k=8, E=4) == -2
+    assert moe(rdt=0) == -2
+    assert moe(flags=2) == -2
+    assert moe(hidden=640) == -2               # hidden % 512
+    assert moe(inter=2048) == -2
+    assert moe(E=2048) == -2
+    assert moe(down_rows=256) == -1            # down must be [hidden x inter]
+    assert moe(sh_rows=128) == -1
+    assert moe(x=FAKE + 4) == -3
+    assert moe(ws=None) == -4
+    need = hca.workspace_bytes(hca.DHP_OP_MOE_DECODE, 8, 2, 64)
+    assert need >= (8 + 3 * 64) * 4
+    assert moe(wsb=need - 1) == -4
+
+
+def hc_read(C=4, H=512, R=64, inject=True, iw=FAKE, ws=FAKE, wsb=1 << 16, eps=1e-6, raw=FAKE, up_cols=None):
+    L = hca.lib()
+    down, up = int4(rows=R, cols=C * H), int4(rows=C * H, cols=up_cols or R)
+    inj = int4(rows=C, cols=C * H)
+    return L.decodehp_hc_read(raw, FAKE, C, H, eps, ctypes.byref(down), ctypes.byref(up),
+                              ctypes.byref(inj) if inject else None, FAKE, iw, ws, wsb, None)
+
+
+def test_hc_read_rejects_bad_calls():
+    assert hc_read(raw=0) == -1
+    assert hc_read(C=3) == -2                  # not a power of two
+    assert hc_read(C=32) == -2
+    assert hc_read(H=96) == -2
+    assert hc_read(C=1, H=1024) == -2          # C*H not a multiple of 2048
+    assert hc_read(R=96) == -2
+    assert hc_read(up_cols=128) == -1
+    assert hc_read(inject=False) == -1         # inject_w without inject
+    assert hc_read(iw=None) == -1              # inject without inject_w
+    assert hc_read(eps=-1.0) == -1
+    assert hc_read(raw=FAKE + 8) == -3
+    assert hc_read(ws=None) == -4
+    assert hc_read(wsb=hca.workspace_bytes(hca.DHP_OP_HC_READ, 4, 64) - 1) == -4
+
+
+def test_hc_inject_rejects_bad_calls():
+    L = hca.lib()
+    f = lambda wide=FAKE, C=4, H=64, out=FAKE: L.decodehp_hc_inject(wide, out, FAKE, C, H, None)
+    assert f(wide=0) == -1
+    assert f(C=0) == -1
+    assert f(C=17) == -2
+    assert f(H=12) == -2
+    assert f(out=FAKE + 2) == -3

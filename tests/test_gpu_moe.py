@@ -1,0 +1,166 @@
+"""GPU parity: decodehp_moe_decode against the fp64 oracle.
+
+Bar: expert ids bit-exact (order included, lowest index first on ties); weights and the fp16
+output within |d| <= 1e-3 + 1e-2 |oracle| elementwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_within_tol, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+hca = pytest.importorskip("hyper_connections_amd")
+
+
+def dev_int4(t):
+    return hca.Int4Weight.from_logical(t.q, t.s_bits, t.b_bits)
+
+
+class DevMoe:
+    def __init__(self, d, router_f32=False):
+        ex = d["experts"]
+        self.gate = hca.Int4Experts.from_logical([e["gate"] for e in ex])
+        self.up = hca.Int4Experts.from_logical([e["up"] for e in ex])
+        self.down = hca.Int4Experts.from_logical([e["down"] for e in ex])
+        self.sg, self.su, self.sd = (dev_int4(d["shared"][k]) for k in ("gate", "up", "down"))
+        if router_f32:
+            self.router = torch.from_numpy(oracle.bf16_bits_to_f64(d["router_bits"]).astype(np.float32)).cuda()
+        else:
+            self.router = hca.bf16_bits_to_tensor(d["router_bits"]).cuda()
+        self.sgate = hca.bf16_bits_to_tensor(d["sgate_bits"]).cuda()
+        self.top_k = d["top_k"]
+
+    def __call__(self, x, fp16_boundary=False):
+        xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        out, ids, w = hca.moe_decode(xd, self.router, self.sgate, self.gate, self.up, self.down, self.sg, self.su,
+                                     self.sd, self.top_k, fp16_boundary=fp16_boundary)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def check(d, dev, x, fp16_boundary=False, what="moe"):
+    out, ids, w = dev(x, fp16_boundary)
+    ref = oracle.moe_decode(x, d["router_bits"], d["sgate_bits"], d["shared"], d["experts"], d["top_k"],
+                            fp16_boundary=fp16_boundary)
+    assert list(ids) == list(ref["ids"]), (list(ids), list(ref["ids"]))
+    assert_within_tol(w, ref["weights"], f"{what} weights")
+    assert abs(float(np.sum(w, dtype=np.float64)) - 1.0) < 1e-5
+    assert_within_tol(out, ref["out"], f"{what} out")
+    l32 = np.sort(ref["logits"].astype(np.float32))[::-1]
+    return float(l32[d["top_k"] - 1] - l32[d["top_k"]]) if len(l32) > d["top_k"] else None
+
+
+@pytest.fixture(scope="module")
+def full():
+    say("moe workload E=256 hidden=2560 inter=512 top8 seed 0 (generating 256 experts)")
+    d = synth.moe_workload(0)
+    return d, DevMoe(d)
+
+
+def test_moe_workload_e256(full):
+    d, dev = full
+    say("moe E=256 seed 0")
+    gap = check(d, dev, d["x"], what="E256")
+    print(f"8th-9th logit gap {gap:.4g}")
+
+
+def test_moe_workload_more_tokens(full):
+    d, dev = full
+    xs = synth.moe_x_ring(0, 4)
+    for i, x in enumerate(xs):
+        say(f"moe E=256 ring token {i}")
+        check(d, dev, x, what=f"token {i}")
+
+
+def test_moe_fp16_boundary_mode(full):
+    d, dev = full
+    say("moe fp16 boundary")
+    out, ids, w = dev(d["x"], fp16_boundary=True)
+    ref = oracle.moe_decode(d["x"], d["router_bits"], d["sgate_bits"], d["shared"], d["experts"], d["top_k"],
+                            fp16_boundary=True)
+    assert list(ids) == list(ref["ids"])
+    assert_within_tol(out, ref["out"], "boundary out")
+
+
+def small(seed, E, hidden, inter, top_k, router_std=0.05):
+    rng = np.random.default_rng([61, seed, E, hidden, inter, top_k])
+    mk = lambda r, c: synth.int4_tensor(rng, r, c)
+    return {"x": synth.normal_f16(rng, (hidden,)),
+            "router_bits": synth.normal_bf16_bits(rng, (E, hidden), std=router_std),
+            "sgate_bits": synth.normal_bf16_bits(rng, (hidden,), std=0.02),
+            "shared": {"gate": mk(inter, hidden), "up": mk(inter, hidden), "down": mk(hidden, inter)},
+            "experts": [{"gate": mk(inter, hidden), "up": mk(inter, hidden), "down": mk(hidden, inter)}
+                        for _ in range(E)],
+            "top_k": top_k}
+
+
+@pytest.mark.parametrize("E,hidden,inter,top_k", [(16, 512, 64, 1), (16, 512, 64, 3), (16, 512, 64, 8),
+                                                  (40, 1024, 128, 8), (8, 512, 192, 8), (300, 1536, 64, 5),
+                                                  (1024, 512, 64, 8), (9, 4096, 1024, 2)])
+def test_moe_shapes(E, hidden, inter, top_k):
+    say(f"moe E={E} hidden={hidden} inter={inter} k={top_k}")
+    d = small(0, E, hidden, inter, top_k)
+    check(d, DevMoe(d), d["x"], what=f"E{E}")
+
+
+def test_moe_fp32_router():
+    say("moe fp32 router")
+    d = small(1, 32, 1024, 128, 4)
+    check(d, DevMoe(d, router_f32=True), d["x"], what="fp32 router")
+
+
+def test_moe_top1_weight_is_one():
+    say("moe top-1")
+    d = small(2, 16, 512, 64, 1)
+    _, _, w = DevMoe(d)(d["x"])
+    assert w.tolist() == [1.0]
+
+
+@pytest.mark.parametrize("case", ["pair_in_topk", "pair_straddles_cut"])
+def test_moe_tie_goes_to_lowest_index(case):
+    say(f"moe tie {case}")
+    d = small(3, 24, 512, 64, 4, router_std=0.3)
+    logits = oracle.router_logits(d["router_bits"], d["x"])
+    order = list(oracle.select_topk(logits, 24))
+    if case == "pair_in_topk":
+        src, dst = order[1], order[-1]           # copy the 2nd best row onto the worst expert
+    else:
+        src, dst = order[3], order[-1]           # copy the 4th (last selected) onto a later/earlier id
+    d["router_bits"][dst] = d["router_bits"][src]
+    dev = DevMoe(d)
+    out, ids, w = dev(d["x"])
+    ref = oracle.moe_decode(d["x"], d["router_bits"], d["sgate_bits"], d["shared"], d["experts"], 4)
+    assert list(ids) == list(ref["ids"])
+    assert min(src, dst) in ids
+    if case == "pair_in_topk":
+        assert max(src, dst) in ids
+        a, b = list(ids).index(min(src, dst)), list(ids).index(max(src, dst))
+        assert b == a + 1 and w[a] == w[b]
+    else:
+        assert max(src, dst) not in ids
+    assert_within_tol(out, ref["out"], "tie out")
+
+
+def test_moe_identical_experts_routing_invariant():
+    say("moe identical experts")
+    d = small(4, 12, 512, 64, 3)
+    d["experts"] = [d["experts"][0]] * 12
+    dev = DevMoe(d)
+    o1, i1, _ = dev(d["x"])
+    d2 = dict(d)
+    d2["router_bits"] = d["router_bits"][::-1].copy()
+    o2, i2, _ = DevMoe(d2)(d["x"])
+    assert list(i1) != list(i2)
+    assert_within_tol(o1, o2, "routing invariance")
+
+
+def test_moe_deterministic(full):
+    d, dev = full
+    say("moe determinism")
+    a = dev(d["x"])
+    b = dev(d["x"])
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
