@@ -128,10 +128,12 @@ int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, 
         if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
         if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
     }
-    if (m != 1) return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d: the multi-row arm is not built yet", m);
     DeviceFacts dev;
     if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
-    return launch_gemv_m1(w, x, y, y_dtype == DHP_F32, argmax, ws, static_cast<hipStream_t>(stream), dev);
+    if (m == 1)
+        return launch_gemv_m1(w, x, y, y_dtype == DHP_F32, argmax, ws, static_cast<hipStream_t>(stream), dev);
+    return launch_gemm_mfma(w, x, m, y, y_dtype == DHP_F32, argmax, ws, dhp_argmax_part_stride(w->rows, m),
+                            static_cast<hipStream_t>(stream));
 }
 
 int decodehp_dequant_gemm_batched(const dhp_int4* w, const void* x, int32_t m, void* y, void* stream) {
@@ -144,8 +146,9 @@ int decodehp_dequant_gemm_batched(const dhp_int4* w, const void* x, int32_t m, v
     if (w->cols > 32768) return dhp_fail(DHP_ERR_UNSUPPORTED, "K=%d above 32768", w->cols);
     if (!aligned(x, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "x not 16-byte aligned");
     if (!aligned(y, 2)) return dhp_fail(DHP_ERR_MISALIGNED, "y misaligned");
-    (void)stream;
-    return dhp_fail(DHP_ERR_UNSUPPORTED, "batched arm not built yet");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_gemm_mfma(w, x, m, y, 0, nullptr, nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
 int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,

@@ -151,3 +151,6 @@ int launch_moe(const void* x, const void* router, int router_f32, const void* sg
                const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
                const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
                void* out, int32_t* ids, float* weights, void* ws, hipStream_t s);
+size_t dhp_argmax_part_stride(int32_t n_rows, int32_t m);
+int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax,
+                     void* ws, size_t ws_part_stride, hipStream_t s);

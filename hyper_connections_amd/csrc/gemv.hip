@@ -216,9 +216,20 @@ hipError_t launch_reg(bool f32, bool am, dim3 g, dim3 b, hipStream_t s, const u3
 
 }  // namespace
 
-size_t dhp_gemv_argmax_ws(int32_t n_rows, int32_t m) {
-    (void)n_rows;
-    return (size_t)GEMV_MAX_BLOCKS * (size_t)m * (sizeof(float) + sizeof(int));
+int dhp_gemm_blocks_n(int N);
+
+// Bytes of the fp32 half of the argmax partials: [m][parts] values, then [m][parts] indices.
+size_t dhp_argmax_part_stride(int32_t n_rows, int32_t m) {
+    int parts = dhp_gemm_blocks_n(n_rows);
+    if (parts < GEMV_MAX_BLOCKS) parts = GEMV_MAX_BLOCKS;
+    return (size_t)parts * (size_t)m * sizeof(float);
+}
+
+size_t dhp_gemv_argmax_ws(int32_t n_rows, int32_t m) { return 2 * dhp_argmax_part_stride(n_rows, m); }
+
+hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)m), dim3(256), 0, s, pv, pi, nparts, out);
+    return hipGetLastError();
 }
 
 int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t* argmax,
@@ -244,7 +255,7 @@ int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t
     const int nparts = (int)blocks;
 
     float* pv = am ? static_cast<float*>(ws) : nullptr;
-    int* pi = am ? reinterpret_cast<int*>(static_cast<char*>(ws) + (size_t)GEMV_MAX_BLOCKS * sizeof(float)) : nullptr;
+    int* pi = am ? reinterpret_cast<int*>(static_cast<char*>(ws) + dhp_argmax_part_stride(N, 1)) : nullptr;
 
     hipError_t e = hipSuccess;
     dim3 g((unsigned)blocks), b((unsigned)block);
@@ -268,8 +279,7 @@ int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t
     }
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemv launch: %s", hipGetErrorString(e));
     if (am) {
-        hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(256), 0, s, pv, pi, nparts, argmax);
-        e = hipGetLastError();
+        e = launch_argmax_final(pv, pi, nparts, 1, argmax, s);
         if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "argmax launch: %s", hipGetErrorString(e));
     }
     return DHP_OK;
