@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X decode hot path (libdecodehp) on one GPU.
+
+One step = one pass of every hot-path call over one batch of seeded synthetic inputs:
+
+  gemv      INT4 dequant GEMV, M=1, 2560 x 2560, fp16 out
+  hc        hyper-connection read (C=4, H=2560, R=320, with inject gate) + inject add
+  moe       routed MoE decode, 256 resident experts, top-8, gated shared expert
+  prefill   batched projection, M=128, N=8192, K=2560 (matrix cores), fp16 out
+  lmhead1   LM head, M=1, 151936 x 2560, fp32 logits + argmax
+  lmhead8   LM head, M=8, same shape, fp32 logits + argmax
+
+`value` is the step's algorithmic bytes (INT4 codes + bf16 scales/biases + activations in +
+outputs, each counted once) divided by the measured step time: whole-job HBM GB/s with every
+input already resident. Rotating weight copies and the 438 MB of LM-head traffic per step keep
+each call's weights out of the 256 MB last-level cache between uses.
+
+Also printed in the same JSON line:
+  roofline      the dominant kernel (the M=1 LM-head GEMV) against 8 TB/s, its average duration
+                from HIP events on the launch stream over the timed region;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload (rank 0);
+  calls         per-call median microseconds and GB/s from a separate, event-timed pass.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "lmhead_gemv_m1_counters.json")
+DOMINANT_SRC = os.path.join(ROOT, "hyper_connections_amd", "csrc", "gemv.hip")
+
+
+def int4_bytes(rows, cols):
+    return rows * cols // 2 + 4 * rows * (cols // 64)
+
+
+def algorithmic_bytes():
+    """Bytes each call must move at least once (weights incl. scales/biases, inputs, outputs)."""
+    K = 2560
+    b = {}
+    b["gemv"] = int4_bytes(2560, K) + 2 * K + 2 * 2560
+    C, H, R = 4, 2560, 320
+    b["hc"] = (int4_bytes(R, C * H) + int4_bytes(C * H, R) + int4_bytes(C, C * H) + 2 * C * H + 2 * C * H
+               + 2 * H + 4 * C) + (2 * C * H * 2 + 2 * H + 4 * C)
+    E, inter, top_k = 256, 512, 8
+    b["moe"] = (2 * E * K + 2 * K + (top_k + 1) * (2 * int4_bytes(inter, K) + int4_bytes(K, inter))
+                + 2 * K + 2 * K + 8 * top_k)
+    b["prefill"] = int4_bytes(8192, K) + 2 * 128 * K + 2 * 128 * 8192
+    V = 151936
+    b["lmhead1"] = int4_bytes(V, K) + 2 * K + 4 * V + 4
+    b["lmhead8"] = int4_bytes(V, K) + 2 * 8 * K + 4 * 8 * V + 4 * 8
+    return b
+
+
+def build_workload(torch, hca, synth, ring: int):
+    """Device inputs for every call, with `ring` rotating copies of the small weight sets."""
+    dev = "cuda"
+    t0 = time.time()
+    W = {}
+
+    def up_int4(t):
+        return hca.Int4Weight.from_logical(t.q, t.s_bits, t.b_bits, dev)
+
+    def clone(w):
+        return hca.Int4Weight(w.codes.clone(), w.scales.clone(), w.biases.clone(), w.rows, w.cols)
+
+    g = synth.gemv_workload(0)
+    w0 = up_int4(g["w"])
+    W["gemv_w"] = [w0] + [clone(w0) for _ in range(ring - 1)]
+    W["gemv_x"] = torch.from_numpy(g["x"]).to(dev)
+    W["gemv_y"] = torch.empty(2560, dtype=torch.float16, device=dev)
+
+    h = synth.hc_workload(0)
+    hw = (up_int4(h["down"]), up_int4(h["up"]), up_int4(h["inject"]))
+    W["hc_w"] = [hw] + [tuple(clone(w) for w in hw) for _ in range(ring - 1)]
+    W["hc_wide"] = torch.from_numpy(h["raw"]).to(dev)
+    W["hc_gamma"] = hca.bf16_bits_to_tensor(h["gamma_bits"]).to(dev)
+    W["hc_out"] = torch.from_numpy(h["out"]).to(dev)
+    W["hc_mixed"] = torch.empty(2560, dtype=torch.float16, device=dev)
+    W["hc_iw"] = torch.empty(4, dtype=torch.float32, device=dev)
+
+    m = synth.moe_workload(0)
+    ex = m["experts"]
+    W["moe"] = dict(
+        gate=hca.Int4Experts.from_logical([e["gate"] for e in ex], dev),
+        up=hca.Int4Experts.from_logical([e["up"] for e in ex], dev),
+        down=hca.Int4Experts.from_logical([e["down"] for e in ex], dev),
+        sg=up_int4(m["shared"]["gate"]), su=up_int4(m["shared"]["up"]), sd=up_int4(m["shared"]["down"]),
+        router=hca.bf16_bits_to_tensor(m["router_bits"]).to(dev),
+        sgate=hca.bf16_bits_to_tensor(m["sgate_bits"]).to(dev))
+    xs = np.concatenate([m["x"][None], synth.moe_x_ring(0, 63)])
+    W["moe_x"] = torch.from_numpy(xs).to(dev)
+    W["moe_out"] = torch.empty(2560, dtype=torch.float16, device=dev)
+    W["moe_ids"] = torch.empty(8, dtype=torch.int32, device=dev)
+    W["moe_w"] = torch.empty(8, dtype=torch.float32, device=dev)
+    del ex, m
+
+    p = synth.prefill_workload(0)
+    p0 = up_int4(p["w"])
+    W["pre_w"] = [p0] + [clone(p0) for _ in range(ring - 1)]
+    W["pre_x"] = torch.from_numpy(p["x"]).to(dev)
+    W["pre_y"] = torch.empty((128, 8192), dtype=torch.float16, device=dev)
+
+    l1 = synth.lmhead_workload(0, m=1)
+    lw = up_int4(l1["w"])
+    W["lm_w"] = [lw, clone(lw)]
+    W["lm_x1"] = torch.from_numpy(l1["x"]).to(dev)
+    W["lm_x8"] = torch.from_numpy(synth.lmhead_x(0, 8)).to(dev)
+    W["lm_y1"] = torch.empty((1, 151936), dtype=torch.float32, device=dev)
+    W["lm_y8"] = torch.empty((8, 151936), dtype=torch.float32, device=dev)
+    W["lm_a1"] = torch.empty(1, dtype=torch.int32, device=dev)
+    W["lm_a8"] = torch.empty(8, dtype=torch.int32, device=dev)
+    del l1
+    torch.cuda.synchronize()
+    print(f"[bench] workload resident in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    return W
+
+
+def prepare_calls(hca, W, ring: int):
+    """calls[name][i] for ring position i (the MoE token ring has its own length)."""
+    C, H = 4, 2560
+    mo = W["moe"]
+    calls = {
+        "gemv": [hca.prepare_gemv(W["gemv_w"][i], W["gemv_x"], W["gemv_y"]) for i in range(ring)],
+        "hc": [(hca.prepare_hc_read(W["hc_wide"], W["hc_gamma"], C, H, *W["hc_w"][i], W["hc_mixed"], W["hc_iw"]),
+                hca.prepare_hc_inject(W["hc_wide"], W["hc_out"], W["hc_iw"], C, H)) for i in range(ring)],
+        "moe": [hca.prepare_moe(W["moe_x"][t], mo["router"], mo["sgate"], mo["gate"], mo["up"], mo["down"], mo["sg"],
+                                mo["su"], mo["sd"], 8, W["moe_out"], W["moe_ids"], W["moe_w"])
+                for t in range(W["moe_x"].shape[0])],
+        "prefill": [hca.prepare_gemm_batched(W["pre_w"][i], W["pre_x"], W["pre_y"]) for i in range(ring)],
+        "lmhead1": [hca.prepare_gemv(W["lm_w"][0], W["lm_x1"], W["lm_y1"], argmax=W["lm_a1"])],
+        "lmhead8": [hca.prepare_gemv(W["lm_w"][1], W["lm_x8"], W["lm_y8"], argmax=W["lm_a8"])],
+    }
+    return calls
+
+
+def run_call(c):
+    if isinstance(c, tuple):
+        for f in c:
+            f()
+    else:
+        c()
+
+
+def step(calls, i, ev=None):
+    run_call(calls["gemv"][i % len(calls["gemv"])])
+    run_call(calls["hc"][i % len(calls["hc"])])
+    run_call(calls["moe"][i % len(calls["moe"])])
+    run_call(calls["prefill"][i % len(calls["prefill"])])
+    if ev is not None:
+        ev[0].record()
+    run_call(calls["lmhead1"][0])
+    if ev is not None:
+        ev[1].record()
+    run_call(calls["lmhead8"][0])
+
+
+def per_call_pass(torch, calls, nbytes, iters: int):
+    """Each call type alone, event-timed per call, cycling its ring (median over iters)."""
+    out = {}
+    for name in ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8"):
+        seq = calls[name]
+        n = max(iters, len(seq)) if name not in ("lmhead1", "lmhead8") else max(8, iters // 4)
+        st = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        en = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for i in range(3):
+            run_call(seq[i % len(seq)])
+        torch.cuda.synchronize()
+        for i in range(n):
+            st[i].record()
+            run_call(seq[i % len(seq)])
+            en[i].record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) for a, b in zip(st, en)]) * 1e3
+        med = float(np.median(us))
+        out[name] = {"us": round(med, 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+                     "p90_us": round(float(np.percentile(us, 90)), 2),
+                     "GBps": round(nbytes[name] / med / 1e3, 1),
+                     "pct_hbm_peak": round(100.0 * nbytes[name] / med / 1e3 / HBM_PEAK_GBS, 1)}
+    return out
+
+
+def copy_probe(torch):
+    """A plain 1 GiB device copy, for scaling the HBM byte counters (FETCH_SIZE / WRITE_SIZE)."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / 5
+    return {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "us": round(dt * 1e6, 1),
+            "GBps_read_plus_write": round(2 * (1 << 30) / dt / 1e9, 1)}
+
+
+def cpu_baseline(synth):
+    """The fp64 oracle on a bounded sample of one step, scaled to GB/s of algorithmic bytes."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    K = 2560
+    g = synth.gemv_workload(0)
+    h = synth.hc_workload(0)
+    m = synth.moe_workload(0, with_experts=False)
+    sel = {}
+    p = synth.prefill_workload(0)
+    lw = synth.lmhead_workload(0, m=1)
+    x8 = synth.lmhead_x(0, 8)
+    PR, LR = 1024, 16384                      # prefill and LM-head row samples
+    done = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.dequant_gemv(g["w"].q, g["w"].s_bits, g["w"].b_bits, g["x"])
+        done += int4_bytes(2560, K) + 4 * K
+        r = oracle.hc_read(h["raw"], h["gamma_bits"], h["down"], h["up"], h["inject"], 4, 2560)
+        oracle.hc_inject(h["raw"], h["out"], r["inject_w"], 4, 2560)
+        done += algorithmic_bytes()["hc"]
+        logits = oracle.router_logits(m["router_bits"], m["x"])
+        ids = oracle.select_topk(logits, 8)
+        experts = {int(e): sel.setdefault(int(e), synth.moe_expert(0, int(e))) for e in ids}
+        oracle.moe_decode(m["x"], m["router_bits"], m["sgate_bits"], m["shared"], experts, 8)
+        done += algorithmic_bytes()["moe"]
+        oracle.dequant_gemv(p["w"].q[:PR], p["w"].s_bits[:PR], p["w"].b_bits[:PR], p["x"])
+        done += int4_bytes(PR, K) + 2 * 128 * K + 2 * 128 * PR
+        y1 = oracle.dequant_gemv(lw["w"].q[:LR], lw["w"].s_bits[:LR], lw["w"].b_bits[:LR], lw["x"][0])
+        oracle.argmax_lowest(y1)
+        done += int4_bytes(LR, K) + 2 * K + 4 * LR
+        y8 = oracle.dequant_gemv(lw["w"].q[:LR], lw["w"].s_bits[:LR], lw["w"].b_bits[:LR], x8)
+        oracle.argmax_lowest(y8)
+        done += int4_bytes(LR, K) + 16 * K + 32 * LR
+        reps += 1
+        if time.perf_counter() - t0 > 8.0 or reps >= 5:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{reps} pass(es) of one step with the prefill projection cut to {PR} of 8192 rows and "
+                       f"both LM-head calls to {LR} of 151936 rows (other calls whole); fp64 NumPy; "
+                       f"{dt:.1f} s wall"),
+            "seconds": round(dt, 2)}
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    try:
+        d = json.load(open(PROFILE_COUNTERS))
+        src = hashlib.sha256(open(DOMINANT_SRC, "rb").read()).hexdigest()
+        if d.get("source_sha256") != src:
+            return None
+        return d.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ring", type=int, default=8, help="rotating copies of each small weight set")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-call", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="also time a plain 1 GiB copy (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the decode hot path here runs on a single MI355X; "
+              f"--gpus {args.gpus} (WORLD_SIZE {world}) is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hyper_connections_amd as hca
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    hca.lib()                                 # fails loudly when the HIP library is not built
+    nbytes = algorithmic_bytes()
+    step_bytes = sum(nbytes.values())
+
+    W = build_workload(torch, hca, synth, args.ring)
+    calls = prepare_calls(hca, W, args.ring)
+
+    for i in range(args.warmup):
+        step(calls, i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(calls, args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (wall / args.steps) / 1e9
+    dom_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    print(f"[bench] {args.steps} steps, {ms_per_step:.3f} ms/step, {value:.1f} GB/s; lmhead1 {dom_us:.2f} us",
+          file=sys.stderr, flush=True)
+
+    dom_ach = nbytes["lmhead1"] / dom_us / 1e3
+    roofline = {"bound": "hbm", "achieved": round(dom_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
+                "kernel": "k_gemv_m1_reg<5,f32,argmax> (LM head 151936 x 2560, M=1)",
+                "algorithmic_bytes_per_launch": nbytes["lmhead1"], "avg_launch_us": round(dom_us, 2)}
+
+    per_call = None if args.no_per_call else per_call_pass(torch, calls, nbytes, iters=100)
+    probe = copy_probe(torch) if args.copy_probe else None
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(synth)
+
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) and us/call for INT4 dequant GEMV + MoE decode",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4-affine weights, f16 operands, f32 accumulate", "data": "synthetic (seeded)",
+        "config": {"workload": "decode hot-path step: gemv 2560x2560 M=1; hc read+inject C=4 H=2560 R=320; "
+                               "moe E=256 top-8 hidden 2560 inter 512 + shared; prefill M=128 N=8192 K=2560; "
+                               "lm head 151936x2560 M=1 and M=8 with argmax",
+                   "step_bytes": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+                   "parallelism": "1 GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "calls": per_call,
+    }
+    if probe:
+        line["copy_probe"] = probe
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -179,11 +179,12 @@ class Int4Experts:
 _ws_cache = {}
 
 
-def _workspace(nbytes: int, device):
+def _workspace(nbytes: int, device, kind: str = "scratch"):
+    """Per (device, stream, kind) workspace, grown on demand."""
     torch = _torch()
     if nbytes == 0:
         return None
-    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream, kind)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -204,7 +205,7 @@ def dequant_gemv(w: Int4Weight, x, y=None, out_dtype=None, argmax=False, stream=
         y = torch.empty((m, w.rows), dtype=out_dtype, device=x.device)
     _need(y, out_dtype, "y", m * w.rows)
     am = torch.empty(m, dtype=torch.int32, device=x.device) if argmax else None
-    ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device) if argmax else None
+    ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device, "argmax") if argmax else None
     d = w.desc()
     _check(lib().decodehp_dequant_gemv(ctypes.byref(d), x2.data_ptr(), m, y.data_ptr(),
                                        DHP_F32 if out_dtype == torch.float32 else DHP_F16,
@@ -297,3 +298,68 @@ def hc_inject(wide, out, inject_w, C: int, H: int, stream=None):
     _need(inject_w, torch.float32, "inject_w", C)
     _check(lib().decodehp_hc_inject(wide.data_ptr(), out.data_ptr(), inject_w.data_ptr(), C, H, _stream(stream)))
     return wide
+
+
+# --------------------------------------------------------------------------- prepared calls
+
+class PreparedCall:
+    """One entry-point call with every argument marshalled up front; calling it only crosses
+    the C boundary (for launch loops where per-call Python work would starve the GPU).
+    Holds references to every tensor and descriptor it points at."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _check(rc)
+
+
+def prepare_gemv(w: Int4Weight, x, y, argmax=None, stream=None) -> PreparedCall:
+    torch = _torch()
+    x2 = x.reshape(-1, w.cols)
+    m = x2.shape[0]
+    _need(x2, torch.float16, "x")
+    _need(y, y.dtype, "y", m * w.rows)
+    ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device, "argmax") if argmax is not None else None
+    d = w.desc()
+    args = (ctypes.byref(d), x2.data_ptr(), m, y.data_ptr(), DHP_F32 if y.dtype == torch.float32 else DHP_F16,
+            _ptr(argmax), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    return PreparedCall(lib().decodehp_dequant_gemv, args, (d, x2, y, argmax, ws, w))
+
+
+def prepare_gemm_batched(w: Int4Weight, x, y, stream=None) -> PreparedCall:
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(y, torch.float16, "y", x.shape[0] * w.rows)
+    d = w.desc()
+    args = (ctypes.byref(d), x.data_ptr(), x.shape[0], y.data_ptr(), _stream(stream))
+    return PreparedCall(lib().decodehp_dequant_gemm_batched, args, (d, x, y, w))
+
+
+def prepare_moe(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k, out, ids,
+                weights, fp16_boundary=False, stream=None) -> PreparedCall:
+    torch = _torch()
+    rdt = DHP_BF16 if router.dtype == torch.int16 else DHP_F32
+    ws = _workspace(workspace_bytes(DHP_OP_MOE_DECODE, gate.count, top_k, gate.rows), x.device)
+    descs = (gate.desc(), up.desc(), down.desc(), shared_gate.desc(), shared_up.desc(), shared_down.desc())
+    args = (x.data_ptr(), router.data_ptr(), rdt, shared_gate_row.data_ptr(), *[ctypes.byref(d) for d in descs],
+            top_k, DHP_MOE_FP16_BOUNDARY if fp16_boundary else 0, out.data_ptr(), ids.data_ptr(),
+            weights.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    return PreparedCall(lib().decodehp_moe_decode, args, (descs, x, router, shared_gate_row, out, ids, weights, ws,
+                                                         gate, up, down, shared_gate, shared_up, shared_down))
+
+
+def prepare_hc_read(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps=1e-6, stream=None) -> PreparedCall:
+    ws = _workspace(workspace_bytes(DHP_OP_HC_READ, C, down.rows), raw.device)
+    descs = (down.desc(), up.desc(), inject.desc() if inject is not None else None)
+    args = (raw.data_ptr(), hc_norm.data_ptr(), C, H, eps, ctypes.byref(descs[0]), ctypes.byref(descs[1]),
+            ctypes.byref(descs[2]) if descs[2] is not None else None, mixed.data_ptr(), _ptr(inject_w), _ptr(ws),
+            0 if ws is None else ws.numel(), _stream(stream))
+    return PreparedCall(lib().decodehp_hc_read, args, (descs, raw, hc_norm, mixed, inject_w, ws, down, up, inject))
+
+
+def prepare_hc_inject(wide, out, inject_w, C, H, stream=None) -> PreparedCall:
+    args = (wide.data_ptr(), out.data_ptr(), inject_w.data_ptr(), C, H, _stream(stream))
+    return PreparedCall(lib().decodehp_hc_inject, args, (wide, out, inject_w))

@@ -110,12 +110,38 @@ DHP_DEV float dot32_f32(const u32x4 c, const float* x) {
     return d;
 }
 
-// Sum across `width` consecutive lanes (width a power of two <= 64); every lane of the
-// group receives the same total, summed in the same tree order for every group.
-template <int WIDTH>
+// Cross-lane data movement with DPP (VALU-speed, no LDS round trip). Within each 16-lane
+// row: XOR1 and XOR2 are quad permutes, then the half-row and row mirrors pair lanes across
+// 4- and 8-lane boundaries. After the levels for width W every lane of an aligned W-lane
+// group holds the same combination (addition is commutative, so partners agree bitwise).
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // reverse within each 8 lanes
+constexpr int DPP_MIRROR = 0x140;       // reverse within each 16 lanes
+
+template <int CTRL>
+DHP_DEV float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+DHP_DEV int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+DHP_DEV float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned groups of W lanes (W in 2, 4, 8, 16, 64), starting at level FROM (a group
+// of FROM lanes already holds equal values). W = 64 returns the wave total, uniform.
+template <int W, int FROM = 1>
 DHP_DEV float group_sum(float v) {
-#pragma unroll
-    for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 64, "group width");
+    if constexpr (FROM <= 1 && W >= 2) v += dpp_f<DPP_XOR1>(v);
+    if constexpr (FROM <= 2 && W >= 4) v += dpp_f<DPP_XOR2>(v);
+    if constexpr (FROM <= 4 && W >= 8) v += dpp_f<DPP_HALF_MIRROR>(v);
+    if constexpr (FROM <= 8 && W >= 16) v += dpp_f<DPP_MIRROR>(v);
+    if constexpr (W == 64)
+        v = (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
     return v;
 }
 
@@ -125,6 +151,31 @@ DHP_DEV float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 // Argmax order: larger value first, lower index first among equal values.
 DHP_DEV bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
+}
+
+template <int CTRL>
+DHP_DEV void best_step(float& v, int& i) {
+    const float ov = dpp_f<CTRL>(v);
+    const int oi = dpp_i<CTRL>(i);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Wave-wide best (value, index); every lane returns the same pair.
+DHP_DEV void wave_best(float& v, int& i) {
+    best_step<DPP_XOR1>(v, i);
+    best_step<DPP_XOR2>(v, i);
+    best_step<DPP_HALF_MIRROR>(v, i);
+    best_step<DPP_MIRROR>(v, i);
+    float bv = readlane_f(v, 0);
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 16; r < 64; r += 16) {
+        const float ov = readlane_f(v, r);
+        const int oi = __builtin_amdgcn_readlane(i, r);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    v = bv;
+    i = bi;
 }
 
 // ------------------------------------------------------------------ host side
@@ -154,3 +205,4 @@ int launch_moe(const void* x, const void* router, int router_f32, const void* sg
 size_t dhp_argmax_part_stride(int32_t n_rows, int32_t m);
 int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax,
                      void* ws, size_t ws_part_stride, hipStream_t s);
+hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s);

@@ -19,7 +19,7 @@
 //    each keeping the whole tile in accumulators; the four partial tiles are summed through
 //    LDS in a fixed order (3, 2, 1, 0), so results are deterministic.
 //  * The epilogue writes fp16 or fp32 and, for the GEMV arm, a per-block argmax partial per
-//    row (reduced by the same final kernel the M=1 path uses).
+//    row, reduced by the same small final kernel the M=1 path uses.
 #include "dhp_internal.hpp"
 
 #include <math.h>
@@ -173,12 +173,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(
         }
     }
     if constexpr (ARGMAX) {
-#pragma unroll
-        for (int o = TPR / 2; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
+        static_assert(TPR == 8 || TPR == 4, "threads per row");
+        best_step<DPP_XOR1>(bv, bi);
+        best_step<DPP_XOR2>(bv, bi);
+        if constexpr (TPR == 8) best_step<DPP_HALF_MIRROR>(bv, bi);
         if (threadIdx.x % TPR == 0 && m < M) {
             part_v[(size_t)m * gridDim.x + blockIdx.x] = bv;
             part_i[(size_t)m * gridDim.x + blockIdx.x] = bi;
@@ -206,8 +204,6 @@ hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4
 // Argmax partial count of the MFMA path for N output columns.
 int dhp_gemm_blocks_n(int N) { return (N + BN - 1) / BN; }
 
-hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s);
-
 int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax,
                      void* ws, size_t ws_part_stride, hipStream_t s) {
     const int N = w->rows;
@@ -216,6 +212,7 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     const dim3 grid((unsigned)dhp_gemm_blocks_n(N), (unsigned)((M + rows - 1) / rows));
     float* pv = argmax ? static_cast<float*>(ws) : nullptr;
     int* pi = argmax ? reinterpret_cast<int*>(static_cast<char*>(ws) + ws_part_stride) : nullptr;
+    if (argmax && grid.y != 1) return dhp_fail(DHP_ERR_UNSUPPORTED, "argmax with m=%d", M);
     const hipError_t e = (MT == 1) ? launch_mt<1>(y_f32, argmax != nullptr, grid, s, w, x, M, y, pv, pi)
                                    : launch_mt<2>(y_f32, argmax != nullptr, grid, s, w, x, M, y, pv, pi);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));

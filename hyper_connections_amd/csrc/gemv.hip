@@ -1,5 +1,6 @@
 // M=1 INT4-affine dequantizing GEMV (decode projections and the LM head) and the
-// deterministic two-stage argmax over its fp32 outputs.
+// deterministic two-stage argmax over its fp32 outputs (per-block partials, then one small
+// reduction kernel per output row).
 //
 // "src/real_forward.rs" (turbospark-runtime 0.3.0), module doc: dequant_int4_gemv_simd
 // streams resident INT4-affine weights/scales/biases with nothing staged per dispatch.
@@ -186,12 +187,7 @@ __global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ 
     int bi = INT_MAX;
     for (int i = threadIdx.x; i < nparts; i += blockDim.x)
         if (better(pv[i], pi[i], bv, bi)) { bv = pv[i]; bi = pi[i]; }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
+    wave_best(bv, bi);
     __shared__ float sv[4];
     __shared__ int si[4];
     if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }

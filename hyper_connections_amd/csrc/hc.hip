@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256) void k_hc_up(
     const int c = lane16 / LPRU;
     const int sub = lane16 % LPRU;
     const int h = blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4);
-    if (h >= H) return;                   // whole 16-lane groups leave together
-    const size_t urow = (size_t)c * H + h;
+    const bool live = h < H;              // whole 16-lane groups share h; no early exit before the DPP sums
+    const size_t urow = (size_t)c * H + (live ? h : 0);
     const u32x4* cr = ucodes + urow * CHR;
     const uint16_t* sr = uscales + urow * G;
     const uint16_t* br = ubiases + urow * G;
@@ -153,10 +153,8 @@ __global__ __launch_bounds__(256) void k_hc_up(
     }
     acc = group_sum<LPRU>(acc);
     const float n = (float)raw[urow] * inv_rms[c] * bf16_to_f32(gamma[urow]);
-    float p = sigmoid_f(acc) * n;
-#pragma unroll
-    for (int o = LPRU; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
-    if (lane16 == 0) mixed[h] = (_Float16)(p / (float)C);
+    const float p = group_sum<16, LPRU>(sigmoid_f(acc) * n);     // over the C streams
+    if (lane16 == 0 && live) mixed[h] = (_Float16)(p / (float)C);
 }
 
 // wide[c*H + h] = fp16(wide + out[h] * w[c]); 8 elements per thread, H % 8 == 0.

@@ -54,33 +54,41 @@ struct MoeArgs {
     float* weights;
 };
 
-// gate and up dots of one expert row pair (K = hidden = 512 * CPL) for the 16-lane group
-// whose lane index is j; returns silu(gate) * up in every lane of the group.
+// Registers of one (gate row, up row) pair for the 16-lane group whose lane index is j.
 template <int CPL>
-DHP_DEV float gate_up_pair(const u32x4* gc, const uint16_t* gs, const uint16_t* gb,
-                           const u32x4* uc, const uint16_t* us, const uint16_t* ub, int row, int j,
-                           const h2 (*xp)[16], const float* xs) {
-    constexpr int CH = LPR * CPL;
-    constexpr int G = CH / 2;
+struct PairRegs {
     u32x4 cg[CPL], cu[CPL];
     uint32_t sg[CPL], bg[CPL], su[CPL], bu[CPL];
+};
+
+// Issue the code/scale/bias loads of gate row `row` and up row `row` (K = hidden = 512 * CPL).
+template <int CPL>
+DHP_DEV void load_pair(PairRegs<CPL>& p, const u32x4* gc, const uint16_t* gs, const uint16_t* gb,
+                       const u32x4* uc, const uint16_t* us, const uint16_t* ub, int row, int j) {
+    constexpr int CH = LPR * CPL;
+    constexpr int G = CH / 2;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = j + LPR * i;
-        cg[i] = __builtin_nontemporal_load(gc + (size_t)row * CH + ch);
-        cu[i] = __builtin_nontemporal_load(uc + (size_t)row * CH + ch);
-        sg[i] = gs[(size_t)row * G + (ch >> 1)];
-        bg[i] = gb[(size_t)row * G + (ch >> 1)];
-        su[i] = us[(size_t)row * G + (ch >> 1)];
-        bu[i] = ub[(size_t)row * G + (ch >> 1)];
+        p.cg[i] = __builtin_nontemporal_load(gc + (size_t)row * CH + ch);
+        p.cu[i] = __builtin_nontemporal_load(uc + (size_t)row * CH + ch);
+        p.sg[i] = gs[(size_t)row * G + (ch >> 1)];
+        p.bg[i] = gb[(size_t)row * G + (ch >> 1)];
+        p.su[i] = us[(size_t)row * G + (ch >> 1)];
+        p.bu[i] = ub[(size_t)row * G + (ch >> 1)];
     }
+}
+
+// silu(gate . x) * (up . x), the same value in every lane of the 16-lane group.
+template <int CPL>
+DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* xs) {
     float ag = 0.0f, au = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        ag = __builtin_fmaf(bf16_to_f32(sg[i]), dot32_f16(cg[i], xp[i]), ag);
-        ag = __builtin_fmaf(bf16_to_f32(bg[i]), xs[i], ag);
-        au = __builtin_fmaf(bf16_to_f32(su[i]), dot32_f16(cu[i], xp[i]), au);
-        au = __builtin_fmaf(bf16_to_f32(bu[i]), xs[i], au);
+        ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_f16(p.cg[i], xp[i]), ag);
+        ag = __builtin_fmaf(bf16_to_f32(p.bg[i]), xs[i], ag);
+        au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_f16(p.cu[i], xp[i]), au);
+        au = __builtin_fmaf(bf16_to_f32(p.bu[i]), xs[i], au);
     }
     ag = group_sum<LPR>(ag);
     au = group_sum<LPR>(au);
@@ -144,42 +152,44 @@ __global__ __launch_bounds__(64) void k_moe_router(MoeArgs a) {
     }
     const int j = lane % LPR;
     const int row = (b - a.E - 1) * 4 + lane / LPR;
-    if (row >= a.inter) return;           // whole 16-lane groups leave together
+    const bool live = row < a.inter;      // 16-lane groups share a row; all lanes stay for the DPP sums
+    PairRegs<CPL> p;
+    load_pair<CPL>(p, a.sg_codes, a.sg_scales, a.sg_biases, a.su_codes, a.su_scales, a.su_biases,
+                   live ? row : 0, j);
     h2 xp[CPL][16];
     float xs[CPL];
     load_x_regs<CPL>(a.x, j, xp, xs);
-    const float v = gate_up_pair<CPL>(a.sg_codes, a.sg_scales, a.sg_biases, a.su_codes, a.su_scales,
-                                      a.su_biases, row, j, xp, xs);
-    if (j == 0) a.act[(size_t)a.top_k * a.inter + row] = v;
+    const float v = pair_act<CPL>(p, xp, xs);
+    if (j == 0 && live) a.act[(size_t)a.top_k * a.inter + row] = v;
 }
 
-// Top-k of the E logits by one wave (values larger first, lower index first among equals).
-// Every lane returns the same ids and logits.
-DHP_DEV void wave_topk(const float* logits, int E, int k, int* ids, float* vals) {
+// The first `rounds` entries of the top-k of the E logits, by one wave: each round takes the
+// wave-wide best untaken (logit, expert) -- larger logit first, lower expert index first among
+// equal logits -- with DPP butterflies and four readlanes. Every lane returns the same ids.
+DHP_DEV void wave_topk(const float* logits, int E, int rounds, int* ids, float* vals) {
     const int lane = threadIdx.x & 63;
     constexpr int PER = MAX_E / 64;
+    const int per = (E + 63) >> 6;
     float v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        const float l = (e < E) ? logits[e] : -INFINITY;
+        const float l = (i < per && e < E) ? logits[e] : -INFINITY;
         v[i] = (l == l) ? l : -INFINITY;   // a NaN logit ranks as -inf, so ids stay valid
     }
     int taken = 0;                         // bit i: v[i] already selected
-    for (int r = 0; r < k; ++r) {
+#pragma unroll
+    for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
+        if (r >= rounds) break;
         float bv = -INFINITY;
         int bi = INT_MAX;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
+            if (i >= per) break;
             const int e = lane + 64 * i;
             if (e < E && !((taken >> i) & 1) && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
+        wave_best(bv, bi);
         ids[r] = bi;
         vals[r] = bv;
         if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
@@ -194,27 +204,18 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     float xs[CPL];
     load_x_regs<CPL>(a.x, j, xp, xs);      // independent of routing: issue first
 
+    // a block only needs the ranks up to its last (slot, row) pair; block 0 also needs all
+    // top_k of them for the softmax weights
+    const int last_pair = min(blockIdx.x * 4 + 3, a.top_k * a.inter - 1);
+    const int rounds = (blockIdx.x == 0) ? a.top_k : last_pair / a.inter + 1;
     int ids[DHP_MOE_MAX_TOP_K];
     float vals[DHP_MOE_MAX_TOP_K];
-    wave_topk(a.logits, a.E, a.top_k, ids, vals);
-
-    if (blockIdx.x == 0 && lane == 0) {
-        float w[DHP_MOE_MAX_TOP_K];
-        float sum = 0.0f;
-        for (int r = 0; r < a.top_k; ++r) {
-            w[r] = __expf(vals[r] - vals[0]);
-            sum += w[r];
-        }
-        for (int r = 0; r < a.top_k; ++r) {
-            a.ids[r] = ids[r];
-            a.weights[r] = w[r] / sum;
-        }
-    }
+    wave_topk(a.logits, a.E, rounds, ids, vals);
 
     const int pair = blockIdx.x * 4 + lane / LPR;      // (slot, row) flattened
-    if (pair >= a.top_k * a.inter) return;
-    const int slot = pair / a.inter;
-    const int row = pair % a.inter;
+    const bool live = pair < a.top_k * a.inter;
+    const int slot = live ? pair / a.inter : 0;
+    const int row = live ? pair % a.inter : 0;
     int e = ids[0];
 #pragma unroll
     for (int r = 1; r < DHP_MOE_MAX_TOP_K; ++r)
@@ -225,14 +226,38 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     const auto* uc = reinterpret_cast<const u32x4*>(a.u_codes + (size_t)e * a.u_cstride);
     const auto* us = reinterpret_cast<const uint16_t*>(a.u_scales + (size_t)e * a.u_sstride);
     const auto* ub = reinterpret_cast<const uint16_t*>(a.u_biases + (size_t)e * a.u_sstride);
-    const float v = gate_up_pair<CPL>(gc, gs, gb, uc, us, ub, row, j, xp, xs);
-    if (j == 0) a.act[(size_t)slot * a.inter + row] = v;
+    PairRegs<CPL> p;
+    load_pair<CPL>(p, gc, gs, gb, uc, us, ub, row, j);
+
+    if (blockIdx.x == 0 && lane == 0) {
+        float w[DHP_MOE_MAX_TOP_K];
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
+            w[r] = (r < a.top_k) ? __expf(vals[r] - vals[0]) : 0.0f;
+            sum += w[r];
+        }
+#pragma unroll
+        for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
+            if (r < a.top_k) {
+                a.ids[r] = ids[r];
+                a.weights[r] = w[r] / sum;
+            }
+        }
+    }
+
+    const float v = pair_act<CPL>(p, xp, xs);
+    if (j == 0 && live) a.act[(size_t)slot * a.inter + row] = v;
 }
 
 // 16 lanes per output element h, RH elements per 16-lane group; a block of 64 lanes covers
-// 4 * RH consecutive outputs. Down rows have K = inter; lane j takes chunks j, j+16, ...
+// 4 * RH consecutive outputs. Down rows have K = inter; lane j takes chunks j + 16 i (i < CPLD).
+// Every code, scale and bias load of all (top_k + 1) experts is issued before any arithmetic,
+// then the activations are staged in LDS while those loads are in flight.
 constexpr int RH = 2;
+constexpr int NSLOT = DHP_MOE_MAX_TOP_K + 1;
 
+template <int CPLD>
 __global__ __launch_bounds__(64) void k_moe_phase2(MoeArgs a) {
     extern __shared__ float lds_act[];     // [(top_k + 1) * inter] then chunk sums
     const int lane = threadIdx.x;
@@ -242,52 +267,74 @@ __global__ __launch_bounds__(64) void k_moe_phase2(MoeArgs a) {
     const int G = a.inter >> 6;
     const int h0 = (blockIdx.x * 4 + lane / LPR) * RH;
 
-    // stage the activations of every slot
+    u32x4 c[NSLOT][RH][CPLD];
+    uint32_t sv[NSLOT][RH][CPLD], bv[NSLOT][RH][CPLD];
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) {
+        if (slot < nslot) {
+            const u32x4* dc;
+            const uint16_t* ds;
+            const uint16_t* db;
+            if (slot == a.top_k) {
+                dc = a.sd_codes; ds = a.sd_scales; db = a.sd_biases;
+            } else {
+                const int e = a.ids[slot];
+                dc = reinterpret_cast<const u32x4*>(a.d_codes + (size_t)e * a.d_cstride);
+                ds = reinterpret_cast<const uint16_t*>(a.d_scales + (size_t)e * a.d_sstride);
+                db = reinterpret_cast<const uint16_t*>(a.d_biases + (size_t)e * a.d_sstride);
+            }
+#pragma unroll
+            for (int r = 0; r < RH; ++r) {
+                const int h = min(h0 + r, a.hidden - 1);
+#pragma unroll
+                for (int i = 0; i < CPLD; ++i) {
+                    const int ch = min(j + LPR * i, CH - 1);
+                    c[slot][r][i] = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
+                    sv[slot][r][i] = ds[(size_t)h * G + (ch >> 1)];
+                    bv[slot][r][i] = db[(size_t)h * G + (ch >> 1)];
+                }
+            }
+        }
+    }
+
+    // stage the activations of every slot, and per-chunk sums
     const int n = nslot * a.inter;
     float* act_sum = lds_act + n;
     for (int i = lane * 4; i < n; i += 64 * 4)
         *reinterpret_cast<f4v*>(lds_act + i) = *reinterpret_cast<const f4v*>(a.act + i);
     __syncthreads();
-    for (int c = lane; c < nslot * CH; c += 64) {
+    for (int q = lane; q < nslot * CH; q += 64) {
         float s = 0.0f;
-        for (int i = 0; i < 32; ++i) s += lds_act[32 * c + i];
-        act_sum[c] = s;
+        for (int i = 0; i < 32; ++i) s += lds_act[32 * q + i];
+        act_sum[q] = s;
     }
     __syncthreads();
 
     float racc[RH], sacc[RH];
 #pragma unroll
     for (int r = 0; r < RH; ++r) { racc[r] = 0.0f; sacc[r] = 0.0f; }
-    for (int slot = 0; slot < nslot; ++slot) {
-        const bool shared = slot == a.top_k;
-        const u32x4* dc;
-        const uint16_t* ds;
-        const uint16_t* db;
-        float wgt = 1.0f;
-        if (shared) {
-            dc = a.sd_codes; ds = a.sd_scales; db = a.sd_biases;
-        } else {
-            const int e = a.ids[slot];
-            dc = reinterpret_cast<const u32x4*>(a.d_codes + (size_t)e * a.d_cstride);
-            ds = reinterpret_cast<const uint16_t*>(a.d_scales + (size_t)e * a.d_sstride);
-            db = reinterpret_cast<const uint16_t*>(a.d_biases + (size_t)e * a.d_sstride);
-            wgt = a.weights[slot];
-        }
-        const float* av = lds_act + (size_t)slot * a.inter;
-        const float* asum = act_sum + (size_t)slot * CH;
 #pragma unroll
-        for (int r = 0; r < RH; ++r) {
-            const int h = h0 + r;
-            if (h >= a.hidden) break;
-            float p = 0.0f;
-            for (int ch = j; ch < CH; ch += LPR) {
-                const u32x4 c = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
-                const float d = dot32_f32(c, av + 32 * ch);
-                p = __builtin_fmaf(bf16_to_f32(ds[(size_t)h * G + (ch >> 1)]), d, p);
-                p = __builtin_fmaf(bf16_to_f32(db[(size_t)h * G + (ch >> 1)]), asum[ch], p);
+    for (int slot = 0; slot < NSLOT; ++slot) {
+        if (slot < nslot) {
+            const bool shared = slot == a.top_k;
+            const float wgt = shared ? 1.0f : a.weights[slot];
+            const float* av = lds_act + (size_t)slot * a.inter;
+            const float* asum = act_sum + (size_t)slot * CH;
+#pragma unroll
+            for (int r = 0; r < RH; ++r) {
+                float p = 0.0f;
+#pragma unroll
+                for (int i = 0; i < CPLD; ++i) {
+                    const int ch = j + LPR * i;
+                    if (ch < CH) {
+                        const float d = dot32_f32(c[slot][r][i], av + 32 * ch);
+                        p = __builtin_fmaf(bf16_to_f32(sv[slot][r][i]), d, p);
+                        p = __builtin_fmaf(bf16_to_f32(bv[slot][r][i]), asum[ch], p);
+                    }
+                }
+                if (shared) sacc[r] += p;
+                else racc[r] = __builtin_fmaf(wgt, p, racc[r]);
             }
-            if (shared) sacc[r] += p;
-            else racc[r] = __builtin_fmaf(wgt, p, racc[r]);
         }
     }
     const float sg = sigmoid_f(a.gate_logit[0]);
@@ -316,8 +363,9 @@ hipError_t launch_all(const MoeArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)(a.top_k + 1) * (a.inter + a.inter / 32) * sizeof(float);
-    const int per_block = 4 * RH;
-    hipLaunchKernelGGL(k_moe_phase2, dim3((a.hidden + per_block - 1) / per_block), dim3(64), lds, s, a);
+    const dim3 g2((a.hidden + 4 * RH - 1) / (4 * RH));
+    if (a.inter <= 512) hipLaunchKernelGGL(k_moe_phase2<1>, g2, dim3(64), lds, s, a);
+    else hipLaunchKernelGGL(k_moe_phase2<2>, g2, dim3(64), lds, s, a);
     return hipGetLastError();
 }
 

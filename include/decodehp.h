@@ -100,7 +100,8 @@ typedef struct dhp_int4_experts {
  *   argmax  : nullable int32 [m]; when set, argmax[r] = lowest n with the largest fp32 value
  *             of row r (computed before any fp16 rounding of y).
  *   ws      : workspace of decodehp_workspace_bytes(DHP_OP_GEMV_ARGMAX, N, m, 0) bytes when
- *             argmax is set (may be NULL otherwise). Scratch only; contents undefined after.
+ *             argmax is set (may be NULL otherwise), 16-byte aligned. Scratch only: contents
+ *             are undefined after the call; calls sharing one buffer must not overlap.
  * Errors: -1 null/size, -2 K % 64, K > 16384, group != 64, m outside 1..16, y_dtype, -3 alignment,
  *         -4 workspace, -5 device, -6 launch.
  */

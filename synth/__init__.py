@@ -173,10 +173,13 @@ def prefill_workload(seed: int = 0, m: int = 128, n: int = 8192, k: int = 2560):
     return {"x": x, "w": w}
 
 
+def lmhead_x(seed: int = 0, m: int = 1, k: int = 2560) -> np.ndarray:
+    """LM-head input rows fp16[m x k]; their own stream, so they can be drawn without the weight."""
+    return normal_f16(rng_for(LMHEAD_151936, seed, m), (m, k))
+
+
 def lmhead_workload(seed: int = 0, m: int = 1, n: int = 151936, k: int = 2560):
     """LM head: hidden fp16[m x k]; INT4 weight [n x k]. The weight stream does not depend on m."""
     rng = rng_for(LMHEAD_151936, seed)
     w = int4_tensor(rng, n, k)
-    xr = rng_for(LMHEAD_151936, seed, m)
-    x = normal_f16(xr, (m, k))
-    return {"x": x, "w": w}
+    return {"x": lmhead_x(seed, m, k), "w": w}
