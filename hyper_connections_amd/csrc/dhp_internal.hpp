@@ -22,22 +22,34 @@ DHP_DEV uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 DHP_DEV float bf16_to_f32(uint32_t b16) { return __builtin_bit_cast(float, b16 << 16); }
 DHP_DEV float f16_to_f32(_Float16 h) { return (float)h; }
 
+// Constants of the nibble unpack, held in VGPRs. An AND-OR with two 32-bit constants needs
+// one of them in a register (one literal per VOP3 instruction); the empty asm hides their values
+// so the compiler keeps them in registers and emits a single v_and_or_b32 per pair of codes
+// instead of a separate AND and OR. Create once per kernel, outside loops.
+struct NibConsts {
+    uint32_t lo, hi, magic;
+};
+DHP_DEV NibConsts nib_consts() {
+    NibConsts k{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+    asm("" : "+v"(k.lo), "+v"(k.hi), "+v"(k.magic));
+    return k;
+}
+
 // Eight INT4 codes k0..k7 of one 32-bit word (byte j holds k=2j low, k=2j+1 high) become
 // four exact fp16 pairs in the order (k0,k4) (k1,k5) (k2,k6) (k3,k7).
 //
 // A nibble OR-ed into the mantissa of fp16 1024.0 (0x6400, ulp 1) gives 1024 + q exactly;
 // a nibble sitting four bits higher gives 1024 + 16 q, and (1024 + 16 q) / 16 - 64 = q.
 // Both halves of a 32-bit word are handled at once, so one AND-OR makes two codes.
-DHP_DEV void unpack8(uint32_t w, h2 q[4]) {
-    const uint32_t MAGIC = 0x64006400u;
+DHP_DEV void unpack8(uint32_t w, h2 q[4], const NibConsts& k) {
     const uint32_t w8 = w >> 8;
     const h2 c1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
     const h2 c64 = {(_Float16)64.0f, (_Float16)64.0f};
     const h2 c16th = {(_Float16)0.0625f, (_Float16)0.0625f};
-    q[0] = as_h2((w & 0x000F000Fu) | MAGIC) - c1024;
-    q[1] = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | MAGIC), c16th, -c64);
-    q[2] = as_h2((w8 & 0x000F000Fu) | MAGIC) - c1024;
-    q[3] = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | MAGIC), c16th, -c64);
+    q[0] = as_h2((w & k.lo) | k.magic) - c1024;
+    q[1] = __builtin_elementwise_fma(as_h2((w & k.hi) | k.magic), c16th, -c64);
+    q[2] = as_h2((w8 & k.lo) | k.magic) - c1024;
+    q[3] = __builtin_elementwise_fma(as_h2((w8 & k.hi) | k.magic), c16th, -c64);
 }
 
 // Eight consecutive fp16 activations (as four 32-bit words, x0x1 x2x3 x4x5 x6x7) rearranged
@@ -51,25 +63,25 @@ DHP_DEV void permute8(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, h2 out
 
 // sum over 32 codes of q * x, fp32 accumulate: c holds 32 codes (16 bytes), xp the 16
 // permuted activation pairs for the same 32 positions.
-DHP_DEV float dot32_f16(const u32x4 c, const h2* xp) {
+DHP_DEV float dot32_f16(const u32x4 c, const h2* xp, const NibConsts& k) {
     float d = 0.0f;
     h2 q[4];
-    unpack8(c.x, q);
+    unpack8(c.x, q, k);
     d = __builtin_amdgcn_fdot2(q[0], xp[0], d, false);
     d = __builtin_amdgcn_fdot2(q[1], xp[1], d, false);
     d = __builtin_amdgcn_fdot2(q[2], xp[2], d, false);
     d = __builtin_amdgcn_fdot2(q[3], xp[3], d, false);
-    unpack8(c.y, q);
+    unpack8(c.y, q, k);
     d = __builtin_amdgcn_fdot2(q[0], xp[4], d, false);
     d = __builtin_amdgcn_fdot2(q[1], xp[5], d, false);
     d = __builtin_amdgcn_fdot2(q[2], xp[6], d, false);
     d = __builtin_amdgcn_fdot2(q[3], xp[7], d, false);
-    unpack8(c.z, q);
+    unpack8(c.z, q, k);
     d = __builtin_amdgcn_fdot2(q[0], xp[8], d, false);
     d = __builtin_amdgcn_fdot2(q[1], xp[9], d, false);
     d = __builtin_amdgcn_fdot2(q[2], xp[10], d, false);
     d = __builtin_amdgcn_fdot2(q[3], xp[11], d, false);
-    unpack8(c.w, q);
+    unpack8(c.w, q, k);
     d = __builtin_amdgcn_fdot2(q[0], xp[12], d, false);
     d = __builtin_amdgcn_fdot2(q[1], xp[13], d, false);
     d = __builtin_amdgcn_fdot2(q[2], xp[14], d, false);

@@ -7,19 +7,22 @@
 // Metal kernels (per-thread accumulator arrays; a simdgroup-matrix variant) are prior art;
 // this is a gfx950 design around v_mfma_f32_32x32x16_f16:
 //
-//  * The weight tile is the B operand. Lane l of a wave owns weight row n0 + (l % 32) and a
-//    32-wide k slice (l / 32 picks the half of a 64-k block): one 16-byte load holds its codes
-//    for four MFMA steps, and the group's scale and bias are one load each. Codes become fp16
-//    q*s + b in registers (the nibble trick of unpack8, then one packed fma): there is no LDS
-//    staging of weights at all.
-//  * The activation tile is the A operand, read from global memory with the same permutation
-//    of k inside each group of eight that the nibble unpack produces, so both operands agree
-//    on which k each register slot holds.
-//  * A block owns a 32*MT x 64 output tile. Its four waves split K (64-k blocks w, w+4, ...),
-//    each keeping the whole tile in accumulators; the four partial tiles are summed through
-//    LDS in a fixed order (3, 2, 1, 0), so results are deterministic.
-//  * The epilogue writes fp16 or fp32 and, for the GEMV arm, a per-block argmax partial per
-//    row, reduced by the same small final kernel the M=1 path uses.
+//  * A block owns a 32*MT x 64 output tile (activation rows x weight rows). Its four waves
+//    split K into four contiguous ranges of stages (S k-blocks of 64 each); each wave keeps the
+//    whole tile in its accumulators and works out of a private LDS region, so waves never wait
+//    for each other until the end.
+//  * Operands reach LDS through fully coalesced 16-byte loads (consecutive lanes walk one row's
+//    bytes), issued a stage ahead and parked in registers while the current stage computes.
+//    Reading MFMA fragments straight from row-major memory would touch 32 separate cache lines
+//    per instruction instead.
+//  * The weight tile is the B operand: lane l takes weight row l % 32 and a 32-wide k slice,
+//    turns its 16 bytes of codes into fp16 q*s+b in registers (the nibble trick of unpack8 and
+//    one packed fma) and feeds four MFMA steps. The activation tile is the A operand, read with
+//    the same permutation of k inside each group of eight, so both operands agree on which k
+//    each register slot holds.
+//  * The four partial tiles are summed through LDS in a fixed order (3, 2, 1, 0), so results
+//    are deterministic. The epilogue writes fp16 or fp32 and, for the GEMV arm, a per-block
+//    argmax partial per row, reduced by the same small final kernel the M=1 path uses.
 #include "dhp_internal.hpp"
 
 #include <math.h>
@@ -32,9 +35,9 @@ namespace {
 constexpr int BN = 64;         // output columns (weight rows) per block
 constexpr int LDW = BN + 4;    // LDS row pitch in floats
 
-DHP_DEV h8 dequant8(uint32_t w, h2 s2, h2 b2) {
+DHP_DEV h8 dequant8(uint32_t w, h2 s2, h2 b2, const NibConsts& k) {
     h2 q[4];
-    unpack8(w, q);
+    unpack8(w, q, k);
     const h2 p0 = __builtin_elementwise_fma(q[0], s2, b2);
     const h2 p1 = __builtin_elementwise_fma(q[1], s2, b2);
     const h2 p2 = __builtin_elementwise_fma(q[2], s2, b2);
@@ -48,13 +51,173 @@ DHP_DEV h8 permute_x8(u32x4 u) {
     return h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
-template <int MT, bool F32OUT, bool ARGMAX>
+// One wave's share of a block: output tile 32*MT (activation rows) x 64 (weight rows), and a
+// contiguous range of 64-k blocks walked in stages of S k-blocks. Each stage is fetched from
+// global memory with fully coalesced 16-byte loads (for S = 4, eight lanes cover one 128-byte
+// line of a weight row), parked in registers while the previous stage computes, then written
+// to this wave's private LDS region, from which the MFMA fragments are read. Row pitches carry
+// 16 extra bytes so consecutive rows start four banks apart.
+template <int MT, int S>
+struct WaveLds {
+    static constexpr int WP = 32 * S + 16;    // bytes per weight row (codes of S k-blocks)
+    static constexpr int XP = 128 * S + 16;   // bytes per activation row (64 * S halves)
+    static constexpr int SBP = S + 1;         // uint32 (scale | bias << 16) per weight row
+    static constexpr int W_BYTES = 64 * WP;
+    static constexpr int X_BYTES = 32 * MT * XP;
+    static constexpr int SB_BYTES = 64 * SBP * 4;
+    static constexpr int BYTES = W_BYTES + X_BYTES + SB_BYTES;
+    static constexpr int WL = 2 * S;          // 16-byte weight loads per lane per stage
+    static constexpr int XL = 4 * MT * S;     // 16-byte activation loads per lane per stage (max)
+};
+
+template <int MT, int S>
+struct StageRegs {
+    u32x4 w[WaveLds<MT, S>::WL];
+    u32x4 x[WaveLds<MT, S>::XL];
+    uint32_t sc[S], bi[S];
+};
+
+// Per-lane load and store addresses of a stage, computed once per wave (only the k offset
+// changes from stage to stage).
+template <int MT, int S>
+struct StagePlan {
+    const uint8_t* wsrc[WaveLds<MT, S>::WL];   // weight row start + byte offset of this lane's chunk
+    int wkb[WaveLds<MT, S>::WL];               // k-block of that chunk within a stage
+    int wdst[WaveLds<MT, S>::WL];              // LDS byte offset
+    const _Float16* xsrc[WaveLds<MT, S>::XL];
+    int xkb[WaveLds<MT, S>::XL];
+    int xdst[WaveLds<MT, S>::XL];              // -1: no store (padding row)
+    const uint16_t* ssrc;
+    const uint16_t* bsrc;
+    int xiters;
+};
+
+template <int MT, int S>
+DHP_DEV void stage_plan(StagePlan<MT, S>& p, int lane, const uint8_t* codes, const uint16_t* scales,
+                        const uint16_t* biases, const _Float16* X, int n0, int N, int m0, int xrows,
+                        int K, int KB) {
+    using L = WaveLds<MT, S>;
+    const size_t row_bytes = (size_t)K >> 1;
+#pragma unroll
+    for (int i = 0; i < L::WL; ++i) {
+        const int c = i * 64 + lane;
+        const int row = c / (2 * S), cc = c % (2 * S);
+        p.wsrc[i] = codes + (size_t)min(n0 + row, N - 1) * row_bytes + (cc & 1) * 16;
+        p.wkb[i] = cc >> 1;
+        p.wdst[i] = row * L::WP + cc * 16;
+    }
+    p.xiters = (xrows * 8 * S + 63) >> 6;
+#pragma unroll
+    for (int i = 0; i < L::XL; ++i) {
+        const int c = i * 64 + lane;
+        const int row = c / (8 * S), cc = c % (8 * S);
+        p.xsrc[i] = X + (size_t)(m0 + min(row, xrows - 1)) * K + (cc & 7) * 8;
+        p.xkb[i] = cc >> 3;
+        p.xdst[i] = (row < xrows) ? L::W_BYTES + row * L::XP + cc * 16 : -1;
+    }
+    const size_t n = (size_t)min(n0 + lane, N - 1);
+    p.ssrc = scales + n * KB;
+    p.bsrc = biases + n * KB;
+}
+
+// Global loads of the stage that starts at k-block kbs (k-blocks at or past kb1 are padding:
+// their addresses are clamped to the last real k-block and their scale and bias read as zero,
+// so they dequantize to exact zeros).
+template <int MT, int S>
+DHP_DEV void stage_load(StageRegs<MT, S>& r, const StagePlan<MT, S>& p, int kbs, int kb1, bool sb_vec) {
+    using L = WaveLds<MT, S>;
+#pragma unroll
+    for (int i = 0; i < L::WL; ++i)
+        r.w[i] = *reinterpret_cast<const u32x4*>(p.wsrc[i] + (size_t)min(kbs + p.wkb[i], kb1 - 1) * 32);
+#pragma unroll
+    for (int i = 0; i < L::XL; ++i)
+        if (i < p.xiters)
+            r.x[i] = *reinterpret_cast<const u32x4*>(p.xsrc[i] + (size_t)min(kbs + p.xkb[i], kb1 - 1) * 64);
+    if (sb_vec) {                            // S groups of this row in one aligned vector load each
+        if constexpr (S == 4) {
+            const uint2 sv = *reinterpret_cast<const uint2*>(p.ssrc + kbs);
+            const uint2 bv = *reinterpret_cast<const uint2*>(p.bsrc + kbs);
+            r.sc[0] = sv.x & 0xFFFFu; r.sc[1] = sv.x >> 16; r.sc[2] = sv.y & 0xFFFFu; r.sc[3] = sv.y >> 16;
+            r.bi[0] = bv.x & 0xFFFFu; r.bi[1] = bv.x >> 16; r.bi[2] = bv.y & 0xFFFFu; r.bi[3] = bv.y >> 16;
+        } else {
+            const uint32_t sv = *reinterpret_cast<const uint32_t*>(p.ssrc + kbs);
+            const uint32_t bv = *reinterpret_cast<const uint32_t*>(p.bsrc + kbs);
+            r.sc[0] = sv & 0xFFFFu; r.sc[1] = sv >> 16;
+            r.bi[0] = bv & 0xFFFFu; r.bi[1] = bv >> 16;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+            const int kb = min(kbs + q, kb1 - 1);
+            r.sc[q] = p.ssrc[kb];
+            r.bi[q] = p.bsrc[kb];
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+        if (kbs + q >= kb1) { r.sc[q] = 0u; r.bi[q] = 0u; }
+}
+
+template <int MT, int S>
+DHP_DEV void stage_store(const StageRegs<MT, S>& r, const StagePlan<MT, S>& p, uint8_t* lds, int lane) {
+    using L = WaveLds<MT, S>;
+#pragma unroll
+    for (int i = 0; i < L::WL; ++i) *reinterpret_cast<u32x4*>(lds + p.wdst[i]) = r.w[i];
+#pragma unroll
+    for (int i = 0; i < L::XL; ++i)
+        if (i < p.xiters && p.xdst[i] >= 0) *reinterpret_cast<u32x4*>(lds + p.xdst[i]) = r.x[i];
+    uint32_t* sb = reinterpret_cast<uint32_t*>(lds + L::W_BYTES + L::X_BYTES);
+#pragma unroll
+    for (int q = 0; q < S; ++q) sb[lane * L::SBP + q] = r.sc[q] | (r.bi[q] << 16);
+}
+
+// MFMAs of one stage from LDS. B fragment of lane (li, g) for k-block q4: weight row 32 nt + li,
+// codes q4*32 + 16 g .. +16 (32 codes, four MFMA steps); A fragment: activation row 32 mt + li,
+// halves q4*64 + 32 g + 8 q .. +8 (permuted like the codes).
+template <int MT, int S>
+DHP_DEV void stage_mfma(const uint8_t* lds, int li, int g, f16x16 (*acc)[2], const NibConsts& nk) {
+    using L = WaveLds<MT, S>;
+    const uint8_t* xl = lds + L::W_BYTES;
+    const uint32_t* sb = reinterpret_cast<const uint32_t*>(lds + L::W_BYTES + L::X_BYTES);
+#pragma unroll
+    for (int q4 = 0; q4 < S; ++q4) {
+        h8 b[2][4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int row = 32 * nt + li;
+            const u32x4 cw = *reinterpret_cast<const u32x4*>(lds + row * L::WP + q4 * 32 + 16 * g);
+            const uint32_t sbv = sb[row * L::SBP + q4];
+            const _Float16 s16 = (_Float16)bf16_to_f32(sbv & 0xFFFFu);
+            const _Float16 b16 = (_Float16)bf16_to_f32(sbv >> 16);
+            const h2 s2 = {s16, s16}, b2 = {b16, b16};
+            b[nt][0] = dequant8(cw.x, s2, b2, nk);
+            b[nt][1] = dequant8(cw.y, s2, b2, nk);
+            b[nt][2] = dequant8(cw.z, s2, b2, nk);
+            b[nt][3] = dequant8(cw.w, s2, b2, nk);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + (32 * mt + li) * L::XP + q4 * 128 + 64 * g + 16 * q);
+                const h8 a = permute_x8(xv);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[nt][q], acc[mt][nt], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int MT, int S, bool F32OUT, bool ARGMAX>
 __global__ __launch_bounds__(256) void k_gemm_mfma(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ X, int M, int N, int K,
-    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i) {
+    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i, int sb_aligned) {
+    using L = WaveLds<MT, S>;
     constexpr int ROWS = 32 * MT;
-    __shared__ float tile[ROWS * LDW];
+    extern __shared__ __align__(16) uint8_t lds_all[];   // 4 wave regions; reused by the epilogue
+    float* tile = reinterpret_cast<float*>(lds_all);
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -63,30 +226,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(
     const int n0 = blockIdx.x * BN;
     const int m0 = blockIdx.y * ROWS;
     const int KB = K >> 6;
-    const size_t row_bytes = (size_t)K >> 1;
-
-    // this lane's weight rows and activation rows (clamped reads, zero operands when out of range)
-    bool nv[2];
-    const uint8_t* crow[2];
-    const uint16_t* srow[2];
-    const uint16_t* brow[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int n = n0 + 32 * nt + li;
-        nv[nt] = n < N;
-        const int nc = nv[nt] ? n : 0;
-        crow[nt] = codes + (size_t)nc * row_bytes + 16 * g;
-        srow[nt] = scales + (size_t)nc * KB;
-        brow[nt] = biases + (size_t)nc * KB;
-    }
-    bool mv[MT];
-    const _Float16* xrow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = m0 + 32 * mt + li;
-        mv[mt] = m < M;
-        xrow[mt] = X + (size_t)(mv[mt] ? m : 0) * K + 32 * g;
-    }
+    const int xrows = min(ROWS, M - m0);       // activation rows that exist in this tile
+    uint8_t* lds = lds_all + wave * L::BYTES;
 
     f16x16 acc[MT][2];
 #pragma unroll
@@ -94,43 +235,26 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f16x16{};
 
-    for (int kb = wave; kb < KB; kb += 4) {
-        u32x4 cw[2];
-        uint32_t sw[2], bw[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            cw[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow[nt] + (size_t)kb * 32));
-            sw[nt] = srow[nt][kb];
-            bw[nt] = brow[nt][kb];
-        }
-        u32x4 xw[MT][4];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const u32x4* xp = reinterpret_cast<const u32x4*>(xrow[mt] + (size_t)kb * 64);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) xw[mt][s] = xp[s];
-        }
-        h8 b[2][4];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const _Float16 s16 = (_Float16)bf16_to_f32(sw[nt]);
-            const _Float16 b16 = (_Float16)bf16_to_f32(bw[nt]);
-            const h2 s2 = {s16, s16}, b2 = {b16, b16};
-            const uint32_t ww[4] = {cw[nt].x, cw[nt].y, cw[nt].z, cw[nt].w};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) b[nt][s] = nv[nt] ? dequant8(ww[s], s2, b2) : h8{};
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const h8 a = mv[mt] ? permute_x8(xw[mt][s]) : h8{};
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[nt][s], acc[mt][nt], 0, 0, 0);
-            }
+    // stage-aligned split of K over the four waves
+    const int ST = (KB + S - 1) / S;
+    const int st0 = (ST * wave) >> 2, st1 = (ST * (wave + 1)) >> 2;
+    const int kb1 = min(st1 * S, KB);
+    const bool sb_vec = sb_aligned && (KB % S) == 0;   // every stage's S groups are vector-aligned
+    if (st0 < st1) {
+        const NibConsts nk = nib_consts();
+        StagePlan<MT, S> plan;
+        stage_plan<MT, S>(plan, lane, codes, scales, biases, X, n0, N, m0, xrows, K, KB);
+        StageRegs<MT, S> r;
+        stage_load<MT, S>(r, plan, st0 * S, kb1, sb_vec);
+        for (int st = st0; st < st1; ++st) {
+            stage_store<MT, S>(r, plan, lds, lane);
+            __builtin_amdgcn_wave_barrier();
+            if (st + 1 < st1) stage_load<MT, S>(r, plan, (st + 1) * S, kb1, sb_vec);
+            stage_mfma<MT, S>(lds, li, g, acc, nk);
+            __builtin_amdgcn_wave_barrier();
         }
     }
+    __syncthreads();                           // staging regions are now free for the epilogue
 
     // fixed-order reduction of the four K slices: wave 3, then 2, 1, 0
 #pragma unroll
@@ -184,7 +308,29 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(
     }
 }
 
-template <int MT>
+template <int MT, int S, bool F32OUT, bool ARGMAX>
+hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t* sc, const uint16_t* bi,
+                      const _Float16* xh, int M, int N, int K, void* y, float* pv, int* pi) {
+    using L = WaveLds<MT, S>;
+    constexpr size_t lds = (4 * L::BYTES > 32 * MT * LDW * 4) ? 4 * L::BYTES : 32 * MT * LDW * 4;
+    // more than 64 KiB of dynamic LDS must be allowed per function (and device) once
+    static unsigned long long configured = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (!(__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & bit)) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, F32OUT, ARGMAX>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        __atomic_fetch_or(&configured, bit, __ATOMIC_RELEASE);
+    }
+    const int sb_aligned = (reinterpret_cast<uintptr_t>(sc) % (2 * S) == 0) && (reinterpret_cast<uintptr_t>(bi) % (2 * S) == 0);
+    hipLaunchKernelGGL((k_gemm_mfma<MT, S, F32OUT, ARGMAX>), grid, dim3(256), lds, s, c, sc, bi, xh, M, N, K, y, pv, pi,
+                       sb_aligned);
+    return hipGetLastError();
+}
+
+template <int MT, int S>
 hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4* w, const void* x,
                      int M, void* y, float* pv, int* pi) {
     const auto* c = static_cast<const uint8_t*>(w->codes);
@@ -192,11 +338,10 @@ hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4
     const auto* bi = static_cast<const uint16_t*>(w->biases);
     const auto* xh = static_cast<const _Float16*>(x);
     const int N = w->rows, K = w->cols;
-    if (f32 && am) hipLaunchKernelGGL((k_gemm_mfma<MT, true, true>), grid, dim3(256), 0, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    else if (f32) hipLaunchKernelGGL((k_gemm_mfma<MT, true, false>), grid, dim3(256), 0, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    else if (am) hipLaunchKernelGGL((k_gemm_mfma<MT, false, true>), grid, dim3(256), 0, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    else hipLaunchKernelGGL((k_gemm_mfma<MT, false, false>), grid, dim3(256), 0, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    return hipGetLastError();
+    if (f32 && am) return launch_one<MT, S, true, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    if (f32) return launch_one<MT, S, true, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    if (am) return launch_one<MT, S, false, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    return launch_one<MT, S, false, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
 }
 
 }  // namespace
@@ -213,8 +358,8 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     float* pv = argmax ? static_cast<float*>(ws) : nullptr;
     int* pi = argmax ? reinterpret_cast<int*>(static_cast<char*>(ws) + ws_part_stride) : nullptr;
     if (argmax && grid.y != 1) return dhp_fail(DHP_ERR_UNSUPPORTED, "argmax with m=%d", M);
-    const hipError_t e = (MT == 1) ? launch_mt<1>(y_f32, argmax != nullptr, grid, s, w, x, M, y, pv, pi)
-                                   : launch_mt<2>(y_f32, argmax != nullptr, grid, s, w, x, M, y, pv, pi);
+    const hipError_t e = (MT == 1) ? launch_mt<1, 2>(y_f32, argmax != nullptr, grid, s, w, x, M, y, pv, pi)
+                                   : launch_mt<2, 2>(y_f32, argmax != nullptr, grid, s, w, x, M, y, pv, pi);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
     if (argmax) {
         const hipError_t e2 = launch_argmax_final(pv, pi, (int)grid.x, M, argmax, s);

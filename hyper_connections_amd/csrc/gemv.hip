@@ -94,6 +94,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
 #pragma unroll
     for (int i = 0; i < CPL; ++i) xs[i] = load_x32(x + (size_t)(j + LPR * i) * 32, xp[i]);
 
+    const NibConsts nk = nib_consts();
     float best_v = -INFINITY;
     int best_i = INT_MAX;
     for (; row < N; row += stride) {
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const float d = dot32_f16(cur[i].c, xp[i]);
+            const float d = dot32_f16(cur[i].c, xp[i], nk);
             acc = __builtin_fmaf(bf16_to_f32(cur[i].s), d, acc);
             acc = __builtin_fmaf(bf16_to_f32(cur[i].b), xs[i], acc);
         }
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
     const int t = threadIdx.x;
     const int j = t % LPR;
     const int rpb = blockDim.x / LPR;
+    const NibConsts nk = nib_consts();
     float best_v = -INFINITY;
     int best_i = INT_MAX;
     for (int row = blockIdx.x * rpb + t / LPR; row < N; row += gridDim.x * rpb) {
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
                 p[4 * i] = as_h2(u.x); p[4 * i + 1] = as_h2(u.y);
                 p[4 * i + 2] = as_h2(u.z); p[4 * i + 3] = as_h2(u.w);
             }
-            const float d = dot32_f16(c, p);
+            const float d = dot32_f16(c, p, nk);
             acc = __builtin_fmaf(bf16_to_f32(sr[ch >> 1]), d, acc);
             acc = __builtin_fmaf(bf16_to_f32(br[ch >> 1]), lds_sum[ch], acc);
         }

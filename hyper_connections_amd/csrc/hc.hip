@@ -23,6 +23,7 @@
 namespace {
 
 constexpr int HC_MAX_THREADS = 1024;
+constexpr int LO_PITCH = 36;           // floats per staged 32-float chunk of the low-rank vector
 
 // raw, gamma: the C*H stream; one block per projection row (down rows first, then inject rows).
 __global__ __launch_bounds__(HC_MAX_THREADS) void k_hc_down(
@@ -122,17 +123,11 @@ __global__ __launch_bounds__(256) void k_hc_up(
     const uint16_t* __restrict__ ubiases, int R, const float* __restrict__ lo,
     const float* __restrict__ inv_rms, _Float16* __restrict__ mixed) {
     constexpr int LPRU = 16 / C;
-    extern __shared__ float lds_lo[];     // [R] then chunk sums [R/32]
+    extern __shared__ float lds_lo[];     // [R/32][LO_PITCH]: 32-float chunks, bank-staggered
     const int CHR = R >> 5;
     const int G = R >> 6;
-    float* lo_sum = lds_lo + R;
-    for (int i = threadIdx.x; i < R; i += blockDim.x) lds_lo[i] = lo[i];
-    __syncthreads();
-    for (int ch = threadIdx.x; ch < CHR; ch += blockDim.x) {
-        float s = 0.0f;
-        for (int i = 0; i < 32; ++i) s += lds_lo[32 * ch + i];
-        lo_sum[ch] = s;
-    }
+    for (int i = threadIdx.x * 4; i < R; i += blockDim.x * 4)
+        *reinterpret_cast<f4v*>(lds_lo + (i >> 5) * LO_PITCH + (i & 31)) = *reinterpret_cast<const f4v*>(lo + i);
     __syncthreads();
 
     const int lane16 = threadIdx.x & 15;
@@ -146,10 +141,19 @@ __global__ __launch_bounds__(256) void k_hc_up(
     const uint16_t* br = ubiases + urow * G;
     float acc = 0.0f;
     for (int ch = sub; ch < CHR; ch += LPRU) {
-        const u32x4 cc = __builtin_nontemporal_load(cr + ch);
-        const float d = dot32_f32(cc, lds_lo + 32 * ch);
+        const u32x4 cc = cr[ch];          // rows are 10 chunks: lines are shared between lane groups
+        const f4v* lp = reinterpret_cast<const f4v*>(lds_lo + ch * LO_PITCH);
+        float lv[32];
+        float ls = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const f4v t = lp[q];
+            lv[4 * q] = t.x; lv[4 * q + 1] = t.y; lv[4 * q + 2] = t.z; lv[4 * q + 3] = t.w;
+            ls += (t.x + t.y) + (t.z + t.w);
+        }
+        const float d = dot32_f32(cc, lv);
         acc = __builtin_fmaf(bf16_to_f32(sr[ch >> 1]), d, acc);
-        acc = __builtin_fmaf(bf16_to_f32(br[ch >> 1]), lo_sum[ch], acc);
+        acc = __builtin_fmaf(bf16_to_f32(br[ch >> 1]), ls, acc);
     }
     acc = group_sum<LPRU>(acc);
     const float n = (float)raw[urow] * inv_rms[c] * bf16_to_f32(gamma[urow]);
@@ -211,7 +215,7 @@ int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, 
 
     const int block = 64;                  // 4 outputs per block
     const dim3 g((unsigned)((H + 3) / 4));
-    const size_t lds = (size_t)(R + R / 32) * sizeof(float);
+    const size_t lds = (size_t)(R / 32) * LO_PITCH * sizeof(float);
     const auto* rw = static_cast<const _Float16*>(raw);
     const auto* gm = static_cast<const uint16_t*>(gamma);
     const auto* uc = static_cast<const u32x4*>(up->codes);

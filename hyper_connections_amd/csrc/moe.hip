@@ -15,10 +15,11 @@
 //                 reductions, cheaper than another launch), then its quarter-waves run one
 //                 (selected expert, row) pair each: gate and up rows against register-resident
 //                 activations, act = silu(gate) * up in fp32. Block 0 writes ids and weights.
-//  k_moe_phase2 : 16 lanes per output element walk the down rows of all selected experts and
+//  k_moe_phase2 : 16 lanes per output element walk the down rows of the selected experts and
 //                 the shared expert (K = inter) against the fp32 activations staged in LDS,
-//                 weighting each expert's partial by its softmax weight; the shared part is
-//                 scaled by sigmoid(g) and both halves meet in one fp16 rounding.
+//                 four waves splitting the experts, each expert's partial weighted by its
+//                 softmax weight; the shared part is scaled by sigmoid(g) and both halves meet
+//                 in one fp16 rounding.
 #include "dhp_internal.hpp"
 
 #include <math.h>
@@ -82,12 +83,13 @@ DHP_DEV void load_pair(PairRegs<CPL>& p, const u32x4* gc, const uint16_t* gs, co
 // silu(gate . x) * (up . x), the same value in every lane of the 16-lane group.
 template <int CPL>
 DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* xs) {
+    const NibConsts nk = nib_consts();
     float ag = 0.0f, au = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_f16(p.cg[i], xp[i]), ag);
+        ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_f16(p.cg[i], xp[i], nk), ag);
         ag = __builtin_fmaf(bf16_to_f32(p.bg[i]), xs[i], ag);
-        au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_f16(p.cu[i], xp[i]), au);
+        au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_f16(p.cu[i], xp[i], nk), au);
         au = __builtin_fmaf(bf16_to_f32(p.bu[i]), xs[i], au);
     }
     ag = group_sum<LPR>(ag);
@@ -250,27 +252,34 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     if (j == 0 && live) a.act[(size_t)slot * a.inter + row] = v;
 }
 
-// 16 lanes per output element h, RH elements per 16-lane group; a block of 64 lanes covers
-// 4 * RH consecutive outputs. Down rows have K = inter; lane j takes chunks j + 16 i (i < CPLD).
-// Every code, scale and bias load of all (top_k + 1) experts is issued before any arithmetic,
-// then the activations are staged in LDS while those loads are in flight.
+// Phase 2. A block of four waves owns 4 * RH consecutive outputs h (16 lanes and RH outputs per
+// 16-lane group, the same rows in every wave). Wave w takes expert slots w, w+4, w+8 (slot
+// top_k is the shared expert): its lanes issue every code, scale and bias load of those slots
+// first, the block stages the fp32 activations in LDS meanwhile, then each lane reduces its own
+// chunk (K = inter; lane j takes chunks j + 16 i) of each down row. The four waves' partial sums
+// meet in LDS in a fixed order, so the result does not depend on timing.
 constexpr int RH = 2;
 constexpr int NSLOT = DHP_MOE_MAX_TOP_K + 1;
+constexpr int SLOTS_PER_WAVE = (NSLOT + 3) / 4;
+constexpr int ACT_PITCH = 36;          // floats per staged 32-float activation chunk
 
 template <int CPLD>
-__global__ __launch_bounds__(64) void k_moe_phase2(MoeArgs a) {
-    extern __shared__ float lds_act[];     // [(top_k + 1) * inter] then chunk sums
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void k_moe_phase2(MoeArgs a) {
+    extern __shared__ float lds_act[];     // [(top_k + 1) * inter / 32][ACT_PITCH]
+    __shared__ float part[4][2][64 * RH];  // [wave][routed, shared][lane-major partials]
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int j = lane % LPR;
     const int nslot = a.top_k + 1;
     const int CH = a.inter >> 5;
     const int G = a.inter >> 6;
     const int h0 = (blockIdx.x * 4 + lane / LPR) * RH;
 
-    u32x4 c[NSLOT][RH][CPLD];
-    uint32_t sv[NSLOT][RH][CPLD], bv[NSLOT][RH][CPLD];
+    u32x4 c[SLOTS_PER_WAVE][RH][CPLD];
+    uint32_t sv[SLOTS_PER_WAVE][RH][CPLD], bv[SLOTS_PER_WAVE][RH][CPLD];
 #pragma unroll
-    for (int slot = 0; slot < NSLOT; ++slot) {
+    for (int t = 0; t < SLOTS_PER_WAVE; ++t) {
+        const int slot = wave + 4 * t;
         if (slot < nslot) {
             const u32x4* dc;
             const uint16_t* ds;
@@ -289,65 +298,81 @@ __global__ __launch_bounds__(64) void k_moe_phase2(MoeArgs a) {
 #pragma unroll
                 for (int i = 0; i < CPLD; ++i) {
                     const int ch = min(j + LPR * i, CH - 1);
-                    c[slot][r][i] = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
-                    sv[slot][r][i] = ds[(size_t)h * G + (ch >> 1)];
-                    bv[slot][r][i] = db[(size_t)h * G + (ch >> 1)];
+                    c[t][r][i] = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
+                    sv[t][r][i] = ds[(size_t)h * G + (ch >> 1)];
+                    bv[t][r][i] = db[(size_t)h * G + (ch >> 1)];
                 }
             }
         }
     }
 
-    // stage the activations of every slot, and per-chunk sums
+    // stage the activations of every slot in LDS, 32-float chunks at a 36-float pitch so the 16
+    // lanes of a group (one chunk each) read distinct banks
     const int n = nslot * a.inter;
-    float* act_sum = lds_act + n;
-    for (int i = lane * 4; i < n; i += 64 * 4)
-        *reinterpret_cast<f4v*>(lds_act + i) = *reinterpret_cast<const f4v*>(a.act + i);
-    __syncthreads();
-    for (int q = lane; q < nslot * CH; q += 64) {
-        float s = 0.0f;
-        for (int i = 0; i < 32; ++i) s += lds_act[32 * q + i];
-        act_sum[q] = s;
-    }
+    for (int i = threadIdx.x * 4; i < n; i += 256 * 4)
+        *reinterpret_cast<f4v*>(lds_act + (i >> 5) * ACT_PITCH + (i & 31)) = *reinterpret_cast<const f4v*>(a.act + i);
     __syncthreads();
 
     float racc[RH], sacc[RH];
 #pragma unroll
     for (int r = 0; r < RH; ++r) { racc[r] = 0.0f; sacc[r] = 0.0f; }
 #pragma unroll
-    for (int slot = 0; slot < NSLOT; ++slot) {
+    for (int t = 0; t < SLOTS_PER_WAVE; ++t) {
+        const int slot = wave + 4 * t;
         if (slot < nslot) {
             const bool shared = slot == a.top_k;
             const float wgt = shared ? 1.0f : a.weights[slot];
-            const float* av = lds_act + (size_t)slot * a.inter;
-            const float* asum = act_sum + (size_t)slot * CH;
+            float p[RH];
 #pragma unroll
-            for (int r = 0; r < RH; ++r) {
-                float p = 0.0f;
+            for (int r = 0; r < RH; ++r) p[r] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < CPLD; ++i) {
-                    const int ch = j + LPR * i;
-                    if (ch < CH) {
-                        const float d = dot32_f32(c[slot][r][i], av + 32 * ch);
-                        p = __builtin_fmaf(bf16_to_f32(sv[slot][r][i]), d, p);
-                        p = __builtin_fmaf(bf16_to_f32(bv[slot][r][i]), asum[ch], p);
+            for (int i = 0; i < CPLD; ++i) {
+                const int ch = j + LPR * i;
+                if (ch < CH) {
+                    const f4v* ap = reinterpret_cast<const f4v*>(lds_act + (slot * CH + ch) * ACT_PITCH);
+                    float av[32];
+                    float xs = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const f4v u = ap[q];
+                        av[4 * q] = u.x; av[4 * q + 1] = u.y; av[4 * q + 2] = u.z; av[4 * q + 3] = u.w;
+                        xs += (u.x + u.y) + (u.z + u.w);
+                    }
+#pragma unroll
+                    for (int r = 0; r < RH; ++r) {
+                        const float d = dot32_f32(c[t][r][i], av);
+                        p[r] = __builtin_fmaf(bf16_to_f32(sv[t][r][i]), d, p[r]);
+                        p[r] = __builtin_fmaf(bf16_to_f32(bv[t][r][i]), xs, p[r]);
                     }
                 }
-                if (shared) sacc[r] += p;
-                else racc[r] = __builtin_fmaf(wgt, p, racc[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < RH; ++r) {
+                if (shared) sacc[r] += p[r];
+                else racc[r] = __builtin_fmaf(wgt, p[r], racc[r]);
             }
         }
     }
-    const float sg = sigmoid_f(a.gate_logit[0]);
 #pragma unroll
     for (int r = 0; r < RH; ++r) {
-        const float rr = group_sum<LPR>(racc[r]);
-        const float ss = group_sum<LPR>(sacc[r]) * sg;
-        const int h = h0 + r;
-        if (j == 0 && h < a.hidden) {
-            float o;
-            if (a.boundary) o = (float)(_Float16)rr + (float)(_Float16)ss;
-            else o = rr + ss;
-            a.out[h] = (_Float16)o;
+        part[wave][0][r * 64 + lane] = group_sum<LPR>(racc[r]);
+        part[wave][1][r * 64 + lane] = group_sum<LPR>(sacc[r]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const float sg = sigmoid_f(a.gate_logit[0]);
+#pragma unroll
+        for (int r = 0; r < RH; ++r) {
+            const int h = h0 + r;
+            if (j == 0 && h < a.hidden) {
+                const int q = r * 64 + lane;
+                const float rr = (part[0][0][q] + part[1][0][q]) + (part[2][0][q] + part[3][0][q]);
+                const float ss = ((part[0][1][q] + part[1][1][q]) + (part[2][1][q] + part[3][1][q])) * sg;
+                float o;
+                if (a.boundary) o = (float)(_Float16)rr + (float)(_Float16)ss;
+                else o = rr + ss;
+                a.out[h] = (_Float16)o;
+            }
         }
     }
 }
@@ -362,10 +387,10 @@ hipError_t launch_all(const MoeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_moe_phase1<CPL>, dim3((pairs + 3) / 4), dim3(64), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)(a.top_k + 1) * (a.inter + a.inter / 32) * sizeof(float);
+    const size_t lds = (size_t)(a.top_k + 1) * (a.inter / 32) * ACT_PITCH * sizeof(float);
     const dim3 g2((a.hidden + 4 * RH - 1) / (4 * RH));
-    if (a.inter <= 512) hipLaunchKernelGGL(k_moe_phase2<1>, g2, dim3(64), lds, s, a);
-    else hipLaunchKernelGGL(k_moe_phase2<2>, g2, dim3(64), lds, s, a);
+    if (a.inter <= 512) hipLaunchKernelGGL(k_moe_phase2<1>, g2, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL(k_moe_phase2<2>, g2, dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
