@@ -1,0 +1,226 @@
+// Multi-row arm of the dequantizing GEMV (2 <= m <= 16, e.g. the LM head over a few rows, with
+// argmax), streamed like the M=1 GEMV but with the m-way reuse on the matrix cores.
+//
+// "src/real_forward.rs" (turbospark-runtime 0.3.0), field batched_gemv_prefill: the multi-row
+// GEMM gives the same outputs as m separate GEMVs. Design for gfx950 (v_mfma_f32_16x16x32_f16):
+//
+//  * The activations (m <= 16 rows, K <= 2560) are staged once per block in LDS, with k permuted
+//    inside every group of eight exactly as the nibble unpack orders the codes, so an A fragment
+//    is one 16-byte LDS read with no shuffling. Lanes of fragment rows m..15 read the last real
+//    row again: they only feed result rows that are never stored.
+//  * Each wave streams 16-row weight tiles over the whole K with a grid stride. Lane (n, g) of a
+//    wave (n = lane % 16, g = lane / 16) loads 16 bytes of weight row n0 + n covering
+//    k = 128 c + 32 g .. +32; the four 32-bit words of that load are the B fragments of the four
+//    MFMA steps of chunk c (virtual k of step t, slot e: 128 c + 32 g + 8 t + perm(e)). Four
+//    lanes read 64 contiguous bytes of a row, the next chunk the following 64.
+//  * The codes of half a tile are loaded ahead while the other half computes, and the first half
+//    of the wave's next tile while the second half of the current one computes.
+//  * Each 16-lane row of the result is summed by the matrix core, so a tile needs no cross-lane
+//    reduction; the argmax keeps, per lane, the best of its four rows over the tiles it saw, then
+//    reduces over lanes (DPP), waves (LDS) and blocks (the shared final kernel).
+#include "dhp_internal.hpp"
+
+#include <math.h>
+#include <limits.h>
+
+typedef float f4x __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int WAVES = 4;
+constexpr int HALF = 10;             // 128-k chunks per half tile (K = 2560: two halves)
+
+DHP_DEV h8 deq8(uint32_t w, h2 s2, h2 b2, const NibConsts& k) {
+    h2 q[4];
+    unpack8(w, q, k);
+    const h2 p0 = __builtin_elementwise_fma(q[0], s2, b2);
+    const h2 p1 = __builtin_elementwise_fma(q[1], s2, b2);
+    const h2 p2 = __builtin_elementwise_fma(q[2], s2, b2);
+    const h2 p3 = __builtin_elementwise_fma(q[3], s2, b2);
+    return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+struct HalfRegs {
+    u32x4 c[HALF];
+    uint32_t s[HALF], b[HALF];
+};
+
+// Loads of chunks [c0, c0 + HALF) of weight row `row` for lane group g (chunks >= nch are
+// clamped to the last chunk and never used).
+DHP_DEV void load_half(HalfRegs& r, const uint8_t* crow, const uint16_t* srow, const uint16_t* brow, int c0,
+                       int nch, int g) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+        const int c = min(c0 + i, nch - 1);
+        r.c[i] = *reinterpret_cast<const u32x4*>(crow + (size_t)c * 64 + 16 * g);
+        r.s[i] = srow[2 * c + (g >> 1)];
+        r.b[i] = brow[2 * c + (g >> 1)];
+    }
+}
+
+DHP_DEV void mfma_half(const HalfRegs& r, const uint8_t* xl, int xpitch, int c0, int nch, int arow, int g,
+                       f4x& acc, const NibConsts& nk) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+        if (c0 + i < nch) {
+            const _Float16 s16 = (_Float16)bf16_to_f32(r.s[i]);
+            const _Float16 b16 = (_Float16)bf16_to_f32(r.b[i]);
+            const h2 s2 = {s16, s16}, b2 = {b16, b16};
+            const uint32_t ww[4] = {r.c[i].x, r.c[i].y, r.c[i].z, r.c[i].w};
+            const uint8_t* ap = xl + arow * xpitch + ((c0 + i) * 128 + 32 * g) * 2;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x4 av = *reinterpret_cast<const u32x4*>(ap + 16 * t);
+                const h8 a = __builtin_bit_cast(h8, av);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, deq8(ww[t], s2, b2, nk), acc, 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <bool F32OUT, bool ARGMAX>
+__global__ __launch_bounds__(WAVES * 64) void k_gemv_mfma16(
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, const _Float16* __restrict__ X, int M, int N, int K,
+    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i) {
+    extern __shared__ __align__(16) uint8_t xl[];      // [M][K halves, permuted by eights] + pad
+    const int xpitch = 2 * K + 16;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int nch = K >> 7;                           // 128-k chunks
+    const int G = K >> 6;
+    const size_t row_bytes = (size_t)K >> 1;
+
+    // stage the activations, permuted (x0,x4,x1,x5,x2,x6,x3,x7) within each group of eight
+    const int per_row = K >> 3;
+    for (int i = threadIdx.x; i < M * per_row; i += blockDim.x) {
+        const int m = i / per_row, j = i % per_row;
+        const u32x4 u = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + 8 * j);
+        h2 p[4];
+        permute8(u.x, u.y, u.z, u.w, p);
+        *reinterpret_cast<u32x4*>(xl + m * xpitch + 16 * j) =
+            u32x4{h2_bits(p[0]), h2_bits(p[1]), h2_bits(p[2]), h2_bits(p[3])};
+    }
+    __syncthreads();
+
+    const NibConsts nk = nib_consts();
+    float bv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    int bi[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+    const int ntiles = (N + 15) >> 4;
+    const int stride = gridDim.x * WAVES;
+    // A rows: lane n reads activation row n, clamped to the last real row (rows >= M only feed
+    // result rows that are never stored)
+    const int arow = min(n, M - 1);
+    const bool two = nch > HALF;                       // K <= 2560: at most two half tiles
+    int tile = blockIdx.x * WAVES + wave;
+    HalfRegs h0, h1;
+    if (tile < ntiles) {
+        const int row = min(tile * 16 + n, N - 1);
+        load_half(h0, codes + (size_t)row * row_bytes, scales + (size_t)row * G, biases + (size_t)row * G, 0, nch, g);
+    }
+    // loads are unconditional (clamped rows and chunks) so the compiler can count them and wait
+    // only for the half about to be used
+    for (; tile < ntiles; tile += stride) {
+        const int n0 = tile * 16;
+        const int row = min(n0 + n, N - 1);
+        f4x acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        load_half(h1, codes + (size_t)row * row_bytes, scales + (size_t)row * G, biases + (size_t)row * G, HALF, nch, g);
+        mfma_half(h0, xl, xpitch, 0, nch, arow, g, acc, nk);
+        const int nrow = min((tile + stride) * 16 + n, N - 1);      // the next tile's first half
+        load_half(h0, codes + (size_t)nrow * row_bytes, scales + (size_t)nrow * G, biases + (size_t)nrow * G, 0, nch, g);
+        if (two) mfma_half(h1, xl, xpitch, HALF, nch, arow, g, acc, nk);
+        // lane (n, g) holds rows 4 g .. 4 g + 3 of column n0 + n
+        const int col = n0 + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * g + r;
+            if (m < M && col < N) {
+                const float v = acc[r];
+                if constexpr (F32OUT) reinterpret_cast<float*>(Y)[(size_t)m * N + col] = v;
+                else reinterpret_cast<_Float16*>(Y)[(size_t)m * N + col] = (_Float16)v;
+                if constexpr (ARGMAX)
+                    if (better(v, col, bv[r], bi[r])) { bv[r] = v; bi[r] = col; }
+            }
+        }
+    }
+
+    if constexpr (ARGMAX) {
+        // over the 16 lanes of each row group (one DPP row), then over the waves of the block
+        __shared__ float sv[WAVES][16];
+        __shared__ int si[WAVES][16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = bv[r];
+            int i = bi[r];
+            best_step<DPP_XOR1>(v, i);
+            best_step<DPP_XOR2>(v, i);
+            best_step<DPP_HALF_MIRROR>(v, i);
+            best_step<DPP_MIRROR>(v, i);
+            if (n == 0) { sv[wave][4 * g + r] = v; si[wave][4 * g + r] = i; }
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < M) {
+            const int m = threadIdx.x;
+            float v = sv[0][m];
+            int i = si[0][m];
+            for (int w = 1; w < WAVES; ++w)
+                if (better(sv[w][m], si[w][m], v, i)) { v = sv[w][m]; i = si[w][m]; }
+            part_v[(size_t)m * gridDim.x + blockIdx.x] = v;
+            part_i[(size_t)m * gridDim.x + blockIdx.x] = i;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s);
+
+// Whether the streamed matrix-core arm takes this shape (else the LDS-staged GEMM does).
+bool dhp_gemv_mfma16_fits(int M, int K) { return M >= 2 && M <= 16 && K % 128 == 0 && K <= 2 * HALF * 128; }
+
+int dhp_gemv_mfma16_blocks(int N, int cus) {
+    const int ntiles = (N + 15) / 16;
+    int blocks = (ntiles + WAVES - 1) / WAVES;
+    const int cap = 3 * cus;
+    return blocks < cap ? blocks : cap;
+}
+
+int launch_gemv_mfma16(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
+                       size_t ws_part_stride, hipStream_t s, int cus) {
+    const int N = w->rows, K = w->cols;
+    const int blocks = dhp_gemv_mfma16_blocks(N, cus);
+    const size_t lds = (size_t)M * (2 * K + 16);
+    const auto* c = static_cast<const uint8_t*>(w->codes);
+    const auto* sc = static_cast<const uint16_t*>(w->scales);
+    const auto* bi = static_cast<const uint16_t*>(w->biases);
+    const auto* xh = static_cast<const _Float16*>(x);
+    float* pv = argmax ? static_cast<float*>(ws) : nullptr;
+    int* pi = argmax ? reinterpret_cast<int*>(static_cast<char*>(ws) + ws_part_stride) : nullptr;
+    static unsigned long long configured = 0;          // > 64 KiB of dynamic LDS, once per device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hipGetDevice");
+    if (!(__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & (1ull << (dev & 63)))) {
+        const void* fns[4] = {reinterpret_cast<const void*>(&k_gemv_mfma16<true, true>),
+                              reinterpret_cast<const void*>(&k_gemv_mfma16<true, false>),
+                              reinterpret_cast<const void*>(&k_gemv_mfma16<false, true>),
+                              reinterpret_cast<const void*>(&k_gemv_mfma16<false, false>)};
+        for (const void* f : fns)
+            if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 16 * (2 * 2 * HALF * 128 + 16)) != hipSuccess)
+                return dhp_fail(DHP_ERR_LAUNCH, "hipFuncSetAttribute");
+        __atomic_fetch_or(&configured, 1ull << (dev & 63), __ATOMIC_RELEASE);
+    }
+    const dim3 g((unsigned)blocks), b(WAVES * 64);
+    if (y_f32 && argmax) hipLaunchKernelGGL((k_gemv_mfma16<true, true>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    else if (y_f32) hipLaunchKernelGGL((k_gemv_mfma16<true, false>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    else if (argmax) hipLaunchKernelGGL((k_gemv_mfma16<false, true>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    else hipLaunchKernelGGL((k_gemv_mfma16<false, false>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemv_mfma16 launch: %s", hipGetErrorString(e));
+    if (argmax) {
+        e = launch_argmax_final(pv, pi, blocks, M, argmax, s);
+        if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "argmax launch: %s", hipGetErrorString(e));
+    }
+    return DHP_OK;
+}

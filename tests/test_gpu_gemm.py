@@ -101,3 +101,17 @@ def test_multirow_argmax_tie_lowest_index():
     y = y.cpu().numpy()
     assert y[2, a] == y[2, b]
     assert int(am.cpu()[2]) == min(a, b)
+
+
+def test_multirow_argmax_repeated_calls():
+    say("multi-row argmax repeated calls")
+    rng = np.random.default_rng(75)
+    n, k, m = 9000, 1024, 5
+    t = synth.int4_tensor(rng, n, k)
+    X = synth.normal_f16(rng, (m, k))
+    ref = oracle.argmax_lowest(oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, X)).tolist()
+    w = dev(t)
+    xd = torch.from_numpy(X).cuda()
+    outs = [hca.dequant_gemv(w, xd, out_dtype=torch.float32, argmax=True)[1] for _ in range(10)]
+    torch.cuda.synchronize()
+    assert all(o.cpu().numpy().tolist() == ref for o in outs)

@@ -109,3 +109,22 @@ def test_argmax_planted_max_at_ends():
         _, am = run_gemv(t2, x, out_dtype=torch.float32, argmax=True)
         ref = oracle.dequant_gemv(t2.q, t2.s_bits, t2.b_bits, x)
         assert int(am.cpu()[0]) == int(oracle.argmax_lowest(ref)) == row
+
+
+def test_argmax_repeated_calls_share_one_workspace():
+    # The argmax workspace (completion counter + keys) is reused across calls and must return
+    # to zero after each one: 12 calls in a row, alternating two inputs, all correct.
+    say("argmax repeated calls, shared workspace")
+    rng = np.random.default_rng(79)
+    n, k = 70000, 2560
+    t = synth.int4_tensor(rng, n, k)
+    xs = [synth.normal_f16(rng, (k,)) for _ in range(2)]
+    refs = [int(oracle.argmax_lowest(oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, x))) for x in xs]
+    w = hca.Int4Weight.from_logical(t.q, t.s_bits, t.b_bits)
+    xd = [torch.from_numpy(x).cuda() for x in xs]
+    got = []
+    for i in range(12):
+        _, am = hca.dequant_gemv(w, xd[i % 2], out_dtype=torch.float32, argmax=True)
+        got.append(am)
+    torch.cuda.synchronize()
+    assert [int(a.cpu()[0]) for a in got] == [refs[i % 2] for i in range(12)]
