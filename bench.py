@@ -62,11 +62,18 @@ def algorithmic_bytes():
     return b
 
 
-def build_workload(torch, hca, synth, ring: int):
-    """Device inputs for every call, with `ring` rotating copies of the small weight sets."""
+CALLS = ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8")
+
+
+def build_workload(torch, hca, synth, ring: int, only=None):
+    """Device inputs for every call (or only the call named), with `ring` rotating copies of the
+    small weight sets."""
     dev = "cuda"
     t0 = time.time()
     W = {}
+
+    def want(*names):
+        return only is None or only in names
 
     def up_int4(t):
         return hca.Int4Weight.from_logical(t.q, t.s_bits, t.b_bits, dev)
@@ -74,20 +81,51 @@ def build_workload(torch, hca, synth, ring: int):
     def clone(w):
         return hca.Int4Weight(w.codes.clone(), w.scales.clone(), w.biases.clone(), w.rows, w.cols)
 
-    g = synth.gemv_workload(0)
-    w0 = up_int4(g["w"])
-    W["gemv_w"] = [w0] + [clone(w0) for _ in range(ring - 1)]
-    W["gemv_x"] = torch.from_numpy(g["x"]).to(dev)
-    W["gemv_y"] = torch.empty(2560, dtype=torch.float16, device=dev)
+    if want("gemv"):
+        g = synth.gemv_workload(0)
+        w0 = up_int4(g["w"])
+        W["gemv_w"] = [w0] + [clone(w0) for _ in range(ring - 1)]
+        W["gemv_x"] = torch.from_numpy(g["x"]).to(dev)
+        W["gemv_y"] = torch.empty(2560, dtype=torch.float16, device=dev)
 
-    h = synth.hc_workload(0)
-    hw = (up_int4(h["down"]), up_int4(h["up"]), up_int4(h["inject"]))
-    W["hc_w"] = [hw] + [tuple(clone(w) for w in hw) for _ in range(ring - 1)]
-    W["hc_wide"] = torch.from_numpy(h["raw"]).to(dev)
-    W["hc_gamma"] = hca.bf16_bits_to_tensor(h["gamma_bits"]).to(dev)
-    W["hc_out"] = torch.from_numpy(h["out"]).to(dev)
-    W["hc_mixed"] = torch.empty(2560, dtype=torch.float16, device=dev)
-    W["hc_iw"] = torch.empty(4, dtype=torch.float32, device=dev)
+    if want("hc"):
+        h = synth.hc_workload(0)
+        hw = (up_int4(h["down"]), up_int4(h["up"]), up_int4(h["inject"]))
+        W["hc_w"] = [hw] + [tuple(clone(w) for w in hw) for _ in range(ring - 1)]
+        W["hc_wide"] = torch.from_numpy(h["raw"]).to(dev)
+        W["hc_gamma"] = hca.bf16_bits_to_tensor(h["gamma_bits"]).to(dev)
+        W["hc_out"] = torch.from_numpy(h["out"]).to(dev)
+        W["hc_mixed"] = torch.empty(2560, dtype=torch.float16, device=dev)
+        W["hc_iw"] = torch.empty(4, dtype=torch.float32, device=dev)
+
+    if want("moe"):
+        _moe_workload(torch, hca, synth, W, dev)
+    if want("prefill"):
+        p = synth.prefill_workload(0)
+        p0 = up_int4(p["w"])
+        W["pre_w"] = [p0] + [clone(p0) for _ in range(ring - 1)]
+        W["pre_x"] = torch.from_numpy(p["x"]).to(dev)
+        W["pre_y"] = torch.empty((128, 8192), dtype=torch.float16, device=dev)
+
+    if want("lmhead1", "lmhead8"):
+        l1 = synth.lmhead_workload(0, m=1)
+        lw = up_int4(l1["w"])
+        W["lm_w"] = [lw, clone(lw)]
+        W["lm_x1"] = torch.from_numpy(l1["x"]).to(dev)
+        W["lm_x8"] = torch.from_numpy(synth.lmhead_x(0, 8)).to(dev)
+        W["lm_y1"] = torch.empty((1, 151936), dtype=torch.float32, device=dev)
+        W["lm_y8"] = torch.empty((8, 151936), dtype=torch.float32, device=dev)
+        W["lm_a1"] = torch.empty(1, dtype=torch.int32, device=dev)
+        W["lm_a8"] = torch.empty(8, dtype=torch.int32, device=dev)
+        del l1
+    torch.cuda.synchronize()
+    print(f"[bench] workload resident in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    return W
+
+
+def _moe_workload(torch, hca, synth, W, dev):
+    def up_int4(t):
+        return hca.Int4Weight.from_logical(t.q, t.s_bits, t.b_bits, dev)
 
     m = synth.moe_workload(0)
     ex = m["experts"]
@@ -103,45 +141,25 @@ def build_workload(torch, hca, synth, ring: int):
     W["moe_out"] = torch.empty(2560, dtype=torch.float16, device=dev)
     W["moe_ids"] = torch.empty(8, dtype=torch.int32, device=dev)
     W["moe_w"] = torch.empty(8, dtype=torch.float32, device=dev)
-    del ex, m
-
-    p = synth.prefill_workload(0)
-    p0 = up_int4(p["w"])
-    W["pre_w"] = [p0] + [clone(p0) for _ in range(ring - 1)]
-    W["pre_x"] = torch.from_numpy(p["x"]).to(dev)
-    W["pre_y"] = torch.empty((128, 8192), dtype=torch.float16, device=dev)
-
-    l1 = synth.lmhead_workload(0, m=1)
-    lw = up_int4(l1["w"])
-    W["lm_w"] = [lw, clone(lw)]
-    W["lm_x1"] = torch.from_numpy(l1["x"]).to(dev)
-    W["lm_x8"] = torch.from_numpy(synth.lmhead_x(0, 8)).to(dev)
-    W["lm_y1"] = torch.empty((1, 151936), dtype=torch.float32, device=dev)
-    W["lm_y8"] = torch.empty((8, 151936), dtype=torch.float32, device=dev)
-    W["lm_a1"] = torch.empty(1, dtype=torch.int32, device=dev)
-    W["lm_a8"] = torch.empty(8, dtype=torch.int32, device=dev)
-    del l1
-    torch.cuda.synchronize()
-    print(f"[bench] workload resident in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
-    return W
 
 
-def prepare_calls(hca, W, ring: int):
+def prepare_calls(hca, W, ring: int, only=None):
     """calls[name][i] for ring position i (the MoE token ring has its own length)."""
     C, H = 4, 2560
-    mo = W["moe"]
-    calls = {
-        "gemv": [hca.prepare_gemv(W["gemv_w"][i], W["gemv_x"], W["gemv_y"]) for i in range(ring)],
-        "hc": [(hca.prepare_hc_read(W["hc_wide"], W["hc_gamma"], C, H, *W["hc_w"][i], W["hc_mixed"], W["hc_iw"]),
-                hca.prepare_hc_inject(W["hc_wide"], W["hc_out"], W["hc_iw"], C, H)) for i in range(ring)],
-        "moe": [hca.prepare_moe(W["moe_x"][t], mo["router"], mo["sgate"], mo["gate"], mo["up"], mo["down"], mo["sg"],
-                                mo["su"], mo["sd"], 8, W["moe_out"], W["moe_ids"], W["moe_w"])
-                for t in range(W["moe_x"].shape[0])],
-        "prefill": [hca.prepare_gemm_batched(W["pre_w"][i], W["pre_x"], W["pre_y"]) for i in range(ring)],
-        "lmhead1": [hca.prepare_gemv(W["lm_w"][0], W["lm_x1"], W["lm_y1"], argmax=W["lm_a1"])],
-        "lmhead8": [hca.prepare_gemv(W["lm_w"][1], W["lm_x8"], W["lm_y8"], argmax=W["lm_a8"])],
+    make = {
+        "gemv": lambda: [hca.prepare_gemv(W["gemv_w"][i], W["gemv_x"], W["gemv_y"]) for i in range(ring)],
+        "hc": lambda: [(hca.prepare_hc_read(W["hc_wide"], W["hc_gamma"], C, H, *W["hc_w"][i], W["hc_mixed"],
+                                            W["hc_iw"]),
+                        hca.prepare_hc_inject(W["hc_wide"], W["hc_out"], W["hc_iw"], C, H)) for i in range(ring)],
+        "moe": lambda: [hca.prepare_moe(W["moe_x"][t], W["moe"]["router"], W["moe"]["sgate"], W["moe"]["gate"],
+                                        W["moe"]["up"], W["moe"]["down"], W["moe"]["sg"], W["moe"]["su"],
+                                        W["moe"]["sd"], 8, W["moe_out"], W["moe_ids"], W["moe_w"])
+                        for t in range(W["moe_x"].shape[0])],
+        "prefill": lambda: [hca.prepare_gemm_batched(W["pre_w"][i], W["pre_x"], W["pre_y"]) for i in range(ring)],
+        "lmhead1": lambda: [hca.prepare_gemv(W["lm_w"][0], W["lm_x1"], W["lm_y1"], argmax=W["lm_a1"])],
+        "lmhead8": lambda: [hca.prepare_gemv(W["lm_w"][1], W["lm_x8"], W["lm_y8"], argmax=W["lm_a8"])],
     }
-    return calls
+    return {name: f() for name, f in make.items() if only is None or name == only}
 
 
 def run_call(c):
@@ -165,12 +183,13 @@ def step(calls, i, ev=None):
     run_call(calls["lmhead8"][0])
 
 
-def per_call_pass(torch, calls, nbytes, iters: int):
-    """Each call type alone, event-timed per call, cycling its ring (median over iters)."""
+def per_call_pass(torch, calls, nbytes, iters: int, exact: bool = False):
+    """Each call type alone, event-timed per call, cycling its ring (median over iters; the LM
+    heads take a quarter as many unless `exact`)."""
     out = {}
-    for name in ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8"):
+    for name in calls:
         seq = calls[name]
-        n = max(iters, len(seq)) if name not in ("lmhead1", "lmhead8") else max(8, iters // 4)
+        n = iters if exact else (max(iters, len(seq)) if name not in ("lmhead1", "lmhead8") else max(8, iters // 4))
         st = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         en = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for i in range(3):
@@ -183,7 +202,7 @@ def per_call_pass(torch, calls, nbytes, iters: int):
         torch.cuda.synchronize()
         us = np.array([a.elapsed_time(b) for a, b in zip(st, en)]) * 1e3
         med = float(np.median(us))
-        out[name] = {"us": round(med, 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+        out[name] = {"launches": n, "us": round(med, 2), "p10_us": round(float(np.percentile(us, 10)), 2),
                      "p90_us": round(float(np.percentile(us, 90)), 2),
                      "GBps": round(nbytes[name] / med / 1e3, 1),
                      "pct_hbm_peak": round(100.0 * nbytes[name] / med / 1e3 / HBM_PEAK_GBS, 1)}
@@ -203,6 +222,38 @@ def copy_probe(torch):
     dt = (time.perf_counter() - t) / 5
     return {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "us": round(dt * 1e6, 1),
             "GBps_read_plus_write": round(2 * (1 << 30) / dt / 1e9, 1)}
+
+
+def summarize_profile(path: str, filt: str = ""):
+    """Per-kernel figures from rocprofv3 SQLite output under `path`: launch count and mean/min
+    duration from a kernel trace, and per-dispatch counter totals (summed over the rows of one
+    dispatch, averaged over dispatches) from --pmc runs."""
+    import glob
+    import sqlite3
+    from collections import defaultdict
+    trace = defaultdict(list)
+    ctr = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    for f in sorted(glob.glob(os.path.join(path, "**", "*.db"), recursive=True)):
+        con = sqlite3.connect(f)
+        tables = {r[0] for r in con.execute("select name from sqlite_master where type in ('table','view')")}
+        if "kernels" in tables:
+            for name, t0, t1 in con.execute("select name, start, end from kernels"):
+                if filt in name:
+                    trace[name].append((t1 - t0) / 1e3)
+        if "counters_collection" in tables:
+            for name, cn, val, disp in con.execute(
+                    "select kernel_name, counter_name, value, dispatch_id from counters_collection"):
+                if filt in name:
+                    ctr[name][cn][(f, disp)] += val
+        con.close()
+    out = {}
+    for name, ds in trace.items():
+        out.setdefault(name, {})["trace"] = {"launches": len(ds), "avg_us": round(sum(ds) / len(ds), 2),
+                                             "min_us": round(min(ds), 2), "total_us": round(sum(ds), 1)}
+    for name, cs in ctr.items():
+        out.setdefault(name, {})["counters"] = {
+            cn: {"dispatches": len(v), "mean": sum(v.values()) / len(v)} for cn, v in sorted(cs.items())}
+    return out
 
 
 def cpu_baseline(synth):
@@ -279,7 +330,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-call", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="also time a plain 1 GiB copy (counter scaling)")
+    ap.add_argument("--only", choices=CALLS + ("copy",),
+                    help="launch just this call (or the plain 1 GiB copy) --steps times after --warmup, and "
+                         "print its timing; for profiler runs")
+    ap.add_argument("--summarize", metavar="DIR", help="print per-kernel figures from rocprofv3 output in DIR")
+    ap.add_argument("--filter", default="", help="kernel-name substring for --summarize")
     args = ap.parse_args()
+
+    if args.summarize:
+        print(json.dumps(summarize_profile(args.summarize, args.filter), indent=1))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -297,6 +357,24 @@ def main():
     hca.lib()                                 # fails loudly when the HIP library is not built
     nbytes = algorithmic_bytes()
     step_bytes = sum(nbytes.values())
+
+    if args.only == "copy":
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(args.warmup + args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                          "launches": args.warmup + args.steps}), flush=True)
+        return
+    if args.only:
+        W = build_workload(torch, hca, synth, args.ring, only=args.only)
+        calls = prepare_calls(hca, W, args.ring, only=args.only)
+        for i in range(args.warmup):
+            run_call(calls[args.only][i % len(calls[args.only])])
+        r = per_call_pass(torch, calls, nbytes, iters=args.steps, exact=True)[args.only]
+        print(json.dumps({"only": args.only, "algorithmic_bytes": nbytes[args.only], **r}), flush=True)
+        return
 
     W = build_workload(torch, hca, synth, args.ring)
     calls = prepare_calls(hca, W, args.ring)

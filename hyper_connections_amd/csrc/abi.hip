@@ -132,7 +132,7 @@ int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, 
     if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
     if (m == 1)
         return launch_gemv_m1(w, x, y, y_dtype == DHP_F32, argmax, ws, static_cast<hipStream_t>(stream), dev);
-    if (dhp_gemv_mfma16_fits(m, w->cols))
+    if (dhp_gemv_mfma16_fits(w, m))
         return launch_gemv_mfma16(w, x, m, y, y_dtype == DHP_F32, argmax, ws, dhp_argmax_part_stride(w->rows, m),
                                   static_cast<hipStream_t>(stream), dev.cus);
     return launch_gemm_mfma(w, x, m, y, y_dtype == DHP_F32, argmax, ws, dhp_argmax_part_stride(w->rows, m),

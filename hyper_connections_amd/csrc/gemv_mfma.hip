@@ -13,8 +13,13 @@
 //    k = 128 c + 32 g .. +32; the four 32-bit words of that load are the B fragments of the four
 //    MFMA steps of chunk c (virtual k of step t, slot e: 128 c + 32 g + 8 t + perm(e)). Four
 //    lanes read 64 contiguous bytes of a row, the next chunk the following 64.
+//  * The scales and biases of a 16-row tile are contiguous in memory (rows n0 .. n0+15), so a
+//    wave fetches them with a few coalesced dword loads, converts each group's pair to fp16 once
+//    and parks it in its own LDS slice as (s, s | b, b), from where every lane reads the pair of
+//    its row and group with one 8-byte LDS read. Fetching them per chunk from 16 rows at a time
+//    would cost one cache-line lookup per row per 2-byte load and starve the address unit.
 //  * The codes of half a tile are loaded ahead while the other half computes, and the first half
-//    of the wave's next tile while the second half of the current one computes.
+//    of the wave's next tile (with its scales) while the second half of the current one computes.
 //  * Each 16-lane row of the result is summed by the matrix core, so a tile needs no cross-lane
 //    reduction; the argmax keeps, per lane, the best of its four rows over the tiles it saw, then
 //    reduces over lanes (DPP), waves (LDS) and blocks (the shared final kernel).
@@ -40,32 +45,67 @@ DHP_DEV h8 deq8(uint32_t w, h2 s2, h2 b2, const NibConsts& k) {
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+constexpr int SB_DW = 5;            // dwords of scales (and of biases) a lane fetches per tile
+constexpr int SB_PITCH = 2 * HALF * 2 + 1;   // LDS (s,s|b,b) entries per tile row (G <= 40, + 1 pad:
+                                             // the 16 rows of one 8-byte read land on distinct banks)
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 struct HalfRegs {
     u32x4 c[HALF];
-    uint32_t s[HALF], b[HALF];
+};
+
+struct TileSB {
+    uint32_t s[SB_DW], b[SB_DW];
 };
 
 // Loads of chunks [c0, c0 + HALF) of weight row `row` for lane group g (chunks >= nch are
 // clamped to the last chunk and never used).
-DHP_DEV void load_half(HalfRegs& r, const uint8_t* crow, const uint16_t* srow, const uint16_t* brow, int c0,
-                       int nch, int g) {
+DHP_DEV void load_half(HalfRegs& r, const uint8_t* crow, int c0, int nch, int g) {
 #pragma unroll
     for (int i = 0; i < HALF; ++i) {
         const int c = min(c0 + i, nch - 1);
         r.c[i] = *reinterpret_cast<const u32x4*>(crow + (size_t)c * 64 + 16 * g);
-        r.s[i] = srow[2 * c + (g >> 1)];
-        r.b[i] = brow[2 * c + (g >> 1)];
     }
 }
 
-DHP_DEV void mfma_half(const HalfRegs& r, const uint8_t* xl, int xpitch, int c0, int nch, int arow, int g,
-                       f4x& acc, const NibConsts& nk) {
+// The tile's scale and bias dwords (two bf16 groups each): tile dword i = lane + 64 j, clamped to
+// the last dword of the arrays (a clamped dword only feeds columns >= N, which are not stored).
+DHP_DEV void load_tile_sb(TileSB& t, const uint32_t* s32, const uint32_t* b32, size_t first, size_t last,
+                          int lane) {
+#pragma unroll
+    for (int j = 0; j < SB_DW; ++j) {
+        const size_t i = min(first + (size_t)(lane + 64 * j), last);
+        t.s[j] = s32[i];
+        t.b[j] = b32[i];
+    }
+}
+
+// Park the tile's pairs in the wave's LDS slice: entry (row, group) = (s, s | b, b) as fp16.
+DHP_DEV void store_tile_sb(const TileSB& t, uint32_t* sbl, int lane, int half_g, int dwords) {
+#pragma unroll
+    for (int j = 0; j < SB_DW; ++j) {
+        const int i = lane + 64 * j;
+        if (i < dwords) {
+            const int row = i / half_g, grp = 2 * (i - row * half_g);
+            const _Float16 s0 = (_Float16)bf16_to_f32(t.s[j] & 0xFFFFu);
+            const _Float16 s1 = (_Float16)__builtin_bit_cast(float, t.s[j] & 0xFFFF0000u);
+            const _Float16 b0 = (_Float16)bf16_to_f32(t.b[j] & 0xFFFFu);
+            const _Float16 b1 = (_Float16)__builtin_bit_cast(float, t.b[j] & 0xFFFF0000u);
+            u32x2* e = reinterpret_cast<u32x2*>(sbl + 2 * (row * SB_PITCH + grp));
+            e[0] = u32x2{h2_bits(h2{s0, s0}), h2_bits(h2{b0, b0})};
+            e[1] = u32x2{h2_bits(h2{s1, s1}), h2_bits(h2{b1, b1})};
+        }
+    }
+}
+
+DHP_DEV void mfma_half(const HalfRegs& r, const uint8_t* xl, int xpitch, const uint32_t* sbrow, int c0, int nch,
+                       int arow, int g, f4x& acc, const NibConsts& nk) {
 #pragma unroll
     for (int i = 0; i < HALF; ++i) {
         if (c0 + i < nch) {
-            const _Float16 s16 = (_Float16)bf16_to_f32(r.s[i]);
-            const _Float16 b16 = (_Float16)bf16_to_f32(r.b[i]);
-            const h2 s2 = {s16, s16}, b2 = {b16, b16};
+            const u32x2 e = *reinterpret_cast<const u32x2*>(sbrow + 2 * (2 * (c0 + i) + (g >> 1)));
+            const h2 s2 = as_h2(e.x), b2 = as_h2(e.y);
             const uint32_t ww[4] = {r.c[i].x, r.c[i].y, r.c[i].z, r.c[i].w};
             const uint8_t* ap = xl + arow * xpitch + ((c0 + i) * 128 + 32 * g) * 2;
 #pragma unroll
@@ -85,12 +125,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_mfma16(
     void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i) {
     extern __shared__ __align__(16) uint8_t xl[];      // [M][K halves, permuted by eights] + pad
     const int xpitch = 2 * K + 16;
+    // after the activations: one (s,s|b,b) slice of 16 x SB_PITCH entries per wave
+    uint32_t* sbl = reinterpret_cast<uint32_t*>(xl + (size_t)M * xpitch) + (threadIdx.x >> 6) * (16 * SB_PITCH * 2);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
     const int nch = K >> 7;                           // 128-k chunks
     const int G = K >> 6;
+    const int half_g = G >> 1;                        // scale dwords per row
+    const int tile_dw = 16 * half_g;                  // scale dwords per tile
+    const size_t last_dw = (size_t)N * half_g - 1;
+    const auto* s32 = reinterpret_cast<const uint32_t*>(scales);
+    const auto* b32 = reinterpret_cast<const uint32_t*>(biases);
     const size_t row_bytes = (size_t)K >> 1;
 
     // stage the activations, permuted (x0,x4,x1,x5,x2,x6,x3,x7) within each group of eight
@@ -116,21 +163,32 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_mfma16(
     const bool two = nch > HALF;                       // K <= 2560: at most two half tiles
     int tile = blockIdx.x * WAVES + wave;
     HalfRegs h0, h1;
+    TileSB sb;
     if (tile < ntiles) {
         const int row = min(tile * 16 + n, N - 1);
-        load_half(h0, codes + (size_t)row * row_bytes, scales + (size_t)row * G, biases + (size_t)row * G, 0, nch, g);
+        load_tile_sb(sb, s32, b32, (size_t)tile * tile_dw, last_dw, lane);
+        load_half(h0, codes + (size_t)row * row_bytes, 0, nch, g);
     }
+    const uint32_t* sbrow = sbl + 2 * n * SB_PITCH;
     // loads are unconditional (clamped rows and chunks) so the compiler can count them and wait
-    // only for the half about to be used
+    // only for the data about to be used
     for (; tile < ntiles; tile += stride) {
         const int n0 = tile * 16;
         const int row = min(n0 + n, N - 1);
         f4x acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        load_half(h1, codes + (size_t)row * row_bytes, scales + (size_t)row * G, biases + (size_t)row * G, HALF, nch, g);
-        mfma_half(h0, xl, xpitch, 0, nch, arow, g, acc, nk);
-        const int nrow = min((tile + stride) * 16 + n, N - 1);      // the next tile's first half
-        load_half(h0, codes + (size_t)nrow * row_bytes, scales + (size_t)nrow * G, biases + (size_t)nrow * G, 0, nch, g);
-        if (two) mfma_half(h1, xl, xpitch, HALF, nch, arow, g, acc, nk);
+        // the previous tile's LDS reads were issued before these writes (one wave, in order)
+        __builtin_amdgcn_wave_barrier();
+        store_tile_sb(sb, sbl, lane, half_g, tile_dw);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        load_half(h1, codes + (size_t)row * row_bytes, HALF, nch, g);
+        mfma_half(h0, xl, xpitch, sbrow, 0, nch, arow, g, acc, nk);
+        const int ntile = tile + stride;                               // the next tile's scales + first half
+        const int nrow = min(ntile * 16 + n, N - 1);
+        load_tile_sb(sb, s32, b32, min((size_t)ntile * tile_dw, last_dw), last_dw, lane);
+        load_half(h0, codes + (size_t)nrow * row_bytes, 0, nch, g);
+        if (two) mfma_half(h1, xl, xpitch, sbrow, HALF, nch, arow, g, acc, nk);
         // lane (n, g) holds rows 4 g .. 4 g + 3 of column n0 + n
         const int col = n0 + n;
 #pragma unroll
@@ -177,21 +235,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_mfma16(
 
 hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s);
 
-// Whether the streamed matrix-core arm takes this shape (else the LDS-staged GEMM does).
-bool dhp_gemv_mfma16_fits(int M, int K) { return M >= 2 && M <= 16 && K % 128 == 0 && K <= 2 * HALF * 128; }
-
-int dhp_gemv_mfma16_blocks(int N, int cus) {
-    const int ntiles = (N + 15) / 16;
-    int blocks = (ntiles + WAVES - 1) / WAVES;
-    const int cap = 3 * cus;
-    return blocks < cap ? blocks : cap;
+// Whether the streamed matrix-core arm takes this call (else the LDS-staged GEMM does): its scale
+// and bias fetches are dword loads, so those arrays must be 4-byte aligned.
+bool dhp_gemv_mfma16_fits(const dhp_int4* w, int M) {
+    const int K = w->cols;
+    return M >= 2 && M <= 16 && K % 128 == 0 && K <= 2 * HALF * 128 &&
+           reinterpret_cast<uintptr_t>(w->scales) % 4 == 0 && reinterpret_cast<uintptr_t>(w->biases) % 4 == 0;
 }
 
 int launch_gemv_mfma16(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
                        size_t ws_part_stride, hipStream_t s, int cus) {
     const int N = w->rows, K = w->cols;
-    const int blocks = dhp_gemv_mfma16_blocks(N, cus);
-    const size_t lds = (size_t)M * (2 * K + 16);
+    const size_t lds = (size_t)M * (2 * K + 16) + (size_t)WAVES * 16 * SB_PITCH * 8;
     const auto* c = static_cast<const uint8_t*>(w->codes);
     const auto* sc = static_cast<const uint16_t*>(w->scales);
     const auto* bi = static_cast<const uint16_t*>(w->biases);
@@ -207,10 +262,28 @@ int launch_gemv_mfma16(const dhp_int4* w, const void* x, int M, void* y, int y_f
                               reinterpret_cast<const void*>(&k_gemv_mfma16<false, true>),
                               reinterpret_cast<const void*>(&k_gemv_mfma16<false, false>)};
         for (const void* f : fns)
-            if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 16 * (2 * 2 * HALF * 128 + 16)) != hipSuccess)
+            if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    16 * (2 * 2 * HALF * 128 + 16) + WAVES * 16 * SB_PITCH * 8) != hipSuccess)
                 return dhp_fail(DHP_ERR_LAUNCH, "hipFuncSetAttribute");
         __atomic_fetch_or(&configured, 1ull << (dev & 63), __ATOMIC_RELEASE);
     }
+    // one resident round of blocks: as many per CU as registers and LDS allow (the waves stride
+    // over the tiles, so more blocks than fit would only run as a tail)
+    static int resident[64][17][4];                   // per device, m and variant; 0 = not yet queried
+    const int variant = (y_f32 ? 2 : 0) + (argmax ? 1 : 0);
+    int per_cu = __atomic_load_n(&resident[dev & 63][M][variant], __ATOMIC_RELAXED);
+    if (per_cu == 0) {
+        const void* f = y_f32 ? (argmax ? reinterpret_cast<const void*>(&k_gemv_mfma16<true, true>)
+                                        : reinterpret_cast<const void*>(&k_gemv_mfma16<true, false>))
+                              : (argmax ? reinterpret_cast<const void*>(&k_gemv_mfma16<false, true>)
+                                        : reinterpret_cast<const void*>(&k_gemv_mfma16<false, false>));
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, WAVES * 64, lds) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        __atomic_store_n(&resident[dev & 63][M][variant], per_cu, __ATOMIC_RELAXED);
+    }
+    const int ntiles = (N + 15) / 16;
+    int blocks = (ntiles + WAVES - 1) / WAVES;
+    if (blocks > per_cu * cus) blocks = per_cu * cus;
     const dim3 g((unsigned)blocks), b(WAVES * 64);
     if (y_f32 && argmax) hipLaunchKernelGGL((k_gemv_mfma16<true, true>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
     else if (y_f32) hipLaunchKernelGGL((k_gemv_mfma16<true, false>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);

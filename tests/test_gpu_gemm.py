@@ -115,3 +115,40 @@ def test_multirow_argmax_repeated_calls():
     outs = [hca.dequant_gemv(w, xd, out_dtype=torch.float32, argmax=True)[1] for _ in range(10)]
     torch.cuda.synchronize()
     assert all(o.cpu().numpy().tolist() == ref for o in outs)
+
+
+@pytest.mark.parametrize("m,n,k", [(2, 33, 128), (5, 17, 640), (9, 4099, 1280), (16, 1000, 2560), (3, 1, 2560),
+                                   (12, 16, 384), (2, 70001, 2560)])
+def test_gemv_multirow_ragged_tiles(m, n, k):
+    # tiles of 16 weight rows with a ragged last tile; K a multiple of 128 up to 2560
+    say(f"gemv multi-row ragged m={m} n={n} k={k}")
+    rng = np.random.default_rng([76, m, n, k])
+    t = synth.int4_tensor(rng, n, k)
+    X = synth.normal_f16(rng, (m, k))
+    y, am = hca.dequant_gemv(dev(t), torch.from_numpy(X).cuda(), out_dtype=torch.float32, argmax=True)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, X)
+    assert_within_tol(y.cpu().numpy(), ref, f"gemv m={m} n={n} k={k}")
+    assert am.cpu().numpy().tolist() == oracle.argmax_lowest(ref).tolist()
+
+
+def test_gemv_multirow_scales_at_odd_halfword():
+    # scale/bias arrays that are only 2-byte aligned take the other matrix-core arm; same results
+    say("gemv multi-row, scales 2-byte aligned")
+    rng = np.random.default_rng(77)
+    m, n, k = 6, 3000, 2560
+    t = synth.int4_tensor(rng, n, k)
+    X = synth.normal_f16(rng, (m, k))
+    w = dev(t)
+    g = k // 64
+    s_store = torch.zeros(n * g + 1, dtype=torch.int16, device="cuda")
+    b_store = torch.zeros(n * g + 1, dtype=torch.int16, device="cuda")
+    s_store[1:] = w.scales.reshape(-1)
+    b_store[1:] = w.biases.reshape(-1)
+    odd = hca.Int4Weight(w.codes, s_store[1:].view(n, g), b_store[1:].view(n, g), n, k)
+    xd = torch.from_numpy(X).cuda()
+    y_odd, am_odd = hca.dequant_gemv(odd, xd, out_dtype=torch.float32, argmax=True)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, X)
+    assert_within_tol(y_odd.cpu().numpy(), ref, "gemv m=6 odd-halfword scales")
+    assert am_odd.cpu().numpy().tolist() == oracle.argmax_lowest(ref).tolist()
