@@ -7,8 +7,8 @@
 // Metal kernels (per-thread accumulator arrays; a simdgroup-matrix variant) are prior art;
 // this is a gfx950 design around v_mfma_f32_32x32x16_f16:
 //
-//  * A block owns a 32*MT x 64 output tile (activation rows x weight rows). Its four waves
-//    split K into four contiguous ranges of stages (S k-blocks of 64 each); each wave keeps the
+//  * A block owns a 32*MT x 64 output tile (activation rows x weight rows). Its waves (four or
+//    eight) split K into contiguous ranges of stages (S k-blocks of 64 each); each wave keeps the
 //    whole tile in its accumulators and works out of a private LDS region, so waves never wait
 //    for each other until the end.
 //  * Operands reach LDS through fully coalesced 16-byte loads (consecutive lanes walk one row's
@@ -20,8 +20,8 @@
 //    one packed fma) and feeds four MFMA steps. The activation tile is the A operand, read with
 //    the same permutation of k inside each group of eight, so both operands agree on which k
 //    each register slot holds.
-//  * The four partial tiles are summed through LDS in a fixed order (3, 2, 1, 0), so results
-//    are deterministic. The epilogue writes fp16 or fp32 and, for the GEMV arm, a per-block
+//  * The waves' partial tiles meet in LDS (one slice each, written at once) and every output
+//    is summed over them in a fixed order, so results are deterministic. The epilogue writes fp16 or fp32 and, for the GEMV arm, a per-block
 //    argmax partial per row, reduced by the same small final kernel the M=1 path uses.
 #include "dhp_internal.hpp"
 
@@ -65,7 +65,8 @@ struct WaveLds {
     static constexpr int W_BYTES = 64 * WP;
     static constexpr int X_BYTES = 32 * MT * XP;
     static constexpr int SB_BYTES = 64 * SBP * 4;
-    static constexpr int BYTES = W_BYTES + X_BYTES + SB_BYTES;
+    static constexpr int TRASH = W_BYTES + X_BYTES + SB_BYTES;   // 16 bytes per lane: rows past the tile
+    static constexpr int BYTES = TRASH + 64 * 16;
     static constexpr int WL = 2 * S;          // 16-byte weight loads per lane per stage
     static constexpr int XL = 4 * MT * S;     // 16-byte activation loads per lane per stage (max)
 };
@@ -75,6 +76,7 @@ struct StageRegs {
     u32x4 w[WaveLds<MT, S>::WL];
     u32x4 x[WaveLds<MT, S>::XL];
     uint32_t sc[S], bi[S];
+    int kbs;                                   // first k-block of the stage
 };
 
 // Per-lane load and store addresses of a stage, computed once per wave (only the k offset
@@ -84,12 +86,12 @@ struct StagePlan {
     const uint8_t* wsrc[WaveLds<MT, S>::WL];   // weight row start + byte offset of this lane's chunk
     int wkb[WaveLds<MT, S>::WL];               // k-block of that chunk within a stage
     int wdst[WaveLds<MT, S>::WL];              // LDS byte offset
-    const _Float16* xsrc[WaveLds<MT, S>::XL];
+    const _Float16* xbase;                     // first activation row of the tile (wave-uniform)
+    int xoff[WaveLds<MT, S>::XL];              // halves from xbase (row clamped into the tile)
     int xkb[WaveLds<MT, S>::XL];
-    int xdst[WaveLds<MT, S>::XL];              // -1: no store (padding row)
+    int xdst[WaveLds<MT, S>::XL];              // LDS byte offset (the trash slot for rows past the tile)
     const uint16_t* ssrc;
     const uint16_t* bsrc;
-    int xiters;
 };
 
 template <int MT, int S>
@@ -106,14 +108,14 @@ DHP_DEV void stage_plan(StagePlan<MT, S>& p, int lane, const uint8_t* codes, con
         p.wkb[i] = cc >> 1;
         p.wdst[i] = row * L::WP + cc * 16;
     }
-    p.xiters = (xrows * 8 * S + 63) >> 6;
+    p.xbase = X + (size_t)m0 * K;
 #pragma unroll
     for (int i = 0; i < L::XL; ++i) {
         const int c = i * 64 + lane;
         const int row = c / (8 * S), cc = c % (8 * S);
-        p.xsrc[i] = X + (size_t)(m0 + min(row, xrows - 1)) * K + (cc & 7) * 8;
+        p.xoff[i] = min(row, xrows - 1) * K + (cc & 7) * 8;
         p.xkb[i] = cc >> 3;
-        p.xdst[i] = (row < xrows) ? L::W_BYTES + row * L::XP + cc * 16 : -1;
+        p.xdst[i] = (row < xrows) ? L::W_BYTES + row * L::XP + cc * 16 : L::TRASH + 16 * lane;
     }
     const size_t n = (size_t)min(n0 + lane, N - 1);
     p.ssrc = scales + n * KB;
@@ -124,51 +126,40 @@ DHP_DEV void stage_plan(StagePlan<MT, S>& p, int lane, const uint8_t* codes, con
 // their addresses are clamped to the last real k-block and their scale and bias read as zero,
 // so they dequantize to exact zeros).
 template <int MT, int S>
-DHP_DEV void stage_load(StageRegs<MT, S>& r, const StagePlan<MT, S>& p, int kbs, int kb1, bool sb_vec) {
+DHP_DEV void stage_load(StageRegs<MT, S>& r, const StagePlan<MT, S>& p, int kbs, int kb1) {
     using L = WaveLds<MT, S>;
 #pragma unroll
     for (int i = 0; i < L::WL; ++i)
         r.w[i] = *reinterpret_cast<const u32x4*>(p.wsrc[i] + (size_t)min(kbs + p.wkb[i], kb1 - 1) * 32);
+    // every activation load is issued (rows past the tile are clamped to its last row and parked
+    // in a trash slot), so loads and stores stay unconditional and the compiler can count them
 #pragma unroll
     for (int i = 0; i < L::XL; ++i)
-        if (i < p.xiters)
-            r.x[i] = *reinterpret_cast<const u32x4*>(p.xsrc[i] + (size_t)min(kbs + p.xkb[i], kb1 - 1) * 64);
-    if (sb_vec) {                            // S groups of this row in one aligned vector load each
-        if constexpr (S == 4) {
-            const uint2 sv = *reinterpret_cast<const uint2*>(p.ssrc + kbs);
-            const uint2 bv = *reinterpret_cast<const uint2*>(p.bsrc + kbs);
-            r.sc[0] = sv.x & 0xFFFFu; r.sc[1] = sv.x >> 16; r.sc[2] = sv.y & 0xFFFFu; r.sc[3] = sv.y >> 16;
-            r.bi[0] = bv.x & 0xFFFFu; r.bi[1] = bv.x >> 16; r.bi[2] = bv.y & 0xFFFFu; r.bi[3] = bv.y >> 16;
-        } else {
-            const uint32_t sv = *reinterpret_cast<const uint32_t*>(p.ssrc + kbs);
-            const uint32_t bv = *reinterpret_cast<const uint32_t*>(p.bsrc + kbs);
-            r.sc[0] = sv & 0xFFFFu; r.sc[1] = sv >> 16;
-            r.bi[0] = bv & 0xFFFFu; r.bi[1] = bv >> 16;
-        }
-    } else {
+        r.x[i] = *reinterpret_cast<const u32x4*>(p.xbase + (p.xoff[i] + min(kbs + p.xkb[i], kb1 - 1) * 64));
+    // scales and biases: the raw 16-bit words (any arithmetic on them here would make the wave
+    // wait for this stage's loads right after issuing them)
 #pragma unroll
-        for (int q = 0; q < S; ++q) {
-            const int kb = min(kbs + q, kb1 - 1);
-            r.sc[q] = p.ssrc[kb];
-            r.bi[q] = p.bsrc[kb];
-        }
+    for (int q = 0; q < S; ++q) {
+        const int kb = min(kbs + q, kb1 - 1);
+        r.sc[q] = p.ssrc[kb];
+        r.bi[q] = p.bsrc[kb];
     }
-#pragma unroll
-    for (int q = 0; q < S; ++q)
-        if (kbs + q >= kb1) { r.sc[q] = 0u; r.bi[q] = 0u; }
+    // k-blocks past kb1 are masked when the stage is parked in LDS, not here: a select on a
+    // loaded value would make the wave wait for this stage's loads right after issuing them
+    r.kbs = kbs;
 }
 
 template <int MT, int S>
-DHP_DEV void stage_store(const StageRegs<MT, S>& r, const StagePlan<MT, S>& p, uint8_t* lds, int lane) {
+DHP_DEV void stage_store(const StageRegs<MT, S>& r, const StagePlan<MT, S>& p, uint8_t* lds, int lane, int kb1) {
     using L = WaveLds<MT, S>;
 #pragma unroll
     for (int i = 0; i < L::WL; ++i) *reinterpret_cast<u32x4*>(lds + p.wdst[i]) = r.w[i];
 #pragma unroll
-    for (int i = 0; i < L::XL; ++i)
-        if (i < p.xiters && p.xdst[i] >= 0) *reinterpret_cast<u32x4*>(lds + p.xdst[i]) = r.x[i];
+    for (int i = 0; i < L::XL; ++i) *reinterpret_cast<u32x4*>(lds + p.xdst[i]) = r.x[i];
     uint32_t* sb = reinterpret_cast<uint32_t*>(lds + L::W_BYTES + L::X_BYTES);
+    // padding k-blocks (at or past kb1) get scale and bias 0: their codes dequantize to zeros
 #pragma unroll
-    for (int q = 0; q < S; ++q) sb[lane * L::SBP + q] = r.sc[q] | (r.bi[q] << 16);
+    for (int q = 0; q < S; ++q) sb[lane * L::SBP + q] = (r.kbs + q < kb1) ? (r.sc[q] | (r.bi[q] << 16)) : 0u;
 }
 
 // MFMAs of one stage from LDS. B fragment of lane (li, g) for k-block q4: weight row 32 nt + li,
@@ -181,42 +172,44 @@ DHP_DEV void stage_mfma(const uint8_t* lds, int li, int g, f16x16 (*acc)[2], con
     const uint32_t* sb = reinterpret_cast<const uint32_t*>(lds + L::W_BYTES + L::X_BYTES);
 #pragma unroll
     for (int q4 = 0; q4 < S; ++q4) {
-        h8 b[2][4];
+        u32x4 cw[2];
+        h2 s2[2], b2[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int row = 32 * nt + li;
-            const u32x4 cw = *reinterpret_cast<const u32x4*>(lds + row * L::WP + q4 * 32 + 16 * g);
+            cw[nt] = *reinterpret_cast<const u32x4*>(lds + row * L::WP + q4 * 32 + 16 * g);
             const uint32_t sbv = sb[row * L::SBP + q4];
             const _Float16 s16 = (_Float16)bf16_to_f32(sbv & 0xFFFFu);
             const _Float16 b16 = (_Float16)bf16_to_f32(sbv >> 16);
-            const h2 s2 = {s16, s16}, b2 = {b16, b16};
-            b[nt][0] = dequant8(cw.x, s2, b2, nk);
-            b[nt][1] = dequant8(cw.y, s2, b2, nk);
-            b[nt][2] = dequant8(cw.z, s2, b2, nk);
-            b[nt][3] = dequant8(cw.w, s2, b2, nk);
+            s2[nt] = h2{s16, s16};
+            b2[nt] = h2{b16, b16};
         }
+        // one MFMA step at a time: its two B fragments, then the MT activation fragments
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            h8 b[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) b[nt] = dequant8(cw[nt][q], s2[nt], b2[nt], nk);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + (32 * mt + li) * L::XP + q4 * 128 + 64 * g + 16 * q);
                 const h8 a = permute_x8(xv);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[nt][q], acc[mt][nt], 0, 0, 0);
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[nt], acc[mt][nt], 0, 0, 0);
             }
         }
     }
 }
 
-template <int MT, int S, bool F32OUT, bool ARGMAX>
-__global__ __launch_bounds__(256) void k_gemm_mfma(
+template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ X, int M, int N, int K,
-    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i, int sb_aligned) {
+    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i) {
     using L = WaveLds<MT, S>;
     constexpr int ROWS = 32 * MT;
-    extern __shared__ __align__(16) uint8_t lds_all[];   // 4 wave regions; reused by the epilogue
+    extern __shared__ __align__(16) uint8_t lds_all[];   // one region per wave; reused by the epilogue
     float* tile = reinterpret_cast<float*>(lds_all);
 
     const int wave = threadIdx.x >> 6;
@@ -235,48 +228,68 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f16x16{};
 
-    // stage-aligned split of K over the four waves
+    // stage-aligned split of K over the waves
     const int ST = (KB + S - 1) / S;
-    const int st0 = (ST * wave) >> 2, st1 = (ST * (wave + 1)) >> 2;
+    const int st0 = (ST * wave) / WAVES, st1 = (ST * (wave + 1)) / WAVES;
     const int kb1 = min(st1 * S, KB);
-    const bool sb_vec = sb_aligned && (KB % S) == 0;   // every stage's S groups are vector-aligned
-    if (st0 < st1) {
-        const NibConsts nk = nib_consts();
-        StagePlan<MT, S> plan;
+    const bool has = st0 < st1;
+    StagePlan<MT, S> plan;
+    StageRegs<MT, S> r0, r1;
+    // two register sets: while stage st computes out of LDS, stages st+1 and st+2 are in flight
+    if (has) {
         stage_plan<MT, S>(plan, lane, codes, scales, biases, X, n0, N, m0, xrows, K, KB);
-        StageRegs<MT, S> r;
-        stage_load<MT, S>(r, plan, st0 * S, kb1, sb_vec);
-        for (int st = st0; st < st1; ++st) {
-            stage_store<MT, S>(r, plan, lds, lane);
+        stage_load<MT, S>(r0, plan, st0 * S, kb1);
+        stage_load<MT, S>(r1, plan, (st0 + 1) * S, kb1);
+    }
+    if (has) {
+        const NibConsts nk = nib_consts();
+        // The steady-state loop has no branch around a load (the compiler then waits for exactly
+        // the set it is about to park): the stage count is padded to even (the padding stage's
+        // k-blocks are past kb1, so it is loaded clamped and never multiplied) and the last pair
+        // is peeled off.
+        const int st1e = st0 + ((st1 - st0 + 1) & ~1);
+        int st = st0;
+        for (; st + 2 < st1e; st += 2) {
+            stage_store<MT, S>(r0, plan, lds, lane, kb1);
             __builtin_amdgcn_wave_barrier();
-            if (st + 1 < st1) stage_load<MT, S>(r, plan, (st + 1) * S, kb1, sb_vec);
+            stage_load<MT, S>(r0, plan, (st + 2) * S, kb1);
             stage_mfma<MT, S>(lds, li, g, acc, nk);
             __builtin_amdgcn_wave_barrier();
+            stage_store<MT, S>(r1, plan, lds, lane, kb1);
+            __builtin_amdgcn_wave_barrier();
+            stage_load<MT, S>(r1, plan, (st + 3) * S, kb1);
+            stage_mfma<MT, S>(lds, li, g, acc, nk);
+            __builtin_amdgcn_wave_barrier();
+        }
+        stage_store<MT, S>(r0, plan, lds, lane, kb1);
+        __builtin_amdgcn_wave_barrier();
+        stage_mfma<MT, S>(lds, li, g, acc, nk);
+        __builtin_amdgcn_wave_barrier();
+        if (st + 1 < st1) {
+            stage_store<MT, S>(r1, plan, lds, lane, kb1);
+            __builtin_amdgcn_wave_barrier();
+            stage_mfma<MT, S>(lds, li, g, acc, nk);
         }
     }
     __syncthreads();                           // staging regions are now free for the epilogue
 
-    // fixed-order reduction of the four K slices: wave 3, then 2, 1, 0
+    // every wave parks its partial tile in a slice of its own; then each thread sums its outputs
+    // over the slices in a fixed order (the last wave's first, down to wave 0), so a result does
+    // not depend on timing
+    constexpr int SLICE = ROWS * LDW;
 #pragma unroll
-    for (int w = 3; w >= 0; --w) {
-        if (wave == w) {
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-                        const int j = 32 * nt + li;
-                        float* p = &tile[i * LDW + j];
-                        *p = (w == 3) ? acc[mt][nt][r] : *p + acc[mt][nt][r];
-                    }
-        }
-        __syncthreads();
-    }
+            for (int r = 0; r < 16; ++r) {
+                const int i = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+                tile[wave * SLICE + i * LDW + 32 * nt + li] = acc[mt][nt][r];
+            }
+    __syncthreads();
 
-    // epilogue: 256 threads over ROWS x 64 outputs; TPR threads per row, contiguous columns
-    constexpr int TPR = 256 / ROWS;
+    // epilogue: all threads over ROWS x 64 outputs; TPR threads per row, contiguous columns
+    constexpr int TPR = 64 * WAVES / ROWS;
     constexpr int CPT = BN / TPR;
     const int row = threadIdx.x / TPR;
     const int c0 = (threadIdx.x % TPR) * CPT;
@@ -284,23 +297,49 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(
     float bv = -INFINITY;
     int bi = INT_MAX;
     if (m < M) {
+        float v[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            const int n = n0 + c0 + c;
-            if (n < N) {
-                const float v = tile[row * LDW + c0 + c];
-                if constexpr (F32OUT) reinterpret_cast<float*>(Y)[(size_t)m * N + n] = v;
-                else reinterpret_cast<_Float16*>(Y)[(size_t)m * N + n] = (_Float16)v;
-                if constexpr (ARGMAX)
-                    if (better(v, n, bv, bi)) { bv = v; bi = n; }
+            v[c] = tile[(WAVES - 1) * SLICE + row * LDW + c0 + c];
+#pragma unroll
+            for (int w = WAVES - 2; w >= 0; --w) v[c] += tile[w * SLICE + row * LDW + c0 + c];
+        }
+        const int nb = n0 + c0;
+        // the thread's CPT contiguous outputs in one or two 16-byte stores when the row allows
+        const bool vec = (reinterpret_cast<uintptr_t>(Y) & 15) == 0 && (N & 7) == 0 && nb + CPT <= N;
+        if (vec) {
+            if constexpr (F32OUT) {
+                float* yp = reinterpret_cast<float*>(Y) + (size_t)m * N + nb;
+#pragma unroll
+                for (int j = 0; j < CPT; j += 4) *reinterpret_cast<f4v*>(yp + j) = f4v{v[j], v[j + 1], v[j + 2], v[j + 3]};
+            } else {
+                _Float16* yp = reinterpret_cast<_Float16*>(Y) + (size_t)m * N + nb;
+#pragma unroll
+                for (int j = 0; j < CPT; j += 4) {
+                    const h2 lo = {(_Float16)v[j], (_Float16)v[j + 1]}, hi = {(_Float16)v[j + 2], (_Float16)v[j + 3]};
+                    *reinterpret_cast<uint2*>(yp + j) = uint2{h2_bits(lo), h2_bits(hi)};
+                }
             }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c)
+                if (nb + c < N) {
+                    if constexpr (F32OUT) reinterpret_cast<float*>(Y)[(size_t)m * N + nb + c] = v[c];
+                    else reinterpret_cast<_Float16*>(Y)[(size_t)m * N + nb + c] = (_Float16)v[c];
+                }
+        }
+        if constexpr (ARGMAX) {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c)
+                if (nb + c < N && better(v[c], nb + c, bv, bi)) { bv = v[c]; bi = nb + c; }
         }
     }
     if constexpr (ARGMAX) {
-        static_assert(TPR == 8 || TPR == 4, "threads per row");
+        static_assert(TPR == 16 || TPR == 8 || TPR == 4, "threads per row");
         best_step<DPP_XOR1>(bv, bi);
         best_step<DPP_XOR2>(bv, bi);
-        if constexpr (TPR == 8) best_step<DPP_HALF_MIRROR>(bv, bi);
+        if constexpr (TPR >= 8) best_step<DPP_HALF_MIRROR>(bv, bi);
+        if constexpr (TPR == 16) best_step<DPP_MIRROR>(bv, bi);
         if (threadIdx.x % TPR == 0 && m < M) {
             part_v[(size_t)m * gridDim.x + blockIdx.x] = bv;
             part_i[(size_t)m * gridDim.x + blockIdx.x] = bi;
@@ -308,29 +347,30 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(
     }
 }
 
-template <int MT, int S, bool F32OUT, bool ARGMAX>
+template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX>
 hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t* sc, const uint16_t* bi,
                       const _Float16* xh, int M, int N, int K, void* y, float* pv, int* pi) {
     using L = WaveLds<MT, S>;
-    constexpr size_t lds = (4 * L::BYTES > 32 * MT * LDW * 4) ? 4 * L::BYTES : 32 * MT * LDW * 4;
+    constexpr size_t red = (size_t)WAVES * 32 * MT * LDW * 4;    // one partial tile per wave
+    constexpr size_t lds = (WAVES * L::BYTES > red) ? WAVES * L::BYTES : red;
     // more than 64 KiB of dynamic LDS must be allowed per function (and device) once
     static unsigned long long configured = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
     const unsigned long long bit = 1ull << (dev & 63);
     if (!(__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & bit)) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, F32OUT, ARGMAX>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         __atomic_fetch_or(&configured, bit, __ATOMIC_RELEASE);
     }
-    const int sb_aligned = (reinterpret_cast<uintptr_t>(sc) % (2 * S) == 0) && (reinterpret_cast<uintptr_t>(bi) % (2 * S) == 0);
-    hipLaunchKernelGGL((k_gemm_mfma<MT, S, F32OUT, ARGMAX>), grid, dim3(256), lds, s, c, sc, bi, xh, M, N, K, y, pv, pi,
-                       sb_aligned);
+    hipLaunchKernelGGL((k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX>), grid, dim3(64 * WAVES), lds, s, c, sc, bi, xh, M,
+                       N, K, y, pv, pi);
     return hipGetLastError();
 }
 
-template <int MT, int S>
+template <int MT, int S, int WAVES>
 hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4* w, const void* x,
                      int M, void* y, float* pv, int* pi) {
     const auto* c = static_cast<const uint8_t*>(w->codes);
@@ -338,10 +378,10 @@ hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4
     const auto* bi = static_cast<const uint16_t*>(w->biases);
     const auto* xh = static_cast<const _Float16*>(x);
     const int N = w->rows, K = w->cols;
-    if (f32 && am) return launch_one<MT, S, true, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    if (f32) return launch_one<MT, S, true, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    if (am) return launch_one<MT, S, false, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    return launch_one<MT, S, false, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    if (f32 && am) return launch_one<MT, S, WAVES, true, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    if (am) return launch_one<MT, S, WAVES, false, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    if (f32) return launch_one<MT, S, WAVES, true, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    return launch_one<MT, S, WAVES, false, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
 }
 
 }  // namespace
@@ -358,8 +398,10 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     float* pv = argmax ? static_cast<float*>(ws) : nullptr;
     int* pi = argmax ? reinterpret_cast<int*>(static_cast<char*>(ws) + ws_part_stride) : nullptr;
     if (argmax && grid.y != 1) return dhp_fail(DHP_ERR_UNSUPPORTED, "argmax with m=%d", M);
-    const hipError_t e = (MT == 1) ? launch_mt<1, 2>(y_f32, argmax != nullptr, grid, s, w, x, M, y, pv, pi)
-                                   : launch_mt<2, 2>(y_f32, argmax != nullptr, grid, s, w, x, M, y, pv, pi);
+    // eight waves of 64-k stages (two per SIMD) with two stages in flight per wave
+    const bool am = argmax != nullptr;
+    const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi)
+                                   : launch_mt<2, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
     if (argmax) {
         const hipError_t e2 = launch_argmax_final(pv, pi, (int)grid.x, M, argmax, s);
