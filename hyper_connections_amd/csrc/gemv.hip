@@ -12,7 +12,7 @@
 //  * The activation slice a lane needs is the same for every row it visits, so it is
 //    loaded once, rearranged into the pair order of the nibble unpack, and kept in
 //    registers (K = 2560: 80 VGPRs). A block walks rows with a grid stride and keeps the
-//    next row's codes in flight while it computes the current one.
+//    next row group's codes in flight while it computes the current one.
 //  * Per 64-weight group the affine form is factored: s * sum(q*x) + b * sum(x); the
 //    inner sum runs on v_dot2_f32_f16 over exactly converted codes (see unpack8).
 //  * The 16 partial sums of a row meet in a fixed butterfly, so a row's value does not
@@ -84,10 +84,17 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     const int j = t % LPR;
     const int rpb = blockDim.x / LPR;
     const int stride = gridDim.x * rpb;
-    int row = blockIdx.x * rpb + t / LPR;
-
-    RowRegs cur[CPL];
-    if (row < N) load_row<CPL>(codes, scales, biases, row, j, cur);
+    // A wave owns four consecutive rows per step. Control flow follows the wave's first row, so
+    // every lane runs the same iterations and the loads stay unconditional (rows past N are
+    // clamped to the last row and their results are not stored). A guard around a load would
+    // make the compiler wait for every load in flight at the first use of any of them.
+    const int rw = (t & 63) / LPR;
+    int base = __builtin_amdgcn_readfirstlane(blockIdx.x * rpb + (t >> 6) * (64 / LPR));
+    // One register set: the compiler issues the next row group's loads (into fresh registers)
+    // before computing the current one, so one group per wave is in flight. More in flight
+    // (three sets) measured slower: past about 40 KB per CU the HBM read rate drops.
+    RowRegs r[CPL];
+    load_row<CPL>(codes, scales, biases, min(base + rw, N - 1), j, r);
 
     h2 xp[CPL][16];
     float xs[CPL];
@@ -97,26 +104,23 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     const NibConsts nk = nib_consts();
     float best_v = -INFINITY;
     int best_i = INT_MAX;
-    for (; row < N; row += stride) {
-        const int nxt = row + stride;
-        RowRegs nx[CPL];
-        if (nxt < N) load_row<CPL>(codes, scales, biases, nxt, j, nx);
+    for (; base < N; base += stride) {
+        const int row = base + rw;
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const float d = dot32_f16(cur[i].c, xp[i], nk);
-            acc = __builtin_fmaf(bf16_to_f32(cur[i].s), d, acc);
-            acc = __builtin_fmaf(bf16_to_f32(cur[i].b), xs[i], acc);
+            const float d = dot32_f16(r[i].c, xp[i], nk);
+            acc = __builtin_fmaf(bf16_to_f32(r[i].s), d, acc);
+            acc = __builtin_fmaf(bf16_to_f32(r[i].b), xs[i], acc);
         }
         acc = group_sum<LPR>(acc);
-        if (j == 0) {
+        if (j == 0 && row < N) {
             if constexpr (F32OUT) reinterpret_cast<float*>(y)[row] = acc;
             else reinterpret_cast<_Float16*>(y)[row] = (_Float16)acc;
             if constexpr (ARGMAX)
                 if (better(acc, row, best_v, best_i)) { best_v = acc; best_i = row; }
         }
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) cur[i] = nx[i];
+        load_row<CPL>(codes, scales, biases, min(base + stride + rw, N - 1), j, r);
     }
     block_argmax_write<ARGMAX>(best_v, best_i, j == 0, part_v, part_i);
 }
