@@ -97,17 +97,25 @@ DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* 
     return silu_f(ag) * au;
 }
 
-// fp32 dot of one bf16 or fp32 row of length `hidden` with the fp16 activations, one wave.
-DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x, int hidden) {
+// fp32 dot of one bf16 or fp32 row of length hidden = 512 * CPL with the fp16 activations, one
+// wave. Every load of the row is issued before the first product, so the row costs one memory
+// round trip.
+template <int CPL>
+DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x) {
     const int lane = threadIdx.x & 63;
     float acc = 0.0f;
     if (!f32) {
-        const u32x4* r = static_cast<const u32x4*>(row);          // 8 bf16 per chunk
-        for (int c = lane; c < hidden / 8; c += 64) {
-            const u32x4 w = __builtin_nontemporal_load(r + c);
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(x + 8 * c);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-            const uint32_t xx[4] = {xv.x, xv.y, xv.z, xv.w};
+        const u32x4* r = static_cast<const u32x4*>(row);          // 8 bf16 per chunk, CPL per lane
+        u32x4 w[CPL], xv[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            w[i] = __builtin_nontemporal_load(r + lane + 64 * i);
+            xv[i] = *reinterpret_cast<const u32x4*>(x + 8 * (lane + 64 * i));
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+            const uint32_t xx[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const h2 xh = as_h2(xx[k]);
@@ -116,15 +124,21 @@ DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x, int hidd
             }
         }
     } else {
-        const f4v* r = static_cast<const f4v*>(row);               // 4 fp32 per chunk
-        for (int c = lane; c < hidden / 4; c += 64) {
-            const f4v w = __builtin_nontemporal_load(r + c);
-            const uint2 xv = *reinterpret_cast<const uint2*>(x + 4 * c);
-            const h2 x0 = as_h2(xv.x), x1 = as_h2(xv.y);
-            acc = __builtin_fmaf(w.x, (float)x0.x, acc);
-            acc = __builtin_fmaf(w.y, (float)x0.y, acc);
-            acc = __builtin_fmaf(w.z, (float)x1.x, acc);
-            acc = __builtin_fmaf(w.w, (float)x1.y, acc);
+        const f4v* r = static_cast<const f4v*>(row);               // 4 fp32 per chunk, 2 CPL per lane
+        f4v w[2 * CPL];
+        uint2 xv[2 * CPL];
+#pragma unroll
+        for (int i = 0; i < 2 * CPL; ++i) {
+            w[i] = __builtin_nontemporal_load(r + lane + 64 * i);
+            xv[i] = *reinterpret_cast<const uint2*>(x + 4 * (lane + 64 * i));
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * CPL; ++i) {
+            const h2 x0 = as_h2(xv[i].x), x1 = as_h2(xv[i].y);
+            acc = __builtin_fmaf(w[i].x, (float)x0.x, acc);
+            acc = __builtin_fmaf(w[i].y, (float)x0.y, acc);
+            acc = __builtin_fmaf(w[i].z, (float)x1.x, acc);
+            acc = __builtin_fmaf(w[i].w, (float)x1.y, acc);
         }
     }
     return group_sum<64>(acc);
@@ -143,12 +157,12 @@ __global__ __launch_bounds__(64) void k_moe_router(MoeArgs a) {
     const int lane = threadIdx.x;
     if (b < a.E) {
         const size_t rb = (size_t)a.hidden * (a.router_f32 ? 4 : 2);
-        const float v = wave_row_dot(static_cast<const uint8_t*>(a.router) + rb * b, a.router_f32, a.x, a.hidden);
+        const float v = wave_row_dot<CPL>(static_cast<const uint8_t*>(a.router) + rb * b, a.router_f32, a.x);
         if (lane == 0) a.logits[b] = v;
         return;
     }
     if (b == a.E) {
-        const float v = wave_row_dot(a.sgate_row, 0, a.x, a.hidden);
+        const float v = wave_row_dot<CPL>(a.sgate_row, 0, a.x);
         if (lane == 0) a.gate_logit[0] = v;
         return;
     }
@@ -165,36 +179,75 @@ __global__ __launch_bounds__(64) void k_moe_router(MoeArgs a) {
     if (j == 0 && live) a.act[(size_t)a.top_k * a.inter + row] = v;
 }
 
+// Top-k keys: the logit's bits in an order-preserving unsigned form above the inverted expert
+// index, so one 64-bit comparison ranks larger logits first and, among equal logits, lower
+// expert indices first. A NaN logit ranks as -inf; -0 is folded into +0 (they compare equal).
+DHP_DEV uint64_t topk_key(float l, int e) {
+    l = (l == l) ? l + 0.0f : -INFINITY;
+    uint32_t u = __builtin_bit_cast(uint32_t, l);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+DHP_DEV float topk_key_value(uint64_t k) {
+    const uint32_t u = (uint32_t)(k >> 32);
+    return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+DHP_DEV int topk_key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+DHP_DEV uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+DHP_DEV uint64_t pack64(uint32_t hi, uint32_t lo) { return ((uint64_t)hi << 32) | lo; }
+
+template <int CTRL>
+DHP_DEV uint64_t dpp64(uint64_t v) {
+    return pack64((uint32_t)dpp_i<CTRL>((int)(v >> 32)), (uint32_t)dpp_i<CTRL>((int)(uint32_t)v));
+}
+
+// Wave-wide maximum key, in every lane: DPP within each 16-lane row, then the gfx950 row swap
+// (odd rows against even rows) and half swap (upper 32 lanes against lower 32).
+DHP_DEV uint64_t wave_max64(uint64_t k) {
+    k = max64(k, dpp64<DPP_XOR1>(k));
+    k = max64(k, dpp64<DPP_XOR2>(k));
+    k = max64(k, dpp64<DPP_HALF_MIRROR>(k));
+    k = max64(k, dpp64<DPP_MIRROR>(k));
+    uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+    const auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    k = max64(pack64(h16[0], l16[0]), pack64(h16[1], l16[1]));
+    hi = (uint32_t)(k >> 32);
+    lo = (uint32_t)k;
+    const auto h32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto l32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    return max64(pack64(h32[0], l32[0]), pack64(h32[1], l32[1]));
+}
+
 // The first `rounds` entries of the top-k of the E logits, by one wave: each round takes the
-// wave-wide best untaken (logit, expert) -- larger logit first, lower expert index first among
-// equal logits -- with DPP butterflies and four readlanes. Every lane returns the same ids.
+// wave-wide maximum key (a short chain of DPP and lane-swap steps, no branch), and the lane
+// holding it clears that entry. Every lane returns the same ids.
 DHP_DEV void wave_topk(const float* logits, int E, int rounds, int* ids, float* vals) {
     const int lane = threadIdx.x & 63;
     constexpr int PER = MAX_E / 64;
-    const int per = (E + 63) >> 6;
-    float v[PER];
+    const int per = (E + 63) >> 6;                 // wave-uniform
+    uint64_t k[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int e = lane + 64 * i;
-        const float l = (i < per && e < E) ? logits[e] : -INFINITY;
-        v[i] = (l == l) ? l : -INFINITY;   // a NaN logit ranks as -inf, so ids stay valid
+        k[i] = 0;                                   // below every real key
+        if (i < per) {
+            const int e = lane + 64 * i;
+            const uint64_t ke = topk_key(logits[min(e, E - 1)], e);
+            k[i] = (e < E) ? ke : 0;
+        }
     }
-    int taken = 0;                         // bit i: v[i] already selected
 #pragma unroll
     for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
         if (r >= rounds) break;
-        float bv = -INFINITY;
-        int bi = INT_MAX;
+        uint64_t m = k[0];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (i >= per) break;
-            const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1) && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
-        }
-        wave_best(bv, bi);
-        ids[r] = bi;
-        vals[r] = bv;
-        if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
+        for (int i = 1; i < PER; ++i)
+            if (i < per) m = max64(m, k[i]);
+        m = wave_max64(m);
+        ids[r] = topk_key_index(m);
+        vals[r] = topk_key_value(m);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) k[i] = (k[i] == m) ? 0 : k[i];
     }
 }
 
@@ -307,10 +360,21 @@ __global__ __launch_bounds__(256) void k_moe_phase2(MoeArgs a) {
     }
 
     // stage the activations of every slot in LDS, 32-float chunks at a 36-float pitch so the 16
-    // lanes of a group (one chunk each) read distinct banks
+    // lanes of a group (one chunk each) read distinct banks; all loads are issued (clamped) before
+    // the first store, so the staging costs one round trip
+    constexpr int AL = (NSLOT * 512 * CPLD + 1023) / 1024;
     const int n = nslot * a.inter;
-    for (int i = threadIdx.x * 4; i < n; i += 256 * 4)
-        *reinterpret_cast<f4v*>(lds_act + (i >> 5) * ACT_PITCH + (i & 31)) = *reinterpret_cast<const f4v*>(a.act + i);
+    f4v av4[AL];
+#pragma unroll
+    for (int k = 0; k < AL; ++k) {
+        const int i = min(threadIdx.x * 4 + k * 1024, n - 4);
+        av4[k] = *reinterpret_cast<const f4v*>(a.act + i);
+    }
+#pragma unroll
+    for (int k = 0; k < AL; ++k) {
+        const int i = threadIdx.x * 4 + k * 1024;
+        if (i < n) *reinterpret_cast<f4v*>(lds_act + (i >> 5) * ACT_PITCH + (i & 31)) = av4[k];
+    }
     __syncthreads();
 
     float racc[RH], sacc[RH];
