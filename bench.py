@@ -16,10 +16,12 @@ input already resident. Rotating weight copies and the 438 MB of LM-head traffic
 each call's weights out of the 256 MB last-level cache between uses.
 
 Also printed in the same JSON line:
-  roofline      the dominant kernel (the M=1 LM-head GEMV) against 8 TB/s, its average duration
-                from HIP events on the launch stream over the timed region;
+  roofline      the dominant call (the M=1 LM head: its GEMV kernel and the small argmax
+                reduction kernel) against 8 TB/s, its average duration from fence-free HIP events
+                on the launch stream around that call in every timed step;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload (rank 0);
-  calls         per-call median microseconds and GB/s from a separate, event-timed pass.
+  calls         per-call microseconds and GB/s from a separate pass: batches of back-to-back
+                launches between fence-free HIP events (median over batches).
 """
 from __future__ import annotations
 
@@ -170,39 +172,93 @@ def run_call(c):
         c()
 
 
-def step(calls, i, ev=None):
+def step(calls, i, ev=None, stream=None):
     run_call(calls["gemv"][i % len(calls["gemv"])])
     run_call(calls["hc"][i % len(calls["hc"])])
     run_call(calls["moe"][i % len(calls["moe"])])
     run_call(calls["prefill"][i % len(calls["prefill"])])
     if ev is not None:
-        ev[0].record()
+        ev[0].record(stream)
     run_call(calls["lmhead1"][0])
     if ev is not None:
-        ev[1].record()
+        ev[1].record(stream)
     run_call(calls["lmhead8"][0])
 
 
+class HipEvent:
+    """A HIP event created without the system-scope fence torch's timing events carry (that fence
+    writes back and invalidates caches at every record and adds microseconds to a short call).
+    Recorded on the given stream through the HIP runtime the process already loaded."""
+
+    _rt = None
+
+    @classmethod
+    def runtime(cls):
+        if cls._rt is None:
+            import ctypes
+            path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+            rt = ctypes.CDLL(path)
+            rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._rt = rt
+        return cls._rt
+
+    def __init__(self):
+        import ctypes
+        self.h = ctypes.c_void_p()
+        if self.runtime().hipEventCreateWithFlags(ctypes.byref(self.h), 0x20000000) != 0:   # hipEventDisableSystemFence
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        import ctypes
+        if self.runtime().hipEventRecord(self.h, ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def us_until(self, end) -> float:
+        import ctypes
+        rt = self.runtime()
+        ms = ctypes.c_float()
+        if rt.hipEventSynchronize(end.h) != 0 or rt.hipEventElapsedTime(ctypes.byref(ms), self.h, end.h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e3
+
+    def __del__(self):
+        if self._rt is not None and self.h:
+            self._rt.hipEventDestroy(self.h)
+
+
 def per_call_pass(torch, calls, nbytes, iters: int, exact: bool = False):
-    """Each call type alone, event-timed per call, cycling its ring (median over iters; the LM
-    heads take a quarter as many unless `exact`)."""
+    """Each call type alone: batches of back-to-back launches (cycling the call's ring) between two
+    fence-free events; microseconds per call = batch time / batch size, median (and p10/p90) over
+    the batches. `iters` launches in total per call type (the LM heads a quarter of that unless
+    `exact`)."""
     out = {}
+    stream = torch.cuda.current_stream()
     for name in calls:
         seq = calls[name]
         n = iters if exact else (max(iters, len(seq)) if name not in ("lmhead1", "lmhead8") else max(8, iters // 4))
-        st = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        en = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        batch = max(1, min(n, 4 if name in ("lmhead1", "lmhead8") else 16))
+        nb = max(1, n // batch)
         for i in range(3):
             run_call(seq[i % len(seq)])
         torch.cuda.synchronize()
-        for i in range(n):
-            st[i].record()
-            run_call(seq[i % len(seq)])
-            en[i].record()
-        torch.cuda.synchronize()
-        us = np.array([a.elapsed_time(b) for a, b in zip(st, en)]) * 1e3
+        us = []
+        k = 0
+        for _ in range(nb):
+            e0, e1 = HipEvent(), HipEvent()
+            e0.record(stream)
+            for _ in range(batch):
+                run_call(seq[k % len(seq)])
+                k += 1
+            e1.record(stream)
+            us.append(e0.us_until(e1) / batch)
+        us = np.array(us)
         med = float(np.median(us))
-        out[name] = {"launches": n, "us": round(med, 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+        out[name] = {"launches": nb * batch, "batch": batch, "us": round(med, 2),
+                     "p10_us": round(float(np.percentile(us, 10)), 2),
                      "p90_us": round(float(np.percentile(us, 90)), 2),
                      "GBps": round(nbytes[name] / med / 1e3, 1),
                      "pct_hbm_peak": round(100.0 * nbytes[name] / med / 1e3 / HBM_PEAK_GBS, 1)}
@@ -383,23 +439,24 @@ def main():
         step(calls, i)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(calls, args.warmup + i, ev[i])
+        step(calls, args.warmup + i, ev[i], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
-    dom_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    dom_us = float(np.mean([a.us_until(b) for a, b in ev]))
     print(f"[bench] {args.steps} steps, {ms_per_step:.3f} ms/step, {value:.1f} GB/s; lmhead1 {dom_us:.2f} us",
           file=sys.stderr, flush=True)
 
     dom_ach = nbytes["lmhead1"] / dom_us / 1e3
     roofline = {"bound": "hbm", "achieved": round(dom_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom_ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                "kernel": "k_gemv_m1_reg<5,f32,argmax> (LM head 151936 x 2560, M=1)",
+                "kernel": "k_gemv_m1_reg<5,f32,argmax> + k_argmax_final (LM head 151936 x 2560, M=1)",
                 "algorithmic_bytes_per_launch": nbytes["lmhead1"], "avg_launch_us": round(dom_us, 2)}
 
     per_call = None if args.no_per_call else per_call_pass(torch, calls, nbytes, iters=100)
