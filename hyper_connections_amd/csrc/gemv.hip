@@ -191,8 +191,24 @@ __global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ 
     const int* pi = part_i + (size_t)blockIdx.x * nparts;
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int i = threadIdx.x; i < nparts; i += blockDim.x)
-        if (better(pv[i], pi[i], bv, bi)) { bv = pv[i]; bi = pi[i]; }
+    // up to 4 partials per thread are loaded together (one round trip); more take further passes
+    constexpr int U = 4;
+    for (int base = 0; base < nparts; base += U * (int)blockDim.x) {
+        float v[U];
+        int ix[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = min(base + u * (int)blockDim.x + (int)threadIdx.x, nparts - 1);
+            v[u] = pv[i];
+            ix[u] = pi[i];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + u * (int)blockDim.x + (int)threadIdx.x < nparts && better(v[u], ix[u], bv, bi)) {
+                bv = v[u];
+                bi = ix[u];
+            }
+    }
     wave_best(bv, bi);
     __shared__ float sv[4];
     __shared__ int si[4];

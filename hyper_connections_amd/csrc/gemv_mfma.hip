@@ -118,12 +118,15 @@ DHP_DEV void mfma_half(const HalfRegs& r, const uint8_t* xl, int xpitch, const u
     }
 }
 
-template <bool F32OUT, bool ARGMAX>
+// NCHT: the number of 128-k chunks when fixed at compile time (K = 128 * NCHT; chunk offsets
+// then become immediate load offsets and the per-chunk guards disappear), 0 for any K.
+template <int NCHT, bool F32OUT, bool ARGMAX>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv_mfma16(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ X, int M, int N, int K,
     void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i) {
     extern __shared__ __align__(16) uint8_t xl[];      // [M][K halves, permuted by eights] + pad
+    if constexpr (NCHT != 0) K = NCHT * 128;
     const int xpitch = 2 * K + 16;
     // after the activations: one (s,s|b,b) slice of 16 x SB_PITCH entries per wave
     uint32_t* sbl = reinterpret_cast<uint32_t*>(xl + (size_t)M * xpitch) + (threadIdx.x >> 6) * (16 * SB_PITCH * 2);
@@ -243,53 +246,64 @@ bool dhp_gemv_mfma16_fits(const dhp_int4* w, int M) {
            reinterpret_cast<uintptr_t>(w->scales) % 4 == 0 && reinterpret_cast<uintptr_t>(w->biases) % 4 == 0;
 }
 
-int launch_gemv_mfma16(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
-                       size_t ws_part_stride, hipStream_t s, int cus) {
+namespace {
+
+template <int NCHT, bool F32OUT, bool ARGMAX>
+hipError_t launch_variant(const dhp_int4* w, const void* x, int M, void* y, float* pv, int* pi, int dev, int cus,
+                          hipStream_t s, int* blocks_out) {
     const int N = w->rows, K = w->cols;
     const size_t lds = (size_t)M * (2 * K + 16) + (size_t)WAVES * 16 * SB_PITCH * 8;
-    const auto* c = static_cast<const uint8_t*>(w->codes);
-    const auto* sc = static_cast<const uint16_t*>(w->scales);
-    const auto* bi = static_cast<const uint16_t*>(w->biases);
-    const auto* xh = static_cast<const _Float16*>(x);
-    float* pv = argmax ? static_cast<float*>(ws) : nullptr;
-    int* pi = argmax ? reinterpret_cast<int*>(static_cast<char*>(ws) + ws_part_stride) : nullptr;
-    static unsigned long long configured = 0;          // > 64 KiB of dynamic LDS, once per device
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hipGetDevice");
+    const void* fn = reinterpret_cast<const void*>(&k_gemv_mfma16<NCHT, F32OUT, ARGMAX>);
+    // more than 64 KiB of dynamic LDS must be allowed once per device; the occupancy (blocks per
+    // CU, from registers and LDS) is cached per device and m
+    static unsigned long long configured = 0;
+    static int resident[64][17];
     if (!(__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & (1ull << (dev & 63)))) {
-        const void* fns[4] = {reinterpret_cast<const void*>(&k_gemv_mfma16<true, true>),
-                              reinterpret_cast<const void*>(&k_gemv_mfma16<true, false>),
-                              reinterpret_cast<const void*>(&k_gemv_mfma16<false, true>),
-                              reinterpret_cast<const void*>(&k_gemv_mfma16<false, false>)};
-        for (const void* f : fns)
-            if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    16 * (2 * 2 * HALF * 128 + 16) + WAVES * 16 * SB_PITCH * 8) != hipSuccess)
-                return dhp_fail(DHP_ERR_LAUNCH, "hipFuncSetAttribute");
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 16 * (2 * 2 * HALF * 128 + 16) + WAVES * 16 * SB_PITCH * 8);
+        if (e != hipSuccess) return e;
         __atomic_fetch_or(&configured, 1ull << (dev & 63), __ATOMIC_RELEASE);
     }
-    // one resident round of blocks: as many per CU as registers and LDS allow (the waves stride
-    // over the tiles, so more blocks than fit would only run as a tail)
-    static int resident[64][17][4];                   // per device, m and variant; 0 = not yet queried
-    const int variant = (y_f32 ? 2 : 0) + (argmax ? 1 : 0);
-    int per_cu = __atomic_load_n(&resident[dev & 63][M][variant], __ATOMIC_RELAXED);
+    int per_cu = __atomic_load_n(&resident[dev & 63][M], __ATOMIC_RELAXED);
     if (per_cu == 0) {
-        const void* f = y_f32 ? (argmax ? reinterpret_cast<const void*>(&k_gemv_mfma16<true, true>)
-                                        : reinterpret_cast<const void*>(&k_gemv_mfma16<true, false>))
-                              : (argmax ? reinterpret_cast<const void*>(&k_gemv_mfma16<false, true>)
-                                        : reinterpret_cast<const void*>(&k_gemv_mfma16<false, false>));
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, WAVES * 64, lds) != hipSuccess || per_cu < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, WAVES * 64, lds) != hipSuccess || per_cu < 1)
             per_cu = 1;
-        __atomic_store_n(&resident[dev & 63][M][variant], per_cu, __ATOMIC_RELAXED);
+        __atomic_store_n(&resident[dev & 63][M], per_cu, __ATOMIC_RELAXED);
     }
+    // one resident round of blocks: the waves stride over the tiles, so more blocks than fit
+    // would only run as a tail
     const int ntiles = (N + 15) / 16;
     int blocks = (ntiles + WAVES - 1) / WAVES;
     if (blocks > per_cu * cus) blocks = per_cu * cus;
-    const dim3 g((unsigned)blocks), b(WAVES * 64);
-    if (y_f32 && argmax) hipLaunchKernelGGL((k_gemv_mfma16<true, true>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    else if (y_f32) hipLaunchKernelGGL((k_gemv_mfma16<true, false>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    else if (argmax) hipLaunchKernelGGL((k_gemv_mfma16<false, true>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    else hipLaunchKernelGGL((k_gemv_mfma16<false, false>), g, b, lds, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    hipError_t e = hipGetLastError();
+    *blocks_out = blocks;
+    hipLaunchKernelGGL((k_gemv_mfma16<NCHT, F32OUT, ARGMAX>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, s,
+                       static_cast<const uint8_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
+                       static_cast<const uint16_t*>(w->biases), static_cast<const _Float16*>(x), M, N, K, y, pv, pi);
+    return hipGetLastError();
+}
+
+template <int NCHT>
+hipError_t launch_nch(const dhp_int4* w, const void* x, int M, void* y, int y_f32, bool am, float* pv, int* pi,
+                      int dev, int cus, hipStream_t s, int* blocks) {
+    if (y_f32 && am) return launch_variant<NCHT, true, true>(w, x, M, y, pv, pi, dev, cus, s, blocks);
+    if (y_f32) return launch_variant<NCHT, true, false>(w, x, M, y, pv, pi, dev, cus, s, blocks);
+    if (am) return launch_variant<NCHT, false, true>(w, x, M, y, pv, pi, dev, cus, s, blocks);
+    return launch_variant<NCHT, false, false>(w, x, M, y, pv, pi, dev, cus, s, blocks);
+}
+
+}  // namespace
+
+int launch_gemv_mfma16(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
+                       size_t ws_part_stride, hipStream_t s, int cus) {
+    float* pv = argmax ? static_cast<float*>(ws) : nullptr;
+    int* pi = argmax ? reinterpret_cast<int*>(static_cast<char*>(ws) + ws_part_stride) : nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hipGetDevice");
+    int blocks = 0;
+    const bool am = argmax != nullptr;
+    hipError_t e = (w->cols == 2 * HALF * 128)
+                       ? launch_nch<2 * HALF>(w, x, M, y, y_f32, am, pv, pi, dev, cus, s, &blocks)
+                       : launch_nch<0>(w, x, M, y, y_f32, am, pv, pi, dev, cus, s, &blocks);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemv_mfma16 launch: %s", hipGetErrorString(e));
     if (argmax) {
         e = launch_argmax_final(pv, pi, blocks, M, argmax, s);

@@ -24,6 +24,7 @@ namespace {
 
 constexpr int HC_MAX_THREADS = 1024;
 constexpr int LO_PITCH = 36;           // floats per staged 32-float chunk of the low-rank vector
+constexpr int UP_THREADS = 64;         // k_hc_up block: four outputs h
 
 // raw, gamma: the C*H stream; one block per projection row (down rows first, then inject rows).
 __global__ __launch_bounds__(HC_MAX_THREADS) void k_hc_down(
@@ -117,18 +118,16 @@ __global__ __launch_bounds__(HC_MAX_THREADS) void k_hc_down(
 
 // 16 lanes per output h; LPRU = 16 / C lanes per stream row.
 template <int C>
-__global__ __launch_bounds__(256) void k_hc_up(
+__global__ __launch_bounds__(UP_THREADS) void k_hc_up(
     const _Float16* __restrict__ raw, const uint16_t* __restrict__ gamma, int H,
     const u32x4* __restrict__ ucodes, const uint16_t* __restrict__ uscales,
     const uint16_t* __restrict__ ubiases, int R, const float* __restrict__ lo,
     const float* __restrict__ inv_rms, _Float16* __restrict__ mixed) {
     constexpr int LPRU = 16 / C;
     extern __shared__ float lds_lo[];     // [R/32][LO_PITCH]: 32-float chunks, bank-staggered
+    constexpr int MAXCH = 32 / LPRU;      // chunks per lane at the largest R (1024)
     const int CHR = R >> 5;
     const int G = R >> 6;
-    for (int i = threadIdx.x * 4; i < R; i += blockDim.x * 4)
-        *reinterpret_cast<f4v*>(lds_lo + (i >> 5) * LO_PITCH + (i & 31)) = *reinterpret_cast<const f4v*>(lo + i);
-    __syncthreads();
 
     const int lane16 = threadIdx.x & 15;
     const int c = lane16 / LPRU;
@@ -139,24 +138,55 @@ __global__ __launch_bounds__(256) void k_hc_up(
     const u32x4* cr = ucodes + urow * CHR;
     const uint16_t* sr = uscales + urow * G;
     const uint16_t* br = ubiases + urow * G;
-    float acc = 0.0f;
-    for (int ch = sub; ch < CHR; ch += LPRU) {
-        const u32x4 cc = cr[ch];          // rows are 10 chunks: lines are shared between lane groups
-        const f4v* lp = reinterpret_cast<const f4v*>(lds_lo + ch * LO_PITCH);
-        float lv[32];
-        float ls = 0.0f;
+
+    // every global load first (chunks past the row are clamped and not used), so the block costs
+    // one memory round trip: this lane's code chunks with their scales and biases, the residual
+    // element, its norm weight and the stream's inverse RMS, and its share of the low-rank vector
+    u32x4 cc[MAXCH];
+    uint32_t sv[MAXCH], bv[MAXCH];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const f4v t = lp[q];
-            lv[4 * q] = t.x; lv[4 * q + 1] = t.y; lv[4 * q + 2] = t.z; lv[4 * q + 3] = t.w;
-            ls += (t.x + t.y) + (t.z + t.w);
+    for (int i = 0; i < MAXCH; ++i) {
+        const int ch = min(sub + LPRU * i, CHR - 1);
+        cc[i] = cr[ch];                   // rows are R/32 chunks: lines are shared between lane groups
+        sv[i] = sr[ch >> 1];
+        bv[i] = br[ch >> 1];
+    }
+    const float rv = (float)raw[urow];
+    const float gv = bf16_to_f32(gamma[urow]);
+    const float ir = inv_rms[c];
+    constexpr int LOADS = (1024 / 4 + UP_THREADS - 1) / UP_THREADS;   // f4v of lo per thread at R = 1024
+    f4v lv4[LOADS];
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k)
+        lv4[k] = *reinterpret_cast<const f4v*>(lo + min((int)(threadIdx.x + UP_THREADS * k) * 4, R - 4));
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+        const int i = (threadIdx.x + UP_THREADS * k) * 4;
+        if (i < R) *reinterpret_cast<f4v*>(lds_lo + (i >> 5) * LO_PITCH + (i & 31)) = lv4[k];
+    }
+    __syncthreads();
+
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXCH; ++i) {
+        const int ch = sub + LPRU * i;
+        if (ch < CHR) {
+            const f4v* lp = reinterpret_cast<const f4v*>(lds_lo + ch * LO_PITCH);
+            float lv[32];
+            float ls = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const f4v t = lp[q];
+                lv[4 * q] = t.x; lv[4 * q + 1] = t.y; lv[4 * q + 2] = t.z; lv[4 * q + 3] = t.w;
+                ls += (t.x + t.y) + (t.z + t.w);
+            }
+            const float d = dot32_f32(cc[i], lv);
+            acc = __builtin_fmaf(bf16_to_f32(sv[i]), d, acc);
+            acc = __builtin_fmaf(bf16_to_f32(bv[i]), ls, acc);
         }
-        const float d = dot32_f32(cc, lv);
-        acc = __builtin_fmaf(bf16_to_f32(sr[ch >> 1]), d, acc);
-        acc = __builtin_fmaf(bf16_to_f32(br[ch >> 1]), ls, acc);
     }
     acc = group_sum<LPRU>(acc);
-    const float n = (float)raw[urow] * inv_rms[c] * bf16_to_f32(gamma[urow]);
+    const float n = rv * ir * gv;
     const float p = group_sum<16, LPRU>(sigmoid_f(acc) * n);     // over the C streams
     if (lane16 == 0 && live) mixed[h] = (_Float16)(p / (float)C);
 }
@@ -213,7 +243,7 @@ int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hc_down launch: %s", hipGetErrorString(e));
 
-    const int block = 64;                  // 4 outputs per block
+    const int block = UP_THREADS;          // 4 outputs per block
     const dim3 g((unsigned)((H + 3) / 4));
     const size_t lds = (size_t)(R / 32) * LO_PITCH * sizeof(float);
     const auto* rw = static_cast<const _Float16*>(raw);

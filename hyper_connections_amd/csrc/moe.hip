@@ -328,6 +328,15 @@ __global__ __launch_bounds__(256) void k_moe_phase2(MoeArgs a) {
     const int G = a.inter >> 6;
     const int h0 = (blockIdx.x * 4 + lane / LPR) * RH;
 
+    // the routing weights and the shared gate logit are read up front, with the expert ids
+    float wgts[SLOTS_PER_WAVE];
+#pragma unroll
+    for (int t = 0; t < SLOTS_PER_WAVE; ++t) {
+        const int slot = wave + 4 * t;
+        wgts[t] = (slot < a.top_k) ? a.weights[slot] : 1.0f;
+    }
+    const float gate_logit = a.gate_logit[0];
+
     u32x4 c[SLOTS_PER_WAVE][RH][CPLD];
     uint32_t sv[SLOTS_PER_WAVE][RH][CPLD], bv[SLOTS_PER_WAVE][RH][CPLD];
 #pragma unroll
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(256) void k_moe_phase2(MoeArgs a) {
         const int slot = wave + 4 * t;
         if (slot < nslot) {
             const bool shared = slot == a.top_k;
-            const float wgt = shared ? 1.0f : a.weights[slot];
+            const float wgt = wgts[t];
             float p[RH];
 #pragma unroll
             for (int r = 0; r < RH; ++r) p[r] = 0.0f;
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(256) void k_moe_phase2(MoeArgs a) {
     }
     __syncthreads();
     if (wave == 0) {
-        const float sg = sigmoid_f(a.gate_logit[0]);
+        const float sg = sigmoid_f(gate_logit);
 #pragma unroll
         for (int r = 0; r < RH; ++r) {
             const int h = h0 + r;
