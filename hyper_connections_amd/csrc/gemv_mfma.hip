@@ -18,8 +18,10 @@
 //    and parks it in its own LDS slice as (s, s | b, b), from where every lane reads the pair of
 //    its row and group with one 8-byte LDS read. Fetching them per chunk from 16 rows at a time
 //    would cost one cache-line lookup per row per 2-byte load and starve the address unit.
-//  * The codes of half a tile are loaded ahead while the other half computes, and the first half
-//    of the wave's next tile (with its scales) while the second half of the current one computes.
+//  * A tile is walked in parts of five chunks: the next part's codes are in flight while one
+//    computes, and the next tile's first part (with its scales) while the last one computes.
+//    Keeping more in flight per CU measured slower: HBM reads slow down past a few tens of KB
+//    outstanding per CU.
 //  * Each 16-lane row of the result is summed by the matrix core, so a tile needs no cross-lane
 //    reduction; the argmax keeps, per lane, the best of its four rows over the tiles it saw, then
 //    reduces over lanes (DPP), waves (LDS) and blocks (the shared final kernel).
@@ -33,7 +35,9 @@ typedef float f4x __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int WAVES = 4;
-constexpr int HALF = 10;             // 128-k chunks per half tile (K = 2560: two halves)
+constexpr int MAXCH = 20;            // 128-k chunks at the largest K (2560)
+constexpr int PART = 5;              // chunks per part: a tile is walked in NPART parts
+constexpr int NPART = MAXCH / PART;
 
 DHP_DEV h8 deq8(uint32_t w, h2 s2, h2 b2, const NibConsts& k) {
     h2 q[4];
@@ -46,24 +50,24 @@ DHP_DEV h8 deq8(uint32_t w, h2 s2, h2 b2, const NibConsts& k) {
 }
 
 constexpr int SB_DW = 5;            // dwords of scales (and of biases) a lane fetches per tile
-constexpr int SB_PITCH = 2 * HALF * 2 + 1;   // LDS (s,s|b,b) entries per tile row (G <= 40, + 1 pad:
+constexpr int SB_PITCH = 2 * MAXCH + 1;     // LDS (s,s|b,b) entries per tile row (G <= 40, + 1 pad:
                                              // the 16 rows of one 8-byte read land on distinct banks)
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-struct HalfRegs {
-    u32x4 c[HALF];
+struct PartRegs {
+    u32x4 c[PART];
 };
 
 struct TileSB {
     uint32_t s[SB_DW], b[SB_DW];
 };
 
-// Loads of chunks [c0, c0 + HALF) of weight row `row` for lane group g (chunks >= nch are
+// Loads of chunks [c0, c0 + PART) of weight row `row` for lane group g (chunks >= nch are
 // clamped to the last chunk and never used).
-DHP_DEV void load_half(HalfRegs& r, const uint8_t* crow, int c0, int nch, int g) {
+DHP_DEV void load_part(PartRegs& r, const uint8_t* crow, int c0, int nch, int g) {
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) {
+    for (int i = 0; i < PART; ++i) {
         const int c = min(c0 + i, nch - 1);
         r.c[i] = *reinterpret_cast<const u32x4*>(crow + (size_t)c * 64 + 16 * g);
     }
@@ -99,10 +103,10 @@ DHP_DEV void store_tile_sb(const TileSB& t, uint32_t* sbl, int lane, int half_g,
     }
 }
 
-DHP_DEV void mfma_half(const HalfRegs& r, const uint8_t* xl, int xpitch, const uint32_t* sbrow, int c0, int nch,
+DHP_DEV void mfma_part(const PartRegs& r, const uint8_t* xl, int xpitch, const uint32_t* sbrow, int c0, int nch,
                        int arow, int g, f4x& acc, const NibConsts& nk) {
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) {
+    for (int i = 0; i < PART; ++i) {
         if (c0 + i < nch) {
             const u32x2 e = *reinterpret_cast<const u32x2*>(sbrow + 2 * (2 * (c0 + i) + (g >> 1)));
             const h2 s2 = as_h2(e.x), b2 = as_h2(e.y);
@@ -143,18 +147,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_mfma16(
     const auto* b32 = reinterpret_cast<const uint32_t*>(biases);
     const size_t row_bytes = (size_t)K >> 1;
 
-    // stage the activations, permuted (x0,x4,x1,x5,x2,x6,x3,x7) within each group of eight
-    const int per_row = K >> 3;
-    for (int i = threadIdx.x; i < M * per_row; i += blockDim.x) {
-        const int m = i / per_row, j = i % per_row;
-        const u32x4 u = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + 8 * j);
-        h2 p[4];
-        permute8(u.x, u.y, u.z, u.w, p);
-        *reinterpret_cast<u32x4*>(xl + m * xpitch + 16 * j) =
-            u32x4{h2_bits(p[0]), h2_bits(p[1]), h2_bits(p[2]), h2_bits(p[3])};
-    }
-    __syncthreads();
-
     const NibConsts nk = nib_consts();
     float bv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     int bi[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
@@ -163,15 +155,44 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_mfma16(
     // A rows: lane n reads activation row n, clamped to the last real row (rows >= M only feed
     // result rows that are never stored)
     const int arow = min(n, M - 1);
-    const bool two = nch > HALF;                       // K <= 2560: at most two half tiles
     int tile = blockIdx.x * WAVES + wave;
-    HalfRegs h0, h1;
+    PartRegs buf[2];
     TileSB sb;
     if (tile < ntiles) {
         const int row = min(tile * 16 + n, N - 1);
         load_tile_sb(sb, s32, b32, (size_t)tile * tile_dw, last_dw, lane);
-        load_half(h0, codes + (size_t)row * row_bytes, 0, nch, g);
+        load_part(buf[0], codes + (size_t)row * row_bytes, 0, nch, g);
     }
+
+    // stage the activations, permuted (x0,x4,x1,x5,x2,x6,x3,x7) within each group of eight, while
+    // the first tile's weights are in flight; every load of a pass is issued before the first
+    // store (a load-then-store loop would pay one memory round trip per iteration)
+    {
+        constexpr int XB = 10;                         // 16-byte loads per thread per pass
+        const int per_row = K >> 3;
+        const int total = M * per_row;
+        for (int base = 0; base < total; base += XB * WAVES * 64) {
+            u32x4 u[XB];
+#pragma unroll
+            for (int k = 0; k < XB; ++k) {
+                const int i = min(base + k * WAVES * 64 + (int)threadIdx.x, total - 1);
+                const int m = i / per_row, j = i - m * per_row;
+                u[k] = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + 8 * j);
+            }
+#pragma unroll
+            for (int k = 0; k < XB; ++k) {
+                const int i = base + k * WAVES * 64 + (int)threadIdx.x;
+                if (i < total) {
+                    const int m = i / per_row, j = i - m * per_row;
+                    h2 p[4];
+                    permute8(u[k].x, u[k].y, u[k].z, u[k].w, p);
+                    *reinterpret_cast<u32x4*>(xl + m * xpitch + 16 * j) =
+                        u32x4{h2_bits(p[0]), h2_bits(p[1]), h2_bits(p[2]), h2_bits(p[3])};
+                }
+            }
+        }
+    }
+    __syncthreads();
     const uint32_t* sbrow = sbl + 2 * n * SB_PITCH;
     // loads are unconditional (clamped rows and chunks) so the compiler can count them and wait
     // only for the data about to be used
@@ -185,13 +206,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv_mfma16(
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        load_half(h1, codes + (size_t)row * row_bytes, HALF, nch, g);
-        mfma_half(h0, xl, xpitch, sbrow, 0, nch, arow, g, acc, nk);
-        const int ntile = tile + stride;                               // the next tile's scales + first half
+        // the tile in NPART parts: one part is in flight while the previous one computes, and the
+        // next tile's scales and first part while the last one computes. More in flight per CU
+        // reads HBM slower (whole half tiles in flight measured 10-15 % slower).
+        const int ntile = tile + stride;
         const int nrow = min(ntile * 16 + n, N - 1);
-        load_tile_sb(sb, s32, b32, min((size_t)ntile * tile_dw, last_dw), last_dw, lane);
-        load_half(h0, codes + (size_t)nrow * row_bytes, 0, nch, g);
-        if (two) mfma_half(h1, xl, xpitch, sbrow, HALF, nch, arow, g, acc, nk);
+#pragma unroll
+        for (int p = 0; p < NPART; ++p) {
+            if (p + 1 < NPART) {
+                load_part(buf[(p + 1) & 1], codes + (size_t)row * row_bytes, (p + 1) * PART, nch, g);
+            } else {
+                load_tile_sb(sb, s32, b32, min((size_t)ntile * tile_dw, last_dw), last_dw, lane);
+                load_part(buf[(p + 1) & 1], codes + (size_t)nrow * row_bytes, 0, nch, g);
+            }
+            mfma_part(buf[p & 1], xl, xpitch, sbrow, p * PART, nch, arow, g, acc, nk);
+        }
         // lane (n, g) holds rows 4 g .. 4 g + 3 of column n0 + n
         const int col = n0 + n;
 #pragma unroll
@@ -242,7 +271,7 @@ hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m
 // and bias fetches are dword loads, so those arrays must be 4-byte aligned.
 bool dhp_gemv_mfma16_fits(const dhp_int4* w, int M) {
     const int K = w->cols;
-    return M >= 2 && M <= 16 && K % 128 == 0 && K <= 2 * HALF * 128 &&
+    return M >= 2 && M <= 16 && K % 128 == 0 && K <= MAXCH * 128 &&
            reinterpret_cast<uintptr_t>(w->scales) % 4 == 0 && reinterpret_cast<uintptr_t>(w->biases) % 4 == 0;
 }
 
@@ -260,7 +289,7 @@ hipError_t launch_variant(const dhp_int4* w, const void* x, int M, void* y, floa
     static int resident[64][17];
     if (!(__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & (1ull << (dev & 63)))) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 16 * (2 * 2 * HALF * 128 + 16) + WAVES * 16 * SB_PITCH * 8);
+                                                 16 * (2 * MAXCH * 128 + 16) + WAVES * 16 * SB_PITCH * 8);
         if (e != hipSuccess) return e;
         __atomic_fetch_or(&configured, 1ull << (dev & 63), __ATOMIC_RELEASE);
     }
@@ -301,8 +330,8 @@ int launch_gemv_mfma16(const dhp_int4* w, const void* x, int M, void* y, int y_f
     if (hipGetDevice(&dev) != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hipGetDevice");
     int blocks = 0;
     const bool am = argmax != nullptr;
-    hipError_t e = (w->cols == 2 * HALF * 128)
-                       ? launch_nch<2 * HALF>(w, x, M, y, y_f32, am, pv, pi, dev, cus, s, &blocks)
+    hipError_t e = (w->cols == MAXCH * 128)
+                       ? launch_nch<MAXCH>(w, x, M, y, y_f32, am, pv, pi, dev, cus, s, &blocks)
                        : launch_nch<0>(w, x, M, y, y_f32, am, pv, pi, dev, cus, s, &blocks);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemv_mfma16 launch: %s", hipGetErrorString(e));
     if (argmax) {
