@@ -105,6 +105,59 @@ DHP_DEV float load_x32(const _Float16* p, h2* xp) {
     return s;
 }
 
+// Raw form of the 32-code dot product. The code pairs stay in their fp16 "magic" form,
+// t = 1024 + q for even k (low nibbles) and t = 1024 + 16 q for odd k (high nibbles), and the
+// activations of the odd-k slots are pre-scaled by 1/16 (a power of two: exact in fp16 outside
+// the subnormal range), so
+//     sum_k t_k x'_k = sum_k q_k x_k + 1024 * sum_even x + 64 * sum_odd x.
+// load_x32_raw returns that correction (to be subtracted) and the plain sum of the 32
+// activations; dot32_f16_raw starts its accumulator at -correction. It saves the exact unpack's
+// subtract and fma per code pair (9 instead of 13 VALU per 8 codes); the price is that the
+// running fp32 sum carries magnitudes ~1024 x sum(x) instead of ~8 x sum(x), i.e. an absolute
+// rounding error of order 1e-3 per 32-code chunk before the group scale (~1e-2) multiplies it.
+DHP_DEV void unpack8_raw(uint32_t w, h2 t[4], const NibConsts& k) {
+    const uint32_t w8 = w >> 8;
+    t[0] = as_h2((w & k.lo) | k.magic);
+    t[1] = as_h2((w & k.hi) | k.magic);
+    t[2] = as_h2((w8 & k.lo) | k.magic);
+    t[3] = as_h2((w8 & k.hi) | k.magic);
+}
+
+DHP_DEV float dot32_f16_raw(const u32x4 c, const h2* xp, float neg_corr, const NibConsts& k) {
+    float d = neg_corr;
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h2 t[4];
+        unpack8_raw(w[i], t, k);
+        d = __builtin_amdgcn_fdot2(t[0], xp[4 * i], d, false);
+        d = __builtin_amdgcn_fdot2(t[1], xp[4 * i + 1], d, false);
+        d = __builtin_amdgcn_fdot2(t[2], xp[4 * i + 2], d, false);
+        d = __builtin_amdgcn_fdot2(t[3], xp[4 * i + 3], d, false);
+    }
+    return d;
+}
+
+// 32 fp16 activations at p (16-byte aligned) as 16 permuted pairs with the odd-k slots scaled
+// by 1/16; returns their plain fp32 sum and sets neg_corr = -(1024 sum_even + 64 sum_odd).
+DHP_DEV float load_x32_raw(const _Float16* p, h2* xp, float& neg_corr) {
+    const u32x4* v = reinterpret_cast<const u32x4*>(p);
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    float even = 0.0f, odd = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 u = v[i];
+        permute8(u.x, u.y, u.z, u.w, xp + 4 * i);
+        const h2 a = as_h2(u.x), b = as_h2(u.y), c = as_h2(u.z), d = as_h2(u.w);
+        even += ((float)a.x + (float)b.x) + ((float)c.x + (float)d.x);
+        odd += ((float)a.y + (float)b.y) + ((float)c.y + (float)d.y);
+        xp[4 * i + 1] = xp[4 * i + 1] * sixteenth;
+        xp[4 * i + 3] = xp[4 * i + 3] * sixteenth;
+    }
+    neg_corr = -(1024.0f * even + 64.0f * odd);
+    return even + odd;
+}
+
 // sum over 32 codes of q * x for fp32 activations x[0..31] (contiguous k order).
 DHP_DEV float dot32_f32(const u32x4 c, const float* x) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};

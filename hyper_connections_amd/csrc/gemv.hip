@@ -97,9 +97,9 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     load_row<CPL>(codes, scales, biases, min(base + rw, N - 1), j, r);
 
     h2 xp[CPL][16];
-    float xs[CPL];
+    float xs[CPL], nc[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) xs[i] = load_x32(x + (size_t)(j + LPR * i) * 32, xp[i]);
+    for (int i = 0; i < CPL; ++i) xs[i] = load_x32_raw(x + (size_t)(j + LPR * i) * 32, xp[i], nc[i]);
 
     const NibConsts nk = nib_consts();
     float best_v = -INFINITY;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const float d = dot32_f16(r[i].c, xp[i], nk);
+            const float d = dot32_f16_raw(r[i].c, xp[i], nc[i], nk);
             acc = __builtin_fmaf(bf16_to_f32(r[i].s), d, acc);
             acc = __builtin_fmaf(bf16_to_f32(r[i].b), xs[i], acc);
         }

@@ -80,16 +80,17 @@ DHP_DEV void load_pair(PairRegs<CPL>& p, const u32x4* gc, const uint16_t* gs, co
     }
 }
 
-// silu(gate . x) * (up . x), the same value in every lane of the 16-lane group.
+// silu(gate . x) * (up . x), the same value in every lane of the 16-lane group. The chunk dots
+// use the raw code form (see dot32_f16_raw) with the activations' per-chunk corrections nc.
 template <int CPL>
-DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* xs) {
+DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* xs, const float* nc) {
     const NibConsts nk = nib_consts();
     float ag = 0.0f, au = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_f16(p.cg[i], xp[i], nk), ag);
+        ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_f16_raw(p.cg[i], xp[i], nc[i], nk), ag);
         ag = __builtin_fmaf(bf16_to_f32(p.bg[i]), xs[i], ag);
-        au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_f16(p.cu[i], xp[i], nk), au);
+        au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_f16_raw(p.cu[i], xp[i], nc[i], nk), au);
         au = __builtin_fmaf(bf16_to_f32(p.bu[i]), xs[i], au);
     }
     ag = group_sum<LPR>(ag);
@@ -145,9 +146,9 @@ DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x) {
 }
 
 template <int CPL>
-DHP_DEV void load_x_regs(const _Float16* x, int j, h2 (*xp)[16], float* xs) {
+DHP_DEV void load_x_regs(const _Float16* x, int j, h2 (*xp)[16], float* xs, float* nc) {
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) xs[i] = load_x32(x + (size_t)(j + LPR * i) * 32, xp[i]);
+    for (int i = 0; i < CPL; ++i) xs[i] = load_x32_raw(x + (size_t)(j + LPR * i) * 32, xp[i], nc[i]);
 }
 
 // Blocks [0, E): router rows. Block E: shared gate logit. Blocks after: 4 shared pairs each.
@@ -173,9 +174,9 @@ __global__ __launch_bounds__(64) void k_moe_router(MoeArgs a) {
     load_pair<CPL>(p, a.sg_codes, a.sg_scales, a.sg_biases, a.su_codes, a.su_scales, a.su_biases,
                    live ? row : 0, j);
     h2 xp[CPL][16];
-    float xs[CPL];
-    load_x_regs<CPL>(a.x, j, xp, xs);
-    const float v = pair_act<CPL>(p, xp, xs);
+    float xs[CPL], nc[CPL];
+    load_x_regs<CPL>(a.x, j, xp, xs, nc);
+    const float v = pair_act<CPL>(p, xp, xs, nc);
     if (j == 0 && live) a.act[(size_t)a.top_k * a.inter + row] = v;
 }
 
@@ -256,8 +257,8 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     const int lane = threadIdx.x;
     const int j = lane % LPR;
     h2 xp[CPL][16];
-    float xs[CPL];
-    load_x_regs<CPL>(a.x, j, xp, xs);      // independent of routing: issue first
+    float xs[CPL], nc[CPL];
+    load_x_regs<CPL>(a.x, j, xp, xs, nc);  // independent of routing: issue first
 
     // a block only needs the ranks up to its last (slot, row) pair; block 0 also needs all
     // top_k of them for the softmax weights
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
         }
     }
 
-    const float v = pair_act<CPL>(p, xp, xs);
+    const float v = pair_act<CPL>(p, xp, xs, nc);
     if (j == 0 && live) a.act[(size_t)slot * a.inter + row] = v;
 }
 
