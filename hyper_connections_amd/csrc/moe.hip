@@ -12,7 +12,7 @@
 //                 shared expert's scalar gate logit, and quarter-waves running the shared
 //                 expert's gate/up pairs, which need no routing decision.
 //  k_moe_phase1 : every block re-derives the top-k from the E logits (a handful of wave
-//                 reductions, cheaper than another launch), then its quarter-waves run one
+//                 maxima, cheaper than another launch), then its quarter-waves run one
 //                 (selected expert, row) pair each: gate and up rows against register-resident
 //                 activations, act = silu(gate) * up in fp32. Block 0 writes ids and weights.
 //  k_moe_phase2 : 16 lanes per output element walk the down rows of the selected experts and
@@ -180,93 +180,138 @@ __global__ __launch_bounds__(64) void k_moe_router(MoeArgs a) {
     if (j == 0 && live) a.act[(size_t)a.top_k * a.inter + row] = v;
 }
 
-// Top-k keys: the logit's bits in an order-preserving unsigned form above the inverted expert
-// index, so one 64-bit comparison ranks larger logits first and, among equal logits, lower
-// expert indices first. A NaN logit ranks as -inf; -0 is folded into +0 (they compare equal).
-DHP_DEV uint64_t topk_key(float l, int e) {
+// Top-k by one wave. Every logit becomes an unsigned word that orders like the float (a NaN
+// ranks as -inf; -0 is folded into +0, they compare equal) and lane l holds the words of the
+// PER consecutive experts l*PER + i, so a lower lane always means lower expert indices. Each
+// round takes the wave-wide maximum word; the lowest lane holding it gives up its entry (the
+// lowest index among equal words), and the next round starts over.
+// Padding entries (e >= E) hold 0, below every real logit (the -inf word is 0x007FFFFF).
+DHP_DEV uint32_t order_word(float l) {
     l = (l == l) ? l + 0.0f : -INFINITY;
-    uint32_t u = __builtin_bit_cast(uint32_t, l);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    const uint32_t u = __builtin_bit_cast(uint32_t, l);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-DHP_DEV float topk_key_value(uint64_t k) {
-    const uint32_t u = (uint32_t)(k >> 32);
+DHP_DEV float order_word_value(uint32_t u) {
     return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
-DHP_DEV int topk_key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
-DHP_DEV uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-DHP_DEV uint64_t pack64(uint32_t hi, uint32_t lo) { return ((uint64_t)hi << 32) | lo; }
 
-template <int CTRL>
-DHP_DEV uint64_t dpp64(uint64_t v) {
-    return pack64((uint32_t)dpp_i<CTRL>((int)(v >> 32)), (uint32_t)dpp_i<CTRL>((int)(uint32_t)v));
-}
-
-// Wave-wide maximum key, in every lane: DPP within each 16-lane row, then the gfx950 row swap
+// Wave-wide maximum, in every lane: DPP within each 16-lane row, then the gfx950 row swap
 // (odd rows against even rows) and half swap (upper 32 lanes against lower 32).
-DHP_DEV uint64_t wave_max64(uint64_t k) {
-    k = max64(k, dpp64<DPP_XOR1>(k));
-    k = max64(k, dpp64<DPP_XOR2>(k));
-    k = max64(k, dpp64<DPP_HALF_MIRROR>(k));
-    k = max64(k, dpp64<DPP_MIRROR>(k));
-    uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
-    const auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    const auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    k = max64(pack64(h16[0], l16[0]), pack64(h16[1], l16[1]));
-    hi = (uint32_t)(k >> 32);
-    lo = (uint32_t)k;
-    const auto h32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    const auto l32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    return max64(pack64(h32[0], l32[0]), pack64(h32[1], l32[1]));
+DHP_DEV uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)dpp_i<DPP_XOR1>((int)v));
+    v = max(v, (uint32_t)dpp_i<DPP_XOR2>((int)v));
+    v = max(v, (uint32_t)dpp_i<DPP_HALF_MIRROR>((int)v));
+    v = max(v, (uint32_t)dpp_i<DPP_MIRROR>((int)v));
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max((uint32_t)r[0], (uint32_t)r[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((uint32_t)h[0], (uint32_t)h[1]);
 }
 
-// The first `rounds` entries of the top-k of the E logits, by one wave: each round takes the
-// wave-wide maximum key (a short chain of DPP and lane-swap steps, no branch), and the lane
-// holding it clears that entry. Every lane returns the same ids.
-DHP_DEV void wave_topk(const float* logits, int E, int rounds, int* ids, float* vals) {
+// The logits a lane ranks: PER consecutive ones from lane * PER, in whole 16-byte loads clamped
+// to the last full vector (the buffer must be readable up to index 4 * ((E - 1) / 4) + 3).
+template <int PER>
+struct TopkIn {
+    u32x4 v[PER / 4];
+};
+template <int PER>
+DHP_DEV void topk_load(TopkIn<PER>& t, const float* logits, int E) {
+    static_assert(PER % 4 == 0, "whole 16-byte loads");
     const int lane = threadIdx.x & 63;
-    constexpr int PER = MAX_E / 64;
-    const int per = (E + 63) >> 6;                 // wave-uniform
-    uint64_t k[PER];
+    const int last4 = ((E - 1) >> 2) << 2;
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q)
+        t.v[q] = *reinterpret_cast<const u32x4*>(logits + min(lane * PER + 4 * q, last4));
+}
+
+// The first `rounds` entries of the top-k of the E logits (E <= 64 * PER); every lane returns
+// the same ids and values.
+template <int PER>
+DHP_DEV void wave_topk(TopkIn<PER>& t, int E, int rounds, int* ids, float* vals) {
+    const int lane = threadIdx.x & 63;
+    uint32_t w[PER];
+    int ix[PER];
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t u = t.v[q][c];
+            asm volatile("" : "+v"(u));  // every element is live: the loads stay whole vectors
+            w[4 * q + c] = order_word(__builtin_bit_cast(float, u));
+        }
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        k[i] = 0;                                   // below every real key
-        if (i < per) {
-            const int e = lane + 64 * i;
-            const uint64_t ke = topk_key(logits[min(e, E - 1)], e);
-            k[i] = (e < E) ? ke : 0;
+        w[i] = (lane * PER + i < E) ? w[i] : 0u;
+        ix[i] = i;
+    }
+    if constexpr (PER <= 4) {
+        // sort each lane's entries: adjacent exchanges on a strict comparison keep equal words
+        // in index order
+#pragma unroll
+        for (int p = 0; p < PER - 1; ++p) {
+#pragma unroll
+            for (int q = 0; q < PER - 1 - p; ++q) {
+                const bool sw = w[q + 1] > w[q];
+                const uint32_t w0 = w[q], w1 = w[q + 1];
+                const int i0 = ix[q], i1 = ix[q + 1];
+                w[q] = sw ? w1 : w0;
+                w[q + 1] = sw ? w0 : w1;
+                ix[q] = sw ? i1 : i0;
+                ix[q + 1] = sw ? i0 : i1;
+            }
         }
     }
 #pragma unroll
     for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
         if (r >= rounds) break;
-        uint64_t m = k[0];
+        if constexpr (PER <= 4) {
+            const uint32_t m = wave_max_u32(w[0]);
+            const int wl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(w[0] == m));
+            ids[r] = wl * PER + __builtin_amdgcn_readlane(ix[0], wl);
+            vals[r] = order_word_value(m);
+            const bool mine = lane == wl;
 #pragma unroll
-        for (int i = 1; i < PER; ++i)
-            if (i < per) m = max64(m, k[i]);
-        m = wave_max64(m);
-        ids[r] = topk_key_index(m);
-        vals[r] = topk_key_value(m);
+            for (int q = 0; q < PER - 1; ++q) {
+                w[q] = mine ? w[q + 1] : w[q];
+                ix[q] = mine ? ix[q + 1] : ix[q];
+            }
+            w[PER - 1] = mine ? 0u : w[PER - 1];
+        } else {
+            uint32_t best = w[0];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) k[i] = (k[i] == m) ? 0 : k[i];
+            for (int i = 1; i < PER; ++i) best = max(best, w[i]);
+            const uint32_t m = wave_max_u32(best);
+            const int wl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(best == m));
+            int first = PER - 1;
+#pragma unroll
+            for (int i = PER - 2; i >= 0; --i) first = (w[i] == m) ? i : first;
+            ids[r] = wl * PER + __builtin_amdgcn_readlane(first, wl);
+            vals[r] = order_word_value(m);
+            const bool mine = lane == wl;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) w[i] = (mine && i == first) ? 0u : w[i];
+        }
     }
 }
 
-template <int CPL>
+template <int CPL, int PER>
 __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     const int lane = threadIdx.x;
     const int j = lane % LPR;
+    TopkIn<PER> tin;
+    topk_load<PER>(tin, a.logits, a.E);    // the routing decision waits on these: issue first
     h2 xp[CPL][16];
     float xs[CPL], nc[CPL];
-    load_x_regs<CPL>(a.x, j, xp, xs, nc);  // independent of routing: issue first
+    load_x_regs<CPL>(a.x, j, xp, xs, nc);  // independent of routing
 
     // a block only needs the ranks up to its last (slot, row) pair; block 0 also needs all
     // top_k of them for the softmax weights
-    const int last_pair = min(blockIdx.x * 4 + 3, a.top_k * a.inter - 1);
+    const int last_pair = min((int)blockIdx.x * 4 + 3, a.top_k * a.inter - 1);
     const int rounds = (blockIdx.x == 0) ? a.top_k : last_pair / a.inter + 1;
     int ids[DHP_MOE_MAX_TOP_K];
     float vals[DHP_MOE_MAX_TOP_K];
-    wave_topk(a.logits, a.E, rounds, ids, vals);
+    wave_topk<PER>(tin, a.E, rounds, ids, vals);
 
     const int pair = blockIdx.x * 4 + lane / LPR;      // (slot, row) flattened
     const bool live = pair < a.top_k * a.inter;
@@ -285,19 +330,20 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     PairRegs<CPL> p;
     load_pair<CPL>(p, gc, gs, gb, uc, us, ub, row, j);
 
+    // block 0 publishes the ids and the softmax over the selected logits
     if (blockIdx.x == 0 && lane == 0) {
-        float w[DHP_MOE_MAX_TOP_K];
+        float wt[DHP_MOE_MAX_TOP_K];
         float sum = 0.0f;
 #pragma unroll
         for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
-            w[r] = (r < a.top_k) ? __expf(vals[r] - vals[0]) : 0.0f;
-            sum += w[r];
+            wt[r] = (r < a.top_k) ? __expf(vals[r] - vals[0]) : 0.0f;
+            sum += wt[r];
         }
 #pragma unroll
         for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
             if (r < a.top_k) {
                 a.ids[r] = ids[r];
-                a.weights[r] = w[r] / sum;
+                a.weights[r] = wt[r] / sum;
             }
         }
     }
@@ -458,7 +504,8 @@ hipError_t launch_all(const MoeArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int pairs = a.top_k * a.inter;
-    hipLaunchKernelGGL(k_moe_phase1<CPL>, dim3((pairs + 3) / 4), dim3(64), 0, s, a);
+    if (a.E <= 256) hipLaunchKernelGGL((k_moe_phase1<CPL, 4>), dim3((pairs + 3) / 4), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((k_moe_phase1<CPL, MAX_E / 64>), dim3((pairs + 3) / 4), dim3(64), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)(a.top_k + 1) * (a.inter / 32) * ACT_PITCH * sizeof(float);

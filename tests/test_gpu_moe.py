@@ -145,6 +145,19 @@ def test_moe_tie_goes_to_lowest_index(case):
     assert_within_tol(out, ref["out"], "tie out")
 
 
+@pytest.mark.parametrize("E,period", [(256, 3), (1024, 5), (37, 2), (64, 1)])
+def test_moe_many_ties(E, period):
+    """Router rows repeat with the given period, so whole classes of experts share one logit and
+    the top-8 is decided by the lowest-index rule alone (ties inside one lane's group of
+    consecutive experts and across lanes)."""
+    say(f"moe many ties E={E} period={period}")
+    d = small(5, E, 512, 64, 8)
+    d["router_bits"] = d["router_bits"][np.arange(E) % period].copy()
+    logits = oracle.router_logits(d["router_bits"], d["x"])
+    assert len(set(logits.tolist())) <= period
+    check(d, DevMoe(d), d["x"], what=f"ties E{E}/{period}")
+
+
 def test_moe_identical_experts_routing_invariant():
     say("moe identical experts")
     d = small(4, 12, 512, 64, 3)
