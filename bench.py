@@ -64,7 +64,20 @@ def algorithmic_bytes():
     return b
 
 
-CALLS = ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8")
+STEP_CALLS = ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8")
+# Timed per call but outside the step: a 128-token chunk through the same MoE layer.
+EXTRA_CALLS = ("moe_prefill",)
+CALLS = STEP_CALLS + EXTRA_CALLS
+MOE_CHUNK = 128
+
+
+def moe_prefill_bytes(distinct_experts: int, m: int = MOE_CHUNK) -> int:
+    """Algorithmic bytes of one chunk call: the router and shared gate row, every expert the chunk
+    routes to once (gate, up and down) plus the shared expert, the chunk's activations in and
+    outputs out, ids and weights."""
+    K, E, inter, top_k = 2560, 256, 512, 8
+    expert = 2 * int4_bytes(inter, K) + int4_bytes(K, inter)
+    return 2 * E * K + 2 * K + (distinct_experts + 1) * expert + 2 * m * K * 2 + 8 * m * top_k
 
 
 def build_workload(torch, hca, synth, ring: int, only=None):
@@ -100,7 +113,7 @@ def build_workload(torch, hca, synth, ring: int, only=None):
         W["hc_mixed"] = torch.empty(2560, dtype=torch.float16, device=dev)
         W["hc_iw"] = torch.empty(4, dtype=torch.float32, device=dev)
 
-    if want("moe"):
+    if want("moe", "moe_prefill"):
         _moe_workload(torch, hca, synth, W, dev)
     if want("prefill"):
         p = synth.prefill_workload(0)
@@ -138,11 +151,14 @@ def _moe_workload(torch, hca, synth, W, dev):
         sg=up_int4(m["shared"]["gate"]), su=up_int4(m["shared"]["up"]), sd=up_int4(m["shared"]["down"]),
         router=hca.bf16_bits_to_tensor(m["router_bits"]).to(dev),
         sgate=hca.bf16_bits_to_tensor(m["sgate_bits"]).to(dev))
-    xs = np.concatenate([m["x"][None], synth.moe_x_ring(0, 63)])
+    xs = np.concatenate([m["x"][None], synth.moe_x_ring(0, MOE_CHUNK - 1)])
     W["moe_x"] = torch.from_numpy(xs).to(dev)
     W["moe_out"] = torch.empty(2560, dtype=torch.float16, device=dev)
     W["moe_ids"] = torch.empty(8, dtype=torch.int32, device=dev)
     W["moe_w"] = torch.empty(8, dtype=torch.float32, device=dev)
+    W["moep_out"] = torch.empty((MOE_CHUNK, 2560), dtype=torch.float16, device=dev)
+    W["moep_ids"] = torch.empty((MOE_CHUNK, 8), dtype=torch.int32, device=dev)
+    W["moep_w"] = torch.empty((MOE_CHUNK, 8), dtype=torch.float32, device=dev)
 
 
 def prepare_calls(hca, W, ring: int, only=None):
@@ -157,11 +173,22 @@ def prepare_calls(hca, W, ring: int, only=None):
                                         W["moe"]["up"], W["moe"]["down"], W["moe"]["sg"], W["moe"]["su"],
                                         W["moe"]["sd"], 8, W["moe_out"], W["moe_ids"], W["moe_w"])
                         for t in range(W["moe_x"].shape[0])],
+        "moe_prefill": lambda: [hca.prepare_moe_prefill(W["moe_x"], W["moe"]["router"], W["moe"]["sgate"],
+                                                        W["moe"]["gate"], W["moe"]["up"], W["moe"]["down"],
+                                                        W["moe"]["sg"], W["moe"]["su"], W["moe"]["sd"], 8,
+                                                        W["moep_out"], W["moep_ids"], W["moep_w"])],
         "prefill": lambda: [hca.prepare_gemm_batched(W["pre_w"][i], W["pre_x"], W["pre_y"]) for i in range(ring)],
         "lmhead1": lambda: [hca.prepare_gemv(W["lm_w"][0], W["lm_x1"], W["lm_y1"], argmax=W["lm_a1"])],
         "lmhead8": lambda: [hca.prepare_gemv(W["lm_w"][1], W["lm_x8"], W["lm_y8"], argmax=W["lm_a8"])],
     }
     return {name: f() for name, f in make.items() if only is None or name == only}
+
+
+def chunk_bytes(torch, W, calls) -> int:
+    """Run the chunk call once and size it by the distinct experts its routing selected."""
+    run_call(calls["moe_prefill"][0])
+    torch.cuda.synchronize()
+    return moe_prefill_bytes(int(torch.unique(W["moep_ids"]).numel()))
 
 
 def run_call(c):
@@ -412,7 +439,7 @@ def main():
         sys.exit(2)
     hca.lib()                                 # fails loudly when the HIP library is not built
     nbytes = algorithmic_bytes()
-    step_bytes = sum(nbytes.values())
+    step_bytes = sum(nbytes[c] for c in STEP_CALLS)
 
     if args.only == "copy":
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -426,6 +453,8 @@ def main():
     if args.only:
         W = build_workload(torch, hca, synth, args.ring, only=args.only)
         calls = prepare_calls(hca, W, args.ring, only=args.only)
+        if args.only == "moe_prefill":
+            nbytes["moe_prefill"] = chunk_bytes(torch, W, calls)
         for i in range(args.warmup):
             run_call(calls[args.only][i % len(calls[args.only])])
         r = per_call_pass(torch, calls, nbytes, iters=args.steps, exact=True)[args.only]
@@ -434,6 +463,7 @@ def main():
 
     W = build_workload(torch, hca, synth, args.ring)
     calls = prepare_calls(hca, W, args.ring)
+    nbytes["moe_prefill"] = chunk_bytes(torch, W, calls)
 
     for i in range(args.warmup):
         step(calls, i)

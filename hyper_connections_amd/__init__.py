@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.decodehp_dequant_gemm_batched.argtypes = [P4, vp, i32, vp, vp]
         L.decodehp_moe_decode.argtypes = [vp, vp, i32, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp,
                                           vp, sz, vp]
+        L.decodehp_moe_prefill.argtypes = [vp, i32, vp, i32, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp,
+                                           vp, sz, vp]
+        L.decodehp_moe_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.decodehp_moe_prefill_workspace_bytes.restype = sz
         L.decodehp_hc_read.argtypes = [vp, vp, i32, i32, ctypes.c_float, P4, P4, P4, vp, vp, vp, sz, vp]
         L.decodehp_hc_inject.argtypes = [vp, vp, vp, i32, i32, vp]
         L.decodehp_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -66,7 +70,7 @@ def lib() -> ctypes.CDLL:
         L.decodehp_last_error.restype = ctypes.c_char_p
         L.decodehp_version.restype = i32
         for name in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
-                     "decodehp_hc_read", "decodehp_hc_inject"):
+                     "decodehp_moe_prefill", "decodehp_hc_read", "decodehp_hc_inject"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -302,6 +306,56 @@ def hc_inject(wide, out, inject_w, C: int, H: int, stream=None):
 
 # --------------------------------------------------------------------------- prepared calls
 
+def moe_prefill_workspace_bytes(m: int, n_experts: int, top_k: int, inter: int, hidden: int) -> int:
+    return int(lib().decodehp_moe_prefill_workspace_bytes(m, n_experts, top_k, inter, hidden))
+
+
+def _moe_prefill_args(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k,
+                      out, ids, weights, fp16_boundary, stream):
+    torch = _torch()
+    hidden = gate.cols
+    m = x.shape[0]
+    _need(x, torch.float16, "x", m * hidden)
+    if router.dtype == torch.int16:
+        rdt = DHP_BF16
+    elif router.dtype == torch.float32:
+        rdt = DHP_F32
+    else:
+        raise TypeError("router: int16 (bf16 bits) or float32")
+    _need(router, router.dtype, "router", gate.count * hidden)
+    _need(shared_gate_row, torch.int16, "shared_gate_row", hidden)
+    _need(out, torch.float16, "out", m * hidden)
+    _need(ids, torch.int32, "ids", m * top_k)
+    _need(weights, torch.float32, "weights", m * top_k)
+    ws = _workspace(moe_prefill_workspace_bytes(m, gate.count, top_k, gate.rows, hidden), x.device, "moe_prefill")
+    descs = (gate.desc(), up.desc(), down.desc(), shared_gate.desc(), shared_up.desc(), shared_down.desc())
+    args = (x.data_ptr(), m, router.data_ptr(), rdt, shared_gate_row.data_ptr(), *[ctypes.byref(d) for d in descs],
+            top_k, DHP_MOE_FP16_BOUNDARY if fp16_boundary else 0, out.data_ptr(), ids.data_ptr(),
+            weights.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    keep = (descs, x, router, shared_gate_row, out, ids, weights, ws, gate, up, down, shared_gate, shared_up,
+            shared_down)
+    return args, keep
+
+
+def moe_prefill(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, down: Int4Experts,
+                shared_gate: Int4Weight, shared_up: Int4Weight, shared_down: Int4Weight, top_k: int,
+                fp16_boundary=False, out=None, ids=None, weights=None, stream=None):
+    """A chunk of m tokens (x fp16 [m, hidden], m <= 128) through the routed MoE layer; row i of
+    every output equals moe_decode of x[i], bit for bit.
+
+    Returns (out fp16 [m, hidden], ids int32 [m, top_k], weights fp32 [m, top_k]).
+    """
+    torch = _torch()
+    m, dev = x.shape[0], x.device
+    out = torch.empty((m, gate.cols), dtype=torch.float16, device=dev) if out is None else out
+    ids = torch.empty((m, top_k), dtype=torch.int32, device=dev) if ids is None else ids
+    weights = torch.empty((m, top_k), dtype=torch.float32, device=dev) if weights is None else weights
+    args, _keep = _moe_prefill_args(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down,
+                                    top_k, out, ids, weights, fp16_boundary, stream)
+    _check(lib().decodehp_moe_prefill(*args))
+    return out, ids, weights
+
+
 class PreparedCall:
     """One entry-point call with every argument marshalled up front; calling it only crosses
     the C boundary (for launch loops where per-call Python work would starve the GPU).
@@ -349,6 +403,13 @@ def prepare_moe(x, router, shared_gate_row, gate, up, down, shared_gate, shared_
             weights.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     return PreparedCall(lib().decodehp_moe_decode, args, (descs, x, router, shared_gate_row, out, ids, weights, ws,
                                                          gate, up, down, shared_gate, shared_up, shared_down))
+
+
+def prepare_moe_prefill(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k, out,
+                        ids, weights, fp16_boundary=False, stream=None) -> PreparedCall:
+    args, keep = _moe_prefill_args(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down,
+                                   top_k, out, ids, weights, fp16_boundary, stream)
+    return PreparedCall(lib().decodehp_moe_prefill, args, keep)
 
 
 def prepare_hc_read(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps=1e-6, stream=None) -> PreparedCall:

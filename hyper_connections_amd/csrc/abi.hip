@@ -100,7 +100,7 @@ extern "C" {
 
 const char* decodehp_last_error(void) { return g_err; }
 
-int32_t decodehp_version(void) { return (0 << 16) | 1; }
+int32_t decodehp_version(void) { return (0 << 16) | 2; }
 
 size_t decodehp_workspace_bytes(int32_t op, int32_t a, int32_t b, int32_t c) {
     switch (op) {
@@ -154,13 +154,14 @@ int decodehp_dequant_gemm_batched(const dhp_int4* w, const void* x, int32_t m, v
     return launch_gemm_mfma(w, x, m, y, 0, nullptr, nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
-int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
-                        const void* shared_gate_row, const dhp_int4_experts* gate,
-                        const dhp_int4_experts* up, const dhp_int4_experts* down,
-                        const dhp_int4* shared_gate, const dhp_int4* shared_up,
-                        const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
-                        int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream) {
-    g_err[0] = 0;
+namespace {
+// Checks shared by the MoE entry points: shapes, limits, dtypes, flags and alignment of the
+// weights and of x/out/ids/weights (x is 16-byte aligned; rows of x and out then stay aligned
+// because hidden is a multiple of 512).
+int check_moe(const void* x, const void* router, int32_t router_dtype, const void* shared_gate_row,
+              const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
+              const dhp_int4* shared_gate, const dhp_int4* shared_up, const dhp_int4* shared_down,
+              int32_t top_k, int32_t flags, const void* out, const int32_t* ids, const float* weights) {
     if (!x || !router || !shared_gate_row || !out || !ids || !weights)
         return dhp_fail(DHP_ERR_INVALID, "null x, router, shared_gate_row, out, ids or weights");
     int rc = check_experts(gate, "gate");
@@ -191,7 +192,21 @@ int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
         return dhp_fail(DHP_ERR_MISALIGNED, "x, router and shared_gate_row must be 16-byte aligned");
     if (!aligned(out, 2) || !aligned(ids, 4) || !aligned(weights, 4))
         return dhp_fail(DHP_ERR_MISALIGNED, "out, ids or weights misaligned");
-    const size_t need = dhp_moe_ws(E, top_k, inter);
+    return DHP_OK;
+}
+}  // namespace
+
+int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
+                        const void* shared_gate_row, const dhp_int4_experts* gate,
+                        const dhp_int4_experts* up, const dhp_int4_experts* down,
+                        const dhp_int4* shared_gate, const dhp_int4* shared_up,
+                        const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
+                        int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    const int rc = check_moe(x, router, router_dtype, shared_gate_row, gate, up, down, shared_gate, shared_up,
+                             shared_down, top_k, flags, out, ids, weights);
+    if (rc) return rc;
+    const size_t need = dhp_moe_ws(gate->count, top_k, gate->first.rows);
     if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
     DeviceFacts dev;
@@ -199,6 +214,36 @@ int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
     return launch_moe(x, router, router_dtype == DHP_F32, shared_gate_row, gate, up, down, shared_gate,
                       shared_up, shared_down, top_k, (flags & DHP_MOE_FP16_BOUNDARY) != 0, out, ids,
                       weights, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t decodehp_moe_prefill_workspace_bytes(int32_t m, int32_t n_experts, int32_t top_k, int32_t inter,
+                                            int32_t hidden) {
+    if (m < 1 || m > DHP_MOE_PREFILL_MAX_M || n_experts < 1 || n_experts > 1024 || top_k < 1 ||
+        top_k > DHP_MOE_MAX_TOP_K || inter < 1 || inter > 1024 || hidden < 1 || hidden > 4096)
+        return 0;
+    return dhp_moe_prefill_ws(m, n_experts, top_k, inter, hidden);
+}
+
+int decodehp_moe_prefill(const void* x, int32_t m, const void* router, int32_t router_dtype,
+                         const void* shared_gate_row, const dhp_int4_experts* gate,
+                         const dhp_int4_experts* up, const dhp_int4_experts* down,
+                         const dhp_int4* shared_gate, const dhp_int4* shared_up,
+                         const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
+                         int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (m < 1 || m > DHP_MOE_PREFILL_MAX_M)
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d (1..%d)", m, DHP_MOE_PREFILL_MAX_M);
+    const int rc = check_moe(x, router, router_dtype, shared_gate_row, gate, up, down, shared_gate, shared_up,
+                             shared_down, top_k, flags, out, ids, weights);
+    if (rc) return rc;
+    const size_t need = dhp_moe_prefill_ws(m, gate->count, top_k, gate->first.rows, gate->first.cols);
+    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_moe_prefill(x, m, router, router_dtype == DHP_F32, shared_gate_row, gate, up, down, shared_gate,
+                              shared_up, shared_down, top_k, (flags & DHP_MOE_FP16_BOUNDARY) != 0, out, ids,
+                              weights, ws, static_cast<hipStream_t>(stream));
 }
 
 int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H, float eps,

@@ -138,10 +138,10 @@ DHP_DEV float dot32_f16_raw(const u32x4 c, const h2* xp, float neg_corr, const N
     return d;
 }
 
-// 32 fp16 activations at p (16-byte aligned) as 16 permuted pairs with the odd-k slots scaled
-// by 1/16; returns their plain fp32 sum and sets neg_corr = -(1024 sum_even + 64 sum_odd).
-DHP_DEV float load_x32_raw(const _Float16* p, h2* xp, float& neg_corr) {
-    const u32x4* v = reinterpret_cast<const u32x4*>(p);
+// 32 fp16 activations (four 16-byte words, k order) as 16 permuted pairs with the odd-k slots
+// scaled by 1/16; returns their plain fp32 sum and sets neg_corr = -(1024 sum_even + 64 sum_odd).
+// (Both products are exact, so the result does not depend on whether they are fused.)
+DHP_DEV float x32_raw_from(const u32x4 (&v)[4], h2* xp, float& neg_corr) {
     const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     float even = 0.0f, odd = 0.0f;
 #pragma unroll
@@ -156,6 +156,13 @@ DHP_DEV float load_x32_raw(const _Float16* p, h2* xp, float& neg_corr) {
     }
     neg_corr = -(1024.0f * even + 64.0f * odd);
     return even + odd;
+}
+
+// The same for the 32 activations at p (16-byte aligned).
+DHP_DEV float load_x32_raw(const _Float16* p, h2* xp, float& neg_corr) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+    const u32x4 v[4] = {q[0], q[1], q[2], q[3]};
+    return x32_raw_from(v, xp, neg_corr);
 }
 
 // sum over 32 codes of q * x for fp32 activations x[0..31] (contiguous k order).
@@ -267,6 +274,11 @@ int launch_moe(const void* x, const void* router, int router_f32, const void* sg
                const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
                const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
                void* out, int32_t* ids, float* weights, void* ws, hipStream_t s);
+int launch_moe_prefill(const void* x, int m, const void* router, int router_f32, const void* sgate_row,
+                       const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
+                       const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
+                       void* out, int32_t* ids, float* weights, void* ws, hipStream_t s);
+size_t dhp_moe_prefill_ws(int32_t m, int32_t n_experts, int32_t top_k, int32_t inter, int32_t hidden);
 size_t dhp_argmax_part_stride(int32_t n_rows, int32_t m);
 int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax,
                      void* ws, size_t ws_part_stride, hipStream_t s);

@@ -25,6 +25,11 @@
 #include <math.h>
 #include <limits.h>
 
+// The batched (chunk of M tokens) kernels below reproduce the decode kernels' results bit for
+// bit, so every product and sum here is spelled out: no multiply and add may be fused unless
+// written as an fma.
+#pragma clang fp contract(off)
+
 namespace {
 
 constexpr int LPR = 16;
@@ -47,12 +52,18 @@ struct MoeArgs {
     const u32x4* su_codes; const uint16_t* su_scales; const uint16_t* su_biases;
     const u32x4* sd_codes; const uint16_t* sd_scales; const uint16_t* sd_biases;
     int E, hidden, inter, top_k, boundary;
-    float* logits;     // ws [E]
-    float* gate_logit; // ws [1]
-    float* act;        // ws [(top_k + 1) * inter]; slot top_k is the shared expert
-    _Float16* out;
-    int32_t* ids;
-    float* weights;
+    int M;             // tokens (1 for decode)
+    int Epad;          // logits row pitch (batched: E rounded up to 4)
+    float* logits;     // ws [M][Epad]
+    float* gate_logit; // ws [M]
+    float* act;        // ws [M][top_k + 1][inter]; slot top_k is the shared expert
+    float* dsum;       // ws [M][top_k + 1][hidden] (batched only): each slot's down-row dots
+    int32_t* route;    // ws [M][top_k + 1] (batched only): (token << 4 | slot), grouped by expert
+    int32_t* items;    // ws [max items][4] (batched only): (expert, first route entry, count, 0)
+    int32_t* nitems;   // ws [1] (batched only): work items in use
+    _Float16* out;     // [M][hidden]
+    int32_t* ids;      // [M][top_k]
+    float* weights;    // [M][top_k]
 };
 
 // Registers of one (gate row, up row) pair for the 16-lane group whose lane index is j.
@@ -99,24 +110,51 @@ DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* 
 }
 
 // fp32 dot of one bf16 or fp32 row of length hidden = 512 * CPL with the fp16 activations, one
-// wave. Every load of the row is issued before the first product, so the row costs one memory
-// round trip.
+// wave: lane l takes the 16-byte row chunks l + 64 i. The row's loads are issued on their own
+// (a batched caller keeps the row and streams tokens past it); a row costs one memory round trip.
 template <int CPL>
-DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x) {
+struct RouterRow {
+    u32x4 w[2 * CPL];      // bf16: CPL chunks of 8; fp32: 2 CPL chunks of 4 (as bits)
+};
+template <int CPL>
+struct RouterX {
+    uint2 h[2 * CPL];      // bf16 rows: chunk i = h[2i], h[2i+1]; fp32 rows: chunk i = h[i]
+};
+template <int CPL>
+DHP_DEV void router_row_load(RouterRow<CPL>& r, const void* row, int f32) {
     const int lane = threadIdx.x & 63;
+    const u32x4* p = static_cast<const u32x4*>(row);
+    if (!f32) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) r.w[i] = __builtin_nontemporal_load(p + lane + 64 * i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2 * CPL; ++i) r.w[i] = __builtin_nontemporal_load(p + lane + 64 * i);
+    }
+}
+template <int CPL>
+DHP_DEV void router_x_load(RouterX<CPL>& v, int f32, const _Float16* x) {
+    const int lane = threadIdx.x & 63;
+    if (!f32) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(x + 8 * (lane + 64 * i));
+            v.h[2 * i] = uint2{q.x, q.y};
+            v.h[2 * i + 1] = uint2{q.z, q.w};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2 * CPL; ++i) v.h[i] = *reinterpret_cast<const uint2*>(x + 4 * (lane + 64 * i));
+    }
+}
+template <int CPL>
+DHP_DEV float router_dot(const RouterRow<CPL>& r, const RouterX<CPL>& v, int f32) {
     float acc = 0.0f;
     if (!f32) {
-        const u32x4* r = static_cast<const u32x4*>(row);          // 8 bf16 per chunk, CPL per lane
-        u32x4 w[CPL], xv[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            w[i] = __builtin_nontemporal_load(r + lane + 64 * i);
-            xv[i] = *reinterpret_cast<const u32x4*>(x + 8 * (lane + 64 * i));
-        }
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-            const uint32_t xx[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            const uint32_t ww[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+            const uint32_t xx[4] = {v.h[2 * i].x, v.h[2 * i].y, v.h[2 * i + 1].x, v.h[2 * i + 1].y};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const h2 xh = as_h2(xx[k]);
@@ -125,26 +163,28 @@ DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x) {
             }
         }
     } else {
-        const f4v* r = static_cast<const f4v*>(row);               // 4 fp32 per chunk, 2 CPL per lane
-        f4v w[2 * CPL];
-        uint2 xv[2 * CPL];
 #pragma unroll
         for (int i = 0; i < 2 * CPL; ++i) {
-            w[i] = __builtin_nontemporal_load(r + lane + 64 * i);
-            xv[i] = *reinterpret_cast<const uint2*>(x + 4 * (lane + 64 * i));
-        }
-#pragma unroll
-        for (int i = 0; i < 2 * CPL; ++i) {
-            const h2 x0 = as_h2(xv[i].x), x1 = as_h2(xv[i].y);
-            acc = __builtin_fmaf(w[i].x, (float)x0.x, acc);
-            acc = __builtin_fmaf(w[i].y, (float)x0.y, acc);
-            acc = __builtin_fmaf(w[i].z, (float)x1.x, acc);
-            acc = __builtin_fmaf(w[i].w, (float)x1.y, acc);
+            const h2 x0 = as_h2(v.h[i].x), x1 = as_h2(v.h[i].y);
+            const f4v wv = __builtin_bit_cast(f4v, r.w[i]);   // whole-vector cast
+            acc = __builtin_fmaf(wv.x, (float)x0.x, acc);
+            acc = __builtin_fmaf(wv.y, (float)x0.y, acc);
+            acc = __builtin_fmaf(wv.z, (float)x1.x, acc);
+            acc = __builtin_fmaf(wv.w, (float)x1.y, acc);
         }
     }
     return group_sum<64>(acc);
 }
+template <int CPL>
+DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x) {
+    RouterRow<CPL> r;
+    RouterX<CPL> v;
+    router_row_load<CPL>(r, row, f32);
+    router_x_load<CPL>(v, f32, x);
+    return router_dot<CPL>(r, v, f32);
+}
 
+// Lane j's activations for pair_act: chunks j + 16 i in the raw form of load_x32_raw.
 template <int CPL>
 DHP_DEV void load_x_regs(const _Float16* x, int j, h2 (*xp)[16], float* xs, float* nc) {
 #pragma unroll
@@ -295,6 +335,24 @@ DHP_DEV void wave_topk(TopkIn<PER>& t, int E, int rounds, int* ids, float* vals)
     }
 }
 
+// The selected ids (largest logit first) and the softmax over their logits, by one thread.
+DHP_DEV void publish_topk(const int* ids, const float* vals, int top_k, int32_t* out_ids, float* out_w) {
+    float wt[DHP_MOE_MAX_TOP_K];
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
+        wt[r] = (r < top_k) ? __expf(vals[r] - vals[0]) : 0.0f;
+        sum += wt[r];
+    }
+#pragma unroll
+    for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
+        if (r < top_k) {
+            out_ids[r] = ids[r];
+            out_w[r] = wt[r] / sum;
+        }
+    }
+}
+
 template <int CPL, int PER>
 __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     const int lane = threadIdx.x;
@@ -331,33 +389,64 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     load_pair<CPL>(p, gc, gs, gb, uc, us, ub, row, j);
 
     // block 0 publishes the ids and the softmax over the selected logits
-    if (blockIdx.x == 0 && lane == 0) {
-        float wt[DHP_MOE_MAX_TOP_K];
-        float sum = 0.0f;
-#pragma unroll
-        for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
-            wt[r] = (r < a.top_k) ? __expf(vals[r] - vals[0]) : 0.0f;
-            sum += wt[r];
-        }
-#pragma unroll
-        for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
-            if (r < a.top_k) {
-                a.ids[r] = ids[r];
-                a.weights[r] = wt[r] / sum;
-            }
-        }
-    }
+    if (blockIdx.x == 0 && lane == 0) publish_topk(ids, vals, a.top_k, a.ids, a.weights);
 
     const float v = pair_act<CPL>(p, xp, xs, nc);
     if (j == 0 && live) a.act[(size_t)slot * a.inter + row] = v;
+}
+
+// Phase 2 pieces shared by the decode and batched kernels, so both compute every value the
+// same way. down_part: lane j's share of RHN down rows against one slot's fp32 activations,
+// chunks j + 16 i of K = inter (the 32 floats of chunk ch at act + ch * pitch): per chunk
+// s * (codes . act) + b * sum(act). group_sum<LPR> of it is the slot's down-row dot.
+template <int RHN, int CPLD>
+DHP_DEV void down_part(float (&p)[RHN], const u32x4 (&c)[RHN][CPLD], const uint32_t (&sv)[RHN][CPLD],
+                       const uint32_t (&bv)[RHN][CPLD], const float* act, int pitch, int j, int CH) {
+#pragma unroll
+    for (int r = 0; r < RHN; ++r) p[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPLD; ++i) {
+        const int ch = j + LPR * i;
+        if (ch < CH) {
+            const f4v* ap = reinterpret_cast<const f4v*>(act + ch * pitch);
+            float av[32];
+            float xs = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const f4v u = ap[q];
+                av[4 * q] = u.x; av[4 * q + 1] = u.y; av[4 * q + 2] = u.z; av[4 * q + 3] = u.w;
+                xs += (u.x + u.y) + (u.z + u.w);
+            }
+#pragma unroll
+            for (int r = 0; r < RHN; ++r) {
+                const float d = dot32_f32(c[r][i], av);
+                p[r] = __builtin_fmaf(bf16_to_f32(sv[r][i]), d, p[r]);
+                p[r] = __builtin_fmaf(bf16_to_f32(bv[r][i]), xs, p[r]);
+            }
+        }
+    }
+}
+
+// One output of the layer from its slots' down-row dots d[s * dstride] (slot top_k is the shared
+// expert): routed = sum_j w_j d_j, one fma per slot in slot order, plus sigmoid(g) * shared;
+// with the fp16 boundary both halves are rounded to fp16 before the add.
+DHP_DEV float moe_combine(const float (&w)[DHP_MOE_MAX_TOP_K], const float* d, int dstride, int top_k,
+                          float gate_logit, int boundary) {
+    float rr = 0.0f;
+#pragma unroll
+    for (int s = 0; s < DHP_MOE_MAX_TOP_K; ++s)
+        if (s < top_k) rr = __builtin_fmaf(w[s], d[s * dstride], rr);
+    const float ss = d[top_k * dstride] * sigmoid_f(gate_logit);
+    if (boundary) return (float)(_Float16)rr + (float)(_Float16)ss;
+    return rr + ss;
 }
 
 // Phase 2. A block of four waves owns 4 * RH consecutive outputs h (16 lanes and RH outputs per
 // 16-lane group, the same rows in every wave). Wave w takes expert slots w, w+4, w+8 (slot
 // top_k is the shared expert): its lanes issue every code, scale and bias load of those slots
 // first, the block stages the fp32 activations in LDS meanwhile, then each lane reduces its own
-// chunk (K = inter; lane j takes chunks j + 16 i) of each down row. The four waves' partial sums
-// meet in LDS in a fixed order, so the result does not depend on timing.
+// chunk (K = inter; lane j takes chunks j + 16 i) of each down row. Each slot's dot is summed
+// over its 16 lanes and parked in LDS; the outputs are combined from those in slot order.
 constexpr int RH = 2;
 constexpr int NSLOT = DHP_MOE_MAX_TOP_K + 1;
 constexpr int SLOTS_PER_WAVE = (NSLOT + 3) / 4;
@@ -366,7 +455,7 @@ constexpr int ACT_PITCH = 36;          // floats per staged 32-float activation 
 template <int CPLD>
 __global__ __launch_bounds__(256) void k_moe_phase2(MoeArgs a) {
     extern __shared__ float lds_act[];     // [(top_k + 1) * inter / 32][ACT_PITCH]
-    __shared__ float part[4][2][64 * RH];  // [wave][routed, shared][lane-major partials]
+    __shared__ float dpart[NSLOT][4 * RH]; // [slot][16-lane group * RH + r]
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int j = lane % LPR;
@@ -376,12 +465,9 @@ __global__ __launch_bounds__(256) void k_moe_phase2(MoeArgs a) {
     const int h0 = (blockIdx.x * 4 + lane / LPR) * RH;
 
     // the routing weights and the shared gate logit are read up front, with the expert ids
-    float wgts[SLOTS_PER_WAVE];
+    float w[DHP_MOE_MAX_TOP_K];
 #pragma unroll
-    for (int t = 0; t < SLOTS_PER_WAVE; ++t) {
-        const int slot = wave + 4 * t;
-        wgts[t] = (slot < a.top_k) ? a.weights[slot] : 1.0f;
-    }
+    for (int s = 0; s < DHP_MOE_MAX_TOP_K; ++s) w[s] = a.weights[min(s, a.top_k - 1)];
     const float gate_logit = a.gate_logit[0];
 
     u32x4 c[SLOTS_PER_WAVE][RH][CPLD];
@@ -433,68 +519,344 @@ __global__ __launch_bounds__(256) void k_moe_phase2(MoeArgs a) {
     }
     __syncthreads();
 
-    float racc[RH], sacc[RH];
-#pragma unroll
-    for (int r = 0; r < RH; ++r) { racc[r] = 0.0f; sacc[r] = 0.0f; }
 #pragma unroll
     for (int t = 0; t < SLOTS_PER_WAVE; ++t) {
         const int slot = wave + 4 * t;
         if (slot < nslot) {
-            const bool shared = slot == a.top_k;
-            const float wgt = wgts[t];
             float p[RH];
-#pragma unroll
-            for (int r = 0; r < RH; ++r) p[r] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPLD; ++i) {
-                const int ch = j + LPR * i;
-                if (ch < CH) {
-                    const f4v* ap = reinterpret_cast<const f4v*>(lds_act + (slot * CH + ch) * ACT_PITCH);
-                    float av[32];
-                    float xs = 0.0f;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const f4v u = ap[q];
-                        av[4 * q] = u.x; av[4 * q + 1] = u.y; av[4 * q + 2] = u.z; av[4 * q + 3] = u.w;
-                        xs += (u.x + u.y) + (u.z + u.w);
-                    }
-#pragma unroll
-                    for (int r = 0; r < RH; ++r) {
-                        const float d = dot32_f32(c[t][r][i], av);
-                        p[r] = __builtin_fmaf(bf16_to_f32(sv[t][r][i]), d, p[r]);
-                        p[r] = __builtin_fmaf(bf16_to_f32(bv[t][r][i]), xs, p[r]);
-                    }
-                }
-            }
+            down_part<RH, CPLD>(p, c[t], sv[t], bv[t], lds_act + slot * CH * ACT_PITCH, ACT_PITCH, j, CH);
 #pragma unroll
             for (int r = 0; r < RH; ++r) {
-                if (shared) sacc[r] += p[r];
-                else racc[r] = __builtin_fmaf(wgt, p[r], racc[r]);
+                const float d = group_sum<LPR>(p[r]);
+                if (j == 0) dpart[slot][(lane / LPR) * RH + r] = d;
             }
         }
     }
-#pragma unroll
-    for (int r = 0; r < RH; ++r) {
-        part[wave][0][r * 64 + lane] = group_sum<LPR>(racc[r]);
-        part[wave][1][r * 64 + lane] = group_sum<LPR>(sacc[r]);
-    }
     __syncthreads();
-    if (wave == 0) {
-        const float sg = sigmoid_f(gate_logit);
+    if (wave == 0 && j == 0) {
 #pragma unroll
         for (int r = 0; r < RH; ++r) {
             const int h = h0 + r;
-            if (j == 0 && h < a.hidden) {
-                const int q = r * 64 + lane;
-                const float rr = (part[0][0][q] + part[1][0][q]) + (part[2][0][q] + part[3][0][q]);
-                const float ss = ((part[0][1][q] + part[1][1][q]) + (part[2][1][q] + part[3][1][q])) * sg;
-                float o;
-                if (a.boundary) o = (float)(_Float16)rr + (float)(_Float16)ss;
-                else o = rr + ss;
+            if (h < a.hidden) {
+                const float o = moe_combine(w, &dpart[0][(lane / LPR) * RH + r], 4 * RH, a.top_k, gate_logit, a.boundary);
                 a.out[h] = (_Float16)o;
             }
         }
     }
+}
+
+// ------------------------------------------------------------------------------------------
+// A chunk of M <= 128 tokens through the layer in one pass over a route list ("src/real_forward.rs",
+// the forward state's routed-batch switch for chunked prefill): the results are identical, bit
+// for bit, to M decode calls, because every per-token value is computed by the same helpers in
+// the same order (router_dot, wave_topk and publish_topk, pair_act, down_part, moe_combine);
+// what changes is that each expert's weights stream once per chunk for all the tokens routed
+// to it.
+//  k_moep_router : one wave per router row (and one for the shared gate row): the row is loaded
+//                  once and dotted with a group of tokens, four tokens' activations in flight.
+//  k_moep_topk   : one wave per token: the decode's top-k and softmax.
+//  k_moep_phase1 : block = (16 rows, expert): the (token, slot) pairs routed to the expert, read
+//                  off the ids, run through pair_act; the tokens' activations are staged in LDS
+//                  (raw form, once per block) a group at a time. Expert E is the shared one,
+//                  taken by every token in slot top_k.
+//  k_moep_phase2 : block = (64 down rows, expert): each routed (token, slot) gets its down-row
+//                  dots (down_part, summed over 16 lanes), written to the workspace per slot.
+//  k_moep_combine: every output of every token from its slots' dots (moe_combine).
+constexpr int RT_TOK = 16;       // tokens per router block
+constexpr int RT_GRP = 4;        // tokens whose activations are in flight together
+// tokens staged per pass (the staging stays under 64 KiB of LDS at the largest shapes)
+template <int CPL> constexpr int p1_tg() { return CPL <= 5 ? 8 : 4; }
+template <int CPLD> constexpr int p2_tg() { return CPLD == 1 ? 16 : 8; }
+constexpr int P2_RH = 4;         // down rows per 16-lane group in the batched phase 2
+constexpr int ITEM_TOK = 16;     // (token, slot) pairs per work item
+
+template <int CPL>
+__global__ __launch_bounds__(256) void k_moep_router(MoeArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + wave;       // router row; E: the shared gate row
+    if (r > a.E) return;                       // whole waves; no block synchronisation below
+    const bool sgr = r == a.E;
+    const int f32 = sgr ? 0 : a.router_f32;
+    const void* row = sgr ? static_cast<const void*>(a.sgate_row)
+                          : static_cast<const void*>(static_cast<const uint8_t*>(a.router) +
+                                                     (size_t)r * a.hidden * (a.router_f32 ? 4 : 2));
+    RouterRow<CPL> rr;
+    router_row_load<CPL>(rr, row, f32);
+    const int m0 = blockIdx.y * RT_TOK, m1 = min(m0 + RT_TOK, a.M);
+    for (int mb = m0; mb < m1; mb += RT_GRP) {
+        RouterX<CPL> v[RT_GRP];
+#pragma unroll
+        for (int g = 0; g < RT_GRP; ++g) router_x_load<CPL>(v[g], f32, a.x + (size_t)min(mb + g, m1 - 1) * a.hidden);
+#pragma unroll
+        for (int g = 0; g < RT_GRP; ++g) {
+            const int m = mb + g;
+            const float d = router_dot<CPL>(rr, v[g], f32);
+            if (lane == 0 && m < m1) {
+                if (sgr) a.gate_logit[m] = d;
+                else a.logits[(size_t)m * a.Epad + r] = d;
+            }
+        }
+    }
+}
+
+template <int PER>
+__global__ __launch_bounds__(64) void k_moep_topk(MoeArgs a) {
+    const int m = blockIdx.x;
+    TopkIn<PER> tin;
+    topk_load<PER>(tin, a.logits + (size_t)m * a.Epad, a.E);
+    int ids[DHP_MOE_MAX_TOP_K];
+    float vals[DHP_MOE_MAX_TOP_K];
+    wave_topk<PER>(tin, a.E, a.top_k, ids, vals);
+    if (threadIdx.x == 0)
+        publish_topk(ids, vals, a.top_k, a.ids + (size_t)m * a.top_k, a.weights + (size_t)m * a.top_k);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+DHP_DEV int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// The route list and the work items, by one block of 1024 threads: the chunk's (token, slot)
+// pairs counting-sorted by expert (the shared expert's M pairs first, then the routed experts in
+// index order; within an expert any order, since every pair's results are computed and stored
+// on their own), cut into items of at most ITEM_TOK pairs of one expert. The shared expert's
+// items come first, so the blocks holding the longest list start first.
+__global__ __launch_bounds__(1024) void k_moep_route(MoeArgs a) {
+    __shared__ int cnt[MAX_E], base[MAX_E], ibase[MAX_E], fill[MAX_E];
+    __shared__ int wsum[16][2];
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int E = a.E, M = a.M, k = a.top_k, n = M * k;
+    if (t < E) { cnt[t] = 0; fill[t] = 0; }
+    __syncthreads();
+    if (t < n) atomicAdd(&cnt[a.ids[t]], 1);
+    __syncthreads();
+    const int c = (t < E) ? cnt[t] : 0;
+    const int ki = (c + ITEM_TOK - 1) / ITEM_TOK;
+    const int sc = wave_incl_scan(c), sk = wave_incl_scan(ki);
+    if (lane == 63) { wsum[wave][0] = sc; wsum[wave][1] = sk; }
+    __syncthreads();
+    int oc = 0, ok = 0;
+    for (int w = 0; w < wave; ++w) { oc += wsum[w][0]; ok += wsum[w][1]; }
+    const int nsh = (M + ITEM_TOK - 1) / ITEM_TOK;
+    if (t < E) { base[t] = M + oc + sc - c; ibase[t] = nsh + ok + sk - ki; }
+    __syncthreads();
+    if (t < n) {
+        const int e = a.ids[t];
+        a.route[base[e] + atomicAdd(&fill[e], 1)] = ((t / k) << 4) | (t % k);
+    }
+    if (t < M) a.route[t] = (t << 4) | k;
+    if (t < nsh) *reinterpret_cast<int4*>(a.items + 4 * t) = int4{E, ITEM_TOK * t, min(ITEM_TOK, M - ITEM_TOK * t), 0};
+    if (t < E)
+        for (int j = 0; j < ki; ++j)
+            *reinterpret_cast<int4*>(a.items + 4 * (ibase[t] + j)) =
+                int4{t, base[t] + ITEM_TOK * j, min(ITEM_TOK, c - ITEM_TOK * j), 0};
+    if (t == 1023) a.nitems[0] = nsh + ok + sk;           // the last thread holds the full totals
+}
+
+// An upper bound on the work items of a chunk: the shared expert's, plus at most one partial
+// item per routed expert that appears on top of the full ones.
+int max_items(int M, int E, int top_k) {
+    return (M + ITEM_TOK - 1) / ITEM_TOK + (M * top_k) / ITEM_TOK + min(E, M * top_k);
+}
+
+template <int CPL>
+__global__ __launch_bounds__(256) void k_moep_phase1(MoeArgs a) {
+    constexpr int CH32 = LPR * CPL;                   // 32-activation chunks per token
+    constexpr int P1_TG = p1_tg<CPL>();
+    constexpr int IT = (P1_TG * CH32 + 255) / 256;    // staged chunks per thread per pass
+    extern __shared__ u32x4 xstage[];                 // [P1_TG][4][CH32] u32x4, then [P1_TG][CH32] float2
+    float2* xsum = reinterpret_cast<float2*>(xstage + P1_TG * 4 * CH32);
+    if ((int)blockIdx.y >= a.nitems[0]) return;        // the whole block
+    const int4 item = *reinterpret_cast<const int4*>(a.items + 4 * blockIdx.y);
+    const int e = item.x, n = item.z;
+    const int32_t* list = a.route + item.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane % LPR;
+    const int row = blockIdx.x * 16 + wave * 4 + lane / LPR;
+    const bool live = row < a.inter;
+    const u32x4 *gc, *uc;
+    const uint16_t *gs, *gb, *us, *ub;
+    if (e == a.E) {
+        gc = a.sg_codes; gs = a.sg_scales; gb = a.sg_biases;
+        uc = a.su_codes; us = a.su_scales; ub = a.su_biases;
+    } else {
+        gc = reinterpret_cast<const u32x4*>(a.g_codes + (size_t)e * a.gu_cstride);
+        gs = reinterpret_cast<const uint16_t*>(a.g_scales + (size_t)e * a.gu_sstride);
+        gb = reinterpret_cast<const uint16_t*>(a.g_biases + (size_t)e * a.gu_sstride);
+        uc = reinterpret_cast<const u32x4*>(a.u_codes + (size_t)e * a.u_cstride);
+        us = reinterpret_cast<const uint16_t*>(a.u_scales + (size_t)e * a.u_sstride);
+        ub = reinterpret_cast<const uint16_t*>(a.u_biases + (size_t)e * a.u_sstride);
+    }
+    PairRegs<CPL> p;
+    load_pair<CPL>(p, gc, gs, gb, uc, us, ub, live ? row : 0, j);
+    const int nslot = a.top_k + 1;
+
+    for (int base = 0; base < n; base += P1_TG) {
+        const int tn = min(P1_TG, n - base);
+        __syncthreads();                               // the previous group's reads are done
+        // every load of the group first (items past the group clamped), then the raw form
+        u32x4 v[IT][4];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int it = min((int)threadIdx.x + 256 * k, tn * CH32 - 1);
+            const int t = it / CH32, c = it - t * CH32;
+            const u32x4* src = reinterpret_cast<const u32x4*>(a.x + (size_t)(list[base + t] >> 4) * a.hidden + 32 * c);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[k][q] = src[q];
+        }
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int it = (int)threadIdx.x + 256 * k;
+            if (it < tn * CH32) {
+                const int t = it / CH32, c = it - t * CH32;
+                h2 xp[16];
+                float nc;
+                const float xs = x32_raw_from(v[k], xp, nc);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xstage[(t * 4 + q) * CH32 + c] = u32x4{h2_bits(xp[4 * q]), h2_bits(xp[4 * q + 1]),
+                                                          h2_bits(xp[4 * q + 2]), h2_bits(xp[4 * q + 3])};
+                xsum[t * CH32 + c] = float2{xs, nc};
+            }
+        }
+        __syncthreads();
+        for (int t = 0; t < tn; ++t) {
+            h2 xp[CPL][16];
+            float xs[CPL], nc[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = j + LPR * i;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 u = xstage[(t * 4 + q) * CH32 + c];
+                    xp[i][4 * q] = as_h2(u.x); xp[i][4 * q + 1] = as_h2(u.y);
+                    xp[i][4 * q + 2] = as_h2(u.z); xp[i][4 * q + 3] = as_h2(u.w);
+                }
+                const float2 sn = xsum[t * CH32 + c];
+                xs[i] = sn.x;
+                nc[i] = sn.y;
+            }
+            const float v1 = pair_act<CPL>(p, xp, xs, nc);
+            const int ms = list[base + t];
+            if (j == 0 && live) a.act[((size_t)(ms >> 4) * nslot + (ms & 15)) * a.inter + row] = v1;
+        }
+    }
+}
+
+template <int CPLD>
+__global__ __launch_bounds__(256) void k_moep_phase2(MoeArgs a) {
+    extern __shared__ float astage[];                  // [P2_TG][inter / 32][ACT_PITCH]
+    if ((int)blockIdx.y >= a.nitems[0]) return;        // the whole block
+    const int4 item = *reinterpret_cast<const int4*>(a.items + 4 * blockIdx.y);
+    const int e = item.x, n = item.z;
+    const int32_t* list = a.route + item.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane % LPR;
+    const int CH = a.inter >> 5, G = a.inter >> 6;
+    const int nslot = a.top_k + 1;
+    const int h0 = (blockIdx.x * 16 + wave * 4 + lane / LPR) * P2_RH;
+    const u32x4* dc;
+    const uint16_t *ds, *db;
+    if (e == a.E) {
+        dc = a.sd_codes; ds = a.sd_scales; db = a.sd_biases;
+    } else {
+        dc = reinterpret_cast<const u32x4*>(a.d_codes + (size_t)e * a.d_cstride);
+        ds = reinterpret_cast<const uint16_t*>(a.d_scales + (size_t)e * a.d_sstride);
+        db = reinterpret_cast<const uint16_t*>(a.d_biases + (size_t)e * a.d_sstride);
+    }
+    u32x4 c[P2_RH][CPLD];
+    uint32_t sv[P2_RH][CPLD], bv[P2_RH][CPLD];
+#pragma unroll
+    for (int r = 0; r < P2_RH; ++r) {
+        const int h = min(h0 + r, a.hidden - 1);
+#pragma unroll
+        for (int i = 0; i < CPLD; ++i) {
+            const int ch = min(j + LPR * i, CH - 1);
+            c[r][i] = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
+            sv[r][i] = ds[(size_t)h * G + (ch >> 1)];
+            bv[r][i] = db[(size_t)h * G + (ch >> 1)];
+        }
+    }
+    constexpr int P2_TG = p2_tg<CPLD>();
+    constexpr int IT = P2_TG * 32 * CPLD * LPR / 4 / 256;   // f4v per thread per pass (inter <= 512 CPLD)
+    for (int base = 0; base < n; base += P2_TG) {
+        const int tn = min(P2_TG, n - base);
+        __syncthreads();                               // the previous group's reads are done
+        const int items = tn * (a.inter >> 2);
+        f4v v[IT];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int it = min((int)threadIdx.x + 256 * k, items - 1);
+            const int t = it / (a.inter >> 2), q = it - t * (a.inter >> 2);
+            const int ms = list[base + t];
+            v[k] = *reinterpret_cast<const f4v*>(a.act + ((size_t)(ms >> 4) * nslot + (ms & 15)) * a.inter + 4 * q);
+        }
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int it = (int)threadIdx.x + 256 * k;
+            if (it < items) {
+                const int t = it / (a.inter >> 2), i4 = 4 * (it - t * (a.inter >> 2));
+                *reinterpret_cast<f4v*>(astage + (t * CH + (i4 >> 5)) * ACT_PITCH + (i4 & 31)) = v[k];
+            }
+        }
+        __syncthreads();
+        for (int t = 0; t < tn; ++t) {
+            float p[P2_RH];
+            down_part<P2_RH, CPLD>(p, c, sv, bv, astage + t * CH * ACT_PITCH, ACT_PITCH, j, CH);
+            const int ms = list[base + t];
+            float* dst = a.dsum + ((size_t)(ms >> 4) * nslot + (ms & 15)) * a.hidden;
+#pragma unroll
+            for (int r = 0; r < P2_RH; ++r) {
+                const float d = group_sum<LPR>(p[r]);
+                if (j == 0 && h0 + r < a.hidden) dst[h0 + r] = d;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_moep_combine(MoeArgs a) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= a.M * a.hidden) return;
+    const int m = idx / a.hidden, h = idx - m * a.hidden;
+    float w[DHP_MOE_MAX_TOP_K];
+#pragma unroll
+    for (int s = 0; s < DHP_MOE_MAX_TOP_K; ++s) w[s] = a.weights[(size_t)m * a.top_k + min(s, a.top_k - 1)];
+    const float o = moe_combine(w, a.dsum + (size_t)m * (a.top_k + 1) * a.hidden + h, a.hidden, a.top_k,
+                                a.gate_logit[m], a.boundary);
+    a.out[idx] = (_Float16)o;
+}
+
+template <int CPL>
+hipError_t launch_prefill_all(const MoeArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_moep_router<CPL>, dim3((a.E + 1 + 3) / 4, (a.M + RT_TOK - 1) / RT_TOK), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.E <= 256) hipLaunchKernelGGL((k_moep_topk<4>), dim3(a.M), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((k_moep_topk<MAX_E / 64>), dim3(a.M), dim3(64), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int CH32 = LPR * CPL;
+    const size_t lds1 = (size_t)p1_tg<CPL>() * CH32 * (4 * sizeof(u32x4) + sizeof(float2));
+    hipLaunchKernelGGL(k_moep_route, dim3(1), dim3(1024), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int items = max_items(a.M, a.E, a.top_k);
+    hipLaunchKernelGGL(k_moep_phase1<CPL>, dim3((a.inter + 15) / 16, items), dim3(256), lds1, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 g2((a.hidden + 16 * P2_RH - 1) / (16 * P2_RH), items);
+    if (a.inter <= 512)
+        hipLaunchKernelGGL(k_moep_phase2<1>, g2, dim3(256), (size_t)p2_tg<1>() * (a.inter / 32) * ACT_PITCH * 4, s, a);
+    else
+        hipLaunchKernelGGL(k_moep_phase2<2>, g2, dim3(256), (size_t)p2_tg<2>() * (a.inter / 32) * ACT_PITCH * 4, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_moep_combine, dim3((a.M * a.hidden + 255) / 256), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 template <int CPL>
@@ -522,11 +884,31 @@ size_t dhp_moe_ws(int32_t n_experts, int32_t top_k, int32_t inter) {
     return (floats * sizeof(float) + 255) & ~(size_t)255;
 }
 
-int launch_moe(const void* x, const void* router, int router_f32, const void* sgate_row,
+namespace {
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+// Batched workspace, in order: logits [m][Epad], gate logits [m], act [m][top_k + 1][inter],
+// slot dots [m][top_k + 1][hidden] (fp32, each part 256-byte aligned).
+struct PrefillWs {
+    size_t logits, gate, act, dsum, route, items, nitems, total;
+};
+PrefillWs prefill_ws(int m, int E, int top_k, int inter, int hidden) {
+    PrefillWs w;
+    const size_t epad = (size_t)((E + 3) & ~3);
+    w.logits = 0;
+    w.gate = w.logits + align256((size_t)m * epad * sizeof(float));
+    w.act = w.gate + align256((size_t)m * sizeof(float));
+    w.dsum = w.act + align256((size_t)m * (top_k + 1) * inter * sizeof(float));
+    w.route = w.dsum + align256((size_t)m * (top_k + 1) * hidden * sizeof(float));
+    w.items = w.route + align256((size_t)m * (top_k + 1) * sizeof(int32_t));
+    w.nitems = w.items + align256((size_t)max_items(m, E, top_k) * 4 * sizeof(int32_t));
+    w.total = w.nitems + 256;
+    return w;
+}
+
+void fill_args(MoeArgs& a, const void* x, const void* router, int router_f32, const void* sgate_row,
                const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
-               const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
-               void* out, int32_t* ids, float* weights, void* ws, hipStream_t s) {
-    MoeArgs a;
+               const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary, void* out,
+               int32_t* ids, float* weights) {
     a.x = static_cast<const _Float16*>(x);
     a.router = router;
     a.router_f32 = router_f32;
@@ -560,13 +942,30 @@ int launch_moe(const void* x, const void* router, int router_f32, const void* sg
     a.inter = gate->first.rows;
     a.top_k = top_k;
     a.boundary = boundary;
+    a.out = static_cast<_Float16*>(out);
+    a.ids = ids;
+    a.weights = weights;
+}
+}  // namespace
+
+size_t dhp_moe_prefill_ws(int32_t m, int32_t n_experts, int32_t top_k, int32_t inter, int32_t hidden) {
+    return prefill_ws(m, n_experts, top_k, inter, hidden).total;
+}
+
+int launch_moe(const void* x, const void* router, int router_f32, const void* sgate_row,
+               const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
+               const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
+               void* out, int32_t* ids, float* weights, void* ws, hipStream_t s) {
+    MoeArgs a;
+    fill_args(a, x, router, router_f32, sgate_row, gate, up, down, sg, su, sd, top_k, boundary, out, ids, weights);
+    a.M = 1;
+    a.Epad = a.E;
     float* w = static_cast<float*>(ws);
     a.logits = w;
     a.gate_logit = w + a.E;
     a.act = w + ((a.E + 4) & ~3);        // 16-byte aligned
-    a.out = static_cast<_Float16*>(out);
-    a.ids = ids;
-    a.weights = weights;
+    a.dsum = nullptr;
+    a.route = a.items = a.nitems = nullptr;
 
     hipError_t e;
     switch (a.hidden / 512) {
@@ -581,5 +980,39 @@ int launch_moe(const void* x, const void* router, int router_f32, const void* sg
         default: return dhp_fail(DHP_ERR_UNSUPPORTED, "hidden=%d", a.hidden);
     }
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "moe launch: %s", hipGetErrorString(e));
+    return DHP_OK;
+}
+
+int launch_moe_prefill(const void* x, int m, const void* router, int router_f32, const void* sgate_row,
+                       const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
+                       const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
+                       void* out, int32_t* ids, float* weights, void* ws, hipStream_t s) {
+    MoeArgs a;
+    fill_args(a, x, router, router_f32, sgate_row, gate, up, down, sg, su, sd, top_k, boundary, out, ids, weights);
+    a.M = m;
+    a.Epad = (a.E + 3) & ~3;
+    const PrefillWs lay = prefill_ws(m, a.E, top_k, a.inter, a.hidden);
+    char* base = static_cast<char*>(ws);
+    a.logits = reinterpret_cast<float*>(base + lay.logits);
+    a.gate_logit = reinterpret_cast<float*>(base + lay.gate);
+    a.act = reinterpret_cast<float*>(base + lay.act);
+    a.dsum = reinterpret_cast<float*>(base + lay.dsum);
+    a.route = reinterpret_cast<int32_t*>(base + lay.route);
+    a.items = reinterpret_cast<int32_t*>(base + lay.items);
+    a.nitems = reinterpret_cast<int32_t*>(base + lay.nitems);
+
+    hipError_t e;
+    switch (a.hidden / 512) {
+        case 1: e = launch_prefill_all<1>(a, s); break;
+        case 2: e = launch_prefill_all<2>(a, s); break;
+        case 3: e = launch_prefill_all<3>(a, s); break;
+        case 4: e = launch_prefill_all<4>(a, s); break;
+        case 5: e = launch_prefill_all<5>(a, s); break;
+        case 6: e = launch_prefill_all<6>(a, s); break;
+        case 7: e = launch_prefill_all<7>(a, s); break;
+        case 8: e = launch_prefill_all<8>(a, s); break;
+        default: return dhp_fail(DHP_ERR_UNSUPPORTED, "hidden=%d", a.hidden);
+    }
+    if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "moe prefill launch: %s", hipGetErrorString(e));
     return DHP_OK;
 }

@@ -66,6 +66,7 @@ extern "C" {
 #define DHP_GEMV_MAX_M 16
 #define DHP_GEMM_MAX_M 128
 #define DHP_MOE_MAX_TOP_K 8
+#define DHP_MOE_PREFILL_MAX_M 128
 #define DHP_HC_MAX_C 16
 
 typedef struct dhp_int4 {
@@ -152,6 +153,31 @@ int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
                         const dhp_int4* shared_gate, const dhp_int4* shared_up,
                         const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
                         int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * decodehp_moe_prefill -- a chunk of m tokens through the same MoE layer in one pass.
+ * "src/real_forward.rs", the forward state's switch that runs a chunked-prefill layer's
+ * routed half as one batched dispatch over a route list, byte-identical to running the
+ * tokens one at a time. Row i of out, ids and weights is bit-identical to what
+ * decodehp_moe_decode returns for row i of x (same weights, top_k and flags); each expert's
+ * weights are streamed once per call for all the tokens routed to it.
+ *   x               : fp16 [m][hidden], 16-byte aligned.   m : 1..DHP_MOE_PREFILL_MAX_M.
+ *   router, shared_gate_row, gate, up, down, shared_*, top_k, flags : as decodehp_moe_decode.
+ *   out             : fp16 [m][hidden].  ids : int32 [m][top_k].  weights : fp32 [m][top_k].
+ *   ws              : decodehp_moe_prefill_workspace_bytes(m, n_experts, top_k, inter, hidden)
+ *                     bytes, 16-byte aligned.
+ * Errors: as decodehp_moe_decode, and -2 for m outside 1..DHP_MOE_PREFILL_MAX_M.
+ */
+int decodehp_moe_prefill(const void* x, int32_t m, const void* router, int32_t router_dtype,
+                         const void* shared_gate_row, const dhp_int4_experts* gate,
+                         const dhp_int4_experts* up, const dhp_int4_experts* down,
+                         const dhp_int4* shared_gate, const dhp_int4* shared_up,
+                         const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
+                         int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes decodehp_moe_prefill needs (0 for arguments out of range). */
+size_t decodehp_moe_prefill_workspace_bytes(int32_t m, int32_t n_experts, int32_t top_k,
+                                            int32_t inter, int32_t hidden);
 
 /*
  * decodehp_hc_read -- one hyper-connection read (attn_hc / mlp_hc / the final mixer).

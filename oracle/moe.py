@@ -106,3 +106,20 @@ def moe_decode(x, router_bits, sgate_bits, shared, experts, top_k: int,
         out = routed + shared_gated
     return {"out": out, "ids": ids, "weights": w, "logits": logits, "routed": routed,
             "shared_gated": shared_gated, "gate": g}
+
+
+def moe_prefill(X, router_bits, sgate_bits, shared, experts, top_k: int,
+                fp16_boundary: bool = False, router_is_bf16_bits: bool = True):
+    """A chunk of M tokens through the routed MoE layer.
+
+    "src/real_forward.rs", the forward state's switch for running a chunk's routed half as
+    one batched dispatch pair over a route list: its output is byte-identical to running
+    the tokens one at a time. So the batched call is defined as the decode call applied to
+    each row of X independently. Returns dict(out [M, hidden], ids [M, k], weights [M, k]).
+    """
+    rows = [moe_decode(x, router_bits, sgate_bits, shared, experts, top_k, fp16_boundary,
+                       router_is_bf16_bits) for x in np.asarray(X)]
+    return {"out": np.stack([r["out"] for r in rows]), "ids": np.stack([r["ids"] for r in rows]),
+            "weights": np.stack([r["weights"] for r in rows]),
+            "logits": np.stack([r["logits"] for r in rows])}
+

@@ -24,6 +24,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
+              "decodehp_moe_prefill", "decodehp_moe_prefill_workspace_bytes",
               "decodehp_hc_read", "decodehp_hc_inject", "decodehp_workspace_bytes", "decodehp_last_error"):
         assert n in names
 
@@ -137,6 +138,33 @@ def test_moe_rejects_bad_calls():
     need = hca.workspace_bytes(hca.DHP_OP_MOE_DECODE, 8, 2, 64)
     assert need >= (8 + 3 * 64) * 4
     assert moe(wsb=need - 1) == -4
+
+
+def moe_prefill(m=4, top_k=2, flags=0, E=8, hidden=512, inter=64, ws=FAKE, wsb=1 << 24, x=FAKE, ids=FAKE):
+    L = hca.lib()
+    g, u = experts(E, inter, hidden), experts(E, inter, hidden)
+    d = experts(E, hidden, inter)
+    sg, su, sd = int4(rows=inter, cols=hidden), int4(rows=inter, cols=hidden), int4(rows=hidden, cols=inter)
+    return L.decodehp_moe_prefill(x, m, FAKE, 2, FAKE, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                  ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), top_k, flags, FAKE,
+                                  ids, FAKE, ws, wsb, None)
+
+
+def test_moe_prefill_rejects_bad_calls():
+    assert moe_prefill(m=0) == -2
+    assert moe_prefill(m=129) == -2
+    assert moe_prefill(ids=0) == -1
+    assert moe_prefill(top_k=9) == -2
+    assert moe_prefill(flags=4) == -2
+    assert moe_prefill(hidden=640) == -2
+    assert moe_prefill(x=FAKE + 4) == -3
+    assert moe_prefill(ws=None) == -4
+    need = hca.moe_prefill_workspace_bytes(4, 8, 2, 64, 512)
+    # logits [4][8], gate logits [4], act [4][3][64] and slot dots [4][3][512], fp32
+    assert need >= (4 * 8 + 4 + 4 * 3 * 64 + 4 * 3 * 512) * 4
+    assert moe_prefill(wsb=need - 1) == -4
+    assert hca.moe_prefill_workspace_bytes(0, 8, 2, 64, 512) == 0
+    assert hca.moe_prefill_workspace_bytes(129, 8, 2, 64, 512) == 0
 
 
 def hc_read(C=4, H=512, R=64, inject=True, iw=FAKE, ws=FAKE, wsb=1 << 16, eps=1e-6, raw=FAKE, up_cols=None):

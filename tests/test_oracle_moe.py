@@ -264,3 +264,37 @@ def test_planted_highest_index_tie_break_fails(monkeypatch):
     monkeypatch.setattr(om, "select_topk", bad_topk)
     monkeypatch.setattr(oracle, "select_topk", bad_topk)
     assert _count_failures() >= 1
+
+
+def _prefill_case(seed, M, E=12, hidden=128, inter=64, top_k=3):
+    rng = np.random.default_rng([71, seed])
+    mk = lambda r, c: synth.int4_tensor(rng, r, c)
+    X = synth.normal_f16(rng, (M, hidden))
+    router = synth.normal_bf16_bits(rng, (E, hidden), std=0.1)
+    sgate = synth.normal_bf16_bits(rng, (hidden,), std=0.02)
+    shared = {"gate": mk(inter, hidden), "up": mk(inter, hidden), "down": mk(hidden, inter)}
+    experts = [{"gate": mk(inter, hidden), "up": mk(inter, hidden), "down": mk(hidden, inter)} for _ in range(E)]
+    return X, router, sgate, shared, experts, top_k
+
+
+def test_moe_prefill_one_token_is_decode():
+    X, router, sgate, shared, experts, k = _prefill_case(0, 1)
+    p = oracle.moe_prefill(X, router, sgate, shared, experts, k)
+    d = oracle.moe_decode(X[0], router, sgate, shared, experts, k)
+    assert np.array_equal(p["out"][0], d["out"])
+    assert list(p["ids"][0]) == list(d["ids"]) and np.array_equal(p["weights"][0], d["weights"])
+
+
+def test_moe_prefill_tokens_are_independent():
+    """A chunk is M separate passes: reordering the tokens reorders the rows of every output,
+    and a token's row does not change when the other tokens of the chunk change."""
+    X, router, sgate, shared, experts, k = _prefill_case(1, 5)
+    base = oracle.moe_prefill(X, router, sgate, shared, experts, k)
+    perm = np.array([3, 0, 4, 2, 1])
+    pp = oracle.moe_prefill(X[perm], router, sgate, shared, experts, k)
+    assert np.array_equal(pp["out"], base["out"][perm])
+    assert np.array_equal(pp["ids"], base["ids"][perm])
+    X2 = X.copy()
+    X2[[0, 1, 3, 4]] = synth.normal_f16(np.random.default_rng(9), (4, X.shape[1]))
+    p2 = oracle.moe_prefill(X2, router, sgate, shared, experts, k)
+    assert np.array_equal(p2["out"][2], base["out"][2]) and list(p2["ids"][2]) == list(base["ids"][2])
