@@ -93,6 +93,7 @@ DHP_DEV void load_pair(PairRegs<CPL>& p, const u32x4* gc, const uint16_t* gs, co
 
 // silu(gate . x) * (up . x), the same value in every lane of the 16-lane group. The chunk dots
 // use the raw code form (see dot32_f16_raw) with the activations' per-chunk corrections nc.
+// k_moep_phase1 repeats these operations in this order (reading its activations from LDS).
 template <int CPL>
 DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* xs, const float* nc) {
     const NibConsts nk = nib_consts();
@@ -666,7 +667,7 @@ int max_items(int M, int E, int top_k) {
 }
 
 template <int CPL>
-__global__ __launch_bounds__(256) void k_moep_phase1(MoeArgs a) {
+__global__ __launch_bounds__(256, CPL <= 5 ? 3 : 2) void k_moep_phase1(MoeArgs a) {
     constexpr int CH32 = LPR * CPL;                   // 32-activation chunks per token
     constexpr int P1_TG = p1_tg<CPL>();
     constexpr int IT = (P1_TG * CH32 + 255) / 256;    // staged chunks per thread per pass
@@ -726,22 +727,28 @@ __global__ __launch_bounds__(256) void k_moep_phase1(MoeArgs a) {
         }
         __syncthreads();
         for (int t = 0; t < tn; ++t) {
-            h2 xp[CPL][16];
-            float xs[CPL], nc[CPL];
+            // pair_act's operations in its order, the activations read a chunk at a time
+            const NibConsts nk = nib_consts();
+            float ag = 0.0f, au = 0.0f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = j + LPR * i;
+                h2 xp[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const u32x4 u = xstage[(t * 4 + q) * CH32 + c];
-                    xp[i][4 * q] = as_h2(u.x); xp[i][4 * q + 1] = as_h2(u.y);
-                    xp[i][4 * q + 2] = as_h2(u.z); xp[i][4 * q + 3] = as_h2(u.w);
+                    xp[4 * q] = as_h2(u.x); xp[4 * q + 1] = as_h2(u.y);
+                    xp[4 * q + 2] = as_h2(u.z); xp[4 * q + 3] = as_h2(u.w);
                 }
                 const float2 sn = xsum[t * CH32 + c];
-                xs[i] = sn.x;
-                nc[i] = sn.y;
+                ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_f16_raw(p.cg[i], xp, sn.y, nk), ag);
+                ag = __builtin_fmaf(bf16_to_f32(p.bg[i]), sn.x, ag);
+                au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_f16_raw(p.cu[i], xp, sn.y, nk), au);
+                au = __builtin_fmaf(bf16_to_f32(p.bu[i]), sn.x, au);
             }
-            const float v1 = pair_act<CPL>(p, xp, xs, nc);
+            ag = group_sum<LPR>(ag);
+            au = group_sum<LPR>(au);
+            const float v1 = silu_f(ag) * au;
             const int ms = list[base + t];
             if (j == 0 && live) a.act[((size_t)(ms >> 4) * nslot + (ms & 15)) * a.inter + row] = v1;
         }
