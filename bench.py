@@ -61,12 +61,20 @@ def algorithmic_bytes():
     V = 151936
     b["lmhead1"] = int4_bytes(V, K) + 2 * K + 4 * V + 4
     b["lmhead8"] = int4_bytes(V, K) + 2 * 8 * K + 4 * 8 * V + 4 * 8
+    # entry replication, the attn and mlp reads (with inject weights) and injects, the stand-in
+    # sublayer GEMV, the MoE layer, and the final mixer's read
+    read = int4_bytes(R, C * H) + int4_bytes(C * H, R) + int4_bytes(C, C * H) + 4 * C * H + 2 * H + 4 * C
+    inject = 4 * C * H + 2 * H + 4 * C
+    mixer = int4_bytes(R, C * H) + int4_bytes(C * H, R) + 4 * C * H + 2 * H
+    layer = 2 * H + 2 * C * H + 2 * (read + inject) + b["gemv"] + b["moe"] + mixer
+    b["layer_eager"] = b["layer_graph"] = layer
     return b
 
 
 STEP_CALLS = ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8")
-# Timed per call but outside the step: a 128-token chunk through the same MoE layer.
-EXTRA_CALLS = ("moe_prefill",)
+# Timed per call but outside the step: a 128-token chunk through the same MoE layer, and one
+# token through a whole decoder layer plus the final mixer, as a launch sequence and as a graph.
+EXTRA_CALLS = ("moe_prefill", "layer_eager", "layer_graph")
 CALLS = STEP_CALLS + EXTRA_CALLS
 MOE_CHUNK = 128
 
@@ -122,6 +130,9 @@ def build_workload(torch, hca, synth, ring: int, only=None):
         W["pre_x"] = torch.from_numpy(p["x"]).to(dev)
         W["pre_y"] = torch.empty((128, 8192), dtype=torch.float16, device=dev)
 
+    if want("layer_eager", "layer_graph"):
+        _layer_workload(torch, hca, synth, W, dev)
+
     if want("lmhead1", "lmhead8"):
         l1 = synth.lmhead_workload(0, m=1)
         lw = up_int4(l1["w"])
@@ -161,6 +172,35 @@ def _moe_workload(torch, hca, synth, W, dev):
     W["moep_w"] = torch.empty((MOE_CHUNK, 8), dtype=torch.float32, device=dev)
 
 
+def _layer_workload(torch, hca, synth, W, dev):
+    d = synth.decode_layer_workload(0, n_layers=1)
+
+    def w4(t):
+        return hca.Int4Weight.from_logical(t.q, t.s_bits, t.b_bits, dev)
+
+    def block(b):
+        return hca.HcBlock(hca.bf16_bits_to_tensor(b["gamma_bits"]).to(dev), w4(b["down"]), w4(b["up"]),
+                           w4(b["inject"]) if b["inject"] is not None else None)
+
+    L = d["layers"][0]
+    m = L["moe"]
+    ex = m["experts"]
+    layer = hca.DecodeLayer(block(L["attn"]), w4(L["stub"]), block(L["mlp"]),
+                            hca.bf16_bits_to_tensor(m["router_bits"]).to(dev),
+                            hca.bf16_bits_to_tensor(m["sgate_bits"]).to(dev),
+                            hca.Int4Experts.from_logical([e["gate"] for e in ex], dev),
+                            hca.Int4Experts.from_logical([e["up"] for e in ex], dev),
+                            hca.Int4Experts.from_logical([e["down"] for e in ex], dev),
+                            w4(m["shared"]["gate"]), w4(m["shared"]["up"]), w4(m["shared"]["down"]), m["top_k"])
+    W["layer"] = dict(layers=[layer], mixer=block(d["mixer"]), C=d["C"], H=d["H"],
+                      x=torch.from_numpy(d["x"]).to(dev),
+                      hidden=torch.empty(d["C"] * d["H"], dtype=torch.float16, device=dev),
+                      mixed=torch.empty(d["H"], dtype=torch.float16, device=dev),
+                      xg=torch.from_numpy(d["x"]).to(dev),
+                      hg=torch.empty(d["C"] * d["H"], dtype=torch.float16, device=dev),
+                      mg=torch.empty(d["H"], dtype=torch.float16, device=dev))
+
+
 def prepare_calls(hca, W, ring: int, only=None):
     """calls[name][i] for ring position i (the MoE token ring has its own length)."""
     C, H = 4, 2560
@@ -178,6 +218,12 @@ def prepare_calls(hca, W, ring: int, only=None):
                                                         W["moe"]["sg"], W["moe"]["su"], W["moe"]["sd"], 8,
                                                         W["moep_out"], W["moep_ids"], W["moep_w"])],
         "prefill": lambda: [hca.prepare_gemm_batched(W["pre_w"][i], W["pre_x"], W["pre_y"]) for i in range(ring)],
+        "layer_eager": lambda: [hca.prepare_decode_layers(W["layer"]["x"], W["layer"]["C"], W["layer"]["H"],
+                                                          W["layer"]["layers"], W["layer"]["mixer"],
+                                                          W["layer"]["hidden"], W["layer"]["mixed"])],
+        "layer_graph": lambda: [hca.LayerGraph(W["layer"]["xg"], W["layer"]["C"], W["layer"]["H"],
+                                               W["layer"]["layers"], W["layer"]["mixer"], W["layer"]["hg"],
+                                               W["layer"]["mg"]).launch],
         "lmhead1": lambda: [hca.prepare_gemv(W["lm_w"][0], W["lm_x1"], W["lm_y1"], argmax=W["lm_a1"])],
         "lmhead8": lambda: [hca.prepare_gemv(W["lm_w"][1], W["lm_x8"], W["lm_y8"], argmax=W["lm_a8"])],
     }
@@ -289,6 +335,28 @@ def per_call_pass(torch, calls, nbytes, iters: int, exact: bool = False):
                      "p90_us": round(float(np.percentile(us, 90)), 2),
                      "GBps": round(nbytes[name] / med / 1e3, 1),
                      "pct_hbm_peak": round(100.0 * nbytes[name] / med / 1e3 / HBM_PEAK_GBS, 1)}
+    return out
+
+
+def single_call_latency(torch, calls, names, reps: int = 30):
+    """One call at a time onto an idle GPU: synchronize, record, call, record, synchronize; the
+    event interval then includes any time the GPU waits for the host to enqueue the next launch.
+    Median microseconds over `reps`."""
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in names:
+        seq = calls[name]
+        us = []
+        for i in range(reps + 3):
+            torch.cuda.synchronize()
+            e0, e1 = HipEvent(), HipEvent()
+            e0.record(stream)
+            run_call(seq[i % len(seq)])
+            e1.record(stream)
+            t = e0.us_until(e1)
+            if i >= 3:
+                us.append(t)
+        out[name] = round(float(np.median(us)), 2)
     return out
 
 
@@ -490,6 +558,9 @@ def main():
                 "algorithmic_bytes_per_launch": nbytes["lmhead1"], "avg_launch_us": round(dom_us, 2)}
 
     per_call = None if args.no_per_call else per_call_pass(torch, calls, nbytes, iters=100)
+    if per_call is not None:
+        for name, us in single_call_latency(torch, calls, ("layer_eager", "layer_graph")).items():
+            per_call[name]["single_call_us"] = us
     probe = copy_probe(torch) if args.copy_probe else None
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(synth)

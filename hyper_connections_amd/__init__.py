@@ -43,6 +43,20 @@ class CInt4Experts(ctypes.Structure):
                 ("count", ctypes.c_int32)]
 
 
+P4_, PE_ = ctypes.POINTER(CInt4), ctypes.POINTER(CInt4Experts)
+
+
+class CHcBlock(ctypes.Structure):
+    _fields_ = [("hc_norm", ctypes.c_void_p), ("down", P4_), ("up", P4_), ("inject", P4_)]
+
+
+class CDecodeLayer(ctypes.Structure):
+    _fields_ = [("attn_hc", CHcBlock), ("sublayer", P4_), ("mlp_hc", CHcBlock), ("router", ctypes.c_void_p),
+                ("router_dtype", ctypes.c_int32), ("shared_gate_row", ctypes.c_void_p), ("gate", PE_),
+                ("up", PE_), ("down", PE_), ("shared_gate", P4_), ("shared_up", P4_), ("shared_down", P4_),
+                ("top_k", ctypes.c_int32), ("moe_flags", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -63,6 +77,15 @@ def lib() -> ctypes.CDLL:
                                            vp, sz, vp]
         L.decodehp_moe_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.decodehp_moe_prefill_workspace_bytes.restype = sz
+        PL, PB = ctypes.POINTER(CDecodeLayer), ctypes.POINTER(CHcBlock)
+        L.decodehp_decode_layers_workspace_bytes.argtypes = [i32, i32, PL, i32, PB]
+        L.decodehp_decode_layers_workspace_bytes.restype = sz
+        L.decodehp_decode_layers.argtypes = [vp, i32, i32, ctypes.c_float, PL, i32, PB, vp, vp, vp, sz, vp]
+        L.decodehp_graph_capture_decode_layers.argtypes = [vp, i32, i32, ctypes.c_float, PL, i32, PB, vp, vp, vp,
+                                                           sz, ctypes.POINTER(vp)]
+        L.decodehp_graph_launch.argtypes = [vp, vp]
+        L.decodehp_graph_destroy.argtypes = [vp]
+        L.decodehp_graph_destroy.restype = None
         L.decodehp_hc_read.argtypes = [vp, vp, i32, i32, ctypes.c_float, P4, P4, P4, vp, vp, vp, sz, vp]
         L.decodehp_hc_inject.argtypes = [vp, vp, vp, i32, i32, vp]
         L.decodehp_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -70,7 +93,8 @@ def lib() -> ctypes.CDLL:
         L.decodehp_last_error.restype = ctypes.c_char_p
         L.decodehp_version.restype = i32
         for name in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
-                     "decodehp_moe_prefill", "decodehp_hc_read", "decodehp_hc_inject"):
+                     "decodehp_moe_prefill", "decodehp_hc_read", "decodehp_hc_inject", "decodehp_decode_layers",
+                     "decodehp_graph_capture_decode_layers", "decodehp_graph_launch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -354,6 +378,98 @@ def moe_prefill(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, 
                                     top_k, out, ids, weights, fp16_boundary, stream)
     _check(lib().decodehp_moe_prefill(*args))
     return out, ids, weights
+
+
+class HcBlock:
+    """One hyper-connection read's weights: hc_norm bf16 bits (int16 tensor) [C*H], down [R x C*H],
+    up [C*H x R], inject [C x C*H] (None for the final mixer)."""
+
+    def __init__(self, hc_norm, down: Int4Weight, up: Int4Weight, inject: Optional[Int4Weight]):
+        self.hc_norm, self.down, self.up, self.inject = hc_norm, down, up, inject
+
+    def c(self, keep: list) -> CHcBlock:
+        d = [self.down.desc(), self.up.desc(), self.inject.desc() if self.inject is not None else None]
+        keep.extend(d)
+        return CHcBlock(self.hc_norm.data_ptr(), ctypes.pointer(d[0]), ctypes.pointer(d[1]),
+                        ctypes.pointer(d[2]) if d[2] is not None else None)
+
+
+class DecodeLayer:
+    """Weights of one decoder layer: the attn and mlp hyper-connection reads, the INT4 [H x H]
+    stand-in for the attention sublayer, and the MoE (as moe_decode takes them)."""
+
+    def __init__(self, attn_hc: HcBlock, sublayer: Int4Weight, mlp_hc: HcBlock, router, shared_gate_row,
+                 gate: Int4Experts, up: Int4Experts, down: Int4Experts, shared_gate: Int4Weight,
+                 shared_up: Int4Weight, shared_down: Int4Weight, top_k: int, fp16_boundary: bool = False):
+        self.__dict__.update(locals())
+        del self.__dict__["self"]
+
+    def c(self, keep: list) -> CDecodeLayer:
+        torch = _torch()
+        e = [self.gate.desc(), self.up.desc(), self.down.desc()]
+        w = [self.sublayer.desc(), self.shared_gate.desc(), self.shared_up.desc(), self.shared_down.desc()]
+        keep.extend(e + w)
+        return CDecodeLayer(self.attn_hc.c(keep), ctypes.pointer(w[0]), self.mlp_hc.c(keep), self.router.data_ptr(),
+                            DHP_BF16 if self.router.dtype == torch.int16 else DHP_F32, self.shared_gate_row.data_ptr(),
+                            ctypes.pointer(e[0]), ctypes.pointer(e[1]), ctypes.pointer(e[2]), ctypes.pointer(w[1]),
+                            ctypes.pointer(w[2]), ctypes.pointer(w[3]), self.top_k,
+                            DHP_MOE_FP16_BOUNDARY if self.fp16_boundary else 0)
+
+
+def _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps):
+    torch = _torch()
+    _need(x, torch.float16, "x", H)
+    _need(hidden, torch.float16, "hidden", C * H)
+    _need(mixed_out, torch.float16, "mixed_out", H)
+    keep = []
+    arr = (CDecodeLayer * max(1, len(layers)))(*[L.c(keep) for L in layers])
+    mix = mixer.c(keep)
+    nbytes = int(lib().decodehp_decode_layers_workspace_bytes(C, H, arr, len(layers), ctypes.byref(mix)))
+    if nbytes == 0:
+        raise DecodeHPError(-1, "null or inconsistent layer descriptors")
+    ws = _workspace(nbytes, x.device, "layers")
+    keep.extend([arr, mix, ws, layers, mixer, x, hidden, mixed_out])
+    return (x.data_ptr(), C, H, eps, arr, len(layers), ctypes.byref(mix), hidden.data_ptr(), mixed_out.data_ptr(),
+            ws.data_ptr(), ws.numel()), keep
+
+
+def decode_layers(x, C: int, H: int, layers, mixer: HcBlock, hidden=None, mixed_out=None, eps=1e-6, stream=None):
+    """One token (x fp16 [H]) through the layers and the final mixer, as a launch sequence.
+    Returns (hidden fp16 [C*H] after the last layer, mixed fp16 [H] from the mixer)."""
+    torch = _torch()
+    hidden = torch.empty(C * H, dtype=torch.float16, device=x.device) if hidden is None else hidden
+    mixed_out = torch.empty(H, dtype=torch.float16, device=x.device) if mixed_out is None else mixed_out
+    args, _keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps)
+    _check(lib().decodehp_decode_layers(*args, _stream(stream)))
+    return hidden, mixed_out
+
+
+def prepare_decode_layers(x, C: int, H: int, layers, mixer: HcBlock, hidden, mixed_out, eps=1e-6,
+                          stream=None) -> PreparedCall:
+    args, keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps)
+    return PreparedCall(lib().decodehp_decode_layers, (*args, _stream(stream)), keep)
+
+
+class LayerGraph:
+    """The decode_layers sequence captured once as a HIP graph over fixed buffers (x, hidden,
+    mixed_out and a workspace). Capture runs the sequence once. launch() replays it on a stream;
+    write the next token into x first."""
+
+    def __init__(self, x, C: int, H: int, layers, mixer: HcBlock, hidden, mixed_out, eps=1e-6):
+        args, self._keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps)
+        self._g = ctypes.c_void_p()
+        _check(lib().decodehp_graph_capture_decode_layers(*args, ctypes.byref(self._g)))
+        self.x, self.hidden, self.mixed = x, hidden, mixed_out
+
+    def launch(self, stream=None):
+        rc = lib().decodehp_graph_launch(self._g, _stream(stream))
+        if rc != 0:
+            _check(rc)
+
+    def __del__(self):
+        if getattr(self, "_g", None) and self._g.value and _lib is not None:
+            _lib.decodehp_graph_destroy(self._g)
+            self._g = ctypes.c_void_p()
 
 
 class PreparedCall:

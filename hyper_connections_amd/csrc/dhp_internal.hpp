@@ -261,7 +261,6 @@ struct DeviceFacts {
 // when there is no usable gfx950 device.
 bool dhp_current_device(DeviceFacts* out);
 int dhp_fail(int code, const char* fmt, ...);
-int dhp_launch_status(const char* what);
 
 // Launchers (validation already done by abi.hip).
 int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t* argmax,

@@ -211,6 +211,77 @@ int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H,
 int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32_t C, int32_t H,
                        void* stream);
 
+/*
+ * Whole decoder layers for one token, and their capture as one HIP graph.
+ * "src/families/qwen4/mod.rs", module doc, "The decoder layer, as pseudocode": the token's
+ * hidden vector is replicated over the C streams at entry; each layer runs
+ *     attn_hc read -> sublayer -> inject -> mlp_hc read -> moe -> inject
+ * with the inject adding the sublayer output, scaled per stream, to the un-normalized residual;
+ * at exit the hyper_connection_mixer (a read with no inject projection) gives the H-wide output.
+ * The attention sublayer is not part of this library: `sublayer` is an INT4 [H x H] linear map
+ * standing in for it (out = sublayer . mixed). The graph form is the counterpart of the pages'
+ * one command buffer per token: the whole sequence replays with one launch.
+ */
+typedef struct dhp_hc_block {
+    const void* hc_norm;     /* bf16 [C*H], 16-byte aligned */
+    const dhp_int4* down;    /* [R x C*H] */
+    const dhp_int4* up;      /* [C*H x R] */
+    const dhp_int4* inject;  /* [C x C*H]; NULL exactly for the final mixer */
+} dhp_hc_block;
+
+typedef struct dhp_decode_layer {
+    dhp_hc_block attn_hc;
+    const dhp_int4* sublayer;               /* [H x H], the attention stand-in */
+    dhp_hc_block mlp_hc;
+    const void* router;                     /* as decodehp_moe_decode */
+    int32_t router_dtype;
+    const void* shared_gate_row;
+    const dhp_int4_experts* gate;
+    const dhp_int4_experts* up;
+    const dhp_int4_experts* down;
+    const dhp_int4* shared_gate;
+    const dhp_int4* shared_up;
+    const dhp_int4* shared_down;
+    int32_t top_k;
+    int32_t moe_flags;
+} dhp_decode_layer;
+
+/* Workspace bytes decodehp_decode_layers needs (0 for invalid arguments). */
+size_t decodehp_decode_layers_workspace_bytes(int32_t C, int32_t H, const dhp_decode_layer* layers,
+                                              int32_t n_layers, const dhp_hc_block* mixer);
+
+/*
+ * decodehp_decode_layers -- one token through n_layers layers and the final mixer, on `stream`.
+ *   x         : fp16 [H], 16-byte aligned (read once, at entry).
+ *   layers    : n_layers >= 0 descriptors (read during the call only).
+ *   mixer     : the final mixer (inject must be NULL).
+ *   hidden    : fp16 [C*H], 16-byte aligned: the residual, replicated from x, then updated in
+ *               place by every inject; holds the residual after the last layer on return.
+ *   mixed_out : fp16 [H], the mixer's output.
+ *   ws        : decodehp_decode_layers_workspace_bytes(...) bytes, 16-byte aligned.
+ * Each step is the entry point of its own (decodehp_hc_read, decodehp_dequant_gemv,
+ * decodehp_hc_inject, decodehp_moe_decode) with its checks and errors; on an error the
+ * sequence stops there and hidden and mixed_out are unspecified.
+ */
+int decodehp_decode_layers(const void* x, int32_t C, int32_t H, float eps, const dhp_decode_layer* layers,
+                           int32_t n_layers, const dhp_hc_block* mixer, void* hidden, void* mixed_out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * A captured decodehp_decode_layers sequence. Capture runs the sequence once on a private
+ * stream (it writes hidden and mixed_out), then records it; every launch replays it on the
+ * given stream with the same buffers (write the next token into x before a launch). The
+ * descriptors may be freed after capture; the weights and buffers must outlive the graph.
+ * Errors: those of decodehp_decode_layers, and -6 when capture or instantiation fails.
+ */
+typedef struct dhp_graph dhp_graph;
+int decodehp_graph_capture_decode_layers(const void* x, int32_t C, int32_t H, float eps,
+                                         const dhp_decode_layer* layers, int32_t n_layers,
+                                         const dhp_hc_block* mixer, void* hidden, void* mixed_out,
+                                         void* ws, size_t ws_bytes, dhp_graph** graph);
+int decodehp_graph_launch(const dhp_graph* graph, void* stream);
+void decodehp_graph_destroy(dhp_graph* graph);
+
 /* Workspace bytes an entry point needs (0 when none). Pure host arithmetic. */
 size_t decodehp_workspace_bytes(int32_t op, int32_t a, int32_t b, int32_t c);
 

@@ -13,6 +13,8 @@ Sources (the turbospark-runtime 0.3.0 docs.rs pages):
     GEMV, 1/C, sigmoid, x2).
   * "src/families/qwen/state.rs" -- struct RealQwenState fields router_ones,
     per_expert_ones, router_logits_f32, moe_x, h1, h2, shared_gate_logit.
+  * "src/families/qwen4/mod.rs", module doc, "The decoder layer, as pseudocode" -- the
+    whole-layer composition (oracle/layer.py).
   * "src/real_forward.rs" -- module doc (INT4-affine resident weights bound as
     weights/scales/biases; MoE phase-1 gate/up + activation and phase-2 down + k-way
     reduce; host top-k + softmax) and field batched_gemv_prefill.
@@ -30,3 +32,4 @@ from .gemv import dequant_gemv, argmax_lowest                      # noqa: F401
 from .moe import (router_logits, select_topk, softmax_selected,   # noqa: F401
                   expert_act, expert_down, moe_decode, moe_prefill)
 from .hc import grouped_rmsnorm, hc_read, hc_inject                # noqa: F401
+from .layer import decode_layers                                    # noqa: F401

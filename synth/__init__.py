@@ -33,6 +33,7 @@ GEMV_2560 = 0
 HC_C4_H2560 = 1
 MOE_E256 = 2
 PREFILL_M128 = 3
+DECODE_LAYERS = 5
 LMHEAD_151936 = 4
 
 
@@ -183,3 +184,38 @@ def lmhead_workload(seed: int = 0, m: int = 1, n: int = 151936, k: int = 2560):
     rng = rng_for(LMHEAD_151936, seed)
     w = int4_tensor(rng, n, k)
     return {"x": lmhead_x(seed, m, k), "w": w}
+
+
+def hc_block(rng: np.random.Generator, c: int, h: int, r: int, inject: bool = True) -> dict:
+    """One hyper-connection read's weights: hc_norm bf16 ~N(1, 0.02) [C*H], down INT4 [R x C*H],
+    up INT4 [C*H x R], inject INT4 [C x C*H] (absent for the final mixer)."""
+    wide = c * h
+    return {"gamma_bits": normal_bf16_bits(rng, (wide,), mean=1.0, std=0.02), "down": int4_tensor(rng, r, wide),
+            "up": int4_tensor(rng, wide, r), "inject": int4_tensor(rng, c, wide) if inject else None}
+
+
+def decode_layer_workload(seed: int = 0, n_layers: int = 1, c: int = 4, h: int = 2560, r: int = 320,
+                          n_experts: int = 256, inter: int = 512, top_k: int = 8):
+    """Whole decoder layers for one token: x fp16 [H]; per layer the attn and mlp hyper-connection
+    weights, an INT4 [H x H] stand-in for the attention sublayer and an MoE layer of the MoE
+    workload's distributions (router bf16 N(0, 0.02), experts INT4 from their own streams); the
+    final mixer's read weights."""
+    rng = rng_for(DECODE_LAYERS, seed)
+    x = normal_f16(rng, (h,))
+    layers = []
+    for li in range(n_layers):
+        lr = rng_for(DECODE_LAYERS, seed, 1 + li)
+        attn, stub, mlp = hc_block(lr, c, h, r), int4_tensor(lr, h, h), hc_block(lr, c, h, r)
+        moe = {"router_bits": normal_bf16_bits(lr, (n_experts, h), std=0.02),
+               "sgate_bits": normal_bf16_bits(lr, (h,), std=0.02),
+               "shared": {"gate": int4_tensor(lr, inter, h), "up": int4_tensor(lr, inter, h),
+                          "down": int4_tensor(lr, h, inter)},
+               "experts": [], "top_k": top_k}
+        for e in range(n_experts):
+            er = rng_for(DECODE_LAYERS, seed, 1 + li, 1 + e)
+            moe["experts"].append({"gate": int4_tensor(er, inter, h), "up": int4_tensor(er, inter, h),
+                                   "down": int4_tensor(er, h, inter)})
+        layers.append({"attn": attn, "stub": stub, "mlp": mlp, "moe": moe})
+    mixer = hc_block(rng, c, h, r, inject=False)
+    return {"x": x, "layers": layers, "mixer": mixer, "C": c, "H": h, "R": r}
+

@@ -199,3 +199,32 @@ def test_hc_inject_rejects_bad_calls():
     assert f(C=17) == -2
     assert f(H=12) == -2
     assert f(out=FAKE + 2) == -3
+
+
+def _layer_descs(E=8, C=4, H=512, R=64, inter=64, mixer_inject=False):
+    hb = lambda inj: hca.CHcBlock(FAKE, ctypes.pointer(int4(rows=R, cols=C * H)), ctypes.pointer(int4(rows=C * H, cols=R)),
+                                  ctypes.pointer(int4(rows=C, cols=C * H)) if inj else None)
+    L = hca.CDecodeLayer(hb(True), ctypes.pointer(int4(rows=H, cols=H)), hb(True), FAKE, 2, FAKE,
+                         ctypes.pointer(experts(E, inter, H)), ctypes.pointer(experts(E, inter, H)),
+                         ctypes.pointer(experts(E, H, inter)), ctypes.pointer(int4(rows=inter, cols=H)),
+                         ctypes.pointer(int4(rows=inter, cols=H)), ctypes.pointer(int4(rows=H, cols=inter)), 2, 0)
+    return (hca.CDecodeLayer * 1)(L), hb(mixer_inject)
+
+
+def test_decode_layers_rejects_bad_calls():
+    L = hca.lib()
+    layers, mixer = _layer_descs()
+    need = L.decodehp_decode_layers_workspace_bytes(4, 512, layers, 1, ctypes.byref(mixer))
+    assert need >= 2 * 512 * 2 + 4 * 4
+    _, bad_mixer = _layer_descs(mixer_inject=True)                 # the final mixer has no inject
+    assert L.decodehp_decode_layers_workspace_bytes(4, 512, layers, 1, ctypes.byref(bad_mixer)) == 0
+    assert L.decodehp_decode_layers(None, 4, 512, 1e-6, layers, 1, ctypes.byref(mixer), FAKE, FAKE, FAKE, need,
+                                    None) == -1
+    assert L.decodehp_decode_layers(FAKE, 4, 512, 1e-6, layers, 1, ctypes.byref(mixer), FAKE, FAKE, FAKE, need - 1,
+                                    None) == -4
+    assert L.decodehp_decode_layers(FAKE + 8, 4, 512, 1e-6, layers, 1, ctypes.byref(mixer), FAKE, FAKE, FAKE, need,
+                                    None) == -3
+    assert L.decodehp_graph_capture_decode_layers(FAKE, 4, 512, 1e-6, layers, 1, ctypes.byref(mixer), FAKE, FAKE,
+                                                  FAKE, need, None) == -1
+    assert L.decodehp_graph_launch(None, None) == -1
+    L.decodehp_graph_destroy(None)
