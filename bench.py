@@ -68,13 +68,17 @@ def algorithmic_bytes():
     mixer = int4_bytes(R, C * H) + int4_bytes(C * H, R) + 4 * C * H + 2 * H
     layer = 2 * H + 2 * C * H + 2 * (read + inject) + b["gemv"] + b["moe"] + mixer
     b["layer_eager"] = b["layer_graph"] = layer
+    # a 128-token chunk's read (weights once; raw, hc_norm, mixed, gates) and inject
+    m = MOE_CHUNK
+    b["hc_chunk"] = (int4_bytes(R, C * H) + int4_bytes(C * H, R) + int4_bytes(C, C * H) + 2 * C * H
+                     + m * (2 * C * H + 2 * H + 4 * C) + m * (4 * C * H + 2 * H + 4 * C))
     return b
 
 
 STEP_CALLS = ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8")
 # Timed per call but outside the step: a 128-token chunk through the same MoE layer, and one
 # token through a whole decoder layer plus the final mixer, as a launch sequence and as a graph.
-EXTRA_CALLS = ("moe_prefill", "layer_eager", "layer_graph")
+EXTRA_CALLS = ("moe_prefill", "hc_chunk", "layer_eager", "layer_graph")
 CALLS = STEP_CALLS + EXTRA_CALLS
 MOE_CHUNK = 128
 
@@ -132,6 +136,18 @@ def build_workload(torch, hca, synth, ring: int, only=None):
 
     if want("layer_eager", "layer_graph"):
         _layer_workload(torch, hca, synth, W, dev)
+
+    if want("hc_chunk"):
+        h = synth.hc_workload(0)
+        rows = np.concatenate([h["raw"][None], synth.normal_f16(np.random.default_rng([64, 0]),
+                                                                  (MOE_CHUNK - 1, 4 * 2560))])
+        W["hcc"] = dict(w=(up_int4(h["down"]), up_int4(h["up"]), up_int4(h["inject"])),
+                        gamma=hca.bf16_bits_to_tensor(h["gamma_bits"]).to(dev),
+                        raw=torch.from_numpy(rows).to(dev),
+                        out=torch.from_numpy(synth.normal_f16(np.random.default_rng([64, 1]),
+                                                              (MOE_CHUNK, 2560))).to(dev),
+                        mixed=torch.empty((MOE_CHUNK, 2560), dtype=torch.float16, device=dev),
+                        iw=torch.empty((MOE_CHUNK, 4), dtype=torch.float32, device=dev))
 
     if want("lmhead1", "lmhead8"):
         l1 = synth.lmhead_workload(0, m=1)
@@ -218,6 +234,9 @@ def prepare_calls(hca, W, ring: int, only=None):
                                                         W["moe"]["sg"], W["moe"]["su"], W["moe"]["sd"], 8,
                                                         W["moep_out"], W["moep_ids"], W["moep_w"])],
         "prefill": lambda: [hca.prepare_gemm_batched(W["pre_w"][i], W["pre_x"], W["pre_y"]) for i in range(ring)],
+        "hc_chunk": lambda: [(hca.prepare_hc_read_batched(W["hcc"]["raw"], W["hcc"]["gamma"], C, H, *W["hcc"]["w"],
+                                                          W["hcc"]["mixed"], W["hcc"]["iw"]),
+                              hca.prepare_hc_inject_batched(W["hcc"]["raw"], W["hcc"]["out"], W["hcc"]["iw"], C, H))],
         "layer_eager": lambda: [hca.prepare_decode_layers(W["layer"]["x"], W["layer"]["C"], W["layer"]["H"],
                                                           W["layer"]["layers"], W["layer"]["mixer"],
                                                           W["layer"]["hidden"], W["layer"]["mixed"])],

@@ -87,6 +87,11 @@ def lib() -> ctypes.CDLL:
         L.decodehp_graph_destroy.argtypes = [vp]
         L.decodehp_graph_destroy.restype = None
         L.decodehp_hc_read.argtypes = [vp, vp, i32, i32, ctypes.c_float, P4, P4, P4, vp, vp, vp, sz, vp]
+        L.decodehp_hc_read_batched.argtypes = [vp, i32, vp, i32, i32, ctypes.c_float, P4, P4, P4, vp, vp, vp, sz,
+                                               vp]
+        L.decodehp_hc_read_batched_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.decodehp_hc_read_batched_workspace_bytes.restype = sz
+        L.decodehp_hc_inject_batched.argtypes = [vp, i32, vp, vp, i32, i32, vp]
         L.decodehp_hc_inject.argtypes = [vp, vp, vp, i32, i32, vp]
         L.decodehp_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.decodehp_workspace_bytes.restype = sz
@@ -94,6 +99,7 @@ def lib() -> ctypes.CDLL:
         L.decodehp_version.restype = i32
         for name in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
                      "decodehp_moe_prefill", "decodehp_hc_read", "decodehp_hc_inject", "decodehp_decode_layers",
+                     "decodehp_hc_read_batched", "decodehp_hc_inject_batched",
                      "decodehp_graph_capture_decode_layers", "decodehp_graph_launch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -378,6 +384,59 @@ def moe_prefill(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, 
                                     top_k, out, ids, weights, fp16_boundary, stream)
     _check(lib().decodehp_moe_prefill(*args))
     return out, ids, weights
+
+
+def _hcb_args(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps, stream):
+    torch = _torch()
+    m = raw.shape[0]
+    _need(raw, torch.float16, "raw", m * C * H)
+    _need(hc_norm, torch.int16, "hc_norm", C * H)
+    _need(mixed, torch.float16, "mixed", m * H)
+    if inject_w is not None:
+        _need(inject_w, torch.float32, "inject_w", m * C)
+    ws = _workspace(int(lib().decodehp_hc_read_batched_workspace_bytes(m, C, H, down.rows)), raw.device, "hc_batched")
+    descs = (down.desc(), up.desc(), inject.desc() if inject is not None else None)
+    args = (raw.data_ptr(), m, hc_norm.data_ptr(), C, H, eps, ctypes.byref(descs[0]), ctypes.byref(descs[1]),
+            ctypes.byref(descs[2]) if descs[2] is not None else None, mixed.data_ptr(), _ptr(inject_w), _ptr(ws),
+            0 if ws is None else ws.numel(), _stream(stream))
+    return args, (descs, raw, hc_norm, mixed, inject_w, ws, down, up, inject)
+
+
+def hc_read_batched(raw, hc_norm, C: int, H: int, down: Int4Weight, up: Int4Weight, inject: Optional[Int4Weight],
+                    eps: float = 1e-6, mixed=None, inject_w=None, stream=None):
+    """The read for the m tokens of a chunk: raw fp16 [m, C*H]. Returns (mixed fp16 [m, H],
+    inject_w fp32 [m, C] or None)."""
+    torch = _torch()
+    m, dev = raw.shape[0], raw.device
+    mixed = torch.empty((m, H), dtype=torch.float16, device=dev) if mixed is None else mixed
+    if inject is not None and inject_w is None:
+        inject_w = torch.empty((m, C), dtype=torch.float32, device=dev)
+    args, _keep = _hcb_args(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps, stream)
+    _check(lib().decodehp_hc_read_batched(*args))
+    return mixed, (inject_w if inject is not None else None)
+
+
+def prepare_hc_read_batched(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps=1e-6,
+                            stream=None) -> "PreparedCall":
+    args, keep = _hcb_args(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps, stream)
+    return PreparedCall(lib().decodehp_hc_read_batched, args, keep)
+
+
+def hc_inject_batched(wide, out, inject_w, C: int, H: int, stream=None):
+    """wide[t, c*H + h] += out[t, h] * inject_w[t, c] in place for the m rows; returns wide."""
+    torch = _torch()
+    m = wide.shape[0]
+    _need(wide, torch.float16, "wide", m * C * H)
+    _need(out, torch.float16, "out", m * H)
+    _need(inject_w, torch.float32, "inject_w", m * C)
+    _check(lib().decodehp_hc_inject_batched(wide.data_ptr(), m, out.data_ptr(), inject_w.data_ptr(), C, H,
+                                            _stream(stream)))
+    return wide
+
+
+def prepare_hc_inject_batched(wide, out, inject_w, C, H, stream=None) -> "PreparedCall":
+    args = (wide.data_ptr(), wide.shape[0], out.data_ptr(), inject_w.data_ptr(), C, H, _stream(stream))
+    return PreparedCall(lib().decodehp_hc_inject_batched, args, (wide, out, inject_w))
 
 
 class HcBlock:

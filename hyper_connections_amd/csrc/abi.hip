@@ -246,10 +246,12 @@ int decodehp_moe_prefill(const void* x, int32_t m, const void* router, int32_t r
                               weights, ws, static_cast<hipStream_t>(stream));
 }
 
-int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H, float eps,
-                     const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject,
-                     void* mixed, float* inject_w, void* ws, size_t ws_bytes, void* stream) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+// Checks shared by the single-token and batched hyper-connection reads.
+int check_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H, float eps, const dhp_int4* down,
+                  const dhp_int4* up, const dhp_int4* inject, const void* mixed, const float* inject_w) {
     if (!raw || !hc_norm || !mixed) return dhp_fail(DHP_ERR_INVALID, "null raw, hc_norm or mixed");
     if (C <= 0 || H <= 0) return dhp_fail(DHP_ERR_INVALID, "C=%d H=%d", C, H);
     if (C > DHP_HC_MAX_C || (C & (C - 1)))
@@ -280,7 +282,29 @@ int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H,
     }
     if (!aligned(raw, 16) || !aligned(hc_norm, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "raw/hc_norm not 16-byte aligned");
     if (!aligned(mixed, 2)) return dhp_fail(DHP_ERR_MISALIGNED, "mixed misaligned");
-    const size_t need = dhp_hc_ws(C, R);
+    return DHP_OK;
+}
+
+int check_hc_inject(const void* wide, const void* out, const float* inject_w, int32_t C, int32_t H) {
+    if (!wide || !out || !inject_w) return dhp_fail(DHP_ERR_INVALID, "null wide, out or inject_w");
+    if (C <= 0 || H <= 0) return dhp_fail(DHP_ERR_INVALID, "C=%d H=%d", C, H);
+    if (C > DHP_HC_MAX_C) return dhp_fail(DHP_ERR_UNSUPPORTED, "C=%d above %d", C, DHP_HC_MAX_C);
+    if (H % 8) return dhp_fail(DHP_ERR_UNSUPPORTED, "H=%d not a multiple of 8", H);
+    if (!aligned(wide, 16) || !aligned(out, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "wide/out not 16-byte aligned");
+    if (!aligned(inject_w, 4)) return dhp_fail(DHP_ERR_MISALIGNED, "inject_w misaligned");
+    return DHP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H, float eps,
+                     const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject,
+                     void* mixed, float* inject_w, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    const int rc = check_hc_read(raw, hc_norm, C, H, eps, down, up, inject, mixed, inject_w);
+    if (rc) return rc;
+    const size_t need = dhp_hc_ws(C, down->rows);
     if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
     DeviceFacts dev;
@@ -292,15 +316,44 @@ int decodehp_hc_read(const void* raw, const void* hc_norm, int32_t C, int32_t H,
 int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32_t C, int32_t H,
                        void* stream) {
     g_err[0] = 0;
-    if (!wide || !out || !inject_w) return dhp_fail(DHP_ERR_INVALID, "null wide, out or inject_w");
-    if (C <= 0 || H <= 0) return dhp_fail(DHP_ERR_INVALID, "C=%d H=%d", C, H);
-    if (C > DHP_HC_MAX_C) return dhp_fail(DHP_ERR_UNSUPPORTED, "C=%d above %d", C, DHP_HC_MAX_C);
-    if (H % 8) return dhp_fail(DHP_ERR_UNSUPPORTED, "H=%d not a multiple of 8", H);
-    if (!aligned(wide, 16) || !aligned(out, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "wide/out not 16-byte aligned");
-    if (!aligned(inject_w, 4)) return dhp_fail(DHP_ERR_MISALIGNED, "inject_w misaligned");
+    const int rc = check_hc_inject(wide, out, inject_w, C, H);
+    if (rc) return rc;
     DeviceFacts dev;
     if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
     return launch_hc_inject(wide, out, inject_w, C, H, static_cast<hipStream_t>(stream));
+}
+
+size_t decodehp_hc_read_batched_workspace_bytes(int32_t m, int32_t C, int32_t H, int32_t R) {
+    if (m < 1 || m > DHP_GEMM_MAX_M || C < 1 || C > DHP_HC_MAX_C || H < 1 || R < 1 || R > 1024) return 0;
+    return dhp_hc_read_batched_ws(m, C, H, R);
+}
+
+int decodehp_hc_read_batched(const void* raw, int32_t m, const void* hc_norm, int32_t C, int32_t H, float eps,
+                             const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject, void* mixed,
+                             float* inject_w, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (m < 1 || m > DHP_GEMM_MAX_M) return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d (1..%d)", m, DHP_GEMM_MAX_M);
+    const int rc = check_hc_read(raw, hc_norm, C, H, eps, down, up, inject, mixed, inject_w);
+    if (rc) return rc;
+    if (!aligned(mixed, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "mixed not 16-byte aligned");
+    const size_t need = dhp_hc_read_batched_ws(m, C, H, down->rows);
+    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_hc_read_batched(raw, m, hc_norm, C, H, eps, down, up, inject, mixed, inject_w, ws,
+                                  static_cast<hipStream_t>(stream));
+}
+
+int decodehp_hc_inject_batched(void* wide, int32_t m, const void* out, const float* inject_w, int32_t C,
+                               int32_t H, void* stream) {
+    g_err[0] = 0;
+    if (m < 1 || m > DHP_GEMM_MAX_M) return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d (1..%d)", m, DHP_GEMM_MAX_M);
+    const int rc = check_hc_inject(wide, out, inject_w, C, H);
+    if (rc) return rc;
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_hc_inject_batched(wide, m, out, inject_w, C, H, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -278,7 +278,13 @@ int launch_moe_prefill(const void* x, int m, const void* router, int router_f32,
                        const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
                        void* out, int32_t* ids, float* weights, void* ws, hipStream_t s);
 size_t dhp_moe_prefill_ws(int32_t m, int32_t n_experts, int32_t top_k, int32_t inter, int32_t hidden);
+size_t dhp_hc_read_batched_ws(int32_t m, int32_t C, int32_t H, int32_t R);
+int launch_hc_read_batched(const void* raw, int m, const void* gamma, int C, int H, float eps, const dhp_int4* down,
+                           const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w, void* ws,
+                           hipStream_t s);
+int launch_hc_inject_batched(void* wide, int m, const void* out, const float* w, int C, int H, hipStream_t s);
 size_t dhp_argmax_part_stride(int32_t n_rows, int32_t m);
+int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_partials, int splits, hipStream_t s);
 int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax,
                      void* ws, size_t ws_part_stride, hipStream_t s);
 hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s);

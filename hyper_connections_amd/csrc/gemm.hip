@@ -206,7 +206,7 @@ template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ X, int M, int N, int K,
-    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i) {
+    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i, int kb_split) {
     using L = WaveLds<MT, S>;
     constexpr int ROWS = 32 * MT;
     extern __shared__ __align__(16) uint8_t lds_all[];   // one region per wave; reused by the epilogue
@@ -228,10 +228,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f16x16{};
 
-    // stage-aligned split of K over the waves
-    const int ST = (KB + S - 1) / S;
-    const int st0 = (ST * wave) / WAVES, st1 = (ST * (wave + 1)) / WAVES;
-    const int kb1 = min(st1 * S, KB);
+    // the block's share of K (blockIdx.z of a split-K launch: k-blocks [zb0, zb1), a multiple of
+    // S apart; the whole of K otherwise), then a stage-aligned split of it over the waves
+    const int zb0 = blockIdx.z * kb_split, zb1 = min(KB, zb0 + kb_split);
+    const int ST = (zb1 - zb0 + S - 1) / S;
+    const int st0 = zb0 / S + (ST * wave) / WAVES, st1 = zb0 / S + (ST * (wave + 1)) / WAVES;
+    const int kb1 = min(st1 * S, zb1);
+    if constexpr (F32OUT) Y = reinterpret_cast<float*>(Y) + (size_t)blockIdx.z * M * N;   // the split's partial
     const bool has = st0 < st1;
     StagePlan<MT, S> plan;
     StageRegs<MT, S> r0, r1;
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
 
 template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX>
 hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t* sc, const uint16_t* bi,
-                      const _Float16* xh, int M, int N, int K, void* y, float* pv, int* pi) {
+                      const _Float16* xh, int M, int N, int K, void* y, float* pv, int* pi, int kb_split) {
     using L = WaveLds<MT, S>;
     constexpr size_t red = (size_t)WAVES * 32 * MT * LDW * 4;    // one partial tile per wave
     constexpr size_t lds = (WAVES * L::BYTES > red) ? WAVES * L::BYTES : red;
@@ -366,22 +369,22 @@ hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t
         __atomic_fetch_or(&configured, bit, __ATOMIC_RELEASE);
     }
     hipLaunchKernelGGL((k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX>), grid, dim3(64 * WAVES), lds, s, c, sc, bi, xh, M,
-                       N, K, y, pv, pi);
+                       N, K, y, pv, pi, kb_split);
     return hipGetLastError();
 }
 
 template <int MT, int S, int WAVES>
 hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4* w, const void* x,
-                     int M, void* y, float* pv, int* pi) {
+                     int M, void* y, float* pv, int* pi, int kb_split) {
     const auto* c = static_cast<const uint8_t*>(w->codes);
     const auto* sc = static_cast<const uint16_t*>(w->scales);
     const auto* bi = static_cast<const uint16_t*>(w->biases);
     const auto* xh = static_cast<const _Float16*>(x);
     const int N = w->rows, K = w->cols;
-    if (f32 && am) return launch_one<MT, S, WAVES, true, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    if (am) return launch_one<MT, S, WAVES, false, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    if (f32) return launch_one<MT, S, WAVES, true, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
-    return launch_one<MT, S, WAVES, false, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi);
+    if (f32 && am) return launch_one<MT, S, WAVES, true, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
+    if (am) return launch_one<MT, S, WAVES, false, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
+    if (f32) return launch_one<MT, S, WAVES, true, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
+    return launch_one<MT, S, WAVES, false, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
 }
 
 }  // namespace
@@ -400,8 +403,9 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     if (argmax && grid.y != 1) return dhp_fail(DHP_ERR_UNSUPPORTED, "argmax with m=%d", M);
     // eight waves of 64-k stages (two per SIMD) with two stages in flight per wave
     const bool am = argmax != nullptr;
-    const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi)
-                                   : launch_mt<2, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi);
+    const int KB = w->cols / 64;
+    const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB)
+                                   : launch_mt<2, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
     if (argmax) {
         const hipError_t e2 = launch_argmax_final(pv, pi, (int)grid.x, M, argmax, s);
@@ -409,3 +413,20 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     }
     return DHP_OK;
 }
+
+// Split-K form for long, narrow contractions (few output columns, many k): `splits` blocks share
+// the K of every output tile, each writing its fp32 partial to y + split * M * N; the caller sums
+// the `splits` partials in split order. The K / 64 k-blocks must divide evenly into the splits.
+int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_partials, int splits, hipStream_t s) {
+    const int N = w->rows, KB = w->cols / 64;
+    if (splits < 1 || KB % splits) return dhp_fail(DHP_ERR_UNSUPPORTED, "%d k-blocks in %d splits", KB, splits);
+    const int MT = (M <= 32) ? 1 : 2;
+    const int rows = 32 * MT;
+    const int kb_split = KB / splits;
+    const dim3 grid((unsigned)dhp_gemm_blocks_n(N), (unsigned)((M + rows - 1) / rows), (unsigned)splits);
+    const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split)
+                                   : launch_mt<2, 1, 8>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split);
+    if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "split-K gemm launch: %s", hipGetErrorString(e));
+    return DHP_OK;
+}
+

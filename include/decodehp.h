@@ -212,6 +212,26 @@ int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32
                        void* stream);
 
 /*
+ * decodehp_hc_read_batched / decodehp_hc_inject_batched -- the read and the inject for the m
+ * tokens of a chunked-prefill micro-batch ("src/families/qwen4/hc.rs", encode_hyper_connection:
+ * inside a micro-batch every token's inject gate has a row of its own). Row t of each output is
+ * the per-token call's on row t of the inputs, within the tolerance (the low-rank projections
+ * run as matrix-core GEMMs over the m rows, with normed and lo rounded to fp16 as their
+ * operands).
+ *   raw, wide : fp16 [m][C*H], 16-byte aligned.   mixed, out : fp16 [m][H], 16-byte aligned.
+ *   inject_w  : fp32 [m][C] (NULL exactly when inject is NULL).   m : 1..DHP_GEMM_MAX_M.
+ *   C, H, eps, hc_norm, down, up, inject : as decodehp_hc_read.
+ *   ws        : decodehp_hc_read_batched_workspace_bytes(m, C, H, R) bytes, 16-byte aligned.
+ * Errors: as decodehp_hc_read / decodehp_hc_inject, and -2 for m outside 1..128.
+ */
+size_t decodehp_hc_read_batched_workspace_bytes(int32_t m, int32_t C, int32_t H, int32_t R);
+int decodehp_hc_read_batched(const void* raw, int32_t m, const void* hc_norm, int32_t C, int32_t H, float eps,
+                             const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject, void* mixed,
+                             float* inject_w, void* ws, size_t ws_bytes, void* stream);
+int decodehp_hc_inject_batched(void* wide, int32_t m, const void* out, const float* inject_w, int32_t C,
+                               int32_t H, void* stream);
+
+/*
  * Whole decoder layers for one token, and their capture as one HIP graph.
  * "src/families/qwen4/mod.rs", module doc, "The decoder layer, as pseudocode": the token's
  * hidden vector is replicated over the C streams at entry; each layer runs

@@ -31,5 +31,5 @@ from .int4 import bf16_bits_to_f64, dequant                        # noqa: F401
 from .gemv import dequant_gemv, argmax_lowest                      # noqa: F401
 from .moe import (router_logits, select_topk, softmax_selected,   # noqa: F401
                   expert_act, expert_down, moe_decode, moe_prefill)
-from .hc import grouped_rmsnorm, hc_read, hc_inject                # noqa: F401
+from .hc import grouped_rmsnorm, hc_read, hc_inject, hc_read_batched, hc_inject_batched  # noqa: F401
 from .layer import decode_layers                                    # noqa: F401

@@ -74,3 +74,18 @@ def hc_inject(raw, out, inject_w, C: int, H: int) -> np.ndarray:
     o = np.asarray(out, dtype=np.float64).reshape(1, H)
     w = np.asarray(inject_w, dtype=np.float64).reshape(C, 1)
     return (r + o * w).reshape(C * H)
+
+
+def hc_read_batched(raw_rows, gamma_bits, down, up, inject, C: int, H: int, eps: float = RMS_EPS):
+    """The read for the m tokens of a chunked-prefill micro-batch: "src/families/qwen4/hc.rs",
+    encode_hyper_connection, run once per token (each token's inject gate in its own row). So
+    the definition is hc_read on each row. Returns dict(mixed [m, H], inject_w [m, C] or None)."""
+    rows = [hc_read(r, gamma_bits, down, up, inject, C, H, eps) for r in np.asarray(raw_rows)]
+    iw = None if inject is None else np.stack([r["inject_w"] for r in rows])
+    return {"mixed": np.stack([r["mixed"] for r in rows]), "inject_w": iw}
+
+
+def hc_inject_batched(raw_rows, out_rows, inject_w_rows, C: int, H: int) -> np.ndarray:
+    """hc_inject on each row of a chunk, each with its own gate row; [m, C*H]."""
+    return np.stack([hc_inject(r, o, w, C, H) for r, o, w in zip(raw_rows, out_rows, inject_w_rows)])
+

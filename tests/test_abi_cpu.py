@@ -228,3 +228,20 @@ def test_decode_layers_rejects_bad_calls():
                                                   FAKE, need, None) == -1
     assert L.decodehp_graph_launch(None, None) == -1
     L.decodehp_graph_destroy(None)
+
+
+def test_hc_batched_rejects_bad_calls():
+    L = hca.lib()
+    C, H, R = 4, 512, 64
+    down, up, inj = int4(rows=R, cols=C * H), int4(rows=C * H, cols=R), int4(rows=C, cols=C * H)
+    need = L.decodehp_hc_read_batched_workspace_bytes(8, C, H, R)
+    assert need >= 8 * C * H * (2 + 4)                      # normed fp16 and the up output fp32
+    assert L.decodehp_hc_read_batched_workspace_bytes(0, C, H, R) == 0
+    f = lambda m=8, iw=FAKE, ws=FAKE, wsb=need, mixed=FAKE: L.decodehp_hc_read_batched(
+        FAKE, m, FAKE, C, H, 1e-6, ctypes.byref(down), ctypes.byref(up), ctypes.byref(inj), mixed, iw, ws, wsb, None)
+    assert f(m=0) == -2 and f(m=129) == -2
+    assert f(iw=None) == -1
+    assert f(mixed=FAKE + 8) == -3
+    assert f(wsb=need - 1) == -4
+    g = lambda m=8, wide=FAKE: L.decodehp_hc_inject_batched(wide, m, FAKE, FAKE, C, H, None)
+    assert g(m=0) == -2 and g(wide=None) == -1 and g(wide=FAKE + 8) == -3

@@ -228,3 +228,29 @@ def test_planted_transposed_inject_layout_fails(monkeypatch):
     monkeypatch.setattr(oracle, "hc_inject", bad)
     with pytest.raises(AssertionError):
         test_inject_golden_c2()
+
+
+def test_hc_read_batched_rows_are_independent_reads():
+    """A chunk's read is the per-token read on every row: one row equals hc_read, reordering the
+    rows reorders the outputs, and a row does not depend on the other rows."""
+    rng = np.random.default_rng(77)
+    C, H, R = 2, 128, 64
+    blk = synth.hc_block(rng, C, H, R)
+    rows = synth.normal_f16(rng, (4, C * H))
+    b = oracle.hc_read_batched(rows, blk["gamma_bits"], blk["down"], blk["up"], blk["inject"], C, H)
+    one = oracle.hc_read(rows[2], blk["gamma_bits"], blk["down"], blk["up"], blk["inject"], C, H)
+    assert np.array_equal(b["mixed"][2], one["mixed"]) and np.array_equal(b["inject_w"][2], one["inject_w"])
+    perm = [3, 1, 0, 2]
+    p = oracle.hc_read_batched(rows[perm], blk["gamma_bits"], blk["down"], blk["up"], blk["inject"], C, H)
+    assert np.array_equal(p["mixed"], b["mixed"][perm])
+    mixer = oracle.hc_read_batched(rows, blk["gamma_bits"], blk["down"], blk["up"], None, C, H)
+    assert mixer["inject_w"] is None and np.array_equal(mixer["mixed"], b["mixed"])
+
+
+def test_hc_inject_batched_uses_each_rows_gate():
+    C, H = 2, 64
+    raw = np.zeros((2, C * H))
+    out = np.ones((2, H))
+    w = np.array([[1.0, 2.0], [3.0, 4.0]])
+    got = oracle.hc_inject_batched(raw, out, w, C, H)
+    assert np.array_equal(got[0], np.repeat([1.0, 2.0], H)) and np.array_equal(got[1], np.repeat([3.0, 4.0], H))
