@@ -20,7 +20,8 @@ from .layout import pack_int4_codes, bf16_bits_to_tensor  # noqa: F401
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdecodehp.so")
 
-DHP_F16, DHP_F32, DHP_BF16 = 0, 1, 2
+DHP_F16, DHP_F32, DHP_BF16, DHP_I8 = 0, 1, 2, 3
+DHP_MOE_MAX_TOP_K = 10
 DHP_OP_GEMV_ARGMAX, DHP_OP_MOE_DECODE, DHP_OP_HC_READ = 1, 2, 3
 DHP_MOE_FP16_BOUNDARY = 1
 ERRORS = {-1: "invalid argument", -2: "unsupported", -3: "misaligned", -4: "workspace",
@@ -44,6 +45,11 @@ class CInt4Experts(ctypes.Structure):
 
 
 P4_, PE_ = ctypes.POINTER(CInt4), ctypes.POINTER(CInt4Experts)
+
+
+class CRouter(ctypes.Structure):
+    _fields_ = [("weights", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("elem_scale", ctypes.c_void_p),
+                ("expert_scale", ctypes.c_void_p)]
 
 
 class CHcBlock(ctypes.Structure):
@@ -75,6 +81,10 @@ def lib() -> ctypes.CDLL:
                                           vp, sz, vp]
         L.decodehp_moe_prefill.argtypes = [vp, i32, vp, i32, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp,
                                            vp, sz, vp]
+        PR = ctypes.POINTER(CRouter)
+        L.decodehp_moe_decode_ex.argtypes = [vp, PR, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.decodehp_moe_prefill_ex.argtypes = [vp, i32, PR, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp, vp,
+                                              sz, vp]
         L.decodehp_moe_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.decodehp_moe_prefill_workspace_bytes.restype = sz
         PL, PB = ctypes.POINTER(CDecodeLayer), ctypes.POINTER(CHcBlock)
@@ -261,40 +271,92 @@ def dequant_gemm_batched(w: Int4Weight, x, y=None, stream=None):
     return y
 
 
-def moe_decode(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, down: Int4Experts,
-               shared_gate: Int4Weight, shared_up: Int4Weight, shared_down: Int4Weight, top_k: int,
-               fp16_boundary=False, out=None, ids=None, weights=None, stream=None):
-    """One token through the routed MoE layer. router bf16 (int16 bits) or fp32 [E, hidden].
+class Router:
+    """A router with the optional scales of the _ex entry points.
 
-    Returns (out fp16 [hidden], ids int32 [top_k], weights fp32 [top_k]).
+    weights [E, hidden]: bf16 bits (int16), float32, or int8 codes; elem_scale: bf16 bits (int16)
+    [hidden] that multiply x before the dot products, or None; expert_scale: float32 [E] that
+    multiplies each selected expert's routing weight after the softmax, or None.
     """
+
+    def __init__(self, weights, elem_scale=None, expert_scale=None):
+        torch = _torch()
+        kinds = {torch.int16: DHP_BF16, torch.float32: DHP_F32, torch.int8: DHP_I8}
+        if weights.dtype not in kinds:
+            raise TypeError("router weights: int16 (bf16 bits), float32 or int8")
+        self.weights, self.dtype = weights, kinds[weights.dtype]
+        self.elem_scale, self.expert_scale = elem_scale, expert_scale
+
+    def desc(self, n_experts: int, hidden: int) -> CRouter:
+        torch = _torch()
+        _need(self.weights, self.weights.dtype, "router", n_experts * hidden)
+        if self.elem_scale is not None:
+            _need(self.elem_scale, torch.int16, "elem_scale", hidden)
+        if self.expert_scale is not None:
+            _need(self.expert_scale, torch.float32, "expert_scale", n_experts)
+        return CRouter(self.weights.data_ptr(), self.dtype, _ptr(self.elem_scale), _ptr(self.expert_scale))
+
+
+def _plain_router(router, n_experts, hidden):
     torch = _torch()
-    hidden = gate.cols
-    _need(x, torch.float16, "x", hidden)
     if router.dtype == torch.int16:
         rdt = DHP_BF16
     elif router.dtype == torch.float32:
         rdt = DHP_F32
     else:
-        raise TypeError("router: int16 (bf16 bits) or float32")
-    _need(router, router.dtype, "router", gate.count * hidden)
+        raise TypeError("router: int16 (bf16 bits) or float32 (int8 routers go through Router)")
+    _need(router, router.dtype, "router", n_experts * hidden)
+    return rdt
+
+
+def _moe_args(x, m, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k, out, ids,
+              weights, fp16_boundary, stream):
+    """(entry point, its arguments, what must stay alive) of one MoE call; m None: the decode
+    entry points (one token), else the prefill ones over m tokens."""
+    torch = _torch()
+    hidden, rows = gate.cols, 1 if m is None else m
+    _need(x, torch.float16, "x", rows * hidden)
     _need(shared_gate_row, torch.int16, "shared_gate_row", hidden)
+    _need(out, torch.float16, "out", rows * hidden)
+    _need(ids, torch.int32, "ids", rows * top_k)
+    _need(weights, torch.float32, "weights", rows * top_k)
+    if m is None:
+        ws = _workspace(workspace_bytes(DHP_OP_MOE_DECODE, gate.count, top_k, gate.rows), x.device)
+    else:
+        ws = _workspace(moe_prefill_workspace_bytes(m, gate.count, top_k, gate.rows, hidden), x.device, "moe_prefill")
+    descs = (gate.desc(), up.desc(), down.desc(), shared_gate.desc(), shared_up.desc(), shared_down.desc())
+    if isinstance(router, Router):
+        rd = router.desc(gate.count, hidden)
+        head, keep_r = (ctypes.byref(rd),), rd
+        fn = lib().decodehp_moe_decode_ex if m is None else lib().decodehp_moe_prefill_ex
+    else:
+        head, keep_r = (router.data_ptr(), _plain_router(router, gate.count, hidden)), None
+        fn = lib().decodehp_moe_decode if m is None else lib().decodehp_moe_prefill
+    args = (x.data_ptr(), *(() if m is None else (m,)), *head, shared_gate_row.data_ptr(),
+            *[ctypes.byref(d) for d in descs], top_k, DHP_MOE_FP16_BOUNDARY if fp16_boundary else 0,
+            out.data_ptr(), ids.data_ptr(), weights.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(),
+            _stream(stream))
+    keep = (descs, keep_r, x, router, shared_gate_row, out, ids, weights, ws, gate, up, down, shared_gate, shared_up,
+            shared_down)
+    return fn, args, keep
+
+
+def moe_decode(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, down: Int4Experts,
+               shared_gate: Int4Weight, shared_up: Int4Weight, shared_down: Int4Weight, top_k: int,
+               fp16_boundary=False, out=None, ids=None, weights=None, stream=None):
+    """One token through the routed MoE layer. router: bf16 bits (int16) or fp32 [E, hidden], or a
+    Router (int8 codes and/or scales).
+
+    Returns (out fp16 [hidden], ids int32 [top_k], weights fp32 [top_k]).
+    """
+    torch = _torch()
     dev = x.device
-    out = torch.empty(hidden, dtype=torch.float16, device=dev) if out is None else out
+    out = torch.empty(gate.cols, dtype=torch.float16, device=dev) if out is None else out
     ids = torch.empty(top_k, dtype=torch.int32, device=dev) if ids is None else ids
     weights = torch.empty(top_k, dtype=torch.float32, device=dev) if weights is None else weights
-    _need(out, torch.float16, "out", hidden)
-    _need(ids, torch.int32, "ids", top_k)
-    _need(weights, torch.float32, "weights", top_k)
-    ws = _workspace(workspace_bytes(DHP_OP_MOE_DECODE, gate.count, top_k, gate.rows), dev)
-    g, u, d = gate.desc(), up.desc(), down.desc()
-    sg, su, sd = shared_gate.desc(), shared_up.desc(), shared_down.desc()
-    _check(lib().decodehp_moe_decode(x.data_ptr(), router.data_ptr(), rdt, shared_gate_row.data_ptr(),
-                                     ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(sg),
-                                     ctypes.byref(su), ctypes.byref(sd), top_k,
-                                     DHP_MOE_FP16_BOUNDARY if fp16_boundary else 0, out.data_ptr(),
-                                     ids.data_ptr(), weights.data_ptr(), _ptr(ws),
-                                     0 if ws is None else ws.numel(), _stream(stream)))
+    fn, args, _keep = _moe_args(x, None, router, shared_gate_row, gate, up, down, shared_gate, shared_up,
+                                shared_down, top_k, out, ids, weights, fp16_boundary, stream)
+    _check(fn(*args))
     return out, ids, weights
 
 
@@ -340,33 +402,6 @@ def moe_prefill_workspace_bytes(m: int, n_experts: int, top_k: int, inter: int, 
     return int(lib().decodehp_moe_prefill_workspace_bytes(m, n_experts, top_k, inter, hidden))
 
 
-def _moe_prefill_args(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k,
-                      out, ids, weights, fp16_boundary, stream):
-    torch = _torch()
-    hidden = gate.cols
-    m = x.shape[0]
-    _need(x, torch.float16, "x", m * hidden)
-    if router.dtype == torch.int16:
-        rdt = DHP_BF16
-    elif router.dtype == torch.float32:
-        rdt = DHP_F32
-    else:
-        raise TypeError("router: int16 (bf16 bits) or float32")
-    _need(router, router.dtype, "router", gate.count * hidden)
-    _need(shared_gate_row, torch.int16, "shared_gate_row", hidden)
-    _need(out, torch.float16, "out", m * hidden)
-    _need(ids, torch.int32, "ids", m * top_k)
-    _need(weights, torch.float32, "weights", m * top_k)
-    ws = _workspace(moe_prefill_workspace_bytes(m, gate.count, top_k, gate.rows, hidden), x.device, "moe_prefill")
-    descs = (gate.desc(), up.desc(), down.desc(), shared_gate.desc(), shared_up.desc(), shared_down.desc())
-    args = (x.data_ptr(), m, router.data_ptr(), rdt, shared_gate_row.data_ptr(), *[ctypes.byref(d) for d in descs],
-            top_k, DHP_MOE_FP16_BOUNDARY if fp16_boundary else 0, out.data_ptr(), ids.data_ptr(),
-            weights.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
-    keep = (descs, x, router, shared_gate_row, out, ids, weights, ws, gate, up, down, shared_gate, shared_up,
-            shared_down)
-    return args, keep
-
-
 def moe_prefill(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, down: Int4Experts,
                 shared_gate: Int4Weight, shared_up: Int4Weight, shared_down: Int4Weight, top_k: int,
                 fp16_boundary=False, out=None, ids=None, weights=None, stream=None):
@@ -380,9 +415,9 @@ def moe_prefill(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, 
     out = torch.empty((m, gate.cols), dtype=torch.float16, device=dev) if out is None else out
     ids = torch.empty((m, top_k), dtype=torch.int32, device=dev) if ids is None else ids
     weights = torch.empty((m, top_k), dtype=torch.float32, device=dev) if weights is None else weights
-    args, _keep = _moe_prefill_args(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down,
-                                    top_k, out, ids, weights, fp16_boundary, stream)
-    _check(lib().decodehp_moe_prefill(*args))
+    fn, args, _keep = _moe_args(x, m, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down,
+                                top_k, out, ids, weights, fp16_boundary, stream)
+    _check(fn(*args))
     return out, ids, weights
 
 
@@ -569,22 +604,16 @@ def prepare_gemm_batched(w: Int4Weight, x, y, stream=None) -> PreparedCall:
 
 def prepare_moe(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k, out, ids,
                 weights, fp16_boundary=False, stream=None) -> PreparedCall:
-    torch = _torch()
-    rdt = DHP_BF16 if router.dtype == torch.int16 else DHP_F32
-    ws = _workspace(workspace_bytes(DHP_OP_MOE_DECODE, gate.count, top_k, gate.rows), x.device)
-    descs = (gate.desc(), up.desc(), down.desc(), shared_gate.desc(), shared_up.desc(), shared_down.desc())
-    args = (x.data_ptr(), router.data_ptr(), rdt, shared_gate_row.data_ptr(), *[ctypes.byref(d) for d in descs],
-            top_k, DHP_MOE_FP16_BOUNDARY if fp16_boundary else 0, out.data_ptr(), ids.data_ptr(),
-            weights.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
-    return PreparedCall(lib().decodehp_moe_decode, args, (descs, x, router, shared_gate_row, out, ids, weights, ws,
-                                                         gate, up, down, shared_gate, shared_up, shared_down))
+    fn, args, keep = _moe_args(x, None, router, shared_gate_row, gate, up, down, shared_gate, shared_up,
+                               shared_down, top_k, out, ids, weights, fp16_boundary, stream)
+    return PreparedCall(fn, args, keep)
 
 
 def prepare_moe_prefill(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k, out,
                         ids, weights, fp16_boundary=False, stream=None) -> PreparedCall:
-    args, keep = _moe_prefill_args(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down,
-                                   top_k, out, ids, weights, fp16_boundary, stream)
-    return PreparedCall(lib().decodehp_moe_prefill, args, keep)
+    fn, args, keep = _moe_args(x, x.shape[0], router, shared_gate_row, gate, up, down, shared_gate, shared_up,
+                               shared_down, top_k, out, ids, weights, fp16_boundary, stream)
+    return PreparedCall(fn, args, keep)
 
 
 def prepare_hc_read(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps=1e-6, stream=None) -> PreparedCall:

@@ -100,7 +100,7 @@ extern "C" {
 
 const char* decodehp_last_error(void) { return g_err; }
 
-int32_t decodehp_version(void) { return (0 << 16) | 2; }
+int32_t decodehp_version(void) { return (0 << 16) | 3; }
 
 size_t decodehp_workspace_bytes(int32_t op, int32_t a, int32_t b, int32_t c) {
     switch (op) {
@@ -185,14 +185,63 @@ int check_moe(const void* x, const void* router, int32_t router_dtype, const voi
     if (E > 1024) return dhp_fail(DHP_ERR_UNSUPPORTED, "n_experts=%d above 1024", E);
     if (top_k < 1 || top_k > DHP_MOE_MAX_TOP_K || top_k > E)
         return dhp_fail(DHP_ERR_UNSUPPORTED, "top_k=%d (1..%d and at most n_experts=%d)", top_k, DHP_MOE_MAX_TOP_K, E);
-    if (router_dtype != DHP_BF16 && router_dtype != DHP_F32)
-        return dhp_fail(DHP_ERR_UNSUPPORTED, "router_dtype %d (bf16 or fp32)", router_dtype);
+    if (router_dtype != DHP_BF16 && router_dtype != DHP_F32 && router_dtype != DHP_I8)
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "router_dtype %d (bf16, fp32 or int8)", router_dtype);
     if (flags & ~DHP_MOE_FP16_BOUNDARY) return dhp_fail(DHP_ERR_UNSUPPORTED, "flags 0x%x", flags);
-    if (!aligned(x, 16) || !aligned(router, 16) || !aligned(shared_gate_row, 16))
-        return dhp_fail(DHP_ERR_MISALIGNED, "x, router and shared_gate_row must be 16-byte aligned");
+    if (!aligned(x, 16) || !aligned(router, router_dtype == DHP_I8 ? 8 : 16) || !aligned(shared_gate_row, 16))
+        return dhp_fail(DHP_ERR_MISALIGNED, "x and shared_gate_row must be 16-byte aligned, router rows 16 (int8: 8)");
     if (!aligned(out, 2) || !aligned(ids, 4) || !aligned(weights, 4))
         return dhp_fail(DHP_ERR_MISALIGNED, "out, ids or weights misaligned");
     return DHP_OK;
+}
+}  // namespace
+
+namespace {
+int check_router_scales(const dhp_router* r) {
+    if (r->elem_scale && !aligned(r->elem_scale, 16))
+        return dhp_fail(DHP_ERR_MISALIGNED, "router elem_scale not 16-byte aligned");
+    if (r->expert_scale && !aligned(r->expert_scale, 4))
+        return dhp_fail(DHP_ERR_MISALIGNED, "router expert_scale misaligned");
+    return DHP_OK;
+}
+
+int moe_decode_impl(const void* x, const dhp_router* router, const void* shared_gate_row,
+                    const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
+                    const dhp_int4* shared_gate, const dhp_int4* shared_up, const dhp_int4* shared_down,
+                    int32_t top_k, int32_t flags, void* out, int32_t* ids, float* weights, void* ws,
+                    size_t ws_bytes, void* stream) {
+    int rc = check_moe(x, router->weights, router->dtype, shared_gate_row, gate, up, down, shared_gate, shared_up,
+                       shared_down, top_k, flags, out, ids, weights);
+    if (!rc) rc = check_router_scales(router);
+    if (rc) return rc;
+    const size_t need = dhp_moe_ws(gate->count, top_k, gate->first.rows);
+    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_moe(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k,
+                      (flags & DHP_MOE_FP16_BOUNDARY) != 0, out, ids, weights, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_prefill_impl(const void* x, int32_t m, const dhp_router* router, const void* shared_gate_row,
+                     const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
+                     const dhp_int4* shared_gate, const dhp_int4* shared_up, const dhp_int4* shared_down,
+                     int32_t top_k, int32_t flags, void* out, int32_t* ids, float* weights, void* ws,
+                     size_t ws_bytes, void* stream) {
+    if (m < 1 || m > DHP_MOE_PREFILL_MAX_M)
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d (1..%d)", m, DHP_MOE_PREFILL_MAX_M);
+    int rc = check_moe(x, router->weights, router->dtype, shared_gate_row, gate, up, down, shared_gate, shared_up,
+                       shared_down, top_k, flags, out, ids, weights);
+    if (!rc) rc = check_router_scales(router);
+    if (rc) return rc;
+    const size_t need = dhp_moe_prefill_ws(m, gate->count, top_k, gate->first.rows, gate->first.cols);
+    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_moe_prefill(x, m, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down,
+                              top_k, (flags & DHP_MOE_FP16_BOUNDARY) != 0, out, ids, weights, ws,
+                              static_cast<hipStream_t>(stream));
 }
 }  // namespace
 
@@ -203,17 +252,21 @@ int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
                         const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
                         int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
-    const int rc = check_moe(x, router, router_dtype, shared_gate_row, gate, up, down, shared_gate, shared_up,
-                             shared_down, top_k, flags, out, ids, weights);
-    if (rc) return rc;
-    const size_t need = dhp_moe_ws(gate->count, top_k, gate->first.rows);
-    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
-    DeviceFacts dev;
-    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
-    return launch_moe(x, router, router_dtype == DHP_F32, shared_gate_row, gate, up, down, shared_gate,
-                      shared_up, shared_down, top_k, (flags & DHP_MOE_FP16_BOUNDARY) != 0, out, ids,
-                      weights, ws, static_cast<hipStream_t>(stream));
+    const dhp_router r{router, router_dtype, nullptr, nullptr};
+    return moe_decode_impl(x, &r, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k, flags,
+                           out, ids, weights, ws, ws_bytes, stream);
+}
+
+int decodehp_moe_decode_ex(const void* x, const dhp_router* router, const void* shared_gate_row,
+                           const dhp_int4_experts* gate, const dhp_int4_experts* up,
+                           const dhp_int4_experts* down, const dhp_int4* shared_gate,
+                           const dhp_int4* shared_up, const dhp_int4* shared_down, int32_t top_k,
+                           int32_t flags, void* out, int32_t* ids, float* weights, void* ws,
+                           size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!router) return dhp_fail(DHP_ERR_INVALID, "null router");
+    return moe_decode_impl(x, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k,
+                           flags, out, ids, weights, ws, ws_bytes, stream);
 }
 
 size_t decodehp_moe_prefill_workspace_bytes(int32_t m, int32_t n_experts, int32_t top_k, int32_t inter,
@@ -231,19 +284,21 @@ int decodehp_moe_prefill(const void* x, int32_t m, const void* router, int32_t r
                          const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
                          int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
-    if (m < 1 || m > DHP_MOE_PREFILL_MAX_M)
-        return dhp_fail(DHP_ERR_UNSUPPORTED, "m=%d (1..%d)", m, DHP_MOE_PREFILL_MAX_M);
-    const int rc = check_moe(x, router, router_dtype, shared_gate_row, gate, up, down, shared_gate, shared_up,
-                             shared_down, top_k, flags, out, ids, weights);
-    if (rc) return rc;
-    const size_t need = dhp_moe_prefill_ws(m, gate->count, top_k, gate->first.rows, gate->first.cols);
-    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
-    DeviceFacts dev;
-    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
-    return launch_moe_prefill(x, m, router, router_dtype == DHP_F32, shared_gate_row, gate, up, down, shared_gate,
-                              shared_up, shared_down, top_k, (flags & DHP_MOE_FP16_BOUNDARY) != 0, out, ids,
-                              weights, ws, static_cast<hipStream_t>(stream));
+    const dhp_router r{router, router_dtype, nullptr, nullptr};
+    return moe_prefill_impl(x, m, &r, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k,
+                            flags, out, ids, weights, ws, ws_bytes, stream);
+}
+
+int decodehp_moe_prefill_ex(const void* x, int32_t m, const dhp_router* router, const void* shared_gate_row,
+                            const dhp_int4_experts* gate, const dhp_int4_experts* up,
+                            const dhp_int4_experts* down, const dhp_int4* shared_gate,
+                            const dhp_int4* shared_up, const dhp_int4* shared_down, int32_t top_k,
+                            int32_t flags, void* out, int32_t* ids, float* weights, void* ws,
+                            size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!router) return dhp_fail(DHP_ERR_INVALID, "null router");
+    return moe_prefill_impl(x, m, router, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k,
+                            flags, out, ids, weights, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

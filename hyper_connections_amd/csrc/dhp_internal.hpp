@@ -269,11 +269,11 @@ int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, 
                    const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w,
                    void* ws, hipStream_t s);
 int launch_hc_inject(void* wide, const void* out, const float* w, int C, int H, hipStream_t s);
-int launch_moe(const void* x, const void* router, int router_f32, const void* sgate_row,
+int launch_moe(const void* x, const dhp_router* router, const void* sgate_row,
                const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
                const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
                void* out, int32_t* ids, float* weights, void* ws, hipStream_t s);
-int launch_moe_prefill(const void* x, int m, const void* router, int router_f32, const void* sgate_row,
+int launch_moe_prefill(const void* x, int m, const dhp_router* router, const void* sgate_row,
                        const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
                        const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
                        void* out, int32_t* ids, float* weights, void* ws, hipStream_t s);

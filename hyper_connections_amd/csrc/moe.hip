@@ -38,7 +38,9 @@ constexpr int MAX_E = 1024;
 struct MoeArgs {
     const _Float16* x;
     const void* router;
-    int router_f32;
+    int router_kind;              // RK_BF16, RK_F32 or RK_I8
+    const uint16_t* router_escale; // bf16 [hidden]: the router's per-element effective scale, or null
+    const float* expert_scale;    // fp32 [E]: per-expert scale of the routing weights, or null
     const uint16_t* sgate_row;
     // routed experts: first tensor and byte strides
     const uint8_t* g_codes; const uint8_t* g_scales; const uint8_t* g_biases;
@@ -110,79 +112,142 @@ DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* 
     return silu_f(ag) * au;
 }
 
-// fp32 dot of one bf16 or fp32 row of length hidden = 512 * CPL with the fp16 activations, one
-// wave: lane l takes the 16-byte row chunks l + 64 i. The row's loads are issued on their own
-// (a batched caller keeps the row and streams tokens past it); a row costs one memory round trip.
-template <int CPL>
+// fp32 dot of one router row of length hidden = 512 * CPL with the fp16 activations, one wave:
+// lane l takes the row chunks l + 64 i (8 bf16 or 8 int8 values, or 4 fp32). With a per-element
+// effective scale (the INT8 router kernel's, "src/families/qwen/state.rs", router_ones), each
+// activation is multiplied by its scale first. The row's loads are issued on their own (a
+// batched caller keeps the row and streams tokens past it); a row costs one memory round trip.
+enum RouterKind { RK_BF16 = 0, RK_F32 = 1, RK_I8 = 2 };
+template <int CPL, int KIND>
 struct RouterRow {
-    u32x4 w[2 * CPL];      // bf16: CPL chunks of 8; fp32: 2 CPL chunks of 4 (as bits)
+    u32x4 w[KIND == RK_F32 ? 2 * CPL : CPL];   // bf16: 8 per chunk; fp32: 4 (as bits); int8: 8 in .x, .y
 };
-template <int CPL>
+template <int CPL, bool SC>
 struct RouterX {
-    uint2 h[2 * CPL];      // bf16 rows: chunk i = h[2i], h[2i+1]; fp32 rows: chunk i = h[i]
+    uint2 h[2 * CPL];      // 8-value chunks: chunk i = h[2i], h[2i+1]; fp32 rows: chunk i = h[i]
+    uint2 e[SC ? 2 * CPL : 1];   // the effective scales, laid out like h (scaled routers only)
 };
-template <int CPL>
-DHP_DEV void router_row_load(RouterRow<CPL>& r, const void* row, int f32) {
+template <int CPL, int KIND>
+DHP_DEV void router_row_load(RouterRow<CPL, KIND>& r, const void* row) {
     const int lane = threadIdx.x & 63;
-    const u32x4* p = static_cast<const u32x4*>(row);
-    if (!f32) {
+    if constexpr (KIND != RK_I8) {
+        const u32x4* p = static_cast<const u32x4*>(row);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) r.w[i] = __builtin_nontemporal_load(p + lane + 64 * i);
+        for (int i = 0; i < (KIND == RK_F32 ? 2 * CPL : CPL); ++i) r.w[i] = __builtin_nontemporal_load(p + lane + 64 * i);
     } else {
+        typedef uint32_t u32x2n __attribute__((ext_vector_type(2)));
+        const u32x2n* p = static_cast<const u32x2n*>(row);
 #pragma unroll
-        for (int i = 0; i < 2 * CPL; ++i) r.w[i] = __builtin_nontemporal_load(p + lane + 64 * i);
+        for (int i = 0; i < CPL; ++i) {
+            const u32x2n q = __builtin_nontemporal_load(p + lane + 64 * i);
+            r.w[i] = u32x4{q.x, q.y, 0u, 0u};
+        }
     }
 }
-template <int CPL>
-DHP_DEV void router_x_load(RouterX<CPL>& v, int f32, const _Float16* x) {
+template <int CPL, int KIND, bool SC>
+DHP_DEV void router_x_load(RouterX<CPL, SC>& v, const _Float16* x, const uint16_t* escale) {
     const int lane = threadIdx.x & 63;
-    if (!f32) {
+    if constexpr (KIND != RK_F32) {
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const u32x4 q = *reinterpret_cast<const u32x4*>(x + 8 * (lane + 64 * i));
             v.h[2 * i] = uint2{q.x, q.y};
             v.h[2 * i + 1] = uint2{q.z, q.w};
+            if constexpr (SC) {
+                const u32x4 g = *reinterpret_cast<const u32x4*>(escale + 8 * (lane + 64 * i));
+                v.e[2 * i] = uint2{g.x, g.y};
+                v.e[2 * i + 1] = uint2{g.z, g.w};
+            }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 2 * CPL; ++i) v.h[i] = *reinterpret_cast<const uint2*>(x + 4 * (lane + 64 * i));
+        for (int i = 0; i < 2 * CPL; ++i) {
+            v.h[i] = *reinterpret_cast<const uint2*>(x + 4 * (lane + 64 * i));
+            if constexpr (SC) v.e[i] = *reinterpret_cast<const uint2*>(escale + 4 * (lane + 64 * i));
+        }
     }
 }
-template <int CPL>
-DHP_DEV float router_dot(const RouterRow<CPL>& r, const RouterX<CPL>& v, int f32) {
+// The two activations of a packed fp16 pair, each times its bf16 scale when scaled.
+template <bool SC>
+DHP_DEV void x_pair(uint32_t xw, uint32_t ew, float& x0, float& x1) {
+    const h2 xh = as_h2(xw);
+    x0 = (float)xh.x;
+    x1 = (float)xh.y;
+    if constexpr (SC) {
+        x0 = x0 * bf16_to_f32(ew & 0xFFFFu);
+        x1 = x1 * bf16_to_f32(ew >> 16);
+    }
+}
+template <int CPL, bool SC>
+DHP_DEV uint32_t escale_word(const RouterX<CPL, SC>& v, int i, int half) {
+    if constexpr (SC) return half ? v.e[i].y : v.e[i].x;
+    else return 0u;
+}
+template <int CPL, int KIND, bool SC>
+DHP_DEV float router_dot(const RouterRow<CPL, KIND>& r, const RouterX<CPL, SC>& v) {
     float acc = 0.0f;
-    if (!f32) {
+    if constexpr (KIND == RK_BF16) {
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const uint32_t ww[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
             const uint32_t xx[4] = {v.h[2 * i].x, v.h[2 * i].y, v.h[2 * i + 1].x, v.h[2 * i + 1].y};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const h2 xh = as_h2(xx[k]);
-                acc = __builtin_fmaf(bf16_to_f32(ww[k] & 0xFFFFu), (float)xh.x, acc);
-                acc = __builtin_fmaf(bf16_to_f32(ww[k] >> 16), (float)xh.y, acc);
+                float x0, x1;
+                x_pair<SC>(xx[k], escale_word<CPL, SC>(v, 2 * i + (k >> 1), k & 1), x0, x1);
+                acc = __builtin_fmaf(bf16_to_f32(ww[k] & 0xFFFFu), x0, acc);
+                acc = __builtin_fmaf(bf16_to_f32(ww[k] >> 16), x1, acc);
             }
+        }
+    } else if constexpr (KIND == RK_F32) {
+#pragma unroll
+        for (int i = 0; i < 2 * CPL; ++i) {
+            const f4v wv = __builtin_bit_cast(f4v, r.w[i]);   // whole-vector cast
+            float x0, x1, x2, x3;
+            x_pair<SC>(v.h[i].x, escale_word<CPL, SC>(v, i, 0), x0, x1);
+            x_pair<SC>(v.h[i].y, escale_word<CPL, SC>(v, i, 1), x2, x3);
+            acc = __builtin_fmaf(wv.x, x0, acc);
+            acc = __builtin_fmaf(wv.y, x1, acc);
+            acc = __builtin_fmaf(wv.z, x2, acc);
+            acc = __builtin_fmaf(wv.w, x3, acc);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 2 * CPL; ++i) {
-            const h2 x0 = as_h2(v.h[i].x), x1 = as_h2(v.h[i].y);
-            const f4v wv = __builtin_bit_cast(f4v, r.w[i]);   // whole-vector cast
-            acc = __builtin_fmaf(wv.x, (float)x0.x, acc);
-            acc = __builtin_fmaf(wv.y, (float)x0.y, acc);
-            acc = __builtin_fmaf(wv.z, (float)x1.x, acc);
-            acc = __builtin_fmaf(wv.w, (float)x1.y, acc);
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t ww[2] = {r.w[i].x, r.w[i].y};
+            const uint32_t xx[4] = {v.h[2 * i].x, v.h[2 * i].y, v.h[2 * i + 1].x, v.h[2 * i + 1].y};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float x0, x1;
+                x_pair<SC>(xx[k], escale_word<CPL, SC>(v, 2 * i + (k >> 1), k & 1), x0, x1);
+                const uint32_t w = ww[k >> 1] >> (16 * (k & 1));      // codes of elements 2k, 2k+1
+                acc = __builtin_fmaf((float)(int8_t)(w & 0xFFu), x0, acc);
+                acc = __builtin_fmaf((float)(int8_t)((w >> 8) & 0xFFu), x1, acc);
+            }
         }
     }
     return group_sum<64>(acc);
 }
+template <int CPL, int KIND, bool SC>
+DHP_DEV float wave_row_dot_t(const void* row, const _Float16* x, const uint16_t* escale) {
+    RouterRow<CPL, KIND> r;
+    RouterX<CPL, SC> v;
+    router_row_load<CPL, KIND>(r, row);
+    router_x_load<CPL, KIND, SC>(v, x, escale);
+    return router_dot<CPL, KIND, SC>(r, v);
+}
 template <int CPL>
-DHP_DEV float wave_row_dot(const void* row, int f32, const _Float16* x) {
-    RouterRow<CPL> r;
-    RouterX<CPL> v;
-    router_row_load<CPL>(r, row, f32);
-    router_x_load<CPL>(v, f32, x);
-    return router_dot<CPL>(r, v, f32);
+DHP_DEV float wave_row_dot(const void* row, int kind, const _Float16* x, const uint16_t* escale) {
+    if (kind == RK_BF16)
+        return escale ? wave_row_dot_t<CPL, RK_BF16, true>(row, x, escale) : wave_row_dot_t<CPL, RK_BF16, false>(row, x, escale);
+    if (kind == RK_F32)
+        return escale ? wave_row_dot_t<CPL, RK_F32, true>(row, x, escale) : wave_row_dot_t<CPL, RK_F32, false>(row, x, escale);
+    return escale ? wave_row_dot_t<CPL, RK_I8, true>(row, x, escale) : wave_row_dot_t<CPL, RK_I8, false>(row, x, escale);
+}
+
+// Bytes of one router row of this kind.
+DHP_DEV size_t router_row_bytes(int kind, int hidden) {
+    return (size_t)hidden * (kind == RK_F32 ? 4 : kind == RK_BF16 ? 2 : 1);
 }
 
 // Lane j's activations for pair_act: chunks j + 16 i in the raw form of load_x32_raw.
@@ -198,13 +263,14 @@ __global__ __launch_bounds__(64) void k_moe_router(MoeArgs a) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     if (b < a.E) {
-        const size_t rb = (size_t)a.hidden * (a.router_f32 ? 4 : 2);
-        const float v = wave_row_dot<CPL>(static_cast<const uint8_t*>(a.router) + rb * b, a.router_f32, a.x);
+        const size_t rb = router_row_bytes(a.router_kind, a.hidden);
+        const float v = wave_row_dot<CPL>(static_cast<const uint8_t*>(a.router) + rb * b, a.router_kind, a.x,
+                                          a.router_escale);
         if (lane == 0) a.logits[b] = v;
         return;
     }
     if (b == a.E) {
-        const float v = wave_row_dot<CPL>(a.sgate_row, 0, a.x);
+        const float v = wave_row_dot<CPL>(a.sgate_row, RK_BF16, a.x, nullptr);
         if (lane == 0) a.gate_logit[0] = v;
         return;
     }
@@ -336,8 +402,11 @@ DHP_DEV void wave_topk(TopkIn<PER>& t, int E, int rounds, int* ids, float* vals)
     }
 }
 
-// The selected ids (largest logit first) and the softmax over their logits, by one thread.
-DHP_DEV void publish_topk(const int* ids, const float* vals, int top_k, int32_t* out_ids, float* out_w) {
+// The selected ids (largest logit first) and the softmax over their logits, each weight times its
+// expert's scale when a per-expert scale is given ("src/families/qwen/state.rs", per_expert_ones),
+// by one thread.
+DHP_DEV void publish_topk(const int* ids, const float* vals, int top_k, const float* expert_scale,
+                          int32_t* out_ids, float* out_w) {
     float wt[DHP_MOE_MAX_TOP_K];
     float sum = 0.0f;
 #pragma unroll
@@ -349,7 +418,8 @@ DHP_DEV void publish_topk(const int* ids, const float* vals, int top_k, int32_t*
     for (int r = 0; r < DHP_MOE_MAX_TOP_K; ++r) {
         if (r < top_k) {
             out_ids[r] = ids[r];
-            out_w[r] = wt[r] / sum;
+            const float w = wt[r] / sum;
+            out_w[r] = expert_scale ? w * expert_scale[ids[r]] : w;
         }
     }
 }
@@ -390,7 +460,7 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     load_pair<CPL>(p, gc, gs, gb, uc, us, ub, row, j);
 
     // block 0 publishes the ids and the softmax over the selected logits
-    if (blockIdx.x == 0 && lane == 0) publish_topk(ids, vals, a.top_k, a.ids, a.weights);
+    if (blockIdx.x == 0 && lane == 0) publish_topk(ids, vals, a.top_k, a.expert_scale, a.ids, a.weights);
 
     const float v = pair_act<CPL>(p, xp, xs, nc);
     if (j == 0 && live) a.act[(size_t)slot * a.inter + row] = v;
@@ -571,32 +641,50 @@ template <int CPLD> constexpr int p2_tg() { return CPLD == 1 ? 16 : 8; }
 constexpr int P2_RH = 4;         // down rows per 16-lane group in the batched phase 2
 constexpr int ITEM_TOK = 16;     // (token, slot) pairs per work item
 
-template <int CPL>
-__global__ __launch_bounds__(256) void k_moep_router(MoeArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = blockIdx.x * 4 + wave;       // router row; E: the shared gate row
-    if (r > a.E) return;                       // whole waves; no block synchronisation below
-    const bool sgr = r == a.E;
-    const int f32 = sgr ? 0 : a.router_f32;
-    const void* row = sgr ? static_cast<const void*>(a.sgate_row)
-                          : static_cast<const void*>(static_cast<const uint8_t*>(a.router) +
-                                                     (size_t)r * a.hidden * (a.router_f32 ? 4 : 2));
-    RouterRow<CPL> rr;
-    router_row_load<CPL>(rr, row, f32);
+template <int CPL, int KIND, bool SC>
+DHP_DEV void router_tokens(const MoeArgs& a, const void* row, const uint16_t* escale, int r, bool sgr) {
+    constexpr int G = SC ? 2 : RT_GRP;                     // the scales take registers too
+    const int lane = threadIdx.x & 63;
+    RouterRow<CPL, KIND> rr;
+    router_row_load<CPL, KIND>(rr, row);
     const int m0 = blockIdx.y * RT_TOK, m1 = min(m0 + RT_TOK, a.M);
-    for (int mb = m0; mb < m1; mb += RT_GRP) {
-        RouterX<CPL> v[RT_GRP];
+    for (int mb = m0; mb < m1; mb += G) {
+        RouterX<CPL, SC> v[G];
 #pragma unroll
-        for (int g = 0; g < RT_GRP; ++g) router_x_load<CPL>(v[g], f32, a.x + (size_t)min(mb + g, m1 - 1) * a.hidden);
+        for (int g = 0; g < G; ++g)
+            router_x_load<CPL, KIND, SC>(v[g], a.x + (size_t)min(mb + g, m1 - 1) * a.hidden, escale);
 #pragma unroll
-        for (int g = 0; g < RT_GRP; ++g) {
+        for (int g = 0; g < G; ++g) {
             const int m = mb + g;
-            const float d = router_dot<CPL>(rr, v[g], f32);
+            const float d = router_dot<CPL, KIND, SC>(rr, v[g]);
             if (lane == 0 && m < m1) {
                 if (sgr) a.gate_logit[m] = d;
                 else a.logits[(size_t)m * a.Epad + r] = d;
             }
         }
+    }
+}
+
+template <int CPL>
+__global__ __launch_bounds__(256) void k_moep_router(MoeArgs a) {
+    const int wave = threadIdx.x >> 6;
+    const int r = blockIdx.x * 4 + wave;       // router row; E: the shared gate row
+    if (r > a.E) return;                       // whole waves; no block synchronisation below
+    const bool sgr = r == a.E;
+    const int kind = sgr ? RK_BF16 : a.router_kind;
+    const uint16_t* escale = sgr ? nullptr : a.router_escale;
+    const void* row = sgr ? static_cast<const void*>(a.sgate_row)
+                          : static_cast<const void*>(static_cast<const uint8_t*>(a.router) +
+                                                     (size_t)r * router_row_bytes(a.router_kind, a.hidden));
+    if (kind == RK_BF16) {
+        if (escale) router_tokens<CPL, RK_BF16, true>(a, row, escale, r, sgr);
+        else router_tokens<CPL, RK_BF16, false>(a, row, escale, r, sgr);
+    } else if (kind == RK_F32) {
+        if (escale) router_tokens<CPL, RK_F32, true>(a, row, escale, r, sgr);
+        else router_tokens<CPL, RK_F32, false>(a, row, escale, r, sgr);
+    } else {
+        if (escale) router_tokens<CPL, RK_I8, true>(a, row, escale, r, sgr);
+        else router_tokens<CPL, RK_I8, false>(a, row, escale, r, sgr);
     }
 }
 
@@ -609,7 +697,8 @@ __global__ __launch_bounds__(64) void k_moep_topk(MoeArgs a) {
     float vals[DHP_MOE_MAX_TOP_K];
     wave_topk<PER>(tin, a.E, a.top_k, ids, vals);
     if (threadIdx.x == 0)
-        publish_topk(ids, vals, a.top_k, a.ids + (size_t)m * a.top_k, a.weights + (size_t)m * a.top_k);
+        publish_topk(ids, vals, a.top_k, a.expert_scale, a.ids + (size_t)m * a.top_k,
+                     a.weights + (size_t)m * a.top_k);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -635,7 +724,7 @@ __global__ __launch_bounds__(1024) void k_moep_route(MoeArgs a) {
     const int E = a.E, M = a.M, k = a.top_k, n = M * k;
     if (t < E) { cnt[t] = 0; fill[t] = 0; }
     __syncthreads();
-    if (t < n) atomicAdd(&cnt[a.ids[t]], 1);
+    for (int i = t; i < n; i += 1024) atomicAdd(&cnt[a.ids[i]], 1);     // n = M * k <= 1280
     __syncthreads();
     const int c = (t < E) ? cnt[t] : 0;
     const int ki = (c + ITEM_TOK - 1) / ITEM_TOK;
@@ -647,9 +736,9 @@ __global__ __launch_bounds__(1024) void k_moep_route(MoeArgs a) {
     const int nsh = (M + ITEM_TOK - 1) / ITEM_TOK;
     if (t < E) { base[t] = M + oc + sc - c; ibase[t] = nsh + ok + sk - ki; }
     __syncthreads();
-    if (t < n) {
-        const int e = a.ids[t];
-        a.route[base[e] + atomicAdd(&fill[e], 1)] = ((t / k) << 4) | (t % k);
+    for (int i = t; i < n; i += 1024) {
+        const int e = a.ids[i];
+        a.route[base[e] + atomicAdd(&fill[e], 1)] = ((i / k) << 4) | (i % k);
     }
     if (t < M) a.route[t] = (t << 4) | k;
     if (t < nsh) *reinterpret_cast<int4*>(a.items + 4 * t) = int4{E, ITEM_TOK * t, min(ITEM_TOK, M - ITEM_TOK * t), 0};
@@ -912,13 +1001,15 @@ PrefillWs prefill_ws(int m, int E, int top_k, int inter, int hidden) {
     return w;
 }
 
-void fill_args(MoeArgs& a, const void* x, const void* router, int router_f32, const void* sgate_row,
+void fill_args(MoeArgs& a, const void* x, const dhp_router* router, const void* sgate_row,
                const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
                const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary, void* out,
                int32_t* ids, float* weights) {
     a.x = static_cast<const _Float16*>(x);
-    a.router = router;
-    a.router_f32 = router_f32;
+    a.router = router->weights;
+    a.router_kind = router->dtype == DHP_F32 ? RK_F32 : router->dtype == DHP_I8 ? RK_I8 : RK_BF16;
+    a.router_escale = static_cast<const uint16_t*>(router->elem_scale);
+    a.expert_scale = router->expert_scale;
     a.sgate_row = static_cast<const uint16_t*>(sgate_row);
     a.g_codes = static_cast<const uint8_t*>(gate->first.codes);
     a.g_scales = static_cast<const uint8_t*>(gate->first.scales);
@@ -959,12 +1050,12 @@ size_t dhp_moe_prefill_ws(int32_t m, int32_t n_experts, int32_t top_k, int32_t i
     return prefill_ws(m, n_experts, top_k, inter, hidden).total;
 }
 
-int launch_moe(const void* x, const void* router, int router_f32, const void* sgate_row,
+int launch_moe(const void* x, const dhp_router* router, const void* sgate_row,
                const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
                const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
                void* out, int32_t* ids, float* weights, void* ws, hipStream_t s) {
     MoeArgs a;
-    fill_args(a, x, router, router_f32, sgate_row, gate, up, down, sg, su, sd, top_k, boundary, out, ids, weights);
+    fill_args(a, x, router, sgate_row, gate, up, down, sg, su, sd, top_k, boundary, out, ids, weights);
     a.M = 1;
     a.Epad = a.E;
     float* w = static_cast<float*>(ws);
@@ -990,12 +1081,12 @@ int launch_moe(const void* x, const void* router, int router_f32, const void* sg
     return DHP_OK;
 }
 
-int launch_moe_prefill(const void* x, int m, const void* router, int router_f32, const void* sgate_row,
+int launch_moe_prefill(const void* x, int m, const dhp_router* router, const void* sgate_row,
                        const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
                        const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,
                        void* out, int32_t* ids, float* weights, void* ws, hipStream_t s) {
     MoeArgs a;
-    fill_args(a, x, router, router_f32, sgate_row, gate, up, down, sg, su, sd, top_k, boundary, out, ids, weights);
+    fill_args(a, x, router, sgate_row, gate, up, down, sg, su, sd, top_k, boundary, out, ids, weights);
     a.M = m;
     a.Epad = (a.E + 3) & ~3;
     const PrefillWs lay = prefill_ws(m, a.E, top_k, a.inter, a.hidden);

@@ -53,6 +53,7 @@ extern "C" {
 #define DHP_F16 0
 #define DHP_F32 1
 #define DHP_BF16 2
+#define DHP_I8 3     /* signed 8-bit codes (the INT8 router) */
 
 /* Workspace queries (decodehp_workspace_bytes `op`). */
 #define DHP_OP_GEMV_ARGMAX 1 /* a = rows (N), b = m                       */
@@ -65,7 +66,7 @@ extern "C" {
 /* Limits. */
 #define DHP_GEMV_MAX_M 16
 #define DHP_GEMM_MAX_M 128
-#define DHP_MOE_MAX_TOP_K 8
+#define DHP_MOE_MAX_TOP_K 10
 #define DHP_MOE_PREFILL_MAX_M 128
 #define DHP_HC_MAX_C 16
 
@@ -136,12 +137,13 @@ int decodehp_dequant_gemm_batched(const dhp_int4* w, const void* x, int32_t m, v
  * With DHP_MOE_FP16_BOUNDARY the routed sum and the gated shared output are each rounded
  * to fp16 before the add ("src/families/qwen4/mod.rs", section MoE, the fp16 boundary).
  *   x               : fp16 [hidden], 16-byte aligned.
- *   router          : [n_experts][hidden], bf16 (router_dtype DHP_BF16) or fp32 (DHP_F32),
- *                     16-byte aligned rows.
+ *   router          : [n_experts][hidden], bf16 (router_dtype DHP_BF16), fp32 (DHP_F32) or
+ *                     signed int8 codes (DHP_I8, taken at unit scale here), rows 16-byte
+ *                     aligned (int8 rows 8-byte).
  *   shared_gate_row : bf16 [hidden], 16-byte aligned.
  *   gate, up        : experts [inter x hidden];  down : experts [hidden x inter]; same count.
  *   shared_*        : one expert of the same shapes.
- *   top_k           : 1..8, <= n_experts.
+ *   top_k           : 1..DHP_MOE_MAX_TOP_K (10), <= n_experts.
  *   out             : fp16 [hidden].  ids : int32 [top_k].  weights : fp32 [top_k].
  *   ws              : decodehp_workspace_bytes(DHP_OP_MOE_DECODE, n_experts, top_k, inter).
  * Errors: -1, -2 (hidden % 512, hidden > 4096, inter % 64, inter > 1024, top_k,
@@ -178,6 +180,36 @@ int decodehp_moe_prefill(const void* x, int32_t m, const void* router, int32_t r
 /* Workspace bytes decodehp_moe_prefill needs (0 for arguments out of range). */
 size_t decodehp_moe_prefill_workspace_bytes(int32_t m, int32_t n_experts, int32_t top_k,
                                             int32_t inter, int32_t hidden);
+
+/*
+ * The router variants ("src/families/qwen/state.rs", struct RealQwenState, fields router_ones and
+ * per_expert_ones): an INT8 router whose kernel multiplies x[n] by an effective scale per
+ * element, and a per-expert scale on each selected expert's routing weight. Both are ones for
+ * this family (the plain entry points above); the _ex entry points take them:
+ *     logits[e]  = sum_n R[e][n] * (elem_scale[n] * x[n])        (elem_scale NULL: ones)
+ *     weights[j] = softmax over the selected logits, then * expert_scale[ids[j]]   (NULL: ones)
+ * R is bf16, fp32 or signed int8 codes (DHP_I8; the scale of an INT8 router lives in elem_scale).
+ * With both NULL and a bf16/fp32 router the results equal the plain entry points' bit for bit.
+ */
+typedef struct dhp_router {
+    const void* weights;         /* [n_experts][hidden], rows 16-byte aligned (int8 rows 8-byte) */
+    int32_t dtype;               /* DHP_BF16, DHP_F32 or DHP_I8 */
+    const void* elem_scale;      /* bf16 [hidden], 16-byte aligned, or NULL */
+    const float* expert_scale;   /* fp32 [n_experts], or NULL */
+} dhp_router;
+
+int decodehp_moe_decode_ex(const void* x, const dhp_router* router, const void* shared_gate_row,
+                           const dhp_int4_experts* gate, const dhp_int4_experts* up,
+                           const dhp_int4_experts* down, const dhp_int4* shared_gate,
+                           const dhp_int4* shared_up, const dhp_int4* shared_down, int32_t top_k,
+                           int32_t flags, void* out, int32_t* ids, float* weights, void* ws,
+                           size_t ws_bytes, void* stream);
+int decodehp_moe_prefill_ex(const void* x, int32_t m, const dhp_router* router, const void* shared_gate_row,
+                            const dhp_int4_experts* gate, const dhp_int4_experts* up,
+                            const dhp_int4_experts* down, const dhp_int4* shared_gate,
+                            const dhp_int4* shared_up, const dhp_int4* shared_down, int32_t top_k,
+                            int32_t flags, void* out, int32_t* ids, float* weights, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /*
  * decodehp_hc_read -- one hyper-connection read (attn_hc / mlp_hc / the final mixer).

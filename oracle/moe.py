@@ -3,15 +3,23 @@
 Steps, in the order the pages give them:
 
 1. Router GEMV. "src/families/qwen/state.rs", struct RealQwenState: the router output
-   is an fp32 buffer of one logit per expert (router_logits_f32); the per-element
-   router scale and the per-expert scale are identically one for this family
-   (router_ones, per_expert_ones), so the logits are the plain product R @ x.
+   is an fp32 buffer of one logit per expert (router_logits_f32). The INT8 router
+   kernel multiplies each x[n] by an effective per-element scale before the dot
+   products (router_ones, a bf16 [hidden] buffer), so in general
+   logits[e] = sum_n R[e][n] * (scale[n] * x[n]); for this family the scale is all ones
+   and the logits are the plain product R @ x. R may be bf16, fp32 or INT8 codes (the
+   codes' values are the weights; an INT8 router's scale lives in the per-element scale).
 2. Selection. "src/families/qwen4/mod.rs", section "MoE": top-k is taken on the raw
    logits and the softmax runs over the selected set only (equivalently: softmax over
    all, top-k, renormalize -- no router bias). The logits are fp32 on the pages, so
    the selection is decided on the fp32-rounded values; ties go to the lowest expert
    index (reading: the pages are silent on ties) and the selected ids are returned in
-   order of decreasing logit.
+   order of decreasing logit. The per-expert scale ("src/families/qwen/state.rs",
+   per_expert_ones, the weighting of the shared top-k routine) multiplies each selected
+   expert's softmax weight afterwards (reading: after the renormalization, not renormalized
+   again, and never part of the selection); all ones for this family. The section's
+   "top-10 renormalization" and the model check on the streamed-expert slot count give
+   k <= 10.
 3. Phase 1. "src/real_forward.rs", module doc: the phase-1 kernel runs each selected
    expert's gate and up projections and the gated-FFN activation, act = silu(gate)*up.
 4. Phase 2: each selected expert's down projection, weighted by its softmax weight and
@@ -23,9 +31,12 @@ Steps, in the order the pages give them:
    (the routed sum is cast to the model dtype before the gated shared expert is added):
    routed and gated-shared are each rounded to fp16 before the add.
 
-Parity: pinned (top-k against exhaustive subset search; softmax closed form for two
-experts; the pages' softmax-order identity; weights sum to one; identical-experts
-invariant; selector-weight closed forms for gate/up/down and the shared gate).
+Parity: pinned (top-k against exhaustive subset search, k up to 10; softmax closed form for
+two experts; the pages' softmax-order identity; weights sum to one; identical-experts
+invariant; selector-weight closed forms for gate/up/down and the shared gate; the router
+scales: a one-hot per-element scale gives one column of R times x[n], a power-of-two scale
+multiplies the logits exactly, INT8 one-hot rows incl. code -128 give signed x values, the
+per-expert scale of a top-1 route is its weight and never changes the selection).
 """
 from __future__ import annotations
 
@@ -47,10 +58,14 @@ def sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def router_logits(router, x, router_is_bf16_bits: bool = True) -> np.ndarray:
-    """l[e] = sum_k R[e,k] x[k] in float64 (R given as bf16 bits, or as float values)."""
+def router_logits(router, x, router_is_bf16_bits: bool = True, elem_scale_bits=None) -> np.ndarray:
+    """l[e] = sum_n R[e,n] (s[n] x[n]) in float64 (R given as bf16 bits, or as values: fp32
+    weights or INT8 codes; s the bf16 per-element scale, ones when None)."""
     R = bf16_bits_to_f64(router) if router_is_bf16_bits else np.asarray(router, dtype=np.float64)
-    return R @ np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    if elem_scale_bits is not None:
+        x = bf16_bits_to_f64(elem_scale_bits) * x
+    return R @ x
 
 
 def select_topk(logits, k: int) -> np.ndarray:
@@ -84,16 +99,21 @@ def expert_down(expert, act) -> np.ndarray:
 
 
 def moe_decode(x, router_bits, sgate_bits, shared, experts, top_k: int,
-               fp16_boundary: bool = False, router_is_bf16_bits: bool = True):
+               fp16_boundary: bool = False, router_is_bf16_bits: bool = True, elem_scale_bits=None,
+               expert_scale=None):
     """Full MoE decode for one token.
 
     ``experts`` is indexable by expert id (a list, or a dict holding at least the
-    selected ids). Returns dict(out, ids, weights, logits, routed, shared_gated, gate).
+    selected ids). elem_scale_bits: bf16 [hidden] per-element router scale, expert_scale:
+    fp32 [E] per-expert weight scale (None: ones; the shared gate row takes neither).
+    Returns dict(out, ids, weights, logits, routed, shared_gated, gate).
     """
     x = np.asarray(x, dtype=np.float64)
-    logits = router_logits(router_bits, x, router_is_bf16_bits)
+    logits = router_logits(router_bits, x, router_is_bf16_bits, elem_scale_bits)
     ids = select_topk(logits, top_k)
     w = softmax_selected(logits, ids)
+    if expert_scale is not None:
+        w = w * np.asarray(expert_scale, dtype=np.float64)[ids]
     routed = np.zeros(shared["down"].q.shape[0], dtype=np.float64)
     for j, e in enumerate(ids):
         ex = experts[int(e)]
@@ -109,7 +129,8 @@ def moe_decode(x, router_bits, sgate_bits, shared, experts, top_k: int,
 
 
 def moe_prefill(X, router_bits, sgate_bits, shared, experts, top_k: int,
-                fp16_boundary: bool = False, router_is_bf16_bits: bool = True):
+                fp16_boundary: bool = False, router_is_bf16_bits: bool = True, elem_scale_bits=None,
+                expert_scale=None):
     """A chunk of M tokens through the routed MoE layer.
 
     "src/real_forward.rs", the forward state's switch for running a chunk's routed half as
@@ -118,7 +139,7 @@ def moe_prefill(X, router_bits, sgate_bits, shared, experts, top_k: int,
     each row of X independently. Returns dict(out [M, hidden], ids [M, k], weights [M, k]).
     """
     rows = [moe_decode(x, router_bits, sgate_bits, shared, experts, top_k, fp16_boundary,
-                       router_is_bf16_bits) for x in np.asarray(X)]
+                       router_is_bf16_bits, elem_scale_bits, expert_scale) for x in np.asarray(X)]
     return {"out": np.stack([r["out"] for r in rows]), "ids": np.stack([r["ids"] for r in rows]),
             "weights": np.stack([r["weights"] for r in rows]),
             "logits": np.stack([r["logits"] for r in rows])}

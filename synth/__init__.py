@@ -17,6 +17,9 @@ Value recipes (the decode runtime's synthetic workloads):
   * per-group scale: bf16(U(0.005, 0.02)); per-group bias: bf16(-8 * scale), which
     is exact because -8 is a power of two times -1
   * router rows and the shared-expert gate row: bf16(N(0, 0.02))
+  * INT8 router (the scaled-router variant): codes uniform on -127..127, per-element
+    scale bf16(2.7e-4 * U(0.5, 1.5)) (logits of about the bf16 router's spread),
+    per-expert scale fp32(U(0.5, 1.5))
   * hyper-connection norm weight: bf16(N(1, 0.02))
   * inject weights: fp32(U(0, 1))
 """
@@ -35,6 +38,7 @@ MOE_E256 = 2
 PREFILL_M128 = 3
 DECODE_LAYERS = 5
 LMHEAD_151936 = 4
+ROUTER_VARIANT = 6
 
 
 def rng_for(workload: int, seed: int = 0, *extra: int) -> np.random.Generator:
@@ -158,6 +162,16 @@ def moe_workload(seed: int = 0, hidden: int = 2560, inter: int = 512, n_experts:
     experts = [moe_expert(seed, e, hidden, inter) for e in range(n_experts)] if with_experts else None
     return {"x": x, "router_bits": router_bits, "sgate_bits": sgate_bits, "shared": shared,
             "experts": experts, "E": n_experts, "top_k": top_k, "hidden": hidden, "inter": inter}
+
+
+def router_variant(seed: int = 0, n_experts: int = 256, hidden: int = 2560) -> dict:
+    """The scaled router: INT8 codes [E x hidden], bf16 per-element scale bits [hidden] and
+    fp32 per-expert scales [E] (recipe in the module doc)."""
+    rng = rng_for(ROUTER_VARIANT, seed, n_experts, hidden)
+    codes = rng.integers(-127, 128, size=(n_experts, hidden)).astype(np.int8)
+    elem_scale_bits = to_bf16_bits(2.7e-4 * rng.uniform(0.5, 1.5, size=hidden))
+    expert_scale = rng.uniform(0.5, 1.5, size=n_experts).astype(np.float32)
+    return {"codes": codes, "elem_scale_bits": elem_scale_bits, "expert_scale": expert_scale}
 
 
 def moe_x_ring(seed: int, count: int, hidden: int = 2560) -> np.ndarray:

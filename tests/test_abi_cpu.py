@@ -124,7 +124,7 @@ def moe(top_k=2, flags=0, rdt=2, E=8, hidden=512, inter=64, ws=FAKE, wsb=1 << 20
 def test_moe_rejects_bad_calls():
     assert moe(x=0) == -1
     assert moe(top_k=0) == -2
-    assert moe(top_k=9) == -2
+    assert moe(top_k=11) == -2                 # at most DHP_MOE_MAX_TOP_K = 10 slots
     assert moe(top_k=8, E=4) == -2
     assert moe(rdt=0) == -2
     assert moe(flags=2) == -2
@@ -138,6 +138,43 @@ def test_moe_rejects_bad_calls():
     need = hca.workspace_bytes(hca.DHP_OP_MOE_DECODE, 8, 2, 64)
     assert need >= (8 + 3 * 64) * 4
     assert moe(wsb=need - 1) == -4
+
+
+def moe_ex(router=True, rdt=3, weights=FAKE, elem=None, escale=None, top_k=2, E=12, prefill=False):
+    L = hca.lib()
+    hidden, inter = 512, 64
+    g, u = experts(E, inter, hidden), experts(E, inter, hidden)
+    d = experts(E, hidden, inter)
+    sg, su, sd = int4(rows=inter, cols=hidden), int4(rows=inter, cols=hidden), int4(rows=hidden, cols=inter)
+    r = hca.CRouter(weights, rdt, elem, escale)
+    rp = ctypes.byref(r) if router else None
+    tail = (FAKE, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(sg), ctypes.byref(su),
+            ctypes.byref(sd), top_k, 0, FAKE, FAKE, FAKE, FAKE, 1 << 24, None)
+    if prefill:
+        return L.decodehp_moe_prefill_ex(FAKE, 4, rp, *tail)
+    return L.decodehp_moe_decode_ex(FAKE, rp, *tail)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_moe_ex_rejects_bad_routers(prefill):
+    assert moe_ex(router=False, prefill=prefill) == -1
+    assert moe_ex(weights=0, prefill=prefill) == -1
+    assert moe_ex(rdt=4, prefill=prefill) == -2
+    assert moe_ex(rdt=0, prefill=prefill) == -2            # fp16 routers are not a variant
+    assert moe_ex(weights=FAKE + 4, prefill=prefill) == -3  # int8 rows need 8-byte alignment
+    assert moe_ex(rdt=2, weights=FAKE + 8, prefill=prefill) == -3
+    assert moe_ex(elem=FAKE + 8, prefill=prefill) == -3
+    assert moe_ex(escale=FAKE + 2, prefill=prefill) == -3
+    assert moe_ex(top_k=11, prefill=prefill) == -2
+    assert moe_ex(top_k=11, E=10, prefill=prefill) == -2
+
+
+@pytest.mark.skipif(gpu_present(), reason="checks the no-device path")
+@pytest.mark.parametrize("prefill", [False, True])
+def test_moe_ex_valid_calls_reach_the_device_check(prefill):
+    assert moe_ex(weights=FAKE + 8, elem=FAKE, escale=FAKE + 4, top_k=10, prefill=prefill) == -5
+    assert moe_ex(rdt=1, top_k=10, E=10, prefill=prefill) == -5
+    assert moe(top_k=10, E=10) == -5
 
 
 def moe_prefill(m=4, top_k=2, flags=0, E=8, hidden=512, inter=64, ws=FAKE, wsb=1 << 24, x=FAKE, ids=FAKE):
@@ -154,7 +191,7 @@ def test_moe_prefill_rejects_bad_calls():
     assert moe_prefill(m=0) == -2
     assert moe_prefill(m=129) == -2
     assert moe_prefill(ids=0) == -1
-    assert moe_prefill(top_k=9) == -2
+    assert moe_prefill(top_k=11) == -2
     assert moe_prefill(flags=4) == -2
     assert moe_prefill(hidden=640) == -2
     assert moe_prefill(x=FAKE + 4) == -3
