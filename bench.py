@@ -59,6 +59,10 @@ def algorithmic_bytes():
                 + 2 * K + 2 * K + 8 * top_k)
     b["prefill"] = int4_bytes(8192, K) + 2 * 128 * K + 2 * 128 * 8192
     V = 151936
+    # the INT8-router variant at top-10: int8 router codes, bf16 per-element and fp32 per-expert
+    # scales, eleven experts (ten routed + the shared one)
+    b["moe_i8k10"] = (E * K + 2 * K + 4 * E + 2 * K + 11 * (2 * int4_bytes(inter, K) + int4_bytes(K, inter))
+                      + 2 * K + 2 * K + 8 * 10)
     b["lmhead1"] = int4_bytes(V, K) + 2 * K + 4 * V + 4
     b["lmhead8"] = int4_bytes(V, K) + 2 * 8 * K + 4 * 8 * V + 4 * 8
     # entry replication, the attn and mlp reads (with inject weights) and injects, the stand-in
@@ -76,9 +80,11 @@ def algorithmic_bytes():
 
 
 STEP_CALLS = ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8")
-# Timed per call but outside the step: a 128-token chunk through the same MoE layer, and one
-# token through a whole decoder layer plus the final mixer, as a launch sequence and as a graph.
-EXTRA_CALLS = ("moe_prefill", "hc_chunk", "layer_eager", "layer_graph")
+# Timed per call but outside the step: a 128-token chunk through the same MoE layer, the MoE
+# layer with the INT8 scaled router at top-10, the hyper-connection read and inject of a
+# 128-token chunk, and one token through a whole decoder layer plus the final mixer, as a
+# launch sequence and as a graph.
+EXTRA_CALLS = ("moe_prefill", "moe_i8k10", "hc_chunk", "layer_eager", "layer_graph")
 CALLS = STEP_CALLS + EXTRA_CALLS
 MOE_CHUNK = 128
 
@@ -125,7 +131,7 @@ def build_workload(torch, hca, synth, ring: int, only=None):
         W["hc_mixed"] = torch.empty(2560, dtype=torch.float16, device=dev)
         W["hc_iw"] = torch.empty(4, dtype=torch.float32, device=dev)
 
-    if want("moe", "moe_prefill"):
+    if want("moe", "moe_prefill", "moe_i8k10"):
         _moe_workload(torch, hca, synth, W, dev)
     if want("prefill"):
         p = synth.prefill_workload(0)
@@ -183,6 +189,12 @@ def _moe_workload(torch, hca, synth, W, dev):
     W["moe_out"] = torch.empty(2560, dtype=torch.float16, device=dev)
     W["moe_ids"] = torch.empty(8, dtype=torch.int32, device=dev)
     W["moe_w"] = torch.empty(8, dtype=torch.float32, device=dev)
+    v = synth.router_variant(0, 256, 2560)
+    W["moe"]["router_i8"] = hca.Router(torch.from_numpy(v["codes"]).to(dev),
+                                       hca.bf16_bits_to_tensor(v["elem_scale_bits"]).to(dev),
+                                       torch.from_numpy(v["expert_scale"]).to(dev))
+    W["moe_ids10"] = torch.empty(10, dtype=torch.int32, device=dev)
+    W["moe_w10"] = torch.empty(10, dtype=torch.float32, device=dev)
     W["moep_out"] = torch.empty((MOE_CHUNK, 2560), dtype=torch.float16, device=dev)
     W["moep_ids"] = torch.empty((MOE_CHUNK, 8), dtype=torch.int32, device=dev)
     W["moep_w"] = torch.empty((MOE_CHUNK, 8), dtype=torch.float32, device=dev)
@@ -229,6 +241,10 @@ def prepare_calls(hca, W, ring: int, only=None):
                                         W["moe"]["up"], W["moe"]["down"], W["moe"]["sg"], W["moe"]["su"],
                                         W["moe"]["sd"], 8, W["moe_out"], W["moe_ids"], W["moe_w"])
                         for t in range(W["moe_x"].shape[0])],
+        "moe_i8k10": lambda: [hca.prepare_moe(W["moe_x"][t], W["moe"]["router_i8"], W["moe"]["sgate"],
+                                              W["moe"]["gate"], W["moe"]["up"], W["moe"]["down"], W["moe"]["sg"],
+                                              W["moe"]["su"], W["moe"]["sd"], 10, W["moe_out"], W["moe_ids10"],
+                                              W["moe_w10"]) for t in range(W["moe_x"].shape[0])],
         "moe_prefill": lambda: [hca.prepare_moe_prefill(W["moe_x"], W["moe"]["router"], W["moe"]["sgate"],
                                                         W["moe"]["gate"], W["moe"]["up"], W["moe"]["down"],
                                                         W["moe"]["sg"], W["moe"]["su"], W["moe"]["sd"], 8,
@@ -466,7 +482,7 @@ def cpu_baseline(synth):
         oracle.argmax_lowest(y8)
         done += int4_bytes(LR, K) + 16 * K + 32 * LR
         reps += 1
-        if time.perf_counter() - t0 > 8.0 or reps >= 5:
+        if time.perf_counter() - t0 > 10.0 or reps >= 200:      # about 10 s of CPU work
             break
     dt = time.perf_counter() - t0
     return {"value": round(done / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
