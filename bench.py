@@ -21,7 +21,12 @@ Also printed in the same JSON line:
                 on the launch stream around that call in every timed step;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload (rank 0);
   calls         per-call microseconds and GB/s from a separate pass: batches of back-to-back
-                launches between fence-free HIP events (median over batches).
+                launches between fence-free HIP events (median over batches);
+  diagnostics   each call with a cold last-level cache (a 1 GiB read before every timed call;
+                median, p10, p90 of 50), the empty-kernel launch floor, the HBM read ceiling of
+                a plain streaming-read kernel, and the M=1 GEMV's GB/s against its row count.
+
+`--oracle-timing` instead times the fp64 oracle per workload on all cores and on one core.
 """
 from __future__ import annotations
 
@@ -395,6 +400,125 @@ def single_call_latency(torch, calls, names, reps: int = 30):
     return out
 
 
+FLUSH_BYTES = 1 << 30          # a read of 1 GiB (more than 4x the 256 MB last-level cache) evicts it
+
+
+def _stats(us):
+    us = np.asarray(us)
+    return {"us": round(float(np.median(us)), 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+            "p90_us": round(float(np.percentile(us, 90)), 2)}
+
+
+def cold_call_pass(torch, hca, calls, nbytes, flush, sink, reps: int = 50):
+    """Each call with a cold last-level cache: the read probe streams 1 GiB through the GPU before
+    every timed call, then fence-free events on the stream bracket the call alone. Median and
+    p10/p90 over `reps` calls (cycling each call's weight copies)."""
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, seq in calls.items():
+        run_call(seq[0])
+        evs = []
+        for i in range(reps):
+            hca.probe_read(flush, 2, 4, sink)
+            e0, e1 = HipEvent(), HipEvent()
+            e0.record(stream)
+            run_call(seq[i % len(seq)])
+            e1.record(stream)
+            evs.append((e0, e1))
+        st = _stats([a.us_until(b) for a, b in evs])
+        out[name] = {**st, "GBps": round(nbytes[name] / st["us"] / 1e3, 1),
+                     "pct_hbm_peak": round(100.0 * nbytes[name] / st["us"] / 1e3 / HBM_PEAK_GBS, 1)}
+    return out
+
+
+def launch_floor(torch, hca, n: int = 200, reps: int = 30):
+    """The empty kernel: n launches back to back from one library call (no host work between
+    them) between two events, the same n launched one library call each from Python (what the
+    per-call pass pays per launch), and one launch onto an idle GPU (median over reps)."""
+    stream = torch.cuda.current_stream()
+    hca.probe_empty(10)
+    torch.cuda.synchronize()
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record(stream)
+    hca.probe_empty(n)
+    e1.record(stream)
+    b2b = e0.us_until(e1) / n
+    torch.cuda.synchronize()
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record(stream)
+    for _ in range(n):
+        hca.probe_empty()
+    e1.record(stream)
+    py = e0.us_until(e1) / n
+    single = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        a, b = HipEvent(), HipEvent()
+        a.record(stream)
+        hca.probe_empty()
+        b.record(stream)
+        single.append(a.us_until(b))
+    return {"back_to_back_us": round(b2b, 2), "one_python_call_each_us": round(py, 2),
+            "single_idle_us": round(float(np.median(single)), 2)}
+
+
+def read_ceiling(torch, hca, flush, sink, target_bytes: int = 219400704, reps: int = 5):
+    """The read probe over a 1 GiB buffer (larger than the last-level cache, so every pass reads
+    HBM) for a grid of (blocks per CU, loads in flight per lane), and the best arrangement over a
+    buffer of the M=1 LM head's size, flushed before each pass."""
+    stream = torch.cuda.current_stream()
+    grid = {}
+    for bpc in (1, 2, 4, 8):
+        for u in (2, 4, 8):
+            hca.probe_read(flush, bpc, u, sink)
+            e0, e1 = HipEvent(), HipEvent()
+            e0.record(stream)
+            for _ in range(reps):
+                hca.probe_read(flush, bpc, u, sink)
+            e1.record(stream)
+            grid[f"{bpc}x{u}"] = round(FLUSH_BYTES * reps / e0.us_until(e1) / 1e3, 1)
+    best = max(grid, key=grid.get)
+    bpc, u = (int(v) for v in best.split("x"))
+    target = torch.empty(target_bytes, dtype=torch.uint8, device="cuda")
+    us = []
+    for _ in range(reps * 4):
+        hca.probe_read(flush, 2, 4, sink)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(stream)
+        hca.probe_read(target, bpc, u, sink)
+        e1.record(stream)
+        us.append(e0.us_until(e1))
+    t = float(np.median(us))
+    return {"GBps_1GiB": grid, "best": best, "GBps_best_1GiB": grid[best],
+            "GBps_lmhead_size_cold": round(target_bytes / t / 1e3, 1), "lmhead_size_us": round(t, 2)}
+
+
+def rows_sweep(torch, hca, W, flush, sink, reps: int = 20):
+    """M=1 GEMV (fp16 out, no argmax) over the first N rows of the LM-head weight, K = 2560, each
+    call after a cache flush: GB/s of algorithmic bytes against N."""
+    stream = torch.cuda.current_stream()
+    w = W["lm_w"][0]
+    x = W["lm_x1"]
+    y = torch.empty(w.rows, dtype=torch.float16, device="cuda")
+    out = {}
+    for n in (2560, 8192, 32768, 65536, 151936):
+        wn = hca.Int4Weight(w.codes[:n], w.scales[:n], w.biases[:n], n, w.cols)
+        c = hca.prepare_gemv(wn, x, y[:n])
+        c()
+        us = []
+        for _ in range(reps):
+            hca.probe_read(flush, 2, 4, sink)
+            e0, e1 = HipEvent(), HipEvent()
+            e0.record(stream)
+            c()
+            e1.record(stream)
+            us.append(e0.us_until(e1))
+        t = float(np.median(us))
+        b = int4_bytes(n, 2560) + 2 * 2560 + 2 * n
+        out[str(n)] = {"us": round(t, 2), "GBps": round(b / t / 1e3, 1)}
+    return out
+
+
 def copy_probe(torch):
     """A plain 1 GiB device copy, for scaling the HBM byte counters (FETCH_SIZE / WRITE_SIZE)."""
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -492,6 +616,58 @@ def cpu_baseline(synth):
             "seconds": round(dt, 2)}
 
 
+def oracle_config_timing(synth, reps: int = 3):
+    """The fp64 oracle per workload, generation excluded: median wall time of `reps` runs in this
+    process (whatever BLAS/OpenMP threads it has)."""
+    import oracle
+    g = synth.gemv_workload(0)
+    h = synth.hc_workload(0)
+    m = synth.moe_workload(0, with_experts=False)
+    ids = oracle.select_topk(oracle.router_logits(m["router_bits"], m["x"]), 8)
+    experts = {int(e): synth.moe_expert(0, int(e)) for e in ids}
+    p = synth.prefill_workload(0)
+    lw = synth.lmhead_workload(0, m=1)
+    x8 = synth.lmhead_x(0, 8)
+    work = {
+        "gemv_2560": lambda: oracle.dequant_gemv(g["w"].q, g["w"].s_bits, g["w"].b_bits, g["x"]),
+        "hc_read_inject": lambda: oracle.hc_inject(
+            h["raw"], h["out"],
+            oracle.hc_read(h["raw"], h["gamma_bits"], h["down"], h["up"], h["inject"], 4, 2560)["inject_w"], 4, 2560),
+        "moe_decode": lambda: oracle.moe_decode(m["x"], m["router_bits"], m["sgate_bits"], m["shared"], experts, 8),
+        "prefill_m128": lambda: oracle.dequant_gemv(p["w"].q, p["w"].s_bits, p["w"].b_bits, p["x"]),
+        "lmhead_m1": lambda: oracle.argmax_lowest(oracle.dequant_gemv(lw["w"].q, lw["w"].s_bits, lw["w"].b_bits,
+                                                                       lw["x"][0])),
+        "lmhead_m8": lambda: oracle.argmax_lowest(oracle.dequant_gemv(lw["w"].q, lw["w"].s_bits, lw["w"].b_bits, x8)),
+    }
+    out = {}
+    for name, f in work.items():
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        out[name] = round(float(np.median(ts)), 4)
+    return out
+
+
+def oracle_timing(synth):
+    """Per-workload oracle seconds on every core visible to the process, then again in a child
+    process limited to one BLAS/OpenMP thread."""
+    import subprocess
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    except Exception:
+        blas = None
+    allc = oracle_config_timing(synth)
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-timing-child"], env=env,
+                       capture_output=True, text=True, check=True)
+    one = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "blas": blas, "seconds_all_cores": allc,
+            "seconds_one_core": one, "reps": 3, "note": "median of 3, input generation excluded"}
+
+
 def traffic_from_profile():
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -520,11 +696,19 @@ def main():
                     help="launch just this call (or the plain 1 GiB copy) --steps times after --warmup, and "
                          "print its timing; for profiler runs")
     ap.add_argument("--summarize", metavar="DIR", help="print per-kernel figures from rocprofv3 output in DIR")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="time the fp64 oracle per workload on all cores and on one core (CPU only), print JSON")
+    ap.add_argument("--oracle-timing-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--filter", default="", help="kernel-name substring for --summarize")
     args = ap.parse_args()
 
     if args.summarize:
         print(json.dumps(summarize_profile(args.summarize, args.filter), indent=1))
+        return
+    if args.oracle_timing or args.oracle_timing_child:
+        import synth
+        r = oracle_config_timing(synth) if args.oracle_timing_child else oracle_timing(synth)
+        print(json.dumps(r), flush=True)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -596,6 +780,15 @@ def main():
     if per_call is not None:
         for name, us in single_call_latency(torch, calls, ("layer_eager", "layer_graph")).items():
             per_call[name]["single_call_us"] = us
+    diag = None
+    if not args.no_per_call:
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        sink = torch.empty(16 * 1024, dtype=torch.int32, device="cuda")
+        diag = {"calls_cold": cold_call_pass(torch, hca, calls, nbytes, flush, sink),
+                "launch_floor": launch_floor(torch, hca),
+                "read_ceiling": read_ceiling(torch, hca, flush, sink),
+                "gemv_rows_sweep_cold": rows_sweep(torch, hca, W, flush, sink)}
+        del flush
     probe = copy_probe(torch) if args.copy_probe else None
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(synth)
@@ -614,6 +807,8 @@ def main():
         "cpu_baseline": cpu,
         "calls": per_call,
     }
+    if diag:
+        line["diagnostics"] = diag
     if probe:
         line["copy_probe"] = probe
     print(json.dumps(line), flush=True)

@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.decodehp_hc_read_batched_workspace_bytes.restype = sz
         L.decodehp_hc_inject_batched.argtypes = [vp, i32, vp, vp, i32, i32, vp]
         L.decodehp_hc_inject.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.decodehp_probe_empty.argtypes = [i32, vp]
+        L.decodehp_probe_read.argtypes = [vp, sz, i32, i32, vp, i32, vp]
         L.decodehp_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.decodehp_workspace_bytes.restype = sz
         L.decodehp_last_error.restype = ctypes.c_char_p
@@ -394,6 +396,26 @@ def hc_inject(wide, out, inject_w, C: int, H: int, stream=None):
     _need(inject_w, torch.float32, "inject_w", C)
     _check(lib().decodehp_hc_inject(wide.data_ptr(), out.data_ptr(), inject_w.data_ptr(), C, H, _stream(stream)))
     return wide
+
+
+# --------------------------------------------------------------------------- measurement probes
+
+def probe_empty(count: int = 1, stream=None):
+    """Launch `count` kernels that do nothing, back to back (the per-launch floor)."""
+    _check(lib().decodehp_probe_empty(count, _stream(stream)))
+
+
+def probe_read(buf, blocks_per_cu: int = 2, loads_in_flight: int = 4, sink=None, stream=None):
+    """Stream the device tensor `buf` once (16-byte nontemporal loads); returns the sink tensor."""
+    torch = _torch()
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(16 * 1024, dtype=torch.int32, device=buf.device)
+    _check(lib().decodehp_probe_read(buf.data_ptr(), nbytes, blocks_per_cu, loads_in_flight, sink.data_ptr(),
+                                     sink.numel(), _stream(stream)))
+    return sink
 
 
 # --------------------------------------------------------------------------- prepared calls

@@ -100,7 +100,7 @@ extern "C" {
 
 const char* decodehp_last_error(void) { return g_err; }
 
-int32_t decodehp_version(void) { return (0 << 16) | 3; }
+int32_t decodehp_version(void) { return (0 << 16) | 4; }
 
 size_t decodehp_workspace_bytes(int32_t op, int32_t a, int32_t b, int32_t c) {
     switch (op) {

@@ -334,6 +334,26 @@ int decodehp_graph_capture_decode_layers(const void* x, int32_t C, int32_t H, fl
 int decodehp_graph_launch(const dhp_graph* graph, void* stream);
 void decodehp_graph_destroy(dhp_graph* graph);
 
+/*
+ * Measurement probes (not steps of the decode path): the launch floor and the HBM read
+ * ceiling the decode kernels are measured against.
+ *
+ * decodehp_probe_empty -- launches `count` (1..100000) kernels that do nothing, back to back
+ * on the stream. Errors: -2 count, -5, -6.
+ *
+ * decodehp_probe_read -- reads `bytes` of `buf` once with 16-byte nontemporal loads:
+ * blocks_per_cu * (compute units) blocks of 256 threads in a grid stride, loads_in_flight
+ * (1, 2, 4 or 8) loads per lane issued together. Block b writes the XOR of the words its
+ * lanes read to sink[b] (so that no load can be dropped); the value means nothing else.
+ *   buf : device memory, 16-byte aligned, bytes a multiple of 16.   sink : uint32 [sink_words],
+ *   at least blocks_per_cu * compute units words.
+ * Errors: -1 null buf/sink or zero bytes, -2 blocks_per_cu outside 1..16 or loads_in_flight,
+ *         -3 alignment, -4 sink too small, -5, -6.
+ */
+int decodehp_probe_empty(int32_t count, void* stream);
+int decodehp_probe_read(const void* buf, size_t bytes, int32_t blocks_per_cu, int32_t loads_in_flight,
+                        uint32_t* sink, int32_t sink_words, void* stream);
+
 /* Workspace bytes an entry point needs (0 when none). Pure host arithmetic. */
 size_t decodehp_workspace_bytes(int32_t op, int32_t a, int32_t b, int32_t c);
 

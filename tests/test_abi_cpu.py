@@ -282,3 +282,14 @@ def test_hc_batched_rejects_bad_calls():
     assert f(wsb=need - 1) == -4
     g = lambda m=8, wide=FAKE: L.decodehp_hc_inject_batched(wide, m, FAKE, FAKE, C, H, None)
     assert g(m=0) == -2 and g(wide=None) == -1 and g(wide=FAKE + 8) == -3
+
+
+def test_probe_read_rejects_bad_calls():
+    L = hca.lib()
+    assert L.decodehp_probe_read(0, 1 << 20, 2, 4, FAKE, 4096, None) == -1
+    assert L.decodehp_probe_read(FAKE, 0, 2, 4, FAKE, 4096, None) == -1
+    assert L.decodehp_probe_read(FAKE, (1 << 20) + 8, 2, 4, FAKE, 4096, None) == -3
+    assert L.decodehp_probe_read(FAKE + 8, 1 << 20, 2, 4, FAKE, 4096, None) == -3
+    assert L.decodehp_probe_read(FAKE, 1 << 20, 0, 4, FAKE, 4096, None) == -2
+    assert L.decodehp_probe_read(FAKE, 1 << 20, 17, 4, FAKE, 4096, None) == -2
+    assert L.decodehp_probe_read(FAKE, 1 << 20, 2, 3, FAKE, 4096, None) == -2
