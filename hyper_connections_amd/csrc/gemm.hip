@@ -401,11 +401,14 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     float* pv = argmax ? static_cast<float*>(ws) : nullptr;
     int* pi = argmax ? reinterpret_cast<int*>(static_cast<char*>(ws) + ws_part_stride) : nullptr;
     if (argmax && grid.y != 1) return dhp_fail(DHP_ERR_UNSUPPORTED, "argmax with m=%d", M);
-    // eight waves of 64-k stages (two per SIMD) with two stages in flight per wave
+    // 64-k stages with two in flight per wave; eight waves for up to 32 rows, four for 64-row
+    // tiles (with eight, the 64-row tile keeps ~160 KB of loads in flight per CU and measured
+    // slower: 16.6 against 16.1 us for M=128, N=8192, K=2560, and 40.9 against 38.4 us for the
+    // hyper-connection chunk, whose K = 320 gives eight waves only five stages to share)
     const bool am = argmax != nullptr;
     const int KB = w->cols / 64;
     const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB)
-                                   : launch_mt<2, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB);
+                                   : launch_mt<2, 1, 4>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
     if (argmax) {
         const hipError_t e2 = launch_argmax_final(pv, pi, (int)grid.x, M, argmax, s);

@@ -36,7 +36,8 @@ def test_prefill_workload_m128():
 
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (2, 48, 128), (5, 80, 320), (31, 64, 2560), (32, 1024, 2560),
                                    (33, 64, 192), (64, 1040, 512), (100, 256, 2560), (128, 16, 64),
-                                   (128, 4096, 4096), (7, 160, 10240)])
+                                   (128, 4096, 4096), (7, 160, 10240), (3, 48, 32768), (65, 80, 16384),
+                                   (127, 208, 1216)])
 def test_batched_shapes(m, n, k):
     say(f"batched m={m} n={n} k={k}")
     rng = np.random.default_rng([71, m, n, k])

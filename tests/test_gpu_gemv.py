@@ -34,7 +34,8 @@ def test_gemv_workload_2560():
 
 
 @pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (17, 192), (33, 512), (100, 2560), (1000, 4096),
-                                 (37, 640), (5, 10240), (4099, 1024), (257, 3072), (16, 2048), (2, 8192)])
+                                 (37, 640), (5, 10240), (4099, 1024), (257, 3072), (16, 2048), (2, 8192),
+                                 (7, 16384), (3, 16320)])
 def test_gemv_shapes_and_ragged_tails(n, k):
     say(f"gemv n={n} k={k}")
     rng = np.random.default_rng([99, n, k])
