@@ -225,15 +225,19 @@ class Int4Experts:
 _ws_cache = {}
 
 
-def _workspace(nbytes: int, device, kind: str = "scratch"):
-    """Per (device, stream, kind) workspace, grown on demand."""
+def _workspace(nbytes: int, device, kind: str = "scratch", stream=None):
+    """Per (device, stream, kind) workspace, grown on demand. It is allocated on the stream the
+    call runs on, so that when a grown workspace replaces it, torch's caching allocator hands the
+    old memory only to later work on that same stream."""
     torch = _torch()
     if nbytes == 0:
         return None
-    key = (str(device), torch.cuda.current_stream(device).cuda_stream, kind)
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (str(device), s.cuda_stream, kind)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
@@ -251,7 +255,7 @@ def dequant_gemv(w: Int4Weight, x, y=None, out_dtype=None, argmax=False, stream=
         y = torch.empty((m, w.rows), dtype=out_dtype, device=x.device)
     _need(y, out_dtype, "y", m * w.rows)
     am = torch.empty(m, dtype=torch.int32, device=x.device) if argmax else None
-    ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device, "argmax") if argmax else None
+    ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device, "argmax", stream=stream) if argmax else None
     d = w.desc()
     _check(lib().decodehp_dequant_gemv(ctypes.byref(d), x2.data_ptr(), m, y.data_ptr(),
                                        DHP_F32 if out_dtype == torch.float32 else DHP_F16,
@@ -323,9 +327,9 @@ def _moe_args(x, m, router, shared_gate_row, gate, up, down, shared_gate, shared
     _need(ids, torch.int32, "ids", rows * top_k)
     _need(weights, torch.float32, "weights", rows * top_k)
     if m is None:
-        ws = _workspace(workspace_bytes(DHP_OP_MOE_DECODE, gate.count, top_k, gate.rows), x.device)
+        ws = _workspace(workspace_bytes(DHP_OP_MOE_DECODE, gate.count, top_k, gate.rows), x.device, stream=stream)
     else:
-        ws = _workspace(moe_prefill_workspace_bytes(m, gate.count, top_k, gate.rows, hidden), x.device, "moe_prefill")
+        ws = _workspace(moe_prefill_workspace_bytes(m, gate.count, top_k, gate.rows, hidden), x.device, "moe_prefill", stream=stream)
     descs = (gate.desc(), up.desc(), down.desc(), shared_gate.desc(), shared_up.desc(), shared_down.desc())
     if isinstance(router, Router):
         rd = router.desc(gate.count, hidden)
@@ -378,7 +382,7 @@ def hc_read(raw, hc_norm, C: int, H: int, down: Int4Weight, up: Int4Weight, inje
         inject_w = torch.empty(C, dtype=torch.float32, device=dev)
     if inject_w is not None:
         _need(inject_w, torch.float32, "inject_w", C)
-    ws = _workspace(workspace_bytes(DHP_OP_HC_READ, C, down.rows), dev)
+    ws = _workspace(workspace_bytes(DHP_OP_HC_READ, C, down.rows), dev, stream=stream)
     dd, ud = down.desc(), up.desc()
     idesc = inject.desc() if inject is not None else None
     _check(lib().decodehp_hc_read(raw.data_ptr(), hc_norm.data_ptr(), C, H, eps, ctypes.byref(dd),
@@ -451,7 +455,7 @@ def _hcb_args(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps, stream
     _need(mixed, torch.float16, "mixed", m * H)
     if inject_w is not None:
         _need(inject_w, torch.float32, "inject_w", m * C)
-    ws = _workspace(int(lib().decodehp_hc_read_batched_workspace_bytes(m, C, H, down.rows)), raw.device, "hc_batched")
+    ws = _workspace(int(lib().decodehp_hc_read_batched_workspace_bytes(m, C, H, down.rows)), raw.device, "hc_batched", stream=stream)
     descs = (down.desc(), up.desc(), inject.desc() if inject is not None else None)
     args = (raw.data_ptr(), m, hc_norm.data_ptr(), C, H, eps, ctypes.byref(descs[0]), ctypes.byref(descs[1]),
             ctypes.byref(descs[2]) if descs[2] is not None else None, mixed.data_ptr(), _ptr(inject_w), _ptr(ws),
@@ -532,7 +536,7 @@ class DecodeLayer:
                             DHP_MOE_FP16_BOUNDARY if self.fp16_boundary else 0)
 
 
-def _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps):
+def _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps, stream=None, private_ws=False):
     torch = _torch()
     _need(x, torch.float16, "x", H)
     _need(hidden, torch.float16, "hidden", C * H)
@@ -543,7 +547,10 @@ def _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps):
     nbytes = int(lib().decodehp_decode_layers_workspace_bytes(C, H, arr, len(layers), ctypes.byref(mix)))
     if nbytes == 0:
         raise DecodeHPError(-1, "null or inconsistent layer descriptors")
-    ws = _workspace(nbytes, x.device, "layers")
+    if private_ws:     # a captured graph pins its workspace for its lifetime: never shared
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    else:
+        ws = _workspace(nbytes, x.device, "layers", stream=stream)
     keep.extend([arr, mix, ws, layers, mixer, x, hidden, mixed_out])
     return (x.data_ptr(), C, H, eps, arr, len(layers), ctypes.byref(mix), hidden.data_ptr(), mixed_out.data_ptr(),
             ws.data_ptr(), ws.numel()), keep
@@ -555,14 +562,14 @@ def decode_layers(x, C: int, H: int, layers, mixer: HcBlock, hidden=None, mixed_
     torch = _torch()
     hidden = torch.empty(C * H, dtype=torch.float16, device=x.device) if hidden is None else hidden
     mixed_out = torch.empty(H, dtype=torch.float16, device=x.device) if mixed_out is None else mixed_out
-    args, _keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps)
+    args, _keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps, stream=stream)
     _check(lib().decodehp_decode_layers(*args, _stream(stream)))
     return hidden, mixed_out
 
 
 def prepare_decode_layers(x, C: int, H: int, layers, mixer: HcBlock, hidden, mixed_out, eps=1e-6,
                           stream=None) -> PreparedCall:
-    args, keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps)
+    args, keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps, stream=stream)
     return PreparedCall(lib().decodehp_decode_layers, (*args, _stream(stream)), keep)
 
 
@@ -572,7 +579,7 @@ class LayerGraph:
     write the next token into x first."""
 
     def __init__(self, x, C: int, H: int, layers, mixer: HcBlock, hidden, mixed_out, eps=1e-6):
-        args, self._keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps)
+        args, self._keep = _layer_args(x, C, H, layers, mixer, hidden, mixed_out, eps, private_ws=True)
         self._g = ctypes.c_void_p()
         _check(lib().decodehp_graph_capture_decode_layers(*args, ctypes.byref(self._g)))
         self.x, self.hidden, self.mixed = x, hidden, mixed_out
@@ -608,7 +615,7 @@ def prepare_gemv(w: Int4Weight, x, y, argmax=None, stream=None) -> PreparedCall:
     m = x2.shape[0]
     _need(x2, torch.float16, "x")
     _need(y, y.dtype, "y", m * w.rows)
-    ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device, "argmax") if argmax is not None else None
+    ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device, "argmax", stream=stream) if argmax is not None else None
     d = w.desc()
     args = (ctypes.byref(d), x2.data_ptr(), m, y.data_ptr(), DHP_F32 if y.dtype == torch.float32 else DHP_F16,
             _ptr(argmax), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
@@ -639,7 +646,7 @@ def prepare_moe_prefill(x, router, shared_gate_row, gate, up, down, shared_gate,
 
 
 def prepare_hc_read(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps=1e-6, stream=None) -> PreparedCall:
-    ws = _workspace(workspace_bytes(DHP_OP_HC_READ, C, down.rows), raw.device)
+    ws = _workspace(workspace_bytes(DHP_OP_HC_READ, C, down.rows), raw.device, stream=stream)
     descs = (down.desc(), up.desc(), inject.desc() if inject is not None else None)
     args = (raw.data_ptr(), hc_norm.data_ptr(), C, H, eps, ctypes.byref(descs[0]), ctypes.byref(descs[1]),
             ctypes.byref(descs[2]) if descs[2] is not None else None, mixed.data_ptr(), _ptr(inject_w), _ptr(ws),
