@@ -46,24 +46,26 @@ HcbWs hcb_ws(int m, int C, int H, int R) {
     return w;
 }
 
-// One block per (token, stream): H / 8 eight-element chunks, all loaded before the reduction.
+// One block per (token, stream): H / 8 eight-element chunks, NCH per thread, all loaded before
+// the reduction (NCH = ceil(H / 2048): two for H = 2560).
 constexpr int NORM_MAX_CHUNKS = 16;         // per thread: H <= 256 * 8 * 16 = 32768
+template <int NCH>
 __global__ __launch_bounds__(256) void k_hcb_norm(const _Float16* __restrict__ raw, const uint16_t* __restrict__ gamma,
                                                   _Float16* __restrict__ normed, int C, int H, float eps) {
     __shared__ float wsum[4];
     const int m = blockIdx.x, c = blockIdx.y;
     const size_t base = ((size_t)m * C + c) * H;           // row m, stream c
     const int n8 = H >> 3;
-    u32x4 v[NORM_MAX_CHUNKS], g[NORM_MAX_CHUNKS];
+    u32x4 v[NCH], g[NCH];
 #pragma unroll
-    for (int k = 0; k < NORM_MAX_CHUNKS; ++k) {
+    for (int k = 0; k < NCH; ++k) {
         const int i = min((int)threadIdx.x + 256 * k, n8 - 1);
         v[k] = *reinterpret_cast<const u32x4*>(raw + base + 8 * i);
         g[k] = *reinterpret_cast<const u32x4*>(gamma + (size_t)c * H + 8 * i);
     }
     float ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NORM_MAX_CHUNKS; ++k) {
+    for (int k = 0; k < NCH; ++k) {
         if ((int)threadIdx.x + 256 * k < n8) {
             const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(256) void k_hcb_norm(const _Float16* __restrict__ r
     __syncthreads();
     const float inv = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)H + eps);
 #pragma unroll
-    for (int k = 0; k < NORM_MAX_CHUNKS; ++k) {
+    for (int k = 0; k < NCH; ++k) {
         const int i = (int)threadIdx.x + 256 * k;
         if (i < n8) {
             const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
@@ -149,6 +151,24 @@ __global__ __launch_bounds__(256) void k_hcb_inject(_Float16* __restrict__ wide,
     *reinterpret_cast<u32x4*>(wp) = u32x4{r[0], r[1], r[2], r[3]};
 }
 
+template <int NCH>
+void launch_norm_n(dim3 g, hipStream_t s, const _Float16* raw, const uint16_t* gamma, _Float16* normed, int C, int H,
+                   float eps) {
+    hipLaunchKernelGGL(k_hcb_norm<NCH>, g, dim3(256), 0, s, raw, gamma, normed, C, H, eps);
+}
+
+void launch_norm(dim3 g, hipStream_t s, const _Float16* raw, const uint16_t* gamma, _Float16* normed, int C, int H,
+                 float eps) {
+    switch ((H / 8 + 255) / 256) {
+        case 1: launch_norm_n<1>(g, s, raw, gamma, normed, C, H, eps); break;
+        case 2: launch_norm_n<2>(g, s, raw, gamma, normed, C, H, eps); break;
+        case 3: launch_norm_n<3>(g, s, raw, gamma, normed, C, H, eps); break;
+        case 4: launch_norm_n<4>(g, s, raw, gamma, normed, C, H, eps); break;
+        case 5: case 6: case 7: case 8: launch_norm_n<8>(g, s, raw, gamma, normed, C, H, eps); break;
+        default: launch_norm_n<NORM_MAX_CHUNKS>(g, s, raw, gamma, normed, C, H, eps); break;
+    }
+}
+
 int launch_status(const char* what) {
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? DHP_OK : dhp_fail(DHP_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
@@ -170,8 +190,8 @@ int launch_hc_read_batched(const void* raw, int m, const void* gamma, int C, int
     float* ipre = reinterpret_cast<float*>(b + lay.ipre);
     float* upre = reinterpret_cast<float*>(b + lay.upre);
 
-    hipLaunchKernelGGL(k_hcb_norm, dim3(m, C), dim3(256), 0, s, static_cast<const _Float16*>(raw),
-                       static_cast<const uint16_t*>(gamma), normed, C, H, eps);
+    launch_norm(dim3(m, C), s, static_cast<const _Float16*>(raw), static_cast<const uint16_t*>(gamma), normed, C, H,
+                eps);
     int rc = launch_status("hc norm");
     if (!rc) rc = launch_gemm_mfma_splitk(down, normed, m, lo_pre, KSPLIT, s);
     if (!rc && inject) rc = launch_gemm_mfma_splitk(inject, normed, m, ipre, KSPLIT, s);
