@@ -117,7 +117,9 @@ __global__ __launch_bounds__(HC_MAX_THREADS) void k_hc_down(
 }
 
 // 16 lanes per output h; LPRU = 16 / C lanes per stream row.
-template <int C>
+// NCH: chunks per lane, ceil((R / 32) / (16 / C)) rounded up to a power of two (4 at R = 320,
+// C = 4); more would only issue clamped loads of chunks past the row and hold their registers.
+template <int C, int NCH>
 __global__ __launch_bounds__(UP_THREADS) void k_hc_up(
     const _Float16* __restrict__ raw, const uint16_t* __restrict__ gamma, int H,
     const u32x4* __restrict__ ucodes, const uint16_t* __restrict__ uscales,
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(UP_THREADS) void k_hc_up(
     const float* __restrict__ inv_rms, _Float16* __restrict__ mixed) {
     constexpr int LPRU = 16 / C;
     extern __shared__ float lds_lo[];     // [R/32][LO_PITCH]: 32-float chunks, bank-staggered
-    constexpr int MAXCH = 32 / LPRU;      // chunks per lane at the largest R (1024)
+    constexpr int MAXCH = NCH;
     const int CHR = R >> 5;
     const int G = R >> 6;
 
@@ -216,6 +218,20 @@ __global__ __launch_bounds__(256) void k_hc_inject(_Float16* __restrict__ wide,
     *reinterpret_cast<u32x4*>(wide + e0) = a;
 }
 
+template <int C>
+void launch_up(dim3 g, int block, size_t lds, hipStream_t s, const _Float16* rw, const uint16_t* gm, int H,
+               const u32x4* uc, const uint16_t* us, const uint16_t* ub, int R, const float* lo, const float* inv_rms,
+               _Float16* mx) {
+    constexpr int LPRU = 16 / C;
+    const int need = ((R >> 5) + LPRU - 1) / LPRU;
+    if (need <= 1) hipLaunchKernelGGL((k_hc_up<C, 1>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
+    else if (need <= 2) hipLaunchKernelGGL((k_hc_up<C, 2>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
+    else if (need <= 4) hipLaunchKernelGGL((k_hc_up<C, 4>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
+    else if (need <= 8) hipLaunchKernelGGL((k_hc_up<C, (8 < 32 / LPRU ? 8 : 32 / LPRU)>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
+    else if (need <= 16) hipLaunchKernelGGL((k_hc_up<C, (16 < 32 / LPRU ? 16 : 32 / LPRU)>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
+    else hipLaunchKernelGGL((k_hc_up<C, 32 / LPRU>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
+}
+
 }  // namespace
 
 size_t dhp_hc_ws(int32_t C, int32_t R) {
@@ -253,11 +269,11 @@ int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, 
     const auto* ub = static_cast<const uint16_t*>(up->biases);
     auto* mx = static_cast<_Float16*>(mixed);
     switch (C) {
-        case 1: hipLaunchKernelGGL(k_hc_up<1>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
-        case 2: hipLaunchKernelGGL(k_hc_up<2>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
-        case 4: hipLaunchKernelGGL(k_hc_up<4>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
-        case 8: hipLaunchKernelGGL(k_hc_up<8>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
-        case 16: hipLaunchKernelGGL(k_hc_up<16>, g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 1: launch_up<1>(g, block, lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 2: launch_up<2>(g, block, lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 4: launch_up<4>(g, block, lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 8: launch_up<8>(g, block, lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
+        case 16: launch_up<16>(g, block, lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx); break;
         default: return dhp_fail(DHP_ERR_UNSUPPORTED, "C=%d", C);
     }
     e = hipGetLastError();
