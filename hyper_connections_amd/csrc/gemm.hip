@@ -202,7 +202,7 @@ DHP_DEV void stage_mfma(const uint8_t* lds, int li, int g, f16x16 (*acc)[2], con
     }
 }
 
-template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX>
+template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ X, int M, int N, int K,
@@ -242,9 +242,24 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     if (has) {
         stage_plan<MT, S>(plan, lane, codes, scales, biases, X, n0, N, m0, xrows, K, KB);
         stage_load<MT, S>(r0, plan, st0 * S, kb1);
-        stage_load<MT, S>(r1, plan, (st0 + 1) * S, kb1);
+        if constexpr (DEPTH == 2) stage_load<MT, S>(r1, plan, (st0 + 1) * S, kb1);
     }
-    if (has) {
+    if (DEPTH == 1 && has) {
+        // one register set: the next stage is in flight while this one computes
+        const NibConsts nk = nib_consts();
+        int st = st0;
+        for (; st + 1 < st1; ++st) {
+            stage_store<MT, S>(r0, plan, lds, lane, kb1);
+            __builtin_amdgcn_wave_barrier();
+            stage_load<MT, S>(r0, plan, (st + 1) * S, kb1);
+            stage_mfma<MT, S>(lds, li, g, acc, nk);
+            __builtin_amdgcn_wave_barrier();
+        }
+        stage_store<MT, S>(r0, plan, lds, lane, kb1);
+        __builtin_amdgcn_wave_barrier();
+        stage_mfma<MT, S>(lds, li, g, acc, nk);
+    }
+    if (DEPTH == 2 && has) {
         const NibConsts nk = nib_consts();
         // The steady-state loop has no branch around a load (the compiler then waits for exactly
         // the set it is about to park): the stage count is padded to even (the padding stage's
@@ -350,7 +365,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     }
 }
 
-template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX>
+template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH>
 hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t* sc, const uint16_t* bi,
                       const _Float16* xh, int M, int N, int K, void* y, float* pv, int* pi, int kb_split) {
     using L = WaveLds<MT, S>;
@@ -363,17 +378,17 @@ hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t
     const unsigned long long bit = 1ull << (dev & 63);
     if (!(__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & bit)) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX>),
+            reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         __atomic_fetch_or(&configured, bit, __ATOMIC_RELEASE);
     }
-    hipLaunchKernelGGL((k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX>), grid, dim3(64 * WAVES), lds, s, c, sc, bi, xh, M,
+    hipLaunchKernelGGL((k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH>), grid, dim3(64 * WAVES), lds, s, c, sc, bi, xh, M,
                        N, K, y, pv, pi, kb_split);
     return hipGetLastError();
 }
 
-template <int MT, int S, int WAVES>
+template <int MT, int S, int WAVES, int DEPTH = 2>
 hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4* w, const void* x,
                      int M, void* y, float* pv, int* pi, int kb_split) {
     const auto* c = static_cast<const uint8_t*>(w->codes);
@@ -381,10 +396,10 @@ hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4
     const auto* bi = static_cast<const uint16_t*>(w->biases);
     const auto* xh = static_cast<const _Float16*>(x);
     const int N = w->rows, K = w->cols;
-    if (f32 && am) return launch_one<MT, S, WAVES, true, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
-    if (am) return launch_one<MT, S, WAVES, false, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
-    if (f32) return launch_one<MT, S, WAVES, true, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
-    return launch_one<MT, S, WAVES, false, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
+    if (f32 && am) return launch_one<MT, S, WAVES, true, true, DEPTH>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
+    if (am) return launch_one<MT, S, WAVES, false, true, DEPTH>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
+    if (f32) return launch_one<MT, S, WAVES, true, false, DEPTH>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
+    return launch_one<MT, S, WAVES, false, false, DEPTH>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
 }
 
 }  // namespace
@@ -401,14 +416,16 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     float* pv = argmax ? static_cast<float*>(ws) : nullptr;
     int* pi = argmax ? reinterpret_cast<int*>(static_cast<char*>(ws) + ws_part_stride) : nullptr;
     if (argmax && grid.y != 1) return dhp_fail(DHP_ERR_UNSUPPORTED, "argmax with m=%d", M);
-    // 64-k stages with two in flight per wave; eight waves for up to 32 rows, four for 64-row
-    // tiles (with eight, the 64-row tile keeps ~160 KB of loads in flight per CU and measured
-    // slower: 16.6 against 16.1 us for M=128, N=8192, K=2560, and 40.9 against 38.4 us for the
-    // hyper-connection chunk, whose K = 320 gives eight waves only five stages to share)
+    // 64-k stages. Up to 32 rows: eight waves, two stages in flight each. 64-row tiles: one stage
+    // in flight per wave, with eight waves when K has at least 16 k-blocks and four otherwise.
+    // Measured for M=128, N=8192, K=2560: 14.2 us (eight waves, one stage in flight) against
+    // 16.2 (four, two) and 16.7 (eight, two: ~160 KB in flight per CU); for the hyper-connection
+    // chunk, whose up projection has K = 320 (five k-blocks), four waves are faster.
     const bool am = argmax != nullptr;
     const int KB = w->cols / 64;
     const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB)
-                                   : launch_mt<2, 1, 4>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB);
+                 : (KB >= 16) ? launch_mt<2, 1, 8, 1>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB)
+                              : launch_mt<2, 1, 4, 1>(y_f32, am, grid, s, w, x, M, y, pv, pi, KB);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemm launch: %s", hipGetErrorString(e));
     if (argmax) {
         const hipError_t e2 = launch_argmax_final(pv, pi, (int)grid.x, M, argmax, s);
@@ -428,7 +445,8 @@ int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_pa
     const int kb_split = KB / splits;
     const dim3 grid((unsigned)dhp_gemm_blocks_n(N), (unsigned)((M + rows - 1) / rows), (unsigned)splits);
     const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split)
-                                   : launch_mt<2, 1, 8>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split);
+                   : (kb_split >= 16) ? launch_mt<2, 1, 8, 1>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split)
+                                      : launch_mt<2, 1, 4, 1>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "split-K gemm launch: %s", hipGetErrorString(e));
     return DHP_OK;
 }
