@@ -820,31 +820,57 @@ __global__ __launch_bounds__(256, CPL <= 5 ? 3 : 2) void k_moep_phase1(MoeArgs a
             }
         }
         __syncthreads();
-        for (int t = 0; t < tn; ++t) {
-            // pair_act's operations in its order, the activations read a chunk at a time
-            const NibConsts nk = nib_consts();
-            float ag = 0.0f, au = 0.0f;
+        // pair_act's operations in its order for every token, the activations read a chunk at a
+        // time. The codes' raw fp16 form depends only on the weights, so each chunk is unpacked
+        // once for all the group's tokens; each token's sums run in pair_act's order, so its value
+        // is the decode call's bit for bit.
+        const NibConsts nk = nib_consts();
+        float ag[P1_TG], au[P1_TG];
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = j + LPR * i;
-                h2 xp[16];
+        for (int u = 0; u < P1_TG; ++u) ag[u] = au[u] = 0.0f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const u32x4 u = xstage[(t * 4 + q) * CH32 + c];
-                    xp[4 * q] = as_h2(u.x); xp[4 * q + 1] = as_h2(u.y);
-                    xp[4 * q + 2] = as_h2(u.z); xp[4 * q + 3] = as_h2(u.w);
-                }
-                const float2 sn = xsum[t * CH32 + c];
-                ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_f16_raw(p.cg[i], xp, sn.y, nk), ag);
-                ag = __builtin_fmaf(bf16_to_f32(p.bg[i]), sn.x, ag);
-                au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_f16_raw(p.cu[i], xp, sn.y, nk), au);
-                au = __builtin_fmaf(bf16_to_f32(p.bu[i]), sn.x, au);
+        for (int i = 0; i < CPL; ++i) {
+            const int c = j + LPR * i;
+            const uint32_t wg[4] = {p.cg[i].x, p.cg[i].y, p.cg[i].z, p.cg[i].w};
+            const uint32_t wu[4] = {p.cu[i].x, p.cu[i].y, p.cu[i].z, p.cu[i].w};
+            h2 tg[16], tu[16];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                unpack8_raw(wg[w], tg + 4 * w, nk);
+                unpack8_raw(wu[w], tu + 4 * w, nk);
             }
-            ag = group_sum<LPR>(ag);
-            au = group_sum<LPR>(au);
-            const float v1 = silu_f(ag) * au;
-            const int ms = list[base + t];
-            if (j == 0 && live) a.act[((size_t)(ms >> 4) * nslot + (ms & 15)) * a.inter + row] = v1;
+#pragma unroll
+            for (int t = 0; t < P1_TG; ++t) {
+                if (t < tn) {
+                    h2 xp[16];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const u32x4 v4 = xstage[(t * 4 + q) * CH32 + c];
+                        xp[4 * q] = as_h2(v4.x); xp[4 * q + 1] = as_h2(v4.y);
+                        xp[4 * q + 2] = as_h2(v4.z); xp[4 * q + 3] = as_h2(v4.w);
+                    }
+                    const float2 sn = xsum[t * CH32 + c];
+                    float dg = sn.y, du = sn.y;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) dg = __builtin_amdgcn_fdot2(tg[e], xp[e], dg, false);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) du = __builtin_amdgcn_fdot2(tu[e], xp[e], du, false);
+                    ag[t] = __builtin_fmaf(bf16_to_f32(p.sg[i]), dg, ag[t]);
+                    ag[t] = __builtin_fmaf(bf16_to_f32(p.bg[i]), sn.x, ag[t]);
+                    au[t] = __builtin_fmaf(bf16_to_f32(p.su[i]), du, au[t]);
+                    au[t] = __builtin_fmaf(bf16_to_f32(p.bu[i]), sn.x, au[t]);
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < P1_TG; ++t) {
+            if (t < tn) {
+                const float g1 = group_sum<LPR>(ag[t]);
+                const float u1 = group_sum<LPR>(au[t]);
+                const float v1 = silu_f(g1) * u1;
+                const int ms = list[base + t];
+                if (j == 0 && live) a.act[((size_t)(ms >> 4) * nslot + (ms & 15)) * a.inter + row] = v1;
+            }
         }
     }
 }
