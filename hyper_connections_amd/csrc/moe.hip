@@ -644,6 +644,7 @@ constexpr int RT_GRP = 4;        // tokens whose activations are in flight toget
 template <int CPL> constexpr int p1_tg() { return CPL <= 5 ? 8 : 4; }
 template <int CPLD> constexpr int p2_tg() { return CPLD == 1 ? 16 : 8; }
 constexpr int P2_RH = 4;         // down rows per 16-lane group in the batched phase 2
+constexpr int P2_NT = 2;         // 64-row tiles per block in the batched phase 2
 constexpr int ITEM_TOK = 16;     // (token, slot) pairs per work item
 
 template <int CPL, int KIND, bool SC>
@@ -875,6 +876,9 @@ __global__ __launch_bounds__(256, CPL <= 5 ? 3 : 2) void k_moep_phase1(MoeArgs a
     }
 }
 
+// A block owns P2_NT tiles of 64 down rows of one work item: the codes of all its tiles are in
+// flight together, the item's activations are staged once for them, and the tiles are computed
+// one after the other (each tile's codes become floats only when its turn comes).
 template <int CPLD>
 __global__ __launch_bounds__(256) void k_moep_phase2(MoeArgs a) {
     extern __shared__ float astage[];                  // [P2_TG][inter / 32][ACT_PITCH]
@@ -885,7 +889,6 @@ __global__ __launch_bounds__(256) void k_moep_phase2(MoeArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane % LPR;
     const int CH = a.inter >> 5, G = a.inter >> 6;
     const int nslot = a.top_k + 1;
-    const int h0 = (blockIdx.x * 16 + wave * 4 + lane / LPR) * P2_RH;
     const u32x4* dc;
     const uint16_t *ds, *db;
     if (e == a.E) {
@@ -895,17 +898,22 @@ __global__ __launch_bounds__(256) void k_moep_phase2(MoeArgs a) {
         ds = reinterpret_cast<const uint16_t*>(a.d_scales + (size_t)e * a.d_sstride);
         db = reinterpret_cast<const uint16_t*>(a.d_biases + (size_t)e * a.d_sstride);
     }
-    u32x4 c[P2_RH][CPLD];
-    uint32_t sv[P2_RH][CPLD], bv[P2_RH][CPLD];
+    int h0[P2_NT];
+    u32x4 c[P2_NT][P2_RH][CPLD];
+    uint32_t sv[P2_NT][P2_RH][CPLD], bv[P2_NT][P2_RH][CPLD];
 #pragma unroll
-    for (int r = 0; r < P2_RH; ++r) {
-        const int h = min(h0 + r, a.hidden - 1);
+    for (int q = 0; q < P2_NT; ++q) {
+        h0[q] = ((blockIdx.x * P2_NT + q) * 16 + wave * 4 + lane / LPR) * P2_RH;
 #pragma unroll
-        for (int i = 0; i < CPLD; ++i) {
-            const int ch = min(j + LPR * i, CH - 1);
-            c[r][i] = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
-            sv[r][i] = ds[(size_t)h * G + (ch >> 1)];
-            bv[r][i] = db[(size_t)h * G + (ch >> 1)];
+        for (int r = 0; r < P2_RH; ++r) {
+            const int h = min(h0[q] + r, a.hidden - 1);
+#pragma unroll
+            for (int i = 0; i < CPLD; ++i) {
+                const int ch = min(j + LPR * i, CH - 1);
+                c[q][r][i] = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
+                sv[q][r][i] = ds[(size_t)h * G + (ch >> 1)];
+                bv[q][r][i] = db[(size_t)h * G + (ch >> 1)];
+            }
         }
     }
     constexpr int P2_TG = p2_tg<CPLD>();
@@ -918,9 +926,9 @@ __global__ __launch_bounds__(256) void k_moep_phase2(MoeArgs a) {
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int it = min((int)threadIdx.x + 256 * k, items - 1);
-            const int t = it / (a.inter >> 2), q = it - t * (a.inter >> 2);
+            const int t = it / (a.inter >> 2), qq = it - t * (a.inter >> 2);
             const int ms = list[base + t];
-            v[k] = *reinterpret_cast<const f4v*>(a.act + ((size_t)(ms >> 4) * nslot + (ms & 15)) * a.inter + 4 * q);
+            v[k] = *reinterpret_cast<const f4v*>(a.act + ((size_t)(ms >> 4) * nslot + (ms & 15)) * a.inter + 4 * qq);
         }
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
@@ -931,15 +939,24 @@ __global__ __launch_bounds__(256) void k_moep_phase2(MoeArgs a) {
             }
         }
         __syncthreads();
-        for (int t = 0; t < tn; ++t) {
-            float p[P2_RH];
-            down_part<P2_RH, CPLD>(p, c, sv, bv, astage + t * CH * ACT_PITCH, ACT_PITCH, j, CH);
-            const int ms = list[base + t];
-            float* dst = a.dsum + ((size_t)(ms >> 4) * nslot + (ms & 15)) * a.hidden;
 #pragma unroll
-            for (int r = 0; r < P2_RH; ++r) {
-                const float d = group_sum<LPR>(p[r]);
-                if (j == 0 && h0 + r < a.hidden) dst[h0 + r] = d;
+        for (int q = 0; q < P2_NT; ++q) {
+            // keeps this tile's code-to-float conversion here rather than hoisted above the loops
+            // with every other tile's (which would hold all tiles' floats at once)
+#pragma unroll
+            for (int r = 0; r < P2_RH; ++r)
+#pragma unroll
+                for (int i = 0; i < CPLD; ++i) asm volatile("" : "+v"(c[q][r][i]));
+            for (int t = 0; t < tn; ++t) {
+                float p[P2_RH];
+                down_part<P2_RH, CPLD>(p, c[q], sv[q], bv[q], astage + t * CH * ACT_PITCH, ACT_PITCH, j, CH);
+                const int ms = list[base + t];
+                float* dst = a.dsum + ((size_t)(ms >> 4) * nslot + (ms & 15)) * a.hidden;
+#pragma unroll
+                for (int r = 0; r < P2_RH; ++r) {
+                    const float d = group_sum<LPR>(p[r]);
+                    if (j == 0 && h0[q] + r < a.hidden) dst[h0[q] + r] = d;
+                }
             }
         }
     }
@@ -975,7 +992,7 @@ hipError_t launch_prefill_all(const MoeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_moep_phase1<CPL>, dim3((a.inter + 15) / 16, items), dim3(256), lds1, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 g2((a.hidden + 16 * P2_RH - 1) / (16 * P2_RH), items);
+    const dim3 g2((a.hidden + 16 * P2_RH * P2_NT - 1) / (16 * P2_RH * P2_NT), items);
     if (a.inter <= 512)
         hipLaunchKernelGGL(k_moep_phase2<1>, g2, dim3(256), (size_t)p2_tg<1>() * (a.inter / 32) * ACT_PITCH * 4, s, a);
     else
