@@ -63,6 +63,9 @@ struct MoeArgs {
     int32_t* route;    // ws [M][top_k + 1] (batched only): (token << 4 | slot), grouped by expert
     int32_t* items;    // ws [max items][4] (batched only): (expert, first route entry, count, 0)
     int32_t* nitems;   // ws [1] (batched only): work items in use
+    u32x4* xraw;       // ws [M][4][hidden / 32] (batched only): each token's activations in the raw form of
+                       // x32_raw_from (16 permuted pairs per 32-value chunk, as 4 u32x4 planes)
+    float2* xrsum;     // ws [M][hidden / 32] (batched only): per chunk, (plain sum, negated correction)
     _Float16* out;     // [M][hidden]
     int32_t* ids;      // [M][top_k]
     float* weights;    // [M][top_k]
@@ -630,11 +633,12 @@ __global__ __launch_bounds__(64 * P2W) void k_moe_phase2(MoeArgs a) {
 // to it.
 //  k_moep_router : one wave per router row (and one for the shared gate row): the row is loaded
 //                  once and dotted with a group of tokens, four tokens' activations in flight.
-//  k_moep_topk   : one wave per token: the decode's top-k and softmax.
+//  k_moep_topk   : one wave per token: the decode's top-k and softmax, and the token's activations
+//                  in the raw form pair_act multiplies (once per token, into the workspace).
 //  k_moep_phase1 : block = (16 rows, expert): the (token, slot) pairs routed to the expert, read
-//                  off the ids, run through pair_act; the tokens' activations are staged in LDS
-//                  (raw form, once per block) a group at a time. Expert E is the shared one,
-//                  taken by every token in slot top_k.
+//                  off the ids, run through pair_act; the tokens' raw-form activations are copied
+//                  into LDS a group at a time. Expert E is the shared one, taken by every token in
+//                  slot top_k.
 //  k_moep_phase2 : block = (64 down rows, expert): each routed (token, slot) gets its down-row
 //                  dots (down_part, summed over 16 lanes), written to the workspace per slot.
 //  k_moep_combine: every output of every token from its slots' dots (moe_combine).
@@ -705,6 +709,21 @@ __global__ __launch_bounds__(64) void k_moep_topk(MoeArgs a) {
     if (threadIdx.x == 0)
         publish_topk(ids, vals, a.top_k, a.expert_scale, a.ids + (size_t)m * a.top_k,
                      a.weights + (size_t)m * a.top_k);
+    // the token's activations in the raw form phase 1 multiplies, once per token (every phase-1
+    // block that stages the token copies them instead of converting them again)
+    const int CH32 = a.hidden >> 5;
+    for (int c = threadIdx.x; c < CH32; c += 64) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.x + (size_t)m * a.hidden + 32 * c);
+        const u32x4 v[4] = {src[0], src[1], src[2], src[3]};
+        h2 xp[16];
+        float nc;
+        const float xs = x32_raw_from(v, xp, nc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            a.xraw[((size_t)m * 4 + q) * CH32 + c] = u32x4{h2_bits(xp[4 * q]), h2_bits(xp[4 * q + 1]),
+                                                         h2_bits(xp[4 * q + 2]), h2_bits(xp[4 * q + 3])};
+        a.xrsum[(size_t)m * CH32 + c] = float2{xs, nc};
+    }
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -795,29 +814,27 @@ __global__ __launch_bounds__(256, CPL <= 5 ? 3 : 2) void k_moep_phase1(MoeArgs a
     for (int base = 0; base < n; base += P1_TG) {
         const int tn = min(P1_TG, n - base);
         __syncthreads();                               // the previous group's reads are done
-        // every load of the group first (items past the group clamped), then the raw form
+        // every load of the group first (items past the group clamped), then the stores
+        // the tokens' activations were put in the raw form once per token (k_moep_topk): copy them
         u32x4 v[IT][4];
+        float2 vs[IT];
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int it = min((int)threadIdx.x + 256 * k, tn * CH32 - 1);
             const int t = it / CH32, c = it - t * CH32;
-            const u32x4* src = reinterpret_cast<const u32x4*>(a.x + (size_t)(list[base + t] >> 4) * a.hidden + 32 * c);
+            const size_t tok = (size_t)(list[base + t] >> 4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[k][q] = src[q];
+            for (int q = 0; q < 4; ++q) v[k][q] = a.xraw[(tok * 4 + q) * CH32 + c];
+            vs[k] = a.xrsum[tok * CH32 + c];
         }
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int it = (int)threadIdx.x + 256 * k;
             if (it < tn * CH32) {
                 const int t = it / CH32, c = it - t * CH32;
-                h2 xp[16];
-                float nc;
-                const float xs = x32_raw_from(v[k], xp, nc);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    xstage[(t * 4 + q) * CH32 + c] = u32x4{h2_bits(xp[4 * q]), h2_bits(xp[4 * q + 1]),
-                                                          h2_bits(xp[4 * q + 2]), h2_bits(xp[4 * q + 3])};
-                xsum[t * CH32 + c] = float2{xs, nc};
+                for (int q = 0; q < 4; ++q) xstage[(t * 4 + q) * CH32 + c] = v[k][q];
+                xsum[t * CH32 + c] = vs[k];
             }
         }
         __syncthreads();
@@ -1033,7 +1050,7 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Batched workspace, in order: logits [m][Epad], gate logits [m], act [m][top_k + 1][inter],
 // slot dots [m][top_k + 1][hidden] (fp32, each part 256-byte aligned).
 struct PrefillWs {
-    size_t logits, gate, act, dsum, route, items, nitems, total;
+    size_t logits, gate, act, dsum, route, items, nitems, xraw, xrsum, total;
 };
 PrefillWs prefill_ws(int m, int E, int top_k, int inter, int hidden) {
     PrefillWs w;
@@ -1045,7 +1062,9 @@ PrefillWs prefill_ws(int m, int E, int top_k, int inter, int hidden) {
     w.route = w.dsum + align256((size_t)m * (top_k + 1) * hidden * sizeof(float));
     w.items = w.route + align256((size_t)m * (top_k + 1) * sizeof(int32_t));
     w.nitems = w.items + align256((size_t)max_items(m, E, top_k) * 4 * sizeof(int32_t));
-    w.total = w.nitems + 256;
+    w.xraw = w.nitems + 256;
+    w.xrsum = w.xraw + align256((size_t)m * (hidden / 32) * 4 * sizeof(u32x4));
+    w.total = w.xrsum + align256((size_t)m * (hidden / 32) * sizeof(float2));
     return w;
 }
 
@@ -1112,6 +1131,8 @@ int launch_moe(const void* x, const dhp_router* router, const void* sgate_row,
     a.act = w + ((a.E + 4) & ~3);        // 16-byte aligned
     a.dsum = nullptr;
     a.route = a.items = a.nitems = nullptr;
+    a.xraw = nullptr;
+    a.xrsum = nullptr;
 
     hipError_t e;
     switch (a.hidden / 512) {
@@ -1146,6 +1167,8 @@ int launch_moe_prefill(const void* x, int m, const dhp_router* router, const voi
     a.route = reinterpret_cast<int32_t*>(base + lay.route);
     a.items = reinterpret_cast<int32_t*>(base + lay.items);
     a.nitems = reinterpret_cast<int32_t*>(base + lay.nitems);
+    a.xraw = reinterpret_cast<u32x4*>(base + lay.xraw);
+    a.xrsum = reinterpret_cast<float2*>(base + lay.xrsum);
 
     hipError_t e;
     switch (a.hidden / 512) {
