@@ -284,7 +284,8 @@ int launch_hc_read_batched(const void* raw, int m, const void* gamma, int C, int
                            hipStream_t s);
 int launch_hc_inject_batched(void* wide, int m, const void* out, const float* w, int C, int H, hipStream_t s);
 size_t dhp_argmax_part_stride(int32_t n_rows, int32_t m);
-int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_partials, int splits, hipStream_t s);
+int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_partials, int splits, hipStream_t s,
+                            const dhp_int4* w2 = nullptr, float* y2_partials = nullptr);
 int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax,
                      void* ws, size_t ws_part_stride, hipStream_t s);
 hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s);

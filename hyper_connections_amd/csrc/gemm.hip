@@ -202,11 +202,22 @@ DHP_DEV void stage_mfma(const uint8_t* lds, int li, int g, f16x16 (*acc)[2], con
     }
 }
 
-template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH>
+// A second weight sharing the activations and K of a launch: column blocks from `nb` on take it
+// (its rows, its output Y with its own N). nb >= the grid's column blocks means none.
+struct GemmAlt {
+    const uint8_t* codes;
+    const uint16_t* scales;
+    const uint16_t* biases;
+    void* Y;
+    int N;
+    int nb;
+};
+
+template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH, bool ALT>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ X, int M, int N, int K,
-    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i, int kb_split) {
+    void* __restrict__ Y, float* __restrict__ part_v, int* __restrict__ part_i, int kb_split, GemmAlt alt) {
     using L = WaveLds<MT, S>;
     constexpr int ROWS = 32 * MT;
     extern __shared__ __align__(16) uint8_t lds_all[];   // one region per wave; reused by the epilogue
@@ -216,7 +227,15 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     const int lane = threadIdx.x & 63;
     const int li = lane & 31;
     const int g = lane >> 5;
-    const int n0 = blockIdx.x * BN;
+    const bool second = ALT && (int)blockIdx.x >= alt.nb;     // the same in the whole block
+    if (second) {
+        codes = alt.codes;
+        scales = alt.scales;
+        biases = alt.biases;
+        Y = alt.Y;
+        N = alt.N;
+    }
+    const int n0 = (second ? (int)blockIdx.x - alt.nb : (int)blockIdx.x) * BN;
     const int m0 = blockIdx.y * ROWS;
     const int KB = K >> 6;
     const int xrows = min(ROWS, M - m0);       // activation rows that exist in this tile
@@ -365,9 +384,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     }
 }
 
-template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH>
+template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH, bool ALT>
 hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t* sc, const uint16_t* bi,
-                      const _Float16* xh, int M, int N, int K, void* y, float* pv, int* pi, int kb_split) {
+                      const _Float16* xh, int M, int N, int K, void* y, float* pv, int* pi, int kb_split,
+                      const GemmAlt& alt) {
     using L = WaveLds<MT, S>;
     constexpr size_t red = (size_t)WAVES * 32 * MT * LDW * 4;    // one partial tile per wave
     constexpr size_t lds = (WAVES * L::BYTES > red) ? WAVES * L::BYTES : red;
@@ -378,28 +398,30 @@ hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t
     const unsigned long long bit = 1ull << (dev & 63);
     if (!(__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & bit)) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH>),
+            reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH, ALT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         __atomic_fetch_or(&configured, bit, __ATOMIC_RELEASE);
     }
-    hipLaunchKernelGGL((k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH>), grid, dim3(64 * WAVES), lds, s, c, sc, bi, xh, M,
-                       N, K, y, pv, pi, kb_split);
+    hipLaunchKernelGGL((k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH, ALT>), grid, dim3(64 * WAVES), lds, s, c, sc, bi, xh, M,
+                       N, K, y, pv, pi, kb_split, alt);
     return hipGetLastError();
 }
 
 template <int MT, int S, int WAVES, int DEPTH = 2>
 hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4* w, const void* x,
-                     int M, void* y, float* pv, int* pi, int kb_split) {
+                     int M, void* y, float* pv, int* pi, int kb_split, const GemmAlt& alt = GemmAlt{nullptr, nullptr, nullptr, nullptr, 0, 1 << 30}) {
     const auto* c = static_cast<const uint8_t*>(w->codes);
     const auto* sc = static_cast<const uint16_t*>(w->scales);
     const auto* bi = static_cast<const uint16_t*>(w->biases);
     const auto* xh = static_cast<const _Float16*>(x);
     const int N = w->rows, K = w->cols;
-    if (f32 && am) return launch_one<MT, S, WAVES, true, true, DEPTH>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
-    if (am) return launch_one<MT, S, WAVES, false, true, DEPTH>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
-    if (f32) return launch_one<MT, S, WAVES, true, false, DEPTH>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
-    return launch_one<MT, S, WAVES, false, false, DEPTH>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split);
+    // the second weight only in split-K launches (fp32 partials, no argmax)
+    if (alt.codes) return launch_one<MT, S, WAVES, true, false, DEPTH, true>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split, alt);
+    if (f32 && am) return launch_one<MT, S, WAVES, true, true, DEPTH, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split, alt);
+    if (am) return launch_one<MT, S, WAVES, false, true, DEPTH, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split, alt);
+    if (f32) return launch_one<MT, S, WAVES, true, false, DEPTH, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split, alt);
+    return launch_one<MT, S, WAVES, false, false, DEPTH, false>(grid, s, c, sc, bi, xh, M, N, K, y, pv, pi, kb_split, alt);
 }
 
 }  // namespace
@@ -437,17 +459,26 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
 // Split-K form for long, narrow contractions (few output columns, many k): `splits` blocks share
 // the K of every output tile, each writing its fp32 partial to y + split * M * N; the caller sums
 // the `splits` partials in split order. The K / 64 k-blocks must divide evenly into the splits.
-int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_partials, int splits, hipStream_t s) {
+// With w2 (same K and group), the same launch also computes x . w2^T into y2_partials (its own
+// N2 columns, laid out the same way): its column blocks follow w's in the grid.
+int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_partials, int splits, hipStream_t s,
+                            const dhp_int4* w2, float* y2_partials) {
     const int N = w->rows, KB = w->cols / 64;
     if (splits < 1 || KB % splits) return dhp_fail(DHP_ERR_UNSUPPORTED, "%d k-blocks in %d splits", KB, splits);
+    if (w2 && (w2->cols != w->cols || !y2_partials))
+        return dhp_fail(DHP_ERR_UNSUPPORTED, "second split-K weight: K %d against %d", w2->cols, w->cols);
     const int MT = (M <= 32) ? 1 : 2;
     const int rows = 32 * MT;
     const int kb_split = KB / splits;
-    const dim3 grid((unsigned)dhp_gemm_blocks_n(N), (unsigned)((M + rows - 1) / rows), (unsigned)splits);
-    const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split)
-                   : (kb_split >= 16) ? launch_mt<2, 1, 8, 1>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split)
-                                      : launch_mt<2, 1, 4, 1>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split);
+    const int nb = dhp_gemm_blocks_n(N);
+    GemmAlt alt{nullptr, nullptr, nullptr, nullptr, 0, 1 << 30};
+    if (w2) alt = GemmAlt{static_cast<const uint8_t*>(w2->codes), static_cast<const uint16_t*>(w2->scales),
+                          static_cast<const uint16_t*>(w2->biases), y2_partials, w2->rows, nb};
+    const int nbx = nb + (w2 ? dhp_gemm_blocks_n(w2->rows) : 0);
+    const dim3 grid((unsigned)nbx, (unsigned)((M + rows - 1) / rows), (unsigned)splits);
+    const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split, alt)
+                   : (kb_split >= 16) ? launch_mt<2, 1, 8, 1>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split, alt)
+                                      : launch_mt<2, 1, 4, 1>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split, alt);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "split-K gemm launch: %s", hipGetErrorString(e));
     return DHP_OK;
 }
-

@@ -193,8 +193,8 @@ int launch_hc_read_batched(const void* raw, int m, const void* gamma, int C, int
     launch_norm(dim3(m, C), s, static_cast<const _Float16*>(raw), static_cast<const uint16_t*>(gamma), normed, C, H,
                 eps);
     int rc = launch_status("hc norm");
-    if (!rc) rc = launch_gemm_mfma_splitk(down, normed, m, lo_pre, KSPLIT, s);
-    if (!rc && inject) rc = launch_gemm_mfma_splitk(inject, normed, m, ipre, KSPLIT, s);
+    // the down and inject projections share the normed rows and K: one launch for both
+    if (!rc) rc = launch_gemm_mfma_splitk(down, normed, m, lo_pre, KSPLIT, s, inject, inject ? ipre : nullptr);
     if (rc) return rc;
     const int n_lo = m * R, n_iw = inject ? m * C : 0;
     hipLaunchKernelGGL(k_hcb_act, dim3((n_lo + n_iw + 255) / 256), dim3(256), 0, s, lo_pre, lo, ipre, inject_w,
