@@ -286,6 +286,9 @@ int launch_hc_inject_batched(void* wide, int m, const void* out, const float* w,
 size_t dhp_argmax_part_stride(int32_t n_rows, int32_t m);
 int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_partials, int splits, hipStream_t s,
                             const dhp_int4* w2 = nullptr, float* y2_partials = nullptr);
+bool dhp_gemm_upmix_fits(const dhp_int4* w, int M, int C, int H);
+int launch_gemm_mfma_upmix(const dhp_int4* w, const void* x, int M, const void* normed, void* mixed, int H,
+                           hipStream_t s);
 int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax,
                      void* ws, size_t ws_part_stride, hipStream_t s);
 hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s);

@@ -97,14 +97,17 @@ struct StagePlan {
 template <int MT, int S>
 DHP_DEV void stage_plan(StagePlan<MT, S>& p, int lane, const uint8_t* codes, const uint16_t* scales,
                         const uint16_t* biases, const _Float16* X, int n0, int N, int m0, int xrows,
-                        int K, int KB) {
+                        int K, int KB, int hmix = 0) {
+    // hmix > 0: tile column r is weight row (r / 16) * hmix + n0 + r % 16 (four streams of 16
+    // positions, for the fused stream mix); otherwise n0 + r
+    auto wrow = [&](int r) { return hmix > 0 ? (r >> 4) * hmix + n0 + (r & 15) : min(n0 + r, N - 1); };
     using L = WaveLds<MT, S>;
     const size_t row_bytes = (size_t)K >> 1;
 #pragma unroll
     for (int i = 0; i < L::WL; ++i) {
         const int c = i * 64 + lane;
         const int row = c / (2 * S), cc = c % (2 * S);
-        p.wsrc[i] = codes + (size_t)min(n0 + row, N - 1) * row_bytes + (cc & 1) * 16;
+        p.wsrc[i] = codes + (size_t)wrow(row) * row_bytes + (cc & 1) * 16;
         p.wkb[i] = cc >> 1;
         p.wdst[i] = row * L::WP + cc * 16;
     }
@@ -117,7 +120,7 @@ DHP_DEV void stage_plan(StagePlan<MT, S>& p, int lane, const uint8_t* codes, con
         p.xkb[i] = cc >> 3;
         p.xdst[i] = (row < xrows) ? L::W_BYTES + row * L::XP + cc * 16 : L::TRASH + 16 * lane;
     }
-    const size_t n = (size_t)min(n0 + lane, N - 1);
+    const size_t n = (size_t)wrow(lane);
     p.ssrc = scales + n * KB;
     p.bsrc = biases + n * KB;
 }
@@ -211,9 +214,14 @@ struct GemmAlt {
     void* Y;
     int N;
     int nb;
+    // the fused stream mix (MIX kernels): mixed[m][h] = (1/4) sum_c sigmoid(y[m][c*H + h]) *
+    // normed[m][c*H + h] over 4 streams of H positions; y itself is not stored
+    const _Float16* normed;
+    _Float16* mixed;
+    int H;
 };
 
-template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH, bool ALT>
+template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH, bool ALT, bool MIX>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ X, int M, int N, int K,
@@ -235,7 +243,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
         Y = alt.Y;
         N = alt.N;
     }
-    const int n0 = (second ? (int)blockIdx.x - alt.nb : (int)blockIdx.x) * BN;
+    // MIX: a block owns 16 positions of each of the 4 streams
+    const int n0 = MIX ? (int)blockIdx.x * 16 : (second ? (int)blockIdx.x - alt.nb : (int)blockIdx.x) * BN;
     const int m0 = blockIdx.y * ROWS;
     const int KB = K >> 6;
     const int xrows = min(ROWS, M - m0);       // activation rows that exist in this tile
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     StageRegs<MT, S> r0, r1;
     // two register sets: while stage st computes out of LDS, stages st+1 and st+2 are in flight
     if (has) {
-        stage_plan<MT, S>(plan, lane, codes, scales, biases, X, n0, N, m0, xrows, K, KB);
+        stage_plan<MT, S>(plan, lane, codes, scales, biases, X, n0, N, m0, xrows, K, KB, MIX ? alt.H : 0);
         stage_load<MT, S>(r0, plan, st0 * S, kb1);
         if constexpr (DEPTH == 2) stage_load<MT, S>(r1, plan, (st0 + 1) * S, kb1);
     }
@@ -344,7 +353,28 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
         const int nb = n0 + c0;
         // the thread's CPT contiguous outputs in one or two 16-byte stores when the row allows
         const bool vec = (reinterpret_cast<uintptr_t>(Y) & 15) == 0 && (N & 7) == 0 && nb + CPT <= N;
-        if (vec) {
+        if constexpr (MIX) {
+            // the row's four threads hold its four streams (16 positions each): sigmoid times the
+            // normed value, summed over the streams across the quad, then the mean; each thread
+            // writes 4 of the 16 positions
+            static_assert(TPR == 4 && CPT == 16, "the fused mix needs 4 threads of 16 columns per row");
+            const int c = threadIdx.x % TPR;
+            const size_t wide = (size_t)4 * alt.H;
+            const u32x4* np = reinterpret_cast<const u32x4*>(alt.normed + (size_t)m * wide + (size_t)c * alt.H + n0);
+            const u32x4 na = np[0], nb8 = np[1];
+            const uint32_t nw[8] = {na.x, na.y, na.z, na.w, nb8.x, nb8.y, nb8.z, nb8.w};
+            float sm[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const h2 pr = as_h2(nw[k >> 1]);
+                sm[k] = sigmoid_f(v[k]) * (float)((k & 1) ? pr.y : pr.x);
+                sm[k] = group_sum<4>(sm[k]);
+            }
+            _Float16* mp = alt.mixed + (size_t)m * alt.H + n0 + 4 * c;
+            const h2 lo = {(_Float16)(sm[4 * c] * 0.25f), (_Float16)(sm[4 * c + 1] * 0.25f)};
+            const h2 hi = {(_Float16)(sm[4 * c + 2] * 0.25f), (_Float16)(sm[4 * c + 3] * 0.25f)};
+            *reinterpret_cast<uint2*>(mp) = uint2{h2_bits(lo), h2_bits(hi)};
+        } else if (vec) {
             if constexpr (F32OUT) {
                 float* yp = reinterpret_cast<float*>(Y) + (size_t)m * N + nb;
 #pragma unroll
@@ -384,7 +414,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(
     }
 }
 
-template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH, bool ALT>
+template <int MT, int S, int WAVES, bool F32OUT, bool ARGMAX, int DEPTH, bool ALT, bool MIX = false>
 hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t* sc, const uint16_t* bi,
                       const _Float16* xh, int M, int N, int K, void* y, float* pv, int* pi, int kb_split,
                       const GemmAlt& alt) {
@@ -398,19 +428,19 @@ hipError_t launch_one(dim3 grid, hipStream_t s, const uint8_t* c, const uint16_t
     const unsigned long long bit = 1ull << (dev & 63);
     if (!(__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & bit)) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH, ALT>),
+            reinterpret_cast<const void*>(&k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH, ALT, MIX>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         __atomic_fetch_or(&configured, bit, __ATOMIC_RELEASE);
     }
-    hipLaunchKernelGGL((k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH, ALT>), grid, dim3(64 * WAVES), lds, s, c, sc, bi, xh, M,
+    hipLaunchKernelGGL((k_gemm_mfma<MT, S, WAVES, F32OUT, ARGMAX, DEPTH, ALT, MIX>), grid, dim3(64 * WAVES), lds, s, c, sc, bi, xh, M,
                        N, K, y, pv, pi, kb_split, alt);
     return hipGetLastError();
 }
 
 template <int MT, int S, int WAVES, int DEPTH = 2>
 hipError_t launch_mt(bool f32, bool am, dim3 grid, hipStream_t s, const dhp_int4* w, const void* x,
-                     int M, void* y, float* pv, int* pi, int kb_split, const GemmAlt& alt = GemmAlt{nullptr, nullptr, nullptr, nullptr, 0, 1 << 30}) {
+                     int M, void* y, float* pv, int* pi, int kb_split, const GemmAlt& alt = GemmAlt{nullptr, nullptr, nullptr, nullptr, 0, 1 << 30, nullptr, nullptr, 0}) {
     const auto* c = static_cast<const uint8_t*>(w->codes);
     const auto* sc = static_cast<const uint16_t*>(w->scales);
     const auto* bi = static_cast<const uint16_t*>(w->biases);
@@ -471,14 +501,37 @@ int launch_gemm_mfma_splitk(const dhp_int4* w, const void* x, int M, float* y_pa
     const int rows = 32 * MT;
     const int kb_split = KB / splits;
     const int nb = dhp_gemm_blocks_n(N);
-    GemmAlt alt{nullptr, nullptr, nullptr, nullptr, 0, 1 << 30};
+    GemmAlt alt{nullptr, nullptr, nullptr, nullptr, 0, 1 << 30, nullptr, nullptr, 0};
     if (w2) alt = GemmAlt{static_cast<const uint8_t*>(w2->codes), static_cast<const uint16_t*>(w2->scales),
-                          static_cast<const uint16_t*>(w2->biases), y2_partials, w2->rows, nb};
+                          static_cast<const uint16_t*>(w2->biases), y2_partials, w2->rows, nb, nullptr, nullptr, 0};
     const int nbx = nb + (w2 ? dhp_gemm_blocks_n(w2->rows) : 0);
     const dim3 grid((unsigned)nbx, (unsigned)((M + rows - 1) / rows), (unsigned)splits);
     const hipError_t e = (MT == 1) ? launch_mt<1, 1, 8>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split, alt)
                    : (kb_split >= 16) ? launch_mt<2, 1, 8, 1>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split, alt)
                                       : launch_mt<2, 1, 4, 1>(true, false, grid, s, w, x, M, y_partials, nullptr, nullptr, kb_split, alt);
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "split-K gemm launch: %s", hipGetErrorString(e));
+    return DHP_OK;
+}
+
+// The up projection of a chunked hyper-connection read with its stream mix fused into the
+// epilogue (4 streams of H positions; the fp32 up result is never stored):
+// mixed[m][h] = (1/4) sum_c sigmoid((x . w^T)[m][c*H + h]) * normed[m][c*H + h]. Only for the
+// configuration whose epilogue gives each row's four streams to four adjacent threads: 64-row
+// tiles (m > 32) on four waves (K / 64 < 16); dhp_gemm_upmix_fits says when.
+bool dhp_gemm_upmix_fits(const dhp_int4* w, int M, int C, int H) {
+    return C == 4 && M > 32 && M <= 128 && w->cols / 64 < 16 && H % 16 == 0 && w->rows == 4 * H;
+}
+
+int launch_gemm_mfma_upmix(const dhp_int4* w, const void* x, int M, const void* normed, void* mixed, int H,
+                           hipStream_t s) {
+    const dim3 grid((unsigned)(H / 16), (unsigned)((M + 63) / 64));
+    const GemmAlt alt{nullptr, nullptr, nullptr, nullptr, 0, 1 << 30, static_cast<const _Float16*>(normed),
+                      static_cast<_Float16*>(mixed), H};
+    const int KB = w->cols / 64;
+    const hipError_t e = launch_one<2, 1, 4, true, false, 1, false, true>(
+        grid, s, static_cast<const uint8_t*>(w->codes), static_cast<const uint16_t*>(w->scales),
+        static_cast<const uint16_t*>(w->biases), static_cast<const _Float16*>(x), M, w->rows, w->cols, nullptr, nullptr,
+        nullptr, KB, alt);
+    if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "up+mix gemm launch: %s", hipGetErrorString(e));
     return DHP_OK;
 }

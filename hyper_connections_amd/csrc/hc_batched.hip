@@ -200,7 +200,10 @@ int launch_hc_read_batched(const void* raw, int m, const void* gamma, int C, int
     hipLaunchKernelGGL(k_hcb_act, dim3((n_lo + n_iw + 255) / 256), dim3(256), 0, s, lo_pre, lo, ipre, inject_w,
                        n_lo, n_iw, 1.0f / (float)C);
     rc = launch_status("hc act");
-    if (!rc) rc = launch_gemm_mfma(up, lo, m, upre, 1, nullptr, nullptr, 0, s);
+    if (rc) return rc;
+    // four streams and a chunk of more than 32 tokens: the up GEMM's epilogue does the stream mix
+    if (dhp_gemm_upmix_fits(up, m, C, H)) return launch_gemm_mfma_upmix(up, lo, m, normed, mixed, H, s);
+    rc = launch_gemm_mfma(up, lo, m, upre, 1, nullptr, nullptr, 0, s);
     if (rc) return rc;
     hipLaunchKernelGGL(k_hcb_mix, dim3((m * H + 255) / 256), dim3(256), 0, s, upre, normed,
                        static_cast<_Float16*>(mixed), m, C, H);

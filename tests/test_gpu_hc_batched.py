@@ -88,3 +88,13 @@ def test_hc_inject_batched_rows(workload):
     torch.cuda.synchronize()
     ref = oracle.hc_inject_batched(rows[:m].astype(np.float64), out.astype(np.float64), w.astype(np.float64), C, H)
     assert_within_tol(wide.float().cpu().numpy(), ref, "inject rows")
+
+
+@pytest.mark.parametrize("m,inject", [(33, True), (100, True), (65, False)])
+def test_hc_read_batched_every_row_past_32(workload, m, inject):
+    # More than 32 tokens at C = 4 take the up projection with the stream mix in its epilogue
+    # (64-row tiles, the last one ragged): every row against the oracle.
+    blk, rows = workload
+    say(f"hc batched every row m={m} inject={inject}")
+    mixed, iw = run(blk, rows[:m], 4, 2560, inject=inject)
+    check_rows(blk, rows, 4, 2560, mixed, iw, list(range(m)), inject=inject, what=f"all m={m}")
