@@ -10,11 +10,12 @@
 //  k_hcb_norm   : one block per (token, stream): the stream's RMS, then normed = raw / rms *
 //                 hc_norm in fp32, stored once as fp16 (the GEMM operand)          -> [m][C*H]
 //  GEMM down    : normed . down^T, split-K (K = C*H is long, R is short: 16 splits give the
-//                 matrix cores enough blocks), fp32 partials                    -> [16][m][R]
-//  GEMM inject  : normed . inject^T, split-K the same way                       -> [16][m][C]
+//   + inject      matrix cores enough blocks), fp32 partials                    -> [16][m][R]
+//                 and, in the same launch, normed . inject^T split the same way  -> [16][m][C]
 //  k_hcb_act    : the partials summed in split order; lo = silu(. / C) (fp16, the next GEMM
 //                 operand); inject_w = 2 sigmoid(. / C)
-//  GEMM up      : lo . up^T (fp32 out)                                                -> [m][C*H]
+//  GEMM up      : lo . up^T; at C = 4 past 32 tokens its epilogue does the mix below (a block
+//                 takes 16 positions of each stream), otherwise fp32 out          -> [m][C*H]
 //  k_hcb_mix    : mixed = mean over the C streams of sigmoid(up) * normed             -> [m][H]
 //
 // The inject is 8 fp16 elements per thread over the m rows, each row with its own gate.
