@@ -70,13 +70,25 @@ __global__ __launch_bounds__(HC_MAX_THREADS) void k_hc_down(
                 ss = __builtin_fmaf(v[8 * i + 2 * k + 1], v[8 * i + 2 * k + 1], ss);
             }
         }
-        part[t] = ss;
+        // a stream's H/32 chunks are whole 16-lane groups when H % 512 == 0: sum within each
+        // group first (DPP), leaving H/512 partials per stream
+        if ((H & 511) == 0) {
+            ss = group_sum<16>(ss);
+            if ((t & 15) == 0) part[t >> 4] = ss;
+        } else {
+            part[t] = ss;
+        }
     }
     __syncthreads();
     const int per = H >> 5;               // chunks per stream
     if (t < C) {
         float acc = 0.0f;
-        for (int i = 0; i < per; ++i) acc += part[t * per + i];
+        if ((H & 511) == 0) {
+            const int pg = per >> 4;      // 16-lane groups per stream
+            for (int i = 0; i < pg; ++i) acc += part[t * pg + i];
+        } else {
+            for (int i = 0; i < per; ++i) acc += part[t * per + i];
+        }
         inv_rms[t] = 1.0f / sqrtf(acc / (float)H + eps);
     }
     __syncthreads();
