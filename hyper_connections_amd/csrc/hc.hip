@@ -129,7 +129,7 @@ __global__ __launch_bounds__(HC_MAX_THREADS) void k_hc_down(
 }
 
 // 16 lanes per output h; LPRU = 16 / C lanes per stream row.
-// NCH: chunks per lane, ceil((R / 32) / (16 / C)) rounded up to a power of two (4 at R = 320,
+// NCH: chunks per lane, ceil((R / 32) / (16 / C)), rounded up to 3 or a power of two (3 at R = 320,
 // C = 4); more would only issue clamped loads of chunks past the row and hold their registers.
 template <int C, int NCH>
 __global__ __launch_bounds__(UP_THREADS) void k_hc_up(
@@ -238,6 +238,7 @@ void launch_up(dim3 g, int block, size_t lds, hipStream_t s, const _Float16* rw,
     const int need = ((R >> 5) + LPRU - 1) / LPRU;
     if (need <= 1) hipLaunchKernelGGL((k_hc_up<C, 1>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
     else if (need <= 2) hipLaunchKernelGGL((k_hc_up<C, 2>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
+    else if (need <= 3) hipLaunchKernelGGL((k_hc_up<C, 3>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
     else if (need <= 4) hipLaunchKernelGGL((k_hc_up<C, 4>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
     else if (need <= 8) hipLaunchKernelGGL((k_hc_up<C, (8 < 32 / LPRU ? 8 : 32 / LPRU)>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
     else if (need <= 16) hipLaunchKernelGGL((k_hc_up<C, (16 < 32 / LPRU ? 16 : 32 / LPRU)>), g, dim3(block), lds, s, rw, gm, H, uc, us, ub, R, lo, inv_rms, mx);
