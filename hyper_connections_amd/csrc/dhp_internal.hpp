@@ -61,75 +61,34 @@ DHP_DEV void permute8(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3, h2 out
     out[3] = as_h2((d1 >> 16) | (d3 & 0xFFFF0000u));
 }
 
-// sum over 32 codes of q * x, fp32 accumulate: c holds 32 codes (16 bytes), xp the 16
-// permuted activation pairs for the same 32 positions.
-DHP_DEV float dot32_f16(const u32x4 c, const h2* xp, const NibConsts& k) {
-    float d = 0.0f;
-    h2 q[4];
-    unpack8(c.x, q, k);
-    d = __builtin_amdgcn_fdot2(q[0], xp[0], d, false);
-    d = __builtin_amdgcn_fdot2(q[1], xp[1], d, false);
-    d = __builtin_amdgcn_fdot2(q[2], xp[2], d, false);
-    d = __builtin_amdgcn_fdot2(q[3], xp[3], d, false);
-    unpack8(c.y, q, k);
-    d = __builtin_amdgcn_fdot2(q[0], xp[4], d, false);
-    d = __builtin_amdgcn_fdot2(q[1], xp[5], d, false);
-    d = __builtin_amdgcn_fdot2(q[2], xp[6], d, false);
-    d = __builtin_amdgcn_fdot2(q[3], xp[7], d, false);
-    unpack8(c.z, q, k);
-    d = __builtin_amdgcn_fdot2(q[0], xp[8], d, false);
-    d = __builtin_amdgcn_fdot2(q[1], xp[9], d, false);
-    d = __builtin_amdgcn_fdot2(q[2], xp[10], d, false);
-    d = __builtin_amdgcn_fdot2(q[3], xp[11], d, false);
-    unpack8(c.w, q, k);
-    d = __builtin_amdgcn_fdot2(q[0], xp[12], d, false);
-    d = __builtin_amdgcn_fdot2(q[1], xp[13], d, false);
-    d = __builtin_amdgcn_fdot2(q[2], xp[14], d, false);
-    d = __builtin_amdgcn_fdot2(q[3], xp[15], d, false);
-    return d;
+// Offset form of the 32-code dot product. Every code is moved four bits into the mantissa of
+// an fp16 whose exponent field is that of 1024 (mantissa ulp 1), so each half reads
+// t = 1024 + 16 q exactly: the pair (k1, k5) of a word is already there (bits 4-7 and 20-23),
+// the pairs (k0, k4), (k2, k6), (k3, k7) need the word shifted by 4 left, 4 right or 8 right
+// first. One AND-OR per pair, three shifts per word: 11 VALU per 8 codes with the four dot2
+// (the exact unpack takes 13). Then
+//     sum_k t_k x_k = 16 sum_k q_k x_k + 1024 sum_k x_k,
+// so a dot whose fp32 accumulator starts at -1024 sum(x) ends at 16 q.x. The running sum
+// carries magnitudes ~64 times those of q.x (the ratio of 1024 to 16), so its absolute rounding
+// error grows with |x|; with the nibble in the low bits (t = 1024 + q) the ratio would be 1024
+// and the error sixteen times larger. Callers keep the factor 16 on both halves of the affine
+// form (s * dot + b * 16 sum(x)) and scale the finished row by 1/16, exact in binary.
+DHP_DEV void unpack8_off(uint32_t w, h2 t[4], const NibConsts& k) {
+    t[0] = as_h2(((w << 4) & k.hi) | k.magic);   // (k0, k4)
+    t[1] = as_h2((w & k.hi) | k.magic);          // (k1, k5)
+    t[2] = as_h2(((w >> 4) & k.hi) | k.magic);   // (k2, k6)
+    t[3] = as_h2(((w >> 8) & k.hi) | k.magic);   // (k3, k7)
 }
 
-// Load 32 fp16 activations starting at p (16-byte aligned) into 16 permuted pairs and
-// return their fp32 sum (the factor multiplying the group bias).
-DHP_DEV float load_x32(const _Float16* p, h2* xp) {
-    const u32x4* v = reinterpret_cast<const u32x4*>(p);
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 u = v[i];
-        permute8(u.x, u.y, u.z, u.w, xp + 4 * i);
-        h2 a = as_h2(u.x), b = as_h2(u.y), c = as_h2(u.z), d = as_h2(u.w);
-        s += ((float)a.x + (float)a.y) + ((float)b.x + (float)b.y) + ((float)c.x + (float)c.y) +
-             ((float)d.x + (float)d.y);
-    }
-    return s;
-}
-
-// Raw form of the 32-code dot product. The code pairs stay in their fp16 "magic" form,
-// t = 1024 + q for even k (low nibbles) and t = 1024 + 16 q for odd k (high nibbles), and the
-// activations of the odd-k slots are pre-scaled by 1/16 (a power of two: exact in fp16 outside
-// the subnormal range), so
-//     sum_k t_k x'_k = sum_k q_k x_k + 1024 * sum_even x + 64 * sum_odd x.
-// load_x32_raw returns that correction (to be subtracted) and the plain sum of the 32
-// activations; dot32_f16_raw starts its accumulator at -correction. It saves the exact unpack's
-// subtract and fma per code pair (9 instead of 13 VALU per 8 codes); the price is that the
-// running fp32 sum carries magnitudes ~1024 x sum(x) instead of ~8 x sum(x), i.e. an absolute
-// rounding error of order 1e-3 per 32-code chunk before the group scale (~1e-2) multiplies it.
-DHP_DEV void unpack8_raw(uint32_t w, h2 t[4], const NibConsts& k) {
-    const uint32_t w8 = w >> 8;
-    t[0] = as_h2((w & k.lo) | k.magic);
-    t[1] = as_h2((w & k.hi) | k.magic);
-    t[2] = as_h2((w8 & k.lo) | k.magic);
-    t[3] = as_h2((w8 & k.hi) | k.magic);
-}
-
-DHP_DEV float dot32_f16_raw(const u32x4 c, const h2* xp, float neg_corr, const NibConsts& k) {
+// 16 * (q . x) over one 32-code chunk: c holds the codes (16 bytes), xp the 16 permuted
+// activation pairs, neg_corr = -1024 * (their sum).
+DHP_DEV float dot32_off(const u32x4 c, const h2* xp, float neg_corr, const NibConsts& k) {
     float d = neg_corr;
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         h2 t[4];
-        unpack8_raw(w[i], t, k);
+        unpack8_off(w[i], t, k);
         d = __builtin_amdgcn_fdot2(t[0], xp[4 * i], d, false);
         d = __builtin_amdgcn_fdot2(t[1], xp[4 * i + 1], d, false);
         d = __builtin_amdgcn_fdot2(t[2], xp[4 * i + 2], d, false);
@@ -138,31 +97,27 @@ DHP_DEV float dot32_f16_raw(const u32x4 c, const h2* xp, float neg_corr, const N
     return d;
 }
 
-// 32 fp16 activations (four 16-byte words, k order) as 16 permuted pairs with the odd-k slots
-// scaled by 1/16; returns their plain fp32 sum and sets neg_corr = -(1024 sum_even + 64 sum_odd).
-// (Both products are exact, so the result does not depend on whether they are fused.)
-DHP_DEV float x32_raw_from(const u32x4 (&v)[4], h2* xp, float& neg_corr) {
-    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-    float even = 0.0f, odd = 0.0f;
+// 32 fp16 activations (four 16-byte words, k order) as 16 permuted pairs; returns 16 times their
+// fp32 sum (the factor of the group bias in the offset form) and sets neg_corr = -1024 * sum.
+DHP_DEV float x32_off_from(const u32x4 (&v)[4], h2* xp, float& neg_corr) {
+    float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const u32x4 u = v[i];
         permute8(u.x, u.y, u.z, u.w, xp + 4 * i);
         const h2 a = as_h2(u.x), b = as_h2(u.y), c = as_h2(u.z), d = as_h2(u.w);
-        even += ((float)a.x + (float)b.x) + ((float)c.x + (float)d.x);
-        odd += ((float)a.y + (float)b.y) + ((float)c.y + (float)d.y);
-        xp[4 * i + 1] = xp[4 * i + 1] * sixteenth;
-        xp[4 * i + 3] = xp[4 * i + 3] * sixteenth;
+        s += (((float)a.x + (float)a.y) + ((float)b.x + (float)b.y)) +
+             (((float)c.x + (float)c.y) + ((float)d.x + (float)d.y));
     }
-    neg_corr = -(1024.0f * even + 64.0f * odd);
-    return even + odd;
+    neg_corr = -1024.0f * s;
+    return 16.0f * s;
 }
 
 // The same for the 32 activations at p (16-byte aligned).
-DHP_DEV float load_x32_raw(const _Float16* p, h2* xp, float& neg_corr) {
+DHP_DEV float load_x32_off(const _Float16* p, h2* xp, float& neg_corr) {
     const u32x4* q = reinterpret_cast<const u32x4*>(p);
     const u32x4 v[4] = {q[0], q[1], q[2], q[3]};
-    return x32_raw_from(v, xp, neg_corr);
+    return x32_off_from(v, xp, neg_corr);
 }
 
 // sum over 32 codes of q * x for fp32 activations x[0..31] (contiguous k order).

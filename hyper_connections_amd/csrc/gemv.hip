@@ -14,7 +14,9 @@
 //    registers (K = 2560: 80 VGPRs). A block walks rows with a grid stride and keeps the
 //    next row group's codes in flight while it computes the current one.
 //  * Per 64-weight group the affine form is factored: s * sum(q*x) + b * sum(x); the
-//    inner sum runs on v_dot2_f32_f16 over exactly converted codes (see unpack8).
+//    inner sum runs on v_dot2_f32_f16 over the codes in their offset fp16 form (see
+//    unpack8_off), which carries a factor 16 through both halves; the finished row is
+//    scaled by 1/16 (exact).
 //  * The 16 partial sums of a row meet in a fixed butterfly, so a row's value does not
 //    depend on which block, wave or lane group computed it: duplicated rows give equal
 //    bits, which is what the argmax tie rule needs.
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     h2 xp[CPL][16];
     float xs[CPL], nc[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) xs[i] = load_x32_raw(x + (size_t)(j + LPR * i) * 32, xp[i], nc[i]);
+    for (int i = 0; i < CPL; ++i) xs[i] = load_x32_off(x + (size_t)(j + LPR * i) * 32, xp[i], nc[i]);
 
     const NibConsts nk = nib_consts();
     float best_v = -INFINITY;
@@ -109,11 +111,11 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const float d = dot32_f16_raw(r[i].c, xp[i], nc[i], nk);
+            const float d = dot32_off(r[i].c, xp[i], nc[i], nk);
             acc = __builtin_fmaf(bf16_to_f32(r[i].s), d, acc);
             acc = __builtin_fmaf(bf16_to_f32(r[i].b), xs[i], acc);
         }
-        acc = group_sum<LPR>(acc);
+        acc = group_sum<LPR>(acc) * 0.0625f;
         if (j == 0 && row < N) {
             if constexpr (F32OUT) reinterpret_cast<float*>(y)[row] = acc;
             else reinterpret_cast<_Float16*>(y)[row] = (_Float16)acc;
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
 }
 
 // Any K (multiple of 64, <= 16384): activations staged once per block in LDS as permuted
-// pairs plus per-chunk sums; lane j walks chunks j, j+16, ... of each row.
+// pairs plus per-chunk (16 sum, -1024 sum); lane j walks chunks j, j+16, ... of each row with
+// the same operations, in the same order, as k_gemv_m1_reg.
 template <bool F32OUT, bool ARGMAX>
 __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales,
@@ -135,10 +138,12 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
     extern __shared__ u32x4 lds_x[];            // [CH][4] u32x4 = 16 permuted pairs per chunk
     const int CH = K / 32;
     const int G = K / 64;
-    float* lds_sum = reinterpret_cast<float*>(lds_x + (size_t)CH * 4);
+    float2* lds_sum = reinterpret_cast<float2*>(lds_x + (size_t)CH * 4);
     for (int ch = threadIdx.x; ch < CH; ch += blockDim.x) {
         h2 p[16];
-        lds_sum[ch] = load_x32(x + (size_t)ch * 32, p);
+        float nc;
+        const float xs = load_x32_off(x + (size_t)ch * 32, p, nc);
+        lds_sum[ch] = float2{xs, nc};
         u32x4* dst = lds_x + (size_t)ch * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -153,6 +158,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
     const NibConsts nk = nib_consts();
     float best_v = -INFINITY;
     int best_i = INT_MAX;
+    // whole 16-lane groups share a row, so the DPP sum below sees only live lanes
     for (int row = blockIdx.x * rpb + t / LPR; row < N; row += gridDim.x * rpb) {
         const u32x4* cr = codes + (size_t)row * CH;
         const uint16_t* sr = scales + (size_t)row * G;
@@ -168,11 +174,12 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
                 p[4 * i] = as_h2(u.x); p[4 * i + 1] = as_h2(u.y);
                 p[4 * i + 2] = as_h2(u.z); p[4 * i + 3] = as_h2(u.w);
             }
-            const float d = dot32_f16(c, p, nk);
+            const float2 sn = lds_sum[ch];
+            const float d = dot32_off(c, p, sn.y, nk);
             acc = __builtin_fmaf(bf16_to_f32(sr[ch >> 1]), d, acc);
-            acc = __builtin_fmaf(bf16_to_f32(br[ch >> 1]), lds_sum[ch], acc);
+            acc = __builtin_fmaf(bf16_to_f32(br[ch >> 1]), sn.x, acc);
         }
-        acc = group_sum<LPR>(acc);
+        acc = group_sum<LPR>(acc) * 0.0625f;
         if (j == 0) {
             if constexpr (F32OUT) reinterpret_cast<float*>(y)[row] = acc;
             else reinterpret_cast<_Float16*>(y)[row] = (_Float16)acc;
@@ -287,7 +294,7 @@ int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t
         case 6: e = launch_reg<6>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
         case 8: e = launch_reg<8>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
         default: {
-            const size_t lds = (size_t)CH * 64 + (size_t)CH * 4;
+            const size_t lds = (size_t)CH * 64 + (size_t)CH * 8;
             if (y_f32 && am) hipLaunchKernelGGL((k_gemv_m1_lds<true, true>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);
             else if (y_f32) hipLaunchKernelGGL((k_gemv_m1_lds<true, false>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);
             else if (am) hipLaunchKernelGGL((k_gemv_m1_lds<false, true>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);

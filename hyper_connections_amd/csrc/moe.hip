@@ -63,9 +63,9 @@ struct MoeArgs {
     int32_t* route;    // ws [M][top_k + 1] (batched only): (token << 4 | slot), grouped by expert
     int32_t* items;    // ws [max items][4] (batched only): (expert, first route entry, count, 0)
     int32_t* nitems;   // ws [1] (batched only): work items in use
-    u32x4* xraw;       // ws [M][4][hidden / 32] (batched only): each token's activations in the raw form of
-                       // x32_raw_from (16 permuted pairs per 32-value chunk, as 4 u32x4 planes)
-    float2* xrsum;     // ws [M][hidden / 32] (batched only): per chunk, (plain sum, negated correction)
+    u32x4* xraw;       // ws [M][4][hidden / 32] (batched only): each token's activations in the form of
+                       // x32_off_from (16 permuted pairs per 32-value chunk, as 4 u32x4 planes)
+    float2* xrsum;     // ws [M][hidden / 32] (batched only): per chunk, (16 * sum, -1024 * sum)
     _Float16* out;     // [M][hidden]
     int32_t* ids;      // [M][top_k]
     float* weights;    // [M][top_k]
@@ -97,7 +97,8 @@ DHP_DEV void load_pair(PairRegs<CPL>& p, const u32x4* gc, const uint16_t* gs, co
 }
 
 // silu(gate . x) * (up . x), the same value in every lane of the 16-lane group. The chunk dots
-// use the raw code form (see dot32_f16_raw) with the activations' per-chunk corrections nc.
+// use the offset code form (see dot32_off) with the activations' per-chunk corrections nc and
+// sixteenfold sums xs; each finished dot is scaled back by 1/16 (exact).
 // k_moep_phase1 repeats these operations in this order (reading its activations from LDS).
 template <int CPL>
 DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* xs, const float* nc) {
@@ -105,13 +106,13 @@ DHP_DEV float pair_act(const PairRegs<CPL>& p, const h2 (*xp)[16], const float* 
     float ag = 0.0f, au = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_f16_raw(p.cg[i], xp[i], nc[i], nk), ag);
+        ag = __builtin_fmaf(bf16_to_f32(p.sg[i]), dot32_off(p.cg[i], xp[i], nc[i], nk), ag);
         ag = __builtin_fmaf(bf16_to_f32(p.bg[i]), xs[i], ag);
-        au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_f16_raw(p.cu[i], xp[i], nc[i], nk), au);
+        au = __builtin_fmaf(bf16_to_f32(p.su[i]), dot32_off(p.cu[i], xp[i], nc[i], nk), au);
         au = __builtin_fmaf(bf16_to_f32(p.bu[i]), xs[i], au);
     }
-    ag = group_sum<LPR>(ag);
-    au = group_sum<LPR>(au);
+    ag = group_sum<LPR>(ag) * 0.0625f;
+    au = group_sum<LPR>(au) * 0.0625f;
     return silu_f(ag) * au;
 }
 
@@ -253,11 +254,11 @@ DHP_DEV size_t router_row_bytes(int kind, int hidden) {
     return (size_t)hidden * (kind == RK_F32 ? 4 : kind == RK_BF16 ? 2 : 1);
 }
 
-// Lane j's activations for pair_act: chunks j + 16 i in the raw form of load_x32_raw.
+// Lane j's activations for pair_act: chunks j + 16 i in the offset form of load_x32_off.
 template <int CPL>
 DHP_DEV void load_x_regs(const _Float16* x, int j, h2 (*xp)[16], float* xs, float* nc) {
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) xs[i] = load_x32_raw(x + (size_t)(j + LPR * i) * 32, xp[i], nc[i]);
+    for (int i = 0; i < CPL; ++i) xs[i] = load_x32_off(x + (size_t)(j + LPR * i) * 32, xp[i], nc[i]);
 }
 
 // Blocks [0, E): router rows. Block E: shared gate logit. Blocks after: 4 shared pairs each.
@@ -634,9 +635,9 @@ __global__ __launch_bounds__(64 * P2W) void k_moe_phase2(MoeArgs a) {
 //  k_moep_router : one wave per router row (and one for the shared gate row): the row is loaded
 //                  once and dotted with a group of tokens, four tokens' activations in flight.
 //  k_moep_topk   : one wave per token: the decode's top-k and softmax, and the token's activations
-//                  in the raw form pair_act multiplies (once per token, into the workspace).
+//                  in the offset form pair_act multiplies (once per token, into the workspace).
 //  k_moep_phase1 : block = (16 rows, expert): the (token, slot) pairs routed to the expert, read
-//                  off the ids, run through pair_act; the tokens' raw-form activations are copied
+//                  off the ids, run through pair_act; the tokens' offset-form activations are copied
 //                  into LDS a group at a time. Expert E is the shared one, taken by every token in
 //                  slot top_k.
 //  k_moep_phase2 : block = (64 down rows, expert): each routed (token, slot) gets its down-row
@@ -709,7 +710,7 @@ __global__ __launch_bounds__(64) void k_moep_topk(MoeArgs a) {
     if (threadIdx.x == 0)
         publish_topk(ids, vals, a.top_k, a.expert_scale, a.ids + (size_t)m * a.top_k,
                      a.weights + (size_t)m * a.top_k);
-    // the token's activations in the raw form phase 1 multiplies, once per token (every phase-1
+    // the token's activations in the form phase 1 multiplies, once per token (every phase-1
     // block that stages the token copies them instead of converting them again)
     const int CH32 = a.hidden >> 5;
     for (int c = threadIdx.x; c < CH32; c += 64) {
@@ -717,7 +718,7 @@ __global__ __launch_bounds__(64) void k_moep_topk(MoeArgs a) {
         const u32x4 v[4] = {src[0], src[1], src[2], src[3]};
         h2 xp[16];
         float nc;
-        const float xs = x32_raw_from(v, xp, nc);
+        const float xs = x32_off_from(v, xp, nc);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             a.xraw[((size_t)m * 4 + q) * CH32 + c] = u32x4{h2_bits(xp[4 * q]), h2_bits(xp[4 * q + 1]),
@@ -815,7 +816,7 @@ __global__ __launch_bounds__(256, CPL <= 5 ? 3 : 2) void k_moep_phase1(MoeArgs a
         const int tn = min(P1_TG, n - base);
         __syncthreads();                               // the previous group's reads are done
         // every load of the group first (items past the group clamped), then the stores
-        // the tokens' activations were put in the raw form once per token (k_moep_topk): copy them
+        // the tokens' activations were put in the offset form once per token (k_moep_topk): copy them
         u32x4 v[IT][4];
         float2 vs[IT];
 #pragma unroll
@@ -839,7 +840,7 @@ __global__ __launch_bounds__(256, CPL <= 5 ? 3 : 2) void k_moep_phase1(MoeArgs a
         }
         __syncthreads();
         // pair_act's operations in its order for every token, the activations read a chunk at a
-        // time. The codes' raw fp16 form depends only on the weights, so each chunk is unpacked
+        // time. The codes' offset fp16 form depends only on the weights, so each chunk is unpacked
         // once for all the group's tokens; each token's sums run in pair_act's order, so its value
         // is the decode call's bit for bit.
         const NibConsts nk = nib_consts();
@@ -854,8 +855,8 @@ __global__ __launch_bounds__(256, CPL <= 5 ? 3 : 2) void k_moep_phase1(MoeArgs a
             h2 tg[16], tu[16];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                unpack8_raw(wg[w], tg + 4 * w, nk);
-                unpack8_raw(wu[w], tu + 4 * w, nk);
+                unpack8_off(wg[w], tg + 4 * w, nk);
+                unpack8_off(wu[w], tu + 4 * w, nk);
             }
 #pragma unroll
             for (int t = 0; t < P1_TG; ++t) {
@@ -883,8 +884,8 @@ __global__ __launch_bounds__(256, CPL <= 5 ? 3 : 2) void k_moep_phase1(MoeArgs a
 #pragma unroll
         for (int t = 0; t < P1_TG; ++t) {
             if (t < tn) {
-                const float g1 = group_sum<LPR>(ag[t]);
-                const float u1 = group_sum<LPR>(au[t]);
+                const float g1 = group_sum<LPR>(ag[t]) * 0.0625f;
+                const float u1 = group_sum<LPR>(au[t]) * 0.0625f;
                 const float v1 = silu_f(g1) * u1;
                 const int ms = list[base + t];
                 if (j == 0 && live) a.act[((size_t)(ms >> 4) * nslot + (ms & 15)) * a.inter + row] = v1;

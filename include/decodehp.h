@@ -214,11 +214,11 @@ int decodehp_moe_prefill_ex(const void* x, int32_t m, const dhp_router* router, 
 /*
  * decodehp_hc_read -- one hyper-connection read (attn_hc / mlp_hc / the final mixer).
  * "src/families/qwen4/mod.rs", section Hyper-connections, and "src/families/qwen4/hc.rs",
- * encode_hyper_connection: with the residual `raw` viewed as C streams of width H,
- *     normed    = raw / sqrt(mean over each stream of raw^2 + eps) * hc_norm  (direct scale)
- *     lo        = silu(down(normed) / C)
- *     mixed     = mean over streams of sigmoid(up(lo)) * normed                -> fp16 [H]
- *     inject_w  = 2 * sigmoid(inject(normed) / C)                              -> fp32 [C]
+ * encode_hyper_connection. Element (c, h) of the C streams of width H sits at c*H + h. With
+ * rho[c] the RMS of stream c (eps inside the root), n[c,h] = raw[c,h] / rho[c] * hc_norm[c,h]
+ * (the stored weight multiplies as is), lo[r] = silu(sum_j down[r][j] n[j] / C),
+ * mixed[h] = (1/C) sum_c sigmoid(sum_r up[c*H+h][r] lo[r]) * n[c,h] (fp16 [H]) and
+ * inject_w[c] = 2 sigmoid(sum_j inject[c][j] n[j] / C) (fp32 [C]).
  * `raw` is read and never written (hc.rs doc); the caller injects separately.
  *   raw     : fp16 [C*H], 16-byte aligned.   hc_norm : bf16 [C*H], 16-byte aligned.
  *   down    : [R x C*H].   up : [C*H x R].   inject : [C x C*H] or NULL (final mixer).

@@ -1,29 +1,29 @@
-"""Hyper-connection read and inject for one token, in float64.
+"""Hyper-connection read and inject for one token, in float64 (test infrastructure: only the
+tests, the smoke check and the benchmark's CPU baseline use this package).
 
-"src/families/qwen4/mod.rs", section "Hyper-connections", and "src/families/qwen4/hc.rs",
-encode_hyper_connection. With C streams of width H (residual C*H wide), in the pages'
-order:
+Defined by "src/families/qwen4/mod.rs", section "Hyper-connections" (with its decoder-layer
+pseudocode and the note on the injection trap), and by "src/families/qwen4/hc.rs",
+encode_hyper_connection. The residual holds C streams of width H; element (c, h) sits at
+index c*H + h. Written per element, with W_d [R x C*H], W_u [C*H x R], W_i [C x C*H] the
+three INT4-affine projections (the pages run them through a dtype-generic GEMV) and
+gamma the stored norm weight:
 
-    normed  = grouped RMS norm of raw, one group per stream, scaled directly by hc_norm
-    lo      = silu(down(normed) / C)                      C*H -> R
-    u       = sigmoid(up(lo))                             R -> C*H, no 1/C here
-    mixed   = mean over the C streams of u * normed       -> H
-    inject  = 2 * sigmoid(block_inject(normed) / C)       C*H -> C  (absent on the final mixer)
+  rho[c]      = sqrt( (1/H) * sum_h raw[c,h]^2 + eps )            one RMS per stream
+  n[c,h]      = raw[c,h] / rho[c] * gamma[c,h]                     gamma applied as stored,
+                                                                   not as 1 + gamma (hc.rs doc)
+  lo[r]       = silu( (1/C) * sum_{c,h} W_d[r, c*H+h] * n[c,h] )   first of the two 1/C
+  u[c,h]      = sigmoid( sum_r W_u[c*H+h, r] * lo[r] )             no 1/C on this projection
+  mixed[h]    = (1/C) * sum_c u[c,h] * n[c,h]                      a mean over streams, not a sum
+  iw[c]       = 2 * sigmoid( (1/C) * sum_{c',h} W_i[c, c'*H+h] * n[c',h] )   second 1/C;
+                                                                   absent on the final mixer
+  hidden[c,h] = raw[c,h] + out[h] * iw[c]                          the sublayer output lands on
+                                                                   the un-normalized stream
 
-and the inject of the decoder-layer pseudocode (same page, "The decoder layer, as
-pseudocode", and "THE INJECTION TRAP"): the sublayer output is added to the
-UN-normalized raw stream, scaled per stream,
-
-    hidden[c*H + h] = raw[c*H + h] + out[h] * inject[c].
-
-RMS norm: x / sqrt(mean(x^2) + eps) * weight with eps = RMS_EPS = 1e-6 (constant on the
-qwen4 page); the weight multiplies directly (hc.rs doc: the stored GGUF scale is
-applied as is, not as 1 + w). The three projections are INT4-affine GEMVs here (the
-pages dispatch them through a dtype-generic GEMV).
+with eps = 1e-6 (the qwen4 page's RMS epsilon) and silu(z) = z * sigmoid(z).
 
 Parity: pinned (constant-input norm closed form, per-group independence, scale
-invariance, zero-weight closed forms for u = 1/2 and inject = 1, selector closed forms
-that fix both 1/C divisions and the MEAN, C=1 plain residual add, hand-worked C=2
+invariance, zero-weight closed forms for u = 1/2 and iw = 1, selector closed forms
+that fix both 1/C divisions and the mean, C=1 plain residual add, hand-worked C=2
 inject fixture; mutated oracles with a third 1/C, a sum for the mean, or the inject
 into the normed stream fail these pins).
 """
@@ -46,34 +46,42 @@ def _sigmoid(z):
 
 
 def grouped_rmsnorm(raw, gamma_bits, C: int, H: int, eps: float = RMS_EPS) -> np.ndarray:
-    """n[c,h] = raw[c,h] / sqrt(mean_h raw[c,:]^2 + eps) * gamma[c,h]; returns flat [C*H]."""
+    """n[c,h] = raw[c,h] / rho[c] * gamma[c,h], rho[c] = sqrt(mean_h raw[c,h]^2 + eps); flat [C*H]."""
     x = np.asarray(raw, dtype=np.float64).reshape(C, H)
     g = bf16_bits_to_f64(gamma_bits).reshape(C, H)
-    rms = np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
-    return (x / rms * g).reshape(C * H)
+    rho = np.sqrt(np.sum(x * x, axis=1) / H + eps)
+    return (x / rho[:, None] * g).reshape(C * H)
+
+
+def _project(w, v) -> np.ndarray:
+    """sum_j W[i, j] * v[j] for an INT4-affine W, in float64."""
+    return dequant_gemv(w.q, w.s_bits, w.b_bits, v)
 
 
 def hc_read(raw, gamma_bits, down, up, inject, C: int, H: int, eps: float = RMS_EPS):
-    """One hyper-connection call. ``inject`` may be None (the final mixer).
+    """One hyper-connection read. ``inject`` may be None (the final mixer).
 
-    Returns dict(mixed [H], inject_w [C] or None, normed, lo, u).
+    Returns dict(mixed [H], inject_w [C] or None, normed [C*H], lo [R], u [C*H]).
     """
     n = grouped_rmsnorm(raw, gamma_bits, C, H, eps)
-    lo = _silu(dequant_gemv(down.q, down.s_bits, down.b_bits, n) / C)
-    u = _sigmoid(dequant_gemv(up.q, up.s_bits, up.b_bits, lo))
-    mixed = (u.reshape(C, H) * n.reshape(C, H)).mean(axis=0)
+    lo = _silu(_project(down, n) / C)
+    u = _sigmoid(_project(up, lo))
+    mixed = np.sum(u.reshape(C, H) * n.reshape(C, H), axis=0) / C
     iw = None
     if inject is not None:
-        iw = 2.0 * _sigmoid(dequant_gemv(inject.q, inject.s_bits, inject.b_bits, n) / C)
+        iw = 2.0 * _sigmoid(_project(inject, n) / C)
     return {"mixed": mixed, "inject_w": iw, "normed": n, "lo": lo, "u": u}
 
 
 def hc_inject(raw, out, inject_w, C: int, H: int) -> np.ndarray:
-    """hidden = raw + (out[None, :] * inject_w[:, None]).flatten(), in float64; flat [C*H]."""
+    """hidden[c*H + h] = raw[c*H + h] + out[h] * iw[c], in float64; flat [C*H]."""
     r = np.asarray(raw, dtype=np.float64).reshape(C, H)
-    o = np.asarray(out, dtype=np.float64).reshape(1, H)
-    w = np.asarray(inject_w, dtype=np.float64).reshape(C, 1)
-    return (r + o * w).reshape(C * H)
+    o = np.asarray(out, dtype=np.float64)
+    w = np.asarray(inject_w, dtype=np.float64)
+    hidden = np.empty((C, H), dtype=np.float64)
+    for c in range(C):
+        hidden[c] = r[c] + o * w[c]
+    return hidden.reshape(C * H)
 
 
 def hc_read_batched(raw_rows, gamma_bits, down, up, inject, C: int, H: int, eps: float = RMS_EPS):

@@ -36,7 +36,9 @@ two experts; the pages' softmax-order identity; weights sum to one; identical-ex
 invariant; selector-weight closed forms for gate/up/down and the shared gate; the router
 scales: a one-hot per-element scale gives one column of R times x[n], a power-of-two scale
 multiplies the logits exactly, INT8 one-hot rows incl. code -128 give signed x values, the
-per-expert scale of a top-1 route is its weight and never changes the selection).
+per-expert scale of a top-1 route is its weight and never changes the selection; the fp16
+boundary by hand-built layers whose routed sum is 1 + 2^-12 and whose gated shared half is
+1/2 + 2^-13, values that fp16 rounds to 1 and 1/2).
 """
 from __future__ import annotations
 
@@ -98,6 +100,18 @@ def expert_down(expert, act) -> np.ndarray:
     return dequant_gemv(d.q, d.s_bits, d.b_bits, act)
 
 
+def combine(routed, shared_gated, fp16_boundary: bool = False) -> np.ndarray:
+    """The layer output from its two halves. Default: routed + shared_gated, unrounded (the
+    caller rounds once to fp16). fp16 boundary ("src/families/qwen4/mod.rs", section "MoE": the
+    routed expert sum is cast to the model dtype before the gated shared expert is added): each
+    half is rounded to fp16 (round to nearest even) first, then they are added."""
+    routed = np.asarray(routed, dtype=np.float64)
+    shared_gated = np.asarray(shared_gated, dtype=np.float64)
+    if fp16_boundary:
+        return routed.astype(np.float16).astype(np.float64) + shared_gated.astype(np.float16).astype(np.float64)
+    return routed + shared_gated
+
+
 def moe_decode(x, router_bits, sgate_bits, shared, experts, top_k: int,
                fp16_boundary: bool = False, router_is_bf16_bits: bool = True, elem_scale_bits=None,
                expert_scale=None):
@@ -120,10 +134,7 @@ def moe_decode(x, router_bits, sgate_bits, shared, experts, top_k: int,
         routed += w[j] * expert_down(ex, expert_act(ex, x))
     g = float(bf16_bits_to_f64(sgate_bits) @ x)
     shared_gated = (1.0 / (1.0 + math.exp(-g))) * expert_down(shared, expert_act(shared, x))
-    if fp16_boundary:
-        out = routed.astype(np.float16).astype(np.float64) + shared_gated.astype(np.float16).astype(np.float64)
-    else:
-        out = routed + shared_gated
+    out = combine(routed, shared_gated, fp16_boundary)
     return {"out": out, "ids": ids, "weights": w, "logits": logits, "routed": routed,
             "shared_gated": shared_gated, "gate": g}
 

@@ -1,0 +1,177 @@
+"""GPU parity at large activations: every call whose dot products run on the offset code form
+(t = 1024 + 16 q, the accumulator started at -1024 sum(x)) against the fp64 oracle with the
+activations scaled up, where that form's rounding (proportional to |x|) is largest.
+
+Bar: |gpu - oracle| <= 1e-3 + 1e-2 |oracle| elementwise, argmax and expert ids exact. Scales:
+activation standard deviation 8 and 32, and N(0, 1) activations with sixteen channels set to
++-64 (outliers). The fp16 outputs of the MoE layer grow with the square of the scale; tokens
+whose oracle output exceeds the fp16 range are left out and counted.
+
+At these scales a few MoE outputs are small differences of large terms: an output of 0.14
+whose routed and gated-shared halves are -7488 and +7488, each a 512-term dot product whose
+terms' magnitudes add up to ~1e5. Any fp32 evaluation of such a dot carries an absolute
+rounding error of order 1e-2 there (the fp32 spacing at 1e4 is 1e-3), above the bar's 1e-3
+floor. The MoE cases therefore add the standard fp32 allowance for a dot product to the bar:
+2^-19 (32 units of fp32 rounding) times the sum of the magnitudes of every term that feeds
+the output, sum_j w_j sum_i |D_j[h,i] a_j[i]| + sigmoid(g) sum_i |D_s[h,i] a_s[i]|, taken
+from the oracle's own fp64 pieces. The GEMV cases use the plain bar.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_within_tol, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+hca = pytest.importorskip("hyper_connections_amd")
+
+F16_MAX = 65504.0
+
+
+def scaled(x, sigma):
+    """fp16(x * sigma) for an fp16 N(0, 1) draw x."""
+    return synth.to_f16(np.asarray(x, np.float64) * sigma)
+
+
+def with_outliers(x, seed, count=16, value=64.0):
+    rng = np.random.default_rng([81, seed])
+    y = np.array(x, dtype=np.float16, copy=True)
+    idx = rng.choice(y.shape[-1], count, replace=False)
+    y[..., idx] = (rng.choice([-1.0, 1.0], count) * value).astype(np.float16)
+    return y
+
+
+def gemv(t, x, out_dtype=None, argmax=False):
+    w = hca.Int4Weight.from_logical(t.q, t.s_bits, t.b_bits)
+    r = hca.dequant_gemv(w, torch.from_numpy(np.ascontiguousarray(x)).cuda(),
+                         out_dtype=out_dtype or torch.float16, argmax=argmax)
+    torch.cuda.synchronize()
+    return r
+
+
+@pytest.mark.parametrize("kind", ["sigma8", "sigma32", "outliers"])
+def test_gemv_2560_large_activations(kind):
+    say(f"gemv 2560 {kind}")
+    d = synth.gemv_workload(0)
+    x = {"sigma8": lambda: scaled(d["x"], 8), "sigma32": lambda: scaled(d["x"], 32),
+         "outliers": lambda: with_outliers(d["x"], 0)}[kind]()
+    y = gemv(d["w"], x, out_dtype=torch.float32)
+    ref = oracle.dequant_gemv(d["w"].q, d["w"].s_bits, d["w"].b_bits, x)
+    assert_within_tol(y.cpu().numpy(), ref, f"gemv {kind}")
+
+
+@pytest.fixture(scope="module")
+def lmhead():
+    say("lm head workload 151936x2560 (generating)")
+    return synth.lmhead_workload(0, m=1)
+
+
+@pytest.mark.parametrize("kind", ["sigma8", "sigma32", "outliers"])
+def test_lmhead_m1_large_activations(lmhead, kind):
+    say(f"lm head M=1 {kind}")
+    d = lmhead
+    x0 = d["x"][0]
+    x = {"sigma8": lambda: scaled(x0, 8), "sigma32": lambda: scaled(x0, 32),
+         "outliers": lambda: with_outliers(x0, 1)}[kind]()
+    logits, am = gemv(d["w"], x, out_dtype=torch.float32, argmax=True)
+    ref = oracle.dequant_gemv(d["w"].q, d["w"].s_bits, d["w"].b_bits, x)
+    g = logits.cpu().numpy().reshape(-1)
+    assert_within_tol(g, ref, f"lm head {kind}")
+    assert int(am.cpu()[0]) == int(oracle.argmax_lowest(ref))
+    near = np.abs(ref) < 0.05
+    err = np.abs(g - ref)
+    print(f"{kind}: {int(near.sum())} logits below 0.05 in magnitude, worst |error| there "
+          f"{float(err[near].max()) if near.any() else 0.0:.3g}, worst |error| overall {float(err.max()):.3g}")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    say("moe workload E=256 (generating 256 experts)")
+    d = synth.moe_workload(0)
+    ex = d["experts"]
+    dev = dict(gate=hca.Int4Experts.from_logical([e["gate"] for e in ex]),
+               up=hca.Int4Experts.from_logical([e["up"] for e in ex]),
+               down=hca.Int4Experts.from_logical([e["down"] for e in ex]),
+               sg=hca.Int4Weight.from_logical(d["shared"]["gate"].q, d["shared"]["gate"].s_bits, d["shared"]["gate"].b_bits),
+               su=hca.Int4Weight.from_logical(d["shared"]["up"].q, d["shared"]["up"].s_bits, d["shared"]["up"].b_bits),
+               sd=hca.Int4Weight.from_logical(d["shared"]["down"].q, d["shared"]["down"].s_bits, d["shared"]["down"].b_bits),
+               router=hca.bf16_bits_to_tensor(d["router_bits"]).cuda(),
+               sgate=hca.bf16_bits_to_tensor(d["sgate_bits"]).cuda())
+    return d, dev
+
+
+def _moe_args(dev, top_k):
+    return (dev["router"], dev["sgate"], dev["gate"], dev["up"], dev["down"], dev["sg"], dev["su"], dev["sd"], top_k)
+
+
+FP32_DOT_ALLOWANCE = 2.0 ** -19
+
+
+def _oracle_rows(d, X):
+    return [oracle.moe_decode(x, d["router_bits"], d["sgate_bits"], d["shared"], d["experts"], d["top_k"]) for x in X]
+
+
+def _term_magnitudes(d, x, ref):
+    """sum over every product feeding out[h] of its magnitude, in fp64 from the oracle's pieces."""
+    def part(ex):
+        a = oracle.expert_act(ex, x)
+        D = oracle.dequant(ex["down"].q, ex["down"].s_bits, ex["down"].b_bits)
+        return np.abs(D) @ np.abs(a)
+    tot = np.zeros(ref["out"].shape[0])
+    for j, e in enumerate(ref["ids"]):
+        tot += abs(ref["weights"][j]) * part(d["experts"][int(e)])
+    return tot + part(d["shared"]) / (1.0 + np.exp(-ref["gate"]))
+
+
+def _check_out(got, ref, mag, what):
+    bar = 1e-3 + 1e-2 * np.abs(ref["out"]) + FP32_DOT_ALLOWANCE * mag
+    err = np.abs(np.asarray(got, np.float64) - ref["out"])
+    bad = np.flatnonzero(err > bar)
+    plain = int(np.sum(err > 1e-3 + 1e-2 * np.abs(ref["out"])))
+    assert bad.size == 0, f"{what}: {bad.size} outside the bar, first [{bad[0]}] gpu={got[bad[0]]} oracle={ref['out'][bad[0]]}"
+    return plain
+
+
+@pytest.mark.parametrize("sigma", [8, 32])
+def test_moe_decode_large_activations(moe, sigma):
+    d, dev = moe
+    X = [scaled(x, sigma) for x in np.concatenate([d["x"][None], synth.moe_x_ring(0, 3)])]
+    refs = _oracle_rows(d, X)
+    checked = plain = 0
+    for i, (x, ref) in enumerate(zip(X, refs)):
+        if np.abs(ref["out"]).max() > F16_MAX:
+            continue
+        say(f"moe decode sigma={sigma} token {i}")
+        out, ids, w = hca.moe_decode(torch.from_numpy(x).cuda(), *_moe_args(dev, d["top_k"]))
+        torch.cuda.synchronize()
+        assert list(ids.cpu().numpy()) == list(ref["ids"])
+        assert_within_tol(w.cpu().numpy(), ref["weights"], f"sigma {sigma} token {i} weights")
+        plain += _check_out(out.float().cpu().numpy(), ref, _term_magnitudes(d, x, ref), f"sigma {sigma} token {i}")
+        checked += 1
+    print(f"sigma {sigma}: {checked} of {len(X)} tokens within the fp16 range, all checked; "
+          f"{plain} outputs needed the fp32 dot allowance")
+    assert checked >= 2
+
+
+@pytest.mark.parametrize("sigma", [8, 32])
+def test_moe_chunk_large_activations_every_row(moe, sigma):
+    d, dev = moe
+    X = np.stack([scaled(x, sigma) for x in synth.moe_x_ring(0, 24)])
+    refs = _oracle_rows(d, X)
+    keep = [i for i, r in enumerate(refs) if np.abs(r["out"]).max() <= F16_MAX]
+    X = X[keep]
+    say(f"moe chunk sigma={sigma} m={len(keep)}")
+    out, ids, w = hca.moe_prefill(torch.from_numpy(np.ascontiguousarray(X)).cuda(), *_moe_args(dev, d["top_k"]))
+    torch.cuda.synchronize()
+    out, ids, w = out.float().cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    plain = 0
+    for r, i in enumerate(keep):
+        assert list(ids[r]) == list(refs[i]["ids"]), r
+        assert_within_tol(w[r], refs[i]["weights"], f"sigma {sigma} row {r} weights")
+        plain += _check_out(out[r], refs[i], _term_magnitudes(d, X[r], refs[i]), f"sigma {sigma} row {r}")
+    print(f"sigma {sigma}: {len(keep)} of 24 tokens within the fp16 range, every row checked; "
+          f"{plain} outputs needed the fp32 dot allowance")
+    assert len(keep) >= 8

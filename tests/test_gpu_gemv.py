@@ -113,8 +113,9 @@ def test_argmax_planted_max_at_ends():
 
 
 def test_argmax_repeated_calls_share_one_workspace():
-    # The argmax workspace (completion counter + keys) is reused across calls and must return
-    # to zero after each one: 12 calls in a row, alternating two inputs, all correct.
+    # The argmax workspace holds the per-block partials that each call writes and its final
+    # reduction reads; one workspace serves 12 calls in a row, alternating two inputs, and
+    # every call must see only its own partials.
     say("argmax repeated calls, shared workspace")
     rng = np.random.default_rng(79)
     n, k = 70000, 2560

@@ -177,3 +177,53 @@ def test_moe_deterministic(full):
     a = dev(d["x"])
     b = dev(d["x"])
     assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+def _rows_int4(rows, cols, entries, scales):
+    """INT4 tensor, bias -8s: row r has codes 8 + m at the (col, m) pairs of entries[r], 8 (weight
+    0) elsewhere, and scale scales[r] (a power of two, exact in bf16)."""
+    q = np.full((rows, cols), 8, np.uint8)
+    for r, pairs in enumerate(entries):
+        for col, mult in pairs:
+            q[r, col] = 8 + mult
+    s = np.repeat(synth.to_bf16_bits(np.asarray(scales, np.float64))[:, None], cols // 64, axis=1)
+    b = np.repeat(synth.to_bf16_bits(-8 * np.asarray(scales, np.float64))[:, None], cols // 64, axis=1)
+    return synth.Int4Tensor(q=q, s_bits=s, b_bits=b)
+
+
+def _hand_expert(hidden, inter, up_scales, down_pairs, down_scale):
+    """gate rows 0..len(up_scales)-1 read x[0] at scale 1 (x[0] = 64: g = 64, silu(g) = g in
+    fp32 and fp64); up row i reads x[0] at up_scales[i]; every down row adds the act entries of
+    down_pairs at down_scale."""
+    n = len(up_scales)
+    rest = [()] * (inter - n)
+    return {"gate": _rows_int4(inter, hidden, [((0, 1),)] * n + rest, [1.0] * inter),
+            "up": _rows_int4(inter, hidden, [((0, 1),)] * n + rest, list(up_scales) + [1.0] * (inter - n)),
+            "down": _rows_int4(hidden, inter, [tuple(down_pairs)] * hidden, [down_scale] * hidden)}
+
+
+def test_moe_fp16_boundary_hand_values():
+    """A layer built by hand so that the two output modes differ in the fp16 output itself.
+
+    Routed (top-1, weight 1): act[0] = 64 * 64 * 2^-12 = 1 and act[1] = 64 * 64 * 2^-23 = 2^-11,
+    summed by every down row: 1 + 2^-11, halfway between two fp16 values. Shared: act[0] = 1
+    read at scale 2^-11, gated by sigmoid(0) = 1/2: 2^-12. Every step is exact in fp32.
+      default:       fp16(1 + 2^-11 + 2^-12) = 1 + 2^-10 (three quarters of an ulp up)
+      fp16 boundary: fp16(fp16(1 + 2^-11) + fp16(2^-12)) = fp16(1 + 2^-12) = 1 (ties to even)
+    The oracle gives the same two values ("src/families/qwen4/mod.rs", section MoE)."""
+    say("moe fp16 boundary hand values")
+    hidden, inter, E = 512, 64, 8
+    x = np.zeros(hidden, np.float16)
+    x[0] = 64.0
+    routed = _hand_expert(hidden, inter, [2.0 ** -12, 2.0 ** -23], [(0, 1), (1, 1)], 1.0)
+    shared = _hand_expert(hidden, inter, [2.0 ** -12], [(0, 1)], 2.0 ** -11)
+    zero = _hand_expert(hidden, inter, [], [], 1.0)
+    d = {"x": x, "router_bits": np.zeros((E, hidden), np.uint16), "sgate_bits": np.zeros(hidden, np.uint16),
+         "shared": shared, "experts": [routed] + [zero] * (E - 1), "top_k": 1}
+    dev = DevMoe(d)
+    for boundary, want in ((False, 1.0 + 2.0 ** -10), (True, 1.0)):
+        out, ids, w = dev(x, fp16_boundary=boundary)
+        ref = oracle.moe_decode(x, d["router_bits"], d["sgate_bits"], shared, d["experts"], 1, fp16_boundary=boundary)
+        assert list(ids) == [0] and w.tolist() == [1.0]
+        assert np.all(ref["out"].astype(np.float16) == np.float16(want))
+        assert np.all(out == want), (boundary, np.unique(out))

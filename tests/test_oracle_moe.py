@@ -203,17 +203,111 @@ def test_shared_gate_zero_is_half_and_routed_zero():
     np.testing.assert_allclose(res2["out"], sh / (1 + math.exp(-g)), rtol=1e-13, atol=1e-14)
 
 
-def test_fp16_boundary_mode_rounds_both_halves():
-    x, router, sgate, shared, experts, k = _tiny_moe(19)
-    a = oracle.moe_decode(x, router, sgate, shared, experts, k, fp16_boundary=True)
-    r16 = a["routed"].astype(np.float16).astype(np.float64)
-    s16 = a["shared_gated"].astype(np.float16).astype(np.float64)
-    np.testing.assert_array_equal(a["out"], r16 + s16)
-    b = oracle.moe_decode(x, router, sgate, shared, experts, k)
-    np.testing.assert_array_equal(b["out"], b["routed"] + b["shared_gated"])
+def _int4_from_rows(rows, cols, entries, scales):
+    """INT4 tensor with bias -8s everywhere: row r has codes 8 + m at the (col, m) pairs of
+    entries[r] and 8 (weight 0) elsewhere, and scale scales[r] (exact in bf16)."""
+    q = np.full((rows, cols), 8, np.uint8)
+    for r, pairs in enumerate(entries):
+        for col, mult in pairs:
+            q[r, col] = 8 + mult
+    s = np.repeat(np.array([[bf16(v)] for v in scales], np.uint16), cols // 64, axis=1)
+    b = np.repeat(np.array([[bf16(-8 * v)] for v in scales], np.uint16), cols // 64, axis=1)
+    return synth.Int4Tensor(q=q, s_bits=s, b_bits=b)
+
+
+def _one_plus_2m12_expert(hidden=128, inter=64):
+    """An expert whose output is 1 + 2^-12 in every element for x with x[0] = 64.
+
+    gate rows 0 and 1 read x[0] at scale 1: g = 64, and silu(64) = 64 in float64 (exp(-64) is
+    below half an ulp of 1). up row 0 reads x[0] at scale 2^-12 (u = 2^-6), up row 1 at 2^-24
+    (u = 2^-18): act[0] = 1, act[1] = 2^-12, the other rows 0. Every down row adds act[0] and
+    act[1] at scale 1: 1 + 2^-12, which needs 13 significant bits; fp16 keeps 11, and rounding
+    to nearest even gives 1."""
+    zeros = [()] * (inter - 2)
+    gate = _int4_from_rows(inter, hidden, [((0, 1),), ((0, 1),)] + zeros, [1.0] * inter)
+    up = _int4_from_rows(inter, hidden, [((0, 1),), ((0, 1),)] + zeros, [2.0 ** -12, 2.0 ** -24] + [1.0] * (inter - 2))
+    down = _int4_from_rows(hidden, inter, [((0, 1), (1, 1))] * hidden, [1.0] * hidden)
+    return {"gate": gate, "up": up, "down": down}
+
+
+def _boundary_case():
+    hidden, inter, E = 128, 64, 4
+    x = np.zeros(hidden, np.float16)
+    x[0] = 64.0
+    router = np.zeros((E, hidden), np.uint16)          # all logits 0: top-1 picks expert 0, weight 1
+    zero = {"gate": zero_int4(inter, hidden), "up": zero_int4(inter, hidden), "down": zero_int4(hidden, inter)}
+    return x, router, _one_plus_2m12_expert(hidden, inter), zero, E
+
+
+def test_fp16_boundary_casts_the_routed_sum():
+    # routed = 1 + 2^-12 (the top-1 expert at weight 1), shared expert zero, gate row zero.
+    x, router, ex, zero, E = _boundary_case()
+    sgate = np.zeros(128, np.uint16)
+    b = oracle.moe_decode(x, router, sgate, zero, [ex] + [zero] * (E - 1), 1, fp16_boundary=True)
+    assert list(b["ids"]) == [0] and list(b["weights"]) == [1.0]
+    assert np.all(b["out"] == 1.0)                     # fp16(1 + 2^-12) + fp16(0)
+    d = oracle.moe_decode(x, router, sgate, zero, [ex] + [zero] * (E - 1), 1)
+    assert np.all(d["out"] == 1.0 + 2.0 ** -12)        # default: unrounded until the end
+
+
+def test_fp16_boundary_casts_the_gated_shared_half():
+    # routed zero (every routed expert zero), shared expert = the 1 + 2^-12 expert, gate row 0:
+    # sigmoid(0) = 1/2, so the gated shared half is 1/2 + 2^-13, which fp16 rounds to 1/2.
+    x, router, ex, zero, E = _boundary_case()
+    sgate = np.zeros(128, np.uint16)
+    b = oracle.moe_decode(x, router, sgate, ex, [zero] * E, 1, fp16_boundary=True)
+    assert np.all(b["out"] == 0.5)
+    d = oracle.moe_decode(x, router, sgate, ex, [zero] * E, 1)
+    assert np.all(d["out"] == 0.5 + 2.0 ** -13)
+
+
+def test_fp16_boundary_rounds_each_half_not_the_sum():
+    # routed = 1 + 2^-12 (fp16: 1); shared expert output 3 * 2^-11 (act[0] = 1 read with
+    # multiplier 3 at scale 2^-11), gated by sigmoid(0) = 1/2: 3 * 2^-12, exact in fp16. Each
+    # half rounded, then added: 1 + 3 * 2^-12; rounding the sum instead, 1 + 2^-10.
+    x, router, ex, zero, E = _boundary_case()
+    hidden, inter = 128, 64
+    zeros = [()] * (inter - 1)
+    sh = {"gate": _int4_from_rows(inter, hidden, [((0, 1),)] + zeros, [1.0] * inter),
+          "up": _int4_from_rows(inter, hidden, [((0, 1),)] + zeros, [2.0 ** -12] + [1.0] * (inter - 1)),
+          "down": _int4_from_rows(hidden, inter, [((0, 3),)] * hidden, [2.0 ** -11] * hidden)}
+    sgate = np.zeros(128, np.uint16)
+    b = oracle.moe_decode(x, router, sgate, sh, [ex] + [zero] * (E - 1), 1, fp16_boundary=True)
+    assert np.all(b["out"] == 1.0 + 3 * 2.0 ** -12)
+    d = oracle.moe_decode(x, router, sgate, sh, [ex] + [zero] * (E - 1), 1)
+    assert np.all(d["out"] == 1.0 + 2.0 ** -10)
 
 
 # ----------------------------------------------------------------- planted mistakes
+
+def _boundary_pins():
+    return (test_fp16_boundary_casts_the_routed_sum, test_fp16_boundary_casts_the_gated_shared_half,
+            test_fp16_boundary_rounds_each_half_not_the_sum)
+
+
+def _count_boundary_failures():
+    n = 0
+    for pin in _boundary_pins():
+        try:
+            pin()
+        except AssertionError:
+            n += 1
+    return n
+
+
+@pytest.mark.parametrize("mutant", ["no_cast", "cast_shared_only", "cast_routed_only", "cast_sum"])
+def test_planted_fp16_boundary_mistakes_fail(monkeypatch, mutant):
+    f16 = lambda v: np.asarray(v, np.float64).astype(np.float16).astype(np.float64)
+
+    def bad(routed, shared_gated, fp16_boundary=False):
+        r, sh = np.asarray(routed, np.float64), np.asarray(shared_gated, np.float64)
+        if not fp16_boundary:
+            return r + sh
+        return {"no_cast": lambda: r + sh, "cast_shared_only": lambda: r + f16(sh),
+                "cast_routed_only": lambda: f16(r) + sh, "cast_sum": lambda: f16(r + sh) + 0.0}[mutant]()
+    monkeypatch.setattr(om, "combine", bad)
+    assert _count_boundary_failures() >= 1
+
 
 def _pins():
     return (test_topk_golden_with_ties, test_softmax_two_expert_closed_form, test_softmax_k1_and_sum_to_one,
