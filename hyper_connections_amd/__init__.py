@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.decodehp_moe_decode_ex.argtypes = [vp, PR, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp, vp, sz, vp]
         L.decodehp_moe_prefill_ex.argtypes = [vp, i32, PR, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp, vp,
                                               sz, vp]
+        L.decodehp_moe_decode_noalloc.argtypes = [vp, vp, i32, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp,
+                                                  vp]
         L.decodehp_moe_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.decodehp_moe_prefill_workspace_bytes.restype = sz
         PL, PB = ctypes.POINTER(CDecodeLayer), ctypes.POINTER(CHcBlock)
@@ -110,6 +112,7 @@ def lib() -> ctypes.CDLL:
         L.decodehp_last_error.restype = ctypes.c_char_p
         L.decodehp_version.restype = i32
         for name in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
+                     "decodehp_moe_decode_noalloc",
                      "decodehp_moe_prefill", "decodehp_hc_read", "decodehp_hc_inject", "decodehp_decode_layers",
                      "decodehp_hc_read_batched", "decodehp_hc_inject_batched",
                      "decodehp_graph_capture_decode_layers", "decodehp_graph_launch"):
@@ -363,6 +366,29 @@ def moe_decode(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, d
     fn, args, _keep = _moe_args(x, None, router, shared_gate_row, gate, up, down, shared_gate, shared_up,
                                 shared_down, top_k, out, ids, weights, fp16_boundary, stream)
     _check(fn(*args))
+    return out, ids, weights
+
+
+def moe_decode_noalloc(x, router, shared_gate_row, gate: Int4Experts, up: Int4Experts, down: Int4Experts,
+                       shared_gate: Int4Weight, shared_up: Int4Weight, shared_down: Int4Weight, top_k: int,
+                       out, ids, weights, fp16_boundary=False, stream=None):
+    """moe_decode through decodehp_moe_decode_noalloc: the library's fixed per-GPU scratch instead of
+    a workspace, so nothing is allocated, here or in the library. The caller passes out fp16 [hidden],
+    ids int32 [top_k] and weights fp32 [top_k]; router: bf16 bits (int16) or fp32 [E, hidden].
+    Calls that overlap in time on one GPU race on the shared scratch."""
+    torch = _torch()
+    hidden = gate.cols
+    _need(x, torch.float16, "x", hidden)
+    _need(shared_gate_row, torch.int16, "shared_gate_row", hidden)
+    _need(out, torch.float16, "out", hidden)
+    _need(ids, torch.int32, "ids", top_k)
+    _need(weights, torch.float32, "weights", top_k)
+    rdt = _plain_router(router, gate.count, hidden)
+    descs = (gate.desc(), up.desc(), down.desc(), shared_gate.desc(), shared_up.desc(), shared_down.desc())
+    _check(lib().decodehp_moe_decode_noalloc(x.data_ptr(), router.data_ptr(), rdt, shared_gate_row.data_ptr(),
+                                             *[ctypes.byref(d) for d in descs], top_k,
+                                             DHP_MOE_FP16_BOUNDARY if fp16_boundary else 0, out.data_ptr(),
+                                             ids.data_ptr(), weights.data_ptr(), _stream(stream)))
     return out, ids, weights
 
 

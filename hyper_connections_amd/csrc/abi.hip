@@ -269,6 +269,62 @@ int decodehp_moe_decode_ex(const void* x, const dhp_router* router, const void* 
                            flags, out, ids, weights, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+// Scratch of decodehp_moe_decode_noalloc: one array per GPU, allocated with the code object when
+// the library loads on that device and held until the process ends. Host code never takes the
+// array's name as a device address: hipGetSymbolAddress gives each device's own copy, once per
+// device (with that device current, on the entry point's first call there), and that address is
+// what the launch receives.
+namespace {
+__device__ __align__(256) unsigned char scratch[DHP_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_addr[MAX_DEVICES];
+
+void* scratch_address(int dev) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            dhp_fail(DHP_ERR_LAUNCH, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_addr[dev] = p;
+    }
+    return g_scratch_addr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int decodehp_moe_decode_noalloc(const void* x, const void* router, int32_t router_dtype,
+                                const void* shared_gate_row, const dhp_int4_experts* gate,
+                                const dhp_int4_experts* up, const dhp_int4_experts* down,
+                                const dhp_int4* shared_gate, const dhp_int4* shared_up,
+                                const dhp_int4* shared_down, int32_t top_k, int32_t flags, void* out,
+                                int32_t* ids, float* weights, void* stream) {
+    g_err[0] = 0;
+    int rc = check_moe(x, router, router_dtype, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down,
+                       top_k, flags, out, ids, weights);
+    if (rc) return rc;
+    const size_t need = dhp_moe_ws(gate->count, top_k, gate->first.rows);
+    if (need > DHP_NOALLOC_SCRATCH_BYTES)
+        return dhp_fail(DHP_ERR_WORKSPACE,
+                        "the layer needs %zu bytes of scratch (n_experts %d, top_k %d, inter %d); the library's "
+                        "own scratch holds %d: call decodehp_moe_decode with a workspace",
+                        need, gate->count, top_k, gate->first.rows, DHP_NOALLOC_SCRATCH_BYTES);
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    void* ws = scratch_address(dev.device);
+    if (!ws) return DHP_ERR_LAUNCH;
+    const dhp_router r{router, router_dtype, nullptr, nullptr};
+    // the router logits, the gate logit and the activations in the scratch are each written before
+    // they are read within the call, so nothing there needs clearing between calls
+    return launch_moe(x, &r, shared_gate_row, gate, up, down, shared_gate, shared_up, shared_down, top_k,
+                      (flags & DHP_MOE_FP16_BOUNDARY) != 0, out, ids, weights, ws, static_cast<hipStream_t>(stream));
+}
+
 size_t decodehp_moe_prefill_workspace_bytes(int32_t m, int32_t n_experts, int32_t top_k, int32_t inter,
                                             int32_t hidden) {
     if (m < 1 || m > DHP_MOE_PREFILL_MAX_M || n_experts < 1 || n_experts > 1024 || top_k < 1 ||

@@ -293,3 +293,24 @@ def test_probe_read_rejects_bad_calls():
     assert L.decodehp_probe_read(FAKE, 1 << 20, 0, 4, FAKE, 4096, None) == -2
     assert L.decodehp_probe_read(FAKE, 1 << 20, 17, 4, FAKE, 4096, None) == -2
     assert L.decodehp_probe_read(FAKE, 1 << 20, 2, 3, FAKE, 4096, None) == -2
+
+
+def moe_noalloc(top_k=2, E=8, hidden=512, inter=64, x=FAKE):
+    L = hca.lib()
+    g, u = experts(E, inter, hidden), experts(E, inter, hidden)
+    d = experts(E, hidden, inter)
+    sg, su, sd = int4(rows=inter, cols=hidden), int4(rows=inter, cols=hidden), int4(rows=hidden, cols=inter)
+    return L.decodehp_moe_decode_noalloc(x, FAKE, 2, FAKE, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                         ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), top_k, 0, FAKE,
+                                         FAKE, FAKE, None)
+
+
+def test_moe_noalloc_checks_and_scratch_limit():
+    # the checks of decodehp_moe_decode, then the fixed scratch's limit, both before any device call
+    assert moe_noalloc(x=0) == -1
+    assert moe_noalloc(top_k=11) == -2
+    assert moe_noalloc(E=1024, inter=1024, top_k=10) == -4      # 49,168 bytes > 32 KiB
+    assert "scratch" in hca.lib().decodehp_last_error().decode()
+    assert hca.workspace_bytes(hca.DHP_OP_MOE_DECODE, 1024, 10, 640) <= 32768
+    assert moe_noalloc(E=1024, inter=640, top_k=10) == -5       # fits; no device here
+    assert moe_noalloc(E=256, inter=512, top_k=8) == -5
