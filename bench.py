@@ -44,7 +44,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "lmhead_gemv_m1_counters.json")
-DOMINANT_SRC = os.path.join(ROOT, "hyper_connections_amd", "csrc", "gemv.hip")
+# every file the dominant kernel is compiled from (its source, the device helpers and declarations
+# it includes, and the build script that holds the compiler flags)
+DOMINANT_SRCS = ("hyper_connections_amd/csrc/gemv.hip", "hyper_connections_amd/csrc/dhp_internal.hpp",
+                 "include/decodehp.h", "hyper_connections_amd/build.py")
+
+
+def dominant_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in DOMINANT_SRCS:
+        h.update(rel.encode() + b"\0")
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()
 
 
 def int4_bytes(rows, cols):
@@ -59,6 +70,10 @@ def algorithmic_bytes():
     C, H, R = 4, 2560, 320
     b["hc"] = (int4_bytes(R, C * H) + int4_bytes(C * H, R) + int4_bytes(C, C * H) + 2 * C * H + 2 * C * H
                + 2 * H + 4 * C) + (2 * C * H * 2 + 2 * H + 4 * C)
+    # an inject fused in front of the next read: the residual is read once, the injected one
+    # written once, plus the sublayer output and both gate sets
+    b["hc_inject_read"] = (int4_bytes(R, C * H) + int4_bytes(C * H, R) + int4_bytes(C, C * H) + 2 * C * H + 2 * H
+                           + 4 * C + 2 * C * H + 2 * C * H + 2 * H + 4 * C)
     E, inter, top_k = 256, 512, 8
     b["moe"] = (2 * E * K + 2 * K + (top_k + 1) * (2 * int4_bytes(inter, K) + int4_bytes(K, inter))
                 + 2 * K + 2 * K + 8 * top_k)
@@ -86,10 +101,11 @@ def algorithmic_bytes():
 
 STEP_CALLS = ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8")
 # Timed per call but outside the step: a 128-token chunk through the same MoE layer, the MoE
-# layer with the INT8 scaled router at top-10, the hyper-connection read and inject of a
+# layer with the INT8 scaled router at top-10, an inject fused in front of the next
+# hyper-connection read (decodehp_hc_inject_read), the hyper-connection read and inject of a
 # 128-token chunk, and one token through a whole decoder layer plus the final mixer, as a
 # launch sequence and as a graph.
-EXTRA_CALLS = ("moe_prefill", "moe_i8k10", "hc_chunk", "layer_eager", "layer_graph")
+EXTRA_CALLS = ("moe_prefill", "moe_i8k10", "hc_inject_read", "hc_chunk", "layer_eager", "layer_graph")
 CALLS = STEP_CALLS + EXTRA_CALLS
 MOE_CHUNK = 128
 
@@ -126,7 +142,7 @@ def build_workload(torch, hca, synth, ring: int, only=None):
         W["gemv_x"] = torch.from_numpy(g["x"]).to(dev)
         W["gemv_y"] = torch.empty(2560, dtype=torch.float16, device=dev)
 
-    if want("hc"):
+    if want("hc", "hc_inject_read"):
         h = synth.hc_workload(0)
         hw = (up_int4(h["down"]), up_int4(h["up"]), up_int4(h["inject"]))
         W["hc_w"] = [hw] + [tuple(clone(w) for w in hw) for _ in range(ring - 1)]
@@ -134,7 +150,9 @@ def build_workload(torch, hca, synth, ring: int, only=None):
         W["hc_gamma"] = hca.bf16_bits_to_tensor(h["gamma_bits"]).to(dev)
         W["hc_out"] = torch.from_numpy(h["out"]).to(dev)
         W["hc_mixed"] = torch.empty(2560, dtype=torch.float16, device=dev)
-        W["hc_iw"] = torch.empty(4, dtype=torch.float32, device=dev)
+        W["hc_iw"] = torch.from_numpy(h["iw"]).to(dev)
+        W["hc_hidden"] = torch.empty(4 * 2560, dtype=torch.float16, device=dev)
+        W["hc_iw_next"] = torch.empty(4, dtype=torch.float32, device=dev)
 
     if want("moe", "moe_prefill", "moe_i8k10"):
         _moe_workload(torch, hca, synth, W, dev)
@@ -242,6 +260,9 @@ def prepare_calls(hca, W, ring: int, only=None):
         "hc": lambda: [(hca.prepare_hc_read(W["hc_wide"], W["hc_gamma"], C, H, *W["hc_w"][i], W["hc_mixed"],
                                             W["hc_iw"]),
                         hca.prepare_hc_inject(W["hc_wide"], W["hc_out"], W["hc_iw"], C, H)) for i in range(ring)],
+        "hc_inject_read": lambda: [hca.prepare_hc_inject_read(W["hc_wide"], W["hc_out"], W["hc_iw"], W["hc_hidden"],
+                                                              W["hc_gamma"], C, H, *W["hc_w"][i], W["hc_mixed"],
+                                                              W["hc_iw_next"]) for i in range(ring)],
         "moe": lambda: [hca.prepare_moe(W["moe_x"][t], W["moe"]["router"], W["moe"]["sgate"], W["moe"]["gate"],
                                         W["moe"]["up"], W["moe"]["down"], W["moe"]["sg"], W["moe"]["su"],
                                         W["moe"]["sd"], 8, W["moe_out"], W["moe_ids"], W["moe_w"])
@@ -670,13 +691,12 @@ def oracle_timing(synth):
 
 def traffic_from_profile():
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current sources of that kernel (every file in DOMINANT_SRCS); else None."""
     if not os.path.exists(PROFILE_COUNTERS):
         return None
     try:
         d = json.load(open(PROFILE_COUNTERS))
-        src = hashlib.sha256(open(DOMINANT_SRC, "rb").read()).hexdigest()
-        if d.get("source_sha256") != src:
+        if d.get("sources_sha256") != dominant_sources_sha256():
             return None
         return d.get("hbm_bytes_per_launch")
     except Exception:

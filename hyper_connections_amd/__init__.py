@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.decodehp_hc_read_batched_workspace_bytes.restype = sz
         L.decodehp_hc_inject_batched.argtypes = [vp, i32, vp, vp, i32, i32, vp]
         L.decodehp_hc_inject.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.decodehp_hc_inject_read.argtypes = [vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, P4, P4, P4, vp, vp, vp,
+                                              sz, vp]
         L.decodehp_probe_empty.argtypes = [i32, vp]
         L.decodehp_probe_read.argtypes = [vp, sz, i32, i32, vp, i32, vp]
         L.decodehp_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -114,6 +116,7 @@ def lib() -> ctypes.CDLL:
         for name in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
                      "decodehp_moe_decode_noalloc",
                      "decodehp_moe_prefill", "decodehp_hc_read", "decodehp_hc_inject", "decodehp_decode_layers",
+                     "decodehp_hc_inject_read",
                      "decodehp_hc_read_batched", "decodehp_hc_inject_batched",
                      "decodehp_graph_capture_decode_layers", "decodehp_graph_launch"):
             getattr(L, name).restype = ctypes.c_int
@@ -428,6 +431,44 @@ def hc_inject(wide, out, inject_w, C: int, H: int, stream=None):
     return wide
 
 
+def _hc_inject_read_args(prev, out, inject_w, hidden, hc_norm, C, H, down, up, inject, mixed, inject_w_next, eps,
+                        stream):
+    torch = _torch()
+    _need(prev, torch.float16, "prev", C * H)
+    _need(out, torch.float16, "out", H)
+    _need(inject_w, torch.float32, "inject_w", C)
+    _need(hidden, torch.float16, "hidden", C * H)
+    _need(hc_norm, torch.int16, "hc_norm", C * H)
+    _need(mixed, torch.float16, "mixed", H)
+    if inject_w_next is not None:
+        _need(inject_w_next, torch.float32, "inject_w_next", C)
+    ws = _workspace(workspace_bytes(DHP_OP_HC_READ, C, down.rows), prev.device, stream=stream)
+    descs = (down.desc(), up.desc(), inject.desc() if inject is not None else None)
+    args = (prev.data_ptr(), out.data_ptr(), inject_w.data_ptr(), hidden.data_ptr(), hc_norm.data_ptr(), C, H, eps,
+            ctypes.byref(descs[0]), ctypes.byref(descs[1]), ctypes.byref(descs[2]) if descs[2] is not None else None,
+            mixed.data_ptr(), _ptr(inject_w_next), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    keep = (descs, prev, out, inject_w, hidden, hc_norm, mixed, inject_w_next, ws, down, up, inject)
+    return args, keep
+
+
+def hc_inject_read(prev, out, inject_w, hc_norm, C: int, H: int, down: Int4Weight, up: Int4Weight,
+                   inject: Optional[Int4Weight], hidden=None, mixed=None, inject_w_next=None, eps: float = 1e-6,
+                   stream=None):
+    """The inject of a sublayer output followed by the next read: hidden = fp16(prev + out * inject_w
+    per stream) (prev is not written), then the read of hidden. Returns (hidden fp16 [C*H], mixed fp16 [H],
+    inject_w_next fp32 [C] or None)."""
+    torch = _torch()
+    dev = prev.device
+    hidden = torch.empty(C * H, dtype=torch.float16, device=dev) if hidden is None else hidden
+    mixed = torch.empty(H, dtype=torch.float16, device=dev) if mixed is None else mixed
+    if inject is not None and inject_w_next is None:
+        inject_w_next = torch.empty(C, dtype=torch.float32, device=dev)
+    args, _keep = _hc_inject_read_args(prev, out, inject_w, hidden, hc_norm, C, H, down, up, inject, mixed,
+                                       inject_w_next, eps, stream)
+    _check(lib().decodehp_hc_inject_read(*args))
+    return hidden, mixed, (inject_w_next if inject is not None else None)
+
+
 # --------------------------------------------------------------------------- measurement probes
 
 def probe_empty(count: int = 1, stream=None):
@@ -683,3 +724,10 @@ def prepare_hc_read(raw, hc_norm, C, H, down, up, inject, mixed, inject_w, eps=1
 def prepare_hc_inject(wide, out, inject_w, C, H, stream=None) -> PreparedCall:
     args = (wide.data_ptr(), out.data_ptr(), inject_w.data_ptr(), C, H, _stream(stream))
     return PreparedCall(lib().decodehp_hc_inject, args, (wide, out, inject_w))
+
+
+def prepare_hc_inject_read(prev, out, inject_w, hidden, hc_norm, C, H, down, up, inject, mixed, inject_w_next,
+                           eps=1e-6, stream=None) -> PreparedCall:
+    args, keep = _hc_inject_read_args(prev, out, inject_w, hidden, hc_norm, C, H, down, up, inject, mixed,
+                                      inject_w_next, eps, stream)
+    return PreparedCall(lib().decodehp_hc_inject_read, args, keep)

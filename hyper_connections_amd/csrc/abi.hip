@@ -434,6 +434,33 @@ int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32
     return launch_hc_inject(wide, out, inject_w, C, H, static_cast<hipStream_t>(stream));
 }
 
+int decodehp_hc_inject_read(const void* prev, const void* out, const float* inject_w, void* hidden,
+                            const void* hc_norm, int32_t C, int32_t H, float eps, const dhp_int4* down,
+                            const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w_next,
+                            void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_hc_inject(prev, out, inject_w, C, H);
+    if (!rc) rc = check_hc_inject(hidden, out, inject_w, C, H);
+    if (!rc) rc = check_hc_read(hidden, hc_norm, C, H, eps, down, up, inject, mixed, inject_w_next);
+    if (rc) return rc;
+    const uintptr_t wide = (uintptr_t)C * H * 2;
+    auto overlap = [](const void* a, uintptr_t na, const void* b, uintptr_t nb) {
+        const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+        return pa < pb + nb && pb < pa + na;
+    };
+    if (overlap(hidden, wide, prev, wide) || overlap(hidden, wide, out, (uintptr_t)H * 2))
+        return dhp_fail(DHP_ERR_INVALID, "hidden overlaps prev or out");
+    if (inject_w_next && overlap(inject_w_next, (uintptr_t)C * 4, inject_w, (uintptr_t)C * 4))
+        return dhp_fail(DHP_ERR_INVALID, "inject_w_next overlaps inject_w");
+    const size_t need = dhp_hc_ws(C, down->rows);
+    if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    return launch_hc_inject_read(prev, out, inject_w, hidden, hc_norm, C, H, eps, down, up, inject, mixed,
+                                 inject_w_next, ws, static_cast<hipStream_t>(stream));
+}
+
 size_t decodehp_hc_read_batched_workspace_bytes(int32_t m, int32_t C, int32_t H, int32_t R) {
     if (m < 1 || m > DHP_GEMM_MAX_M || C < 1 || C > DHP_HC_MAX_C || H < 1 || R < 1 || R > 1024) return 0;
     return dhp_hc_read_batched_ws(m, C, H, R);

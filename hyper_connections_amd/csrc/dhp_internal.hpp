@@ -172,6 +172,18 @@ DHP_DEV float group_sum(float v) {
     return v;
 }
 
+// The inject's add for a pair of residual values: fp16(fp32 fma(out, w, raw)). The empty asm
+// keeps the fp32 result, so the compiler cannot merge the fma and the conversion into one
+// mixed-precision fma that rounds once to fp16: that instruction gives another value when the
+// fp32 result sits on an fp16 rounding midpoint, and every kernel that forms an inject must
+// produce the same bits.
+DHP_DEV h2 inject_pair(h2 raw, h2 out, float w) {
+    float a = __builtin_fmaf((float)out.x, w, (float)raw.x);
+    float b = __builtin_fmaf((float)out.y, w, (float)raw.y);
+    asm volatile("" : "+v"(a), "+v"(b));
+    return h2{(_Float16)a, (_Float16)b};
+}
+
 DHP_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 DHP_DEV float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
@@ -224,6 +236,9 @@ int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, 
                    const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w,
                    void* ws, hipStream_t s);
 int launch_hc_inject(void* wide, const void* out, const float* w, int C, int H, hipStream_t s);
+int launch_hc_inject_read(const void* prev, const void* out, const float* w, void* hidden, const void* gamma, int C,
+                          int H, float eps, const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject,
+                          void* mixed, float* inject_w, void* ws, hipStream_t s);
 int launch_moe(const void* x, const dhp_router* router, const void* sgate_row,
                const dhp_int4_experts* gate, const dhp_int4_experts* up, const dhp_int4_experts* down,
                const dhp_int4* sg, const dhp_int4* su, const dhp_int4* sd, int top_k, int boundary,

@@ -6,11 +6,13 @@
 // sigmoid, scale by 2). Here the read is two kernels:
 //
 //  k_hc_down : one block per output row of the down projection (R rows) and of the inject
-//              projection (C rows). Every block recomputes the C stream RMS values from the
-//              20 KB residual (an L2 hit after the first block), normalizes its own 32-wide
-//              slice in registers, and reduces one dot product over the whole C*H input:
-//              lane t owns input positions 32t..32t+31, so the block is C*H/32 lanes wide.
-//              The epilogue applies the 1/C, then SiLU (down rows) or 2*sigmoid (inject rows).
+//              projection (C rows), C*H/32 lanes wide (lane t owns input positions 32t..32t+31).
+//              Each lane dots its slice of the weight row with raw * hc_norm and sums its squares;
+//              per stream, the dot is scaled by the stream's inverse RMS afterwards, so the norm is
+//              off the dot's path (every block recomputes the C RMS values from the 20 KB residual,
+//              an L2 hit). The epilogue applies the 1/C, then SiLU (down rows) or 2*sigmoid
+//              (inject rows). A variant forms the residual first from the previous sublayer's
+//              inject (raw + out * inject_w, rounded to fp16) and stores it.
 //  k_hc_up   : 16 lanes per output position h: 16/C lanes per stream row c*H+h walk that row's
 //              R/32 code chunks against the low-rank vector staged in LDS, the row sums go
 //              through the sigmoid, multiply the recomputed normed value, and the C products
@@ -26,105 +28,117 @@ constexpr int HC_MAX_THREADS = 1024;
 constexpr int LO_PITCH = 36;           // floats per staged 32-float chunk of the low-rank vector
 constexpr int UP_THREADS = 64;         // k_hc_up block: four outputs h
 
-// raw, gamma: the C*H stream; one block per projection row (down rows first, then inject rows).
+// One block per projection row (down rows first, then inject rows), C*H/32 lanes: lane t owns
+// positions 32t .. 32t+31 of the residual, all in stream c = t / (H/32). With the norm weight
+// applied but not yet the stream's inverse RMS, each lane forms
+//     P_t = s * (q . v) + b * sum(v),   v = raw * gamma   (its share of the row's dot with raw*gamma)
+//     S_t = sum(raw^2)                                     (its share of the stream's sum of squares)
+// The inverse RMS is constant within a stream, so the row's dot with the normed residual is
+//     sum_c ir_c * P_c,   P_c, S_c = the stream's sums of P_t, S_t,   ir_c = 1 / sqrt(S_c / H + eps).
+// The dot therefore does not wait for the norm: every load is issued up front and the block meets
+// once (sums within 16-lane groups by DPP, then one LDS exchange), then the epilogue applies the
+// 1/C and SiLU (down rows) or 2*sigmoid (inject rows).
+// INJ: the previous sublayer's inject is fused in front. Each lane first forms its residual values
+// as fp16(raw_prev + out[h] * iw[c]) with inject_pair, as k_hc_inject does, so the values are the
+// same bits the separate inject would store, and block 0 stores them to `hidden` (which must not
+// overlap raw_prev: the other blocks are still reading it).
+template <bool INJ>
 __global__ __launch_bounds__(HC_MAX_THREADS) void k_hc_down(
     const _Float16* __restrict__ raw, const uint16_t* __restrict__ gamma, int C, int H, float eps,
     const u32x4* __restrict__ dcodes, const uint16_t* __restrict__ dscales,
     const uint16_t* __restrict__ dbiases, int R, const u32x4* __restrict__ icodes,
     const uint16_t* __restrict__ iscales, const uint16_t* __restrict__ ibiases,
+    const _Float16* __restrict__ inj_out, const float* __restrict__ inj_w, _Float16* __restrict__ hidden,
     float* __restrict__ lo_out, float* __restrict__ inv_rms_out, float* __restrict__ inject_w) {
-    __shared__ float part[HC_MAX_THREADS];
-    __shared__ float inv_rms[DHP_HC_MAX_C];
-    __shared__ float wsum[HC_MAX_THREADS / 64];
+    __shared__ float2 part[HC_MAX_THREADS];
 
     const int t = threadIdx.x;            // chunk index, input positions 32t .. 32t+31
-    const int CH = (C * H) >> 5;          // == blockDim.x
     const int G = (C * H) >> 6;
+    const int per = H >> 5;               // chunks (lanes) per stream
+    const int c = t / per;                // this lane's stream
     const int row = blockIdx.x;
     const bool is_inject = row >= R;
     const int r = is_inject ? row - R : row;
 
-    // this block's weight slice first, so it is in flight during the norm
+    // every load up front: the weight slice, the residual (and the inject's inputs), the norm weight
     const u32x4* codes = is_inject ? icodes : dcodes;
     const uint16_t* sc = is_inject ? iscales : dscales;
     const uint16_t* bi = is_inject ? ibiases : dbiases;
-    const u32x4 c = __builtin_nontemporal_load(codes + (size_t)r * CH + t);
+    const u32x4 cw = __builtin_nontemporal_load(codes + (size_t)r * (G * 2) + t);
     const float s = bf16_to_f32(sc[(size_t)r * G + (t >> 1)]);
     const float b = bf16_to_f32(bi[(size_t)r * G + (t >> 1)]);
+    const u32x4* rp = reinterpret_cast<const u32x4*>(raw + 32 * t);
+    const u32x4* gp = reinterpret_cast<const u32x4*>(gamma + 32 * t);
+    u32x4 ru[4], gu[4], ou[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { ru[i] = rp[i]; gu[i] = gp[i]; }
+    float iwc = 0.0f;
+    if constexpr (INJ) {
+        const u32x4* op = reinterpret_cast<const u32x4*>(inj_out + (32 * t) % H);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ou[i] = op[i];
+        iwc = inj_w[c];
+    }
 
-    // residual slice and its squares
     float v[32];
-    {
-        const u32x4* rp = reinterpret_cast<const u32x4*>(raw + 32 * t);
-        float ss = 0.0f;
+    float ss = 0.0f, vs = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 u = rp[i];
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int i = 0; i < 4; ++i) {
+        uint32_t w[4] = {ru[i].x, ru[i].y, ru[i].z, ru[i].w};
+        const uint32_t g[4] = {gu[i].x, gu[i].y, gu[i].z, gu[i].w};
+        if constexpr (INJ) {
+            const uint32_t o[4] = {ou[i].x, ou[i].y, ou[i].z, ou[i].w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const h2 p = as_h2(w[k]);
-                v[8 * i + 2 * k] = (float)p.x;
-                v[8 * i + 2 * k + 1] = (float)p.y;
-                ss = __builtin_fmaf(v[8 * i + 2 * k], v[8 * i + 2 * k], ss);
-                ss = __builtin_fmaf(v[8 * i + 2 * k + 1], v[8 * i + 2 * k + 1], ss);
-            }
+            for (int k = 0; k < 4; ++k) w[k] = h2_bits(inject_pair(as_h2(w[k]), as_h2(o[k]), iwc));
+            if (blockIdx.x == 0)
+                reinterpret_cast<u32x4*>(hidden + 32 * t)[i] = u32x4{w[0], w[1], w[2], w[3]};
         }
-        // a stream's H/32 chunks are whole 16-lane groups when H % 512 == 0: sum within each
-        // group first (DPP), leaving H/512 partials per stream
-        if ((H & 511) == 0) {
-            ss = group_sum<16>(ss);
-            if ((t & 15) == 0) part[t >> 4] = ss;
-        } else {
-            part[t] = ss;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const h2 p = as_h2(w[k]);
+            const float x0 = (float)p.x, x1 = (float)p.y;
+            ss = __builtin_fmaf(x0, x0, ss);
+            ss = __builtin_fmaf(x1, x1, ss);
+            v[8 * i + 2 * k] = x0 * bf16_to_f32(g[k] & 0xFFFFu);
+            v[8 * i + 2 * k + 1] = x1 * bf16_to_f32(g[k] >> 16);
         }
     }
-    __syncthreads();
-    const int per = H >> 5;               // chunks per stream
-    if (t < C) {
-        float acc = 0.0f;
-        if ((H & 511) == 0) {
-            const int pg = per >> 4;      // 16-lane groups per stream
-            for (int i = 0; i < pg; ++i) acc += part[t * pg + i];
-        } else {
-            for (int i = 0; i < per; ++i) acc += part[t * per + i];
-        }
-        inv_rms[t] = 1.0f / sqrtf(acc / (float)H + eps);
-    }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32; ++i) vs += v[i];
+    float pt = __builtin_fmaf(s, dot32_f32(cw, v), b * vs);
 
-    // normalized slice (direct-scale weight), its dot with the codes, and its sum
-    const float ir = inv_rms[t / per];
-    {
-        const u32x4* gp = reinterpret_cast<const u32x4*>(gamma + 32 * t);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 u = gp[i];
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                v[8 * i + 2 * k] = v[8 * i + 2 * k] * ir * bf16_to_f32(w[k] & 0xFFFFu);
-                v[8 * i + 2 * k + 1] = v[8 * i + 2 * k + 1] * ir * bf16_to_f32(w[k] >> 16);
-            }
-        }
+    // per-stream sums: whole 16-lane groups lie in one stream when H % 512 == 0 (DPP first);
+    // otherwise every lane parks its pair
+    const bool grouped = (H & 511) == 0;
+    if (grouped) {
+        pt = group_sum<16>(pt);
+        ss = group_sum<16>(ss);
+        if ((t & 15) == 0) part[t >> 4] = float2{pt, ss};
+    } else {
+        part[t] = float2{pt, ss};
     }
-    float xs = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) xs += v[i];
-    float acc = __builtin_fmaf(s, dot32_f32(c, v), b * xs);
-
-    acc = group_sum<64>(acc);
-    if ((t & 63) == 0) wsum[t >> 6] = acc;
     __syncthreads();
-    if (t == 0) {
-        float tot = 0.0f;
-        const int nw = (CH + 63) >> 6;
-        for (int w = 0; w < nw; ++w) tot += wsum[w];
-        const float z = tot / (float)C;
-        if (is_inject) inject_w[r] = 2.0f * sigmoid_f(z);
-        else lo_out[r] = silu_f(z);
-        if (row == 0)
-            for (int k = 0; k < C; ++k) inv_rms_out[k] = inv_rms[k];
+    if (t < 64) {
+        // lane c < C sums stream c's parts in order, then the C streams meet in a fixed butterfly
+        float z = 0.0f;
+        if (t < C) {
+            const int n = grouped ? per >> 4 : per;
+            const float2* pc = part + t * n;
+            float P = 0.0f, S = 0.0f;
+            for (int i = 0; i < n; ++i) { P += pc[i].x; S += pc[i].y; }
+            const float ir = 1.0f / sqrtf(S / (float)H + eps);
+            z = ir * P;
+            if (row == 0) inv_rms_out[t] = ir;
+        }
+        if (C >= 2) z += dpp_f<DPP_XOR1>(z);
+        if (C >= 4) z += dpp_f<DPP_XOR2>(z);
+        if (C >= 8) z += dpp_f<DPP_HALF_MIRROR>(z);
+        if (C >= 16) z += dpp_f<DPP_MIRROR>(z);
+        if (t == 0) {
+            z = z / (float)C;
+            if (is_inject) inject_w[r] = 2.0f * sigmoid_f(z);
+            else lo_out[r] = silu_f(z);
+        }
     }
 }
 
@@ -219,13 +233,7 @@ __global__ __launch_bounds__(256) void k_hc_inject(_Float16* __restrict__ wide,
     uint32_t av[4] = {a.x, a.y, a.z, a.w};
     const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const h2 x = as_h2(av[k]), y = as_h2(ov[k]);
-        h2 r;
-        r.x = (_Float16)__builtin_fmaf((float)y.x, g, (float)x.x);
-        r.y = (_Float16)__builtin_fmaf((float)y.y, g, (float)x.y);
-        av[k] = h2_bits(r);
-    }
+    for (int k = 0; k < 4; ++k) av[k] = h2_bits(inject_pair(as_h2(av[k]), as_h2(ov[k]), g));
     a = u32x4{av[0], av[1], av[2], av[3]};
     *reinterpret_cast<u32x4*>(wide + e0) = a;
 }
@@ -253,30 +261,40 @@ size_t dhp_hc_ws(int32_t C, int32_t R) {
     return (b + 255) & ~(size_t)255;
 }
 
-int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, const dhp_int4* down,
-                   const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w,
-                   void* ws, hipStream_t s) {
+// The read of residual `raw`; with inj_out set, the residual is first formed as
+// fp16(raw + inj_out[h] * inj_w[c]) and stored to `hidden` (the inject fused in front), and the
+// read runs on those values.
+int launch_hc_read_impl(const void* raw, const void* gamma, int C, int H, float eps, const dhp_int4* down,
+                        const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w, void* ws,
+                        hipStream_t s, const void* inj_out, const float* inj_w, void* hidden) {
     const int R = down->rows;
     float* lo = static_cast<float*>(ws);
     float* inv_rms = lo + R;
     const int rows = R + (inject ? C : 0);
     const int threads = (C * H) / 32;
-    hipLaunchKernelGGL(k_hc_down, dim3(rows), dim3(threads), 0, s,
-                       static_cast<const _Float16*>(raw), static_cast<const uint16_t*>(gamma), C, H, eps,
-                       static_cast<const u32x4*>(down->codes), static_cast<const uint16_t*>(down->scales),
-                       static_cast<const uint16_t*>(down->biases), R,
-                       inject ? static_cast<const u32x4*>(inject->codes) : nullptr,
-                       inject ? static_cast<const uint16_t*>(inject->scales) : nullptr,
-                       inject ? static_cast<const uint16_t*>(inject->biases) : nullptr, lo, inv_rms,
-                       inject_w);
+    const auto* rin = static_cast<const _Float16*>(raw);
+    const auto* gm = static_cast<const uint16_t*>(gamma);
+    const auto* dc = static_cast<const u32x4*>(down->codes);
+    const auto* ds = static_cast<const uint16_t*>(down->scales);
+    const auto* db = static_cast<const uint16_t*>(down->biases);
+    const auto* ic = inject ? static_cast<const u32x4*>(inject->codes) : nullptr;
+    const auto* is = inject ? static_cast<const uint16_t*>(inject->scales) : nullptr;
+    const auto* ib = inject ? static_cast<const uint16_t*>(inject->biases) : nullptr;
+    const auto* io = static_cast<const _Float16*>(inj_out);
+    auto* hid = static_cast<_Float16*>(hidden);
+    if (inj_out)
+        hipLaunchKernelGGL(k_hc_down<true>, dim3(rows), dim3(threads), 0, s, rin, gm, C, H, eps, dc, ds, db, R, ic,
+                           is, ib, io, inj_w, hid, lo, inv_rms, inject_w);
+    else
+        hipLaunchKernelGGL(k_hc_down<false>, dim3(rows), dim3(threads), 0, s, rin, gm, C, H, eps, dc, ds, db, R, ic,
+                           is, ib, io, inj_w, hid, lo, inv_rms, inject_w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hc_down launch: %s", hipGetErrorString(e));
 
     const int block = UP_THREADS;          // 4 outputs per block
     const dim3 g((unsigned)((H + 3) / 4));
     const size_t lds = (size_t)(R / 32) * LO_PITCH * sizeof(float);
-    const auto* rw = static_cast<const _Float16*>(raw);
-    const auto* gm = static_cast<const uint16_t*>(gamma);
+    const auto* rw = inj_out ? static_cast<const _Float16*>(hidden) : rin;   // the residual the read saw
     const auto* uc = static_cast<const u32x4*>(up->codes);
     const auto* us = static_cast<const uint16_t*>(up->scales);
     const auto* ub = static_cast<const uint16_t*>(up->biases);
@@ -292,6 +310,19 @@ int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, 
     e = hipGetLastError();
     if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "hc_up launch: %s", hipGetErrorString(e));
     return DHP_OK;
+}
+
+int launch_hc_read(const void* raw, const void* gamma, int C, int H, float eps, const dhp_int4* down,
+                   const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w,
+                   void* ws, hipStream_t s) {
+    return launch_hc_read_impl(raw, gamma, C, H, eps, down, up, inject, mixed, inject_w, ws, s, nullptr, nullptr,
+                               nullptr);
+}
+
+int launch_hc_inject_read(const void* prev, const void* out, const float* w, void* hidden, const void* gamma, int C,
+                          int H, float eps, const dhp_int4* down, const dhp_int4* up, const dhp_int4* inject,
+                          void* mixed, float* inject_w, void* ws, hipStream_t s) {
+    return launch_hc_read_impl(prev, gamma, C, H, eps, down, up, inject, mixed, inject_w, ws, s, out, w, hidden);
 }
 
 int launch_hc_inject(void* wide, const void* out, const float* w, int C, int H, hipStream_t s) {

@@ -144,11 +144,7 @@ __global__ __launch_bounds__(256) void k_hcb_inject(_Float16* __restrict__ wide,
     const uint32_t av[4] = {a.x, a.y, a.z, a.w}, ov[4] = {o.x, o.y, o.z, o.w};
     uint32_t r[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const h2 x = as_h2(av[k]), y = as_h2(ov[k]);
-        const h2 z = {(_Float16)__builtin_fmaf((float)y.x, g, (float)x.x), (_Float16)__builtin_fmaf((float)y.y, g, (float)x.y)};
-        r[k] = h2_bits(z);
-    }
+    for (int k = 0; k < 4; ++k) r[k] = h2_bits(inject_pair(as_h2(av[k]), as_h2(ov[k]), g));
     *reinterpret_cast<u32x4*>(wp) = u32x4{r[0], r[1], r[2], r[3]};
 }
 

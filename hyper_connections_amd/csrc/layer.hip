@@ -9,10 +9,12 @@
 // The attention sublayer is not built here: an INT4 [H x H] map stands in for it.
 //
 // Every step is the library's own entry point (so each keeps its checks), called in order on the
-// stream; the only kernel of this file replicates the token at entry. The graph form is the
-// counterpart of the pages' one command buffer per token ("src/real_forward.rs", module doc):
-// a decode layer is ~11 dependent launches, and replaying them as one graph removes the host's
-// per-launch work from the token's critical path.
+// stream; the only kernel of this file replicates the token at entry. Each inject is fused into
+// the read that follows it (decodehp_hc_inject_read), so the inject costs no launch of its own;
+// the fused read writes the injected residual to a second buffer, and the two buffers alternate.
+// The graph form is the counterpart of the pages' one command buffer per token
+// ("src/real_forward.rs", module doc): a decode layer is 8 dependent launches, and replaying them
+// as one graph removes the host's per-launch work from the token's critical path.
 #include "dhp_internal.hpp"
 
 #include <algorithm>
@@ -29,7 +31,7 @@ __global__ __launch_bounds__(256) void k_replicate(const uint4* __restrict__ x, 
 size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct LayerWs {
-    size_t scratch, mixed, out, iw, ids, wts, total;
+    size_t scratch, mixed, out, iw, iw2, resid, ids, wts, total;
 };
 
 bool block_ok(const dhp_hc_block* b, bool inject) {
@@ -38,7 +40,8 @@ bool block_ok(const dhp_hc_block* b, bool inject) {
 
 // Workspace layout: one scratch region shared by every step (they run in order on one stream),
 // then the step outputs the next step reads: mixed fp16 [H], the sublayer/MoE output fp16 [H],
-// the inject weights fp32 [C], and the MoE ids and weights (not returned).
+// two sets of inject weights fp32 [C] (a fused inject-read consumes one and writes the other),
+// the second residual buffer fp16 [C*H], and the MoE ids and weights (not returned).
 bool layer_ws(int C, int H, const dhp_decode_layer* layers, int n, const dhp_hc_block* mixer, LayerWs* w) {
     if (C <= 0 || H <= 0 || n < 0 || (n > 0 && !layers) || !block_ok(mixer, false)) return false;
     size_t scratch = decodehp_workspace_bytes(DHP_OP_HC_READ, C, mixer->down->rows, 0);
@@ -54,7 +57,9 @@ bool layer_ws(int C, int H, const dhp_decode_layer* layers, int n, const dhp_hc_
     w->mixed = a256(scratch);
     w->out = w->mixed + a256((size_t)H * 2);
     w->iw = w->out + a256((size_t)H * 2);
-    w->ids = w->iw + a256((size_t)C * 4);
+    w->iw2 = w->iw + a256((size_t)C * 4);
+    w->resid = w->iw2 + a256((size_t)C * 4);
+    w->ids = w->resid + a256((size_t)C * H * 2);
     w->wts = w->ids + a256((size_t)DHP_MOE_MAX_TOP_K * 4);
     w->total = w->wts + a256((size_t)DHP_MOE_MAX_TOP_K * 4);
     return true;
@@ -77,7 +82,8 @@ int run_layers(const void* x, int C, int H, float eps, const dhp_decode_layer* l
     const size_t scratch_bytes = w.mixed - w.scratch;
     void* mixed = base + w.mixed;
     void* out = base + w.out;
-    float* iw = reinterpret_cast<float*>(base + w.iw);
+    float* iw_buf[2] = {reinterpret_cast<float*>(base + w.iw), reinterpret_cast<float*>(base + w.iw2)};
+    void* resid[2] = {hidden, base + w.resid};
     int32_t* ids = reinterpret_cast<int32_t*>(base + w.ids);
     float* wts = reinterpret_cast<float*>(base + w.wts);
 
@@ -86,24 +92,39 @@ int run_layers(const void* x, int C, int H, float eps, const dhp_decode_layer* l
                        static_cast<uint4*>(hidden), n16, total16);
     const hipError_t le = hipGetLastError();
     int rc = (le == hipSuccess) ? DHP_OK : dhp_fail(DHP_ERR_LAUNCH, "replicate launch: %s", hipGetErrorString(le));
+    // cur: the buffer holding the residual; gi: the inject weights the pending inject uses. A read
+    // with an inject pending is the fused inject-read: it forms resid[cur ^ 1] and writes the new
+    // gates to iw_buf[gi ^ 1]. 2 * n injects in all, so the residual ends in resid[0] = hidden.
+    int cur = 0, gi = 0;
+    bool pending = false;
+    auto read = [&](const dhp_hc_block* b, void* mixed_to, bool with_inject) {
+        float* next_iw = with_inject ? iw_buf[pending ? gi ^ 1 : gi] : nullptr;
+        int r;
+        if (pending) {
+            r = decodehp_hc_inject_read(resid[cur], out, iw_buf[gi], resid[cur ^ 1], b->hc_norm, C, H, eps, b->down,
+                                        b->up, b->inject, mixed_to, next_iw, scratch, scratch_bytes, s);
+            cur ^= 1;
+            gi ^= 1;
+        } else {
+            r = decodehp_hc_read(resid[cur], b->hc_norm, C, H, eps, b->down, b->up, b->inject, mixed_to, next_iw,
+                                 scratch, scratch_bytes, s);
+        }
+        pending = false;
+        return r;
+    };
     for (int i = 0; i < n && !rc; ++i) {
         const dhp_decode_layer& L = layers[i];
-        rc = decodehp_hc_read(hidden, L.attn_hc.hc_norm, C, H, eps, L.attn_hc.down, L.attn_hc.up, L.attn_hc.inject,
-                              mixed, iw, scratch, scratch_bytes, s);
+        rc = read(&L.attn_hc, mixed, true);
         if (!rc) rc = decodehp_dequant_gemv(L.sublayer, mixed, 1, out, DHP_F16, nullptr, nullptr, 0, s);
-        if (!rc) rc = decodehp_hc_inject(hidden, out, iw, C, H, s);
-        if (!rc)
-            rc = decodehp_hc_read(hidden, L.mlp_hc.hc_norm, C, H, eps, L.mlp_hc.down, L.mlp_hc.up, L.mlp_hc.inject,
-                                  mixed, iw, scratch, scratch_bytes, s);
+        pending = true;
+        if (!rc) rc = read(&L.mlp_hc, mixed, true);
         if (!rc)
             rc = decodehp_moe_decode(mixed, L.router, L.router_dtype, L.shared_gate_row, L.gate, L.up, L.down,
                                      L.shared_gate, L.shared_up, L.shared_down, L.top_k, L.moe_flags, out, ids, wts,
                                      scratch, scratch_bytes, s);
-        if (!rc) rc = decodehp_hc_inject(hidden, out, iw, C, H, s);
+        pending = true;
     }
-    if (!rc)
-        rc = decodehp_hc_read(hidden, mixer->hc_norm, C, H, eps, mixer->down, mixer->up, nullptr, mixed_out,
-                              nullptr, scratch, scratch_bytes, s);
+    if (!rc) rc = read(mixer, mixed_out, false);
     return rc;
 }
 
@@ -134,6 +155,8 @@ int decodehp_graph_capture_decode_layers(const void* x, int32_t C, int32_t H, fl
                                          void* ws, size_t ws_bytes, dhp_graph** graph) {
     if (!graph) return dhp_fail(DHP_ERR_INVALID, "null graph handle");
     *graph = nullptr;
+    // the inputs may have been written by asynchronous work on any stream: wait for all of it
+    if (hipDeviceSynchronize() != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "device synchronization failed");
     hipStream_t cs;
     if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess)
         return dhp_fail(DHP_ERR_LAUNCH, "stream creation failed");

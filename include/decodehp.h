@@ -269,6 +269,29 @@ int decodehp_hc_inject(void* wide, const void* out, const float* inject_w, int32
                        void* stream);
 
 /*
+ * decodehp_hc_inject_read -- a sublayer's inject followed by the next hyper-connection read, in
+ * one call: the step pair the decoder-layer pseudocode runs between two sublayers
+ * ("src/families/qwen4/mod.rs", decoder-layer pseudocode; "src/families/qwen4/hc.rs",
+ * encode_hyper_connection). First
+ *     hidden[c*H + h] = fp16(prev[c*H + h] + out[h] * inject_w[c])
+ * (the same bits decodehp_hc_inject stores), then decodehp_hc_read of hidden. The inject's add
+ * is formed inside the read's first kernel, which also stores hidden, so the call saves the
+ * separate inject's launch.
+ *   prev     : fp16 [C*H], the residual before the inject, 16-byte aligned (not written).
+ *   out      : fp16 [H], the sublayer output, 16-byte aligned.   inject_w : fp32 [C] (its gates).
+ *   hidden   : fp16 [C*H], 16-byte aligned, the residual after the inject. Must not overlap prev
+ *              or out (the read's blocks are still reading them while one block stores hidden).
+ *   hc_norm, C, H, eps, down, up, inject, mixed, ws : as decodehp_hc_read (of hidden).
+ *   inject_w_next : fp32 [C], the new read's inject weights; must not overlap inject_w.
+ * Errors: those of decodehp_hc_read and decodehp_hc_inject; -1 when hidden overlaps prev or
+ *         out, or inject_w_next overlaps inject_w.
+ */
+int decodehp_hc_inject_read(const void* prev, const void* out, const float* inject_w, void* hidden,
+                            const void* hc_norm, int32_t C, int32_t H, float eps, const dhp_int4* down,
+                            const dhp_int4* up, const dhp_int4* inject, void* mixed, float* inject_w_next,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * decodehp_hc_read_batched / decodehp_hc_inject_batched -- the read and the inject for the m
  * tokens of a chunked-prefill micro-batch ("src/families/qwen4/hc.rs", encode_hyper_connection:
  * inside a micro-batch every token's inject gate has a row of its own). Row t of each output is
@@ -332,21 +355,28 @@ size_t decodehp_decode_layers_workspace_bytes(int32_t C, int32_t H, const dhp_de
  *   x         : fp16 [H], 16-byte aligned (read once, at entry).
  *   layers    : n_layers >= 0 descriptors (read during the call only).
  *   mixer     : the final mixer (inject must be NULL).
- *   hidden    : fp16 [C*H], 16-byte aligned: the residual, replicated from x, then updated in
- *               place by every inject; holds the residual after the last layer on return.
+ *   hidden    : fp16 [C*H], 16-byte aligned: the residual, replicated from x at entry; holds
+ *               the residual after the last layer's inject on return. Between the steps the
+ *               residual alternates between hidden and a buffer in ws (an inject writes a new
+ *               copy instead of updating in place); the count of injects is even, so the last
+ *               one lands in hidden.
  *   mixed_out : fp16 [H], the mixer's output.
  *   ws        : decodehp_decode_layers_workspace_bytes(...) bytes, 16-byte aligned.
- * Each step is the entry point of its own (decodehp_hc_read, decodehp_dequant_gemv,
- * decodehp_hc_inject, decodehp_moe_decode) with its checks and errors; on an error the
- * sequence stops there and hidden and mixed_out are unspecified.
+ * Each step is an entry point of its own with its checks and errors: the first read is
+ * decodehp_hc_read; every later read, the mixer's included, is decodehp_hc_inject_read (the
+ * previous sublayer's inject fused in front); the sublayers are decodehp_dequant_gemv (the
+ * stand-in) and decodehp_moe_decode. On an error the sequence stops there and hidden and
+ * mixed_out are unspecified.
  */
 int decodehp_decode_layers(const void* x, int32_t C, int32_t H, float eps, const dhp_decode_layer* layers,
                            int32_t n_layers, const dhp_hc_block* mixer, void* hidden, void* mixed_out,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
- * A captured decodehp_decode_layers sequence. Capture runs the sequence once on a private
- * stream (it writes hidden and mixed_out), then records it; every launch replays it on the
+ * A captured decodehp_decode_layers sequence. Capture first waits for all work on the device
+ * (hipDeviceSynchronize: inputs written by asynchronous work on any stream are complete), runs
+ * the sequence once on a private stream (it writes hidden and mixed_out), then records it and
+ * waits for the private stream again before returning; every launch replays it on the
  * given stream with the same buffers (write the next token into x before a launch). The
  * descriptors may be freed after capture; the weights and buffers must outlive the graph.
  * Errors: those of decodehp_decode_layers, and -6 when capture or instantiation fails.

@@ -314,3 +314,24 @@ def test_moe_noalloc_checks_and_scratch_limit():
     assert hca.workspace_bytes(hca.DHP_OP_MOE_DECODE, 1024, 10, 640) <= 32768
     assert moe_noalloc(E=1024, inter=640, top_k=10) == -5       # fits; no device here
     assert moe_noalloc(E=256, inter=512, top_k=8) == -5
+
+
+def test_hc_inject_read_rejects_overlaps_and_bad_calls():
+    L = hca.lib()
+    C, H, R = 4, 512, 64
+    down, up, inj = int4(rows=R, cols=C * H), int4(rows=C * H, cols=R), int4(rows=C, cols=C * H)
+    P, O, W, HID, W2 = FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20), FAKE + (4 << 20)
+
+    def f(prev=P, out=O, iw=W, hidden=HID, iw_next=W2, ws=FAKE + (5 << 20), wsb=1 << 16, C=C):
+        return L.decodehp_hc_inject_read(prev, out, iw, hidden, FAKE, C, H, 1e-6, ctypes.byref(down),
+                                         ctypes.byref(up), ctypes.byref(inj), FAKE, iw_next, ws, wsb, None)
+    assert f() == -5                                # valid; no device here
+    assert f(prev=0) == -1
+    assert f(hidden=P + 4096 - 16) == -1            # overlaps prev (C*H*2 = 4096 bytes)
+    assert f(hidden=P + 4096) == -5                 # just past it
+    assert f(hidden=O) == -1                        # overlaps out
+    assert f(iw_next=W + 8) == -1                   # overlaps the consumed gates
+    assert f(iw_next=W + 16) == -5
+    assert f(C=3) == -2
+    assert f(hidden=HID + 8) == -3
+    assert f(ws=None) == -4

@@ -131,3 +131,38 @@ def test_hc_read_deterministic_and_guarded():
     assert torch.equal(a, buf[128:128 + H]) and torch.equal(b, wbuf[4:4 + C])
     assert torch.all(buf[:128] == -7.0) and torch.all(buf[128 + H:] == -7.0)
     assert torch.all(wbuf[:4] == -7.0) and torch.all(wbuf[4 + C:] == -7.0)
+
+
+@pytest.mark.parametrize("C,H,R,inject", [(4, 2560, 320, True), (4, 2560, 320, False), (2, 1024, 128, True),
+                                          (16, 128, 64, True), (1, 8192, 320, True)])
+def test_hc_inject_read_is_inject_then_read_bitwise(C, H, R, inject):
+    """decodehp_hc_inject_read (the inject formed inside the read's first kernel) against
+    decodehp_hc_inject followed by decodehp_hc_read: the same bits for the new residual, mixed and
+    the new inject weights; prev is left unchanged; and the oracle's inject then read."""
+    say(f"hc inject+read C={C} H={H} R={R} inject={inject}")
+    rng = np.random.default_rng([52, C, H, R])
+    blk = synth.hc_block(rng, C, H, R, inject=inject)
+    prev = synth.normal_f16(rng, (C * H,))
+    out = synth.normal_f16(rng, (H,))
+    iw = rng.uniform(0.0, 2.0, size=C).astype(np.float32)
+    gamma = hca.bf16_bits_to_tensor(blk["gamma_bits"]).cuda()
+    down, up = dev_int4(blk["down"]), dev_int4(blk["up"])
+    inj = dev_int4(blk["inject"]) if inject else None
+    prev_d, out_d, iw_d = to_dev(prev), to_dev(out), to_dev(iw)
+    hidden, mixed, iw_next = hca.hc_inject_read(prev_d, out_d, iw_d, gamma, C, H, down, up, inj)
+    wide = prev_d.clone()
+    hca.hc_inject(wide, out_d, iw_d, C, H)
+    mixed2, iw2 = hca.hc_read(wide, gamma, C, H, down, up, inj)
+    torch.cuda.synchronize()
+    assert torch.equal(prev_d.cpu(), torch.from_numpy(prev))
+    assert torch.equal(hidden.view(torch.int16).cpu(), wide.view(torch.int16).cpu())
+    assert torch.equal(mixed.view(torch.int16).cpu(), mixed2.view(torch.int16).cpu())
+    if inject:
+        assert torch.equal(iw_next.view(torch.int32).cpu(), iw2.view(torch.int32).cpu())
+    hid_ref = oracle.hc_inject(prev, out, iw, C, H)
+    assert_within_tol(hidden.float().cpu().numpy(), hid_ref, "hidden")
+    ref = oracle.hc_read(hidden.cpu().numpy(), blk["gamma_bits"], blk["down"], blk["up"], blk["inject"] if inject else None,
+                         C, H)
+    assert_within_tol(mixed.float().cpu().numpy(), ref["mixed"], "mixed after inject")
+    if inject:
+        assert_within_tol(iw_next.cpu().numpy(), ref["inject_w"], "inject_w after inject")
