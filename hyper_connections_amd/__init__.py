@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         P4, PE = ctypes.POINTER(CInt4), ctypes.POINTER(CInt4Experts)
         L.decodehp_dequant_gemv.argtypes = [P4, vp, i32, vp, i32, vp, vp, sz, vp]
+        L.decodehp_dequant_gemv_mc.argtypes = [P4, vp, i32, vp, i32, vp, vp, sz, vp]
         L.decodehp_dequant_gemm_batched.argtypes = [P4, vp, i32, vp, vp]
         L.decodehp_moe_decode.argtypes = [vp, vp, i32, vp, PE, PE, PE, P4, P4, P4, i32, i32, vp, vp, vp,
                                           vp, sz, vp]
@@ -113,7 +114,8 @@ def lib() -> ctypes.CDLL:
         L.decodehp_workspace_bytes.restype = sz
         L.decodehp_last_error.restype = ctypes.c_char_p
         L.decodehp_version.restype = i32
-        for name in ("decodehp_dequant_gemv", "decodehp_dequant_gemm_batched", "decodehp_moe_decode",
+        for name in ("decodehp_dequant_gemv", "decodehp_dequant_gemv_mc", "decodehp_dequant_gemm_batched",
+                     "decodehp_moe_decode",
                      "decodehp_moe_decode_noalloc",
                      "decodehp_moe_prefill", "decodehp_hc_read", "decodehp_hc_inject", "decodehp_decode_layers",
                      "decodehp_hc_inject_read",
@@ -250,8 +252,9 @@ def _workspace(nbytes: int, device, kind: str = "scratch", stream=None):
 
 # --------------------------------------------------------------------------- entry points
 
-def dequant_gemv(w: Int4Weight, x, y=None, out_dtype=None, argmax=False, stream=None):
-    """y[m, n] = sum_k W[n, k] x[m, k]; x fp16 [K] or [m, K] (m <= 16). Returns y (and argmax int32 [m])."""
+def dequant_gemv(w: Int4Weight, x, y=None, out_dtype=None, argmax=False, stream=None, matrix_cores=False):
+    """y[m, n] = sum_k W[n, k] x[m, k]; x fp16 [K] or [m, K] (m <= 16). Returns y (and argmax int32 [m]).
+    matrix_cores: the matrix-core arm (decodehp_dequant_gemv_mc), not bit-equal to per-row calls."""
     torch = _torch()
     out_dtype = out_dtype or torch.float16
     x2 = x.reshape(-1, w.cols)
@@ -263,7 +266,8 @@ def dequant_gemv(w: Int4Weight, x, y=None, out_dtype=None, argmax=False, stream=
     am = torch.empty(m, dtype=torch.int32, device=x.device) if argmax else None
     ws = _workspace(workspace_bytes(DHP_OP_GEMV_ARGMAX, w.rows, m), x.device, "argmax", stream=stream) if argmax else None
     d = w.desc()
-    _check(lib().decodehp_dequant_gemv(ctypes.byref(d), x2.data_ptr(), m, y.data_ptr(),
+    fn = lib().decodehp_dequant_gemv_mc if matrix_cores else lib().decodehp_dequant_gemv
+    _check(fn(ctypes.byref(d), x2.data_ptr(), m, y.data_ptr(),
                                        DHP_F32 if out_dtype == torch.float32 else DHP_F16,
                                        _ptr(am), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     yv = y.reshape(x.shape[:-1] + (w.rows,)) if x.dim() == 1 else y
@@ -676,7 +680,7 @@ class PreparedCall:
             _check(rc)
 
 
-def prepare_gemv(w: Int4Weight, x, y, argmax=None, stream=None) -> PreparedCall:
+def prepare_gemv(w: Int4Weight, x, y, argmax=None, stream=None, matrix_cores=False) -> PreparedCall:
     torch = _torch()
     x2 = x.reshape(-1, w.cols)
     m = x2.shape[0]
@@ -686,7 +690,8 @@ def prepare_gemv(w: Int4Weight, x, y, argmax=None, stream=None) -> PreparedCall:
     d = w.desc()
     args = (ctypes.byref(d), x2.data_ptr(), m, y.data_ptr(), DHP_F32 if y.dtype == torch.float32 else DHP_F16,
             _ptr(argmax), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
-    return PreparedCall(lib().decodehp_dequant_gemv, args, (d, x2, y, argmax, ws, w))
+    fn = lib().decodehp_dequant_gemv_mc if matrix_cores else lib().decodehp_dequant_gemv
+    return PreparedCall(fn, args, (d, x2, y, argmax, ws, w))
 
 
 def prepare_gemm_batched(w: Int4Weight, x, y, stream=None) -> PreparedCall:

@@ -111,9 +111,12 @@ size_t decodehp_workspace_bytes(int32_t op, int32_t a, int32_t b, int32_t c) {
     }
 }
 
-int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, int32_t y_dtype,
-                          int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+// Checks shared by the two GEMV entry points.
+int check_gemv(const dhp_int4* w, const void* x, int32_t m, const void* y, int32_t y_dtype, const int32_t* argmax,
+               const void* ws, size_t ws_bytes) {
     int rc = check_int4(w, "w");
     if (rc) return rc;
     if (!x || !y) return dhp_fail(DHP_ERR_INVALID, "null x or y");
@@ -128,10 +131,32 @@ int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, 
         if (!ws || ws_bytes < need) return dhp_fail(DHP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
         if (!aligned(ws, 16)) return dhp_fail(DHP_ERR_MISALIGNED, "workspace not 16-byte aligned");
     }
+    return DHP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, int32_t y_dtype,
+                          int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    const int rc = check_gemv(w, x, m, y, y_dtype, argmax, ws, ws_bytes);
+    if (rc) return rc;
     DeviceFacts dev;
     if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
     if (m == 1)
         return launch_gemv_m1(w, x, y, y_dtype == DHP_F32, argmax, ws, static_cast<hipStream_t>(stream), dev);
+    return launch_gemv_rows(w, x, m, y, y_dtype == DHP_F32, argmax, ws, dhp_argmax_part_stride(w->rows, m),
+                            static_cast<hipStream_t>(stream));
+}
+
+int decodehp_dequant_gemv_mc(const dhp_int4* w, const void* x, int32_t m, void* y, int32_t y_dtype,
+                             int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    const int rc = check_gemv(w, x, m, y, y_dtype, argmax, ws, ws_bytes);
+    if (rc) return rc;
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
     if (dhp_gemv_mfma16_fits(w, m))
         return launch_gemv_mfma16(w, x, m, y, y_dtype == DHP_F32, argmax, ws, dhp_argmax_part_stride(w->rows, m),
                                   static_cast<hipStream_t>(stream), dev.cus);

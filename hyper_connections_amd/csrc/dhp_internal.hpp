@@ -263,5 +263,7 @@ int launch_gemm_mfma(const dhp_int4* w, const void* x, int M, void* y, int y_f32
                      void* ws, size_t ws_part_stride, hipStream_t s);
 hipError_t launch_argmax_final(const float* pv, const int* pi, int nparts, int m, int32_t* out, hipStream_t s);
 bool dhp_gemv_mfma16_fits(const dhp_int4* w, int M);
+int launch_gemv_rows(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
+                     size_t ws_part_stride, hipStream_t s);
 int launch_gemv_mfma16(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
                        size_t ws_part_stride, hipStream_t s, int cus);

@@ -93,9 +93,13 @@ typedef struct dhp_int4_experts {
 /*
  * decodehp_dequant_gemv -- Y[r, n] = sum_k W[n, k] * X[r, k] for r < m (m <= 16).
  * "src/real_forward.rs": module doc (dequant_int4_gemv_simd against resident INT4-affine
- * weights) and field batched_gemv_prefill (the multi-row GEMM gives the same outputs as
- * m separate GEMVs). The LM head of "src/families/qwen4/mod.rs" (decoder-layer
- * pseudocode, exit) is this call over the vocabulary, with argmax.
+ * weights) and field batched_gemv_prefill (the batched GEMV and the per-row GEMV agree bit for
+ * bit). The LM head of "src/families/qwen4/mod.rs" (decoder-layer pseudocode, exit) is this
+ * call over the vocabulary, with argmax.
+ * Every row r of an m-row call gives exactly the bits (y and argmax) of an m = 1 call on row r
+ * alone, for any weights and biases: both run each output as s * (q . x) + b * sum(x) per
+ * 64-weight group in fp32, in one fixed operation order (see decodehp_dequant_gemv_mc for the
+ * matrix-core arm, which does not).
  *   w       : weight [N x K].
  *   x       : fp16 [m][K], row-major, 16-byte aligned.
  *   y       : [m][N] row-major, fp16 (y_dtype DHP_F16) or fp32 (DHP_F32); fp32 accumulate.
@@ -111,12 +115,26 @@ int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, 
                           int32_t* argmax, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * decodehp_dequant_gemv_mc -- decodehp_dequant_gemv on the matrix cores (the pages' separate
+ * matrix-instruction variant, "src/real_forward.rs", field batched_gemv_prefill): faster for
+ * m >= 8 (the LM head over 8 rows), but NOT bit-equal to the m = 1 call. Each weight is
+ * dequantized once into an fp16 operand, q*s+b rounded to fp16 (exact when the bias is
+ * -8*scale and the scale is a bf16 value in fp16's normal range; otherwise off by up to half
+ * an fp16 ulp per weight, which can put outputs near zero past the 1e-3 + 1e-2|y| bar), and
+ * the products are summed in the matrix cores' order. Arguments, workspace and errors: as
+ * decodehp_dequant_gemv.
+ */
+int decodehp_dequant_gemv_mc(const dhp_int4* w, const void* x, int32_t m, void* y, int32_t y_dtype,
+                             int32_t* argmax, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * decodehp_dequant_gemm_batched -- Y = X W^T for a chunked-prefill block of m <= 128 rows.
  * "src/real_forward.rs", field batched_gemv_prefill: resident GEMVs run as one M-row GEMM;
  * the same field and prefill_steel give the 64-row micro-batched form this replaces.
  * Matrix cores (fp16 operands, fp32 accumulate): each weight is dequantized once into an
  * fp16 operand, q*s+b rounded to fp16 (exact when the bias is -8*scale and the scale is
- * a bf16 value in fp16's normal range).
+ * a bf16 value in fp16's normal range; for other biases each weight can be off by half an
+ * fp16 ulp, which can put outputs near zero past the 1e-3 + 1e-2|y| bar).
  *   w : weight [N x K], N % 16 == 0.   x : fp16 [m][K], 16-byte aligned.   y : fp16 [m][N].
  * Errors: -1, -2 (K % 64, N % 16, m outside 1..128, K > 32768), -3, -5, -6.
  */

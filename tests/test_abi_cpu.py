@@ -335,3 +335,14 @@ def test_hc_inject_read_rejects_overlaps_and_bad_calls():
     assert f(C=3) == -2
     assert f(hidden=HID + 8) == -3
     assert f(ws=None) == -4
+
+
+def test_gemv_mc_checks_like_gemv():
+    L = hca.lib()
+    w = int4(rows=64, cols=512)
+    for fn in (L.decodehp_dequant_gemv, L.decodehp_dequant_gemv_mc):
+        assert fn(ctypes.byref(w), 0, 2, FAKE, 1, None, None, 0, None) == -1
+        assert fn(ctypes.byref(w), FAKE, 17, FAKE, 1, None, None, 0, None) == -2
+        assert fn(ctypes.byref(w), FAKE + 8, 2, FAKE, 1, None, None, 0, None) == -3
+        assert fn(ctypes.byref(w), FAKE, 2, FAKE, 1, FAKE, None, 0, None) == -4
+        assert fn(ctypes.byref(w), FAKE, 2, FAKE, 1, None, None, 0, None) == -5
