@@ -8,7 +8,8 @@ One step = one pass of every hot-path call over one batch of seeded synthetic in
   moe       routed MoE decode, 256 resident experts, top-8, gated shared expert
   prefill   batched projection, M=128, N=8192, K=2560 (matrix cores), fp16 out
   lmhead1   LM head, M=1, 151936 x 2560, fp32 logits + argmax
-  lmhead8   LM head, M=8, same shape, fp32 logits + argmax
+  lmhead8   LM head, M=8, same shape, fp32 logits + argmax (the default multi-row arm, whose
+            logits are bitwise those of eight M=1 calls)
 
 `value` is the step's algorithmic bytes (INT4 codes + bf16 scales/biases + activations in +
 outputs, each counted once) divided by the measured step time: whole-job HBM GB/s with every
@@ -16,9 +17,15 @@ input already resident. Rotating weight copies and the 438 MB of LM-head traffic
 each call's weights out of the 256 MB last-level cache between uses.
 
 Also printed in the same JSON line:
-  roofline      the dominant call (the M=1 LM head: its GEMV kernel and the small argmax
-                reduction kernel) against 8 TB/s, its average duration from fence-free HIP events
-                on the launch stream around that call in every timed step;
+  roofline      the M=1 LM head (its GEMV kernel and the small argmax reduction kernel), the
+                dominant HBM-bound call, against 8 TB/s, its average duration from fence-free HIP
+                events on the launch stream around that call in every timed step;
+  roofline_moe  the MoE decode call (its three launches) against 8 TB/s, timed the same way;
+  roofline_m8   the longest call of the step, the M=8 LM head on the bit-exact multi-row arm,
+                which is bound by the vector ALU: its v_dot2 lane operations (M * N * K / 2, two
+                multiply-adds each, the arithmetic the method fixes) per second against the
+                chip's one v_dot2 per lane per clock (256 CUs * 64 lanes * 2.4 GHz), timed the
+                same way;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload (rank 0);
   calls         per-call microseconds and GB/s from a separate pass: batches of back-to-back
                 launches between fence-free HIP events (median over batches);
@@ -43,6 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12     # one v_dot2 per lane per clock: 39.32 T lane-op/s
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "lmhead_gemv_m1_counters.json")
 # every file the dominant kernel is compiled from (its source, the device helpers and declarations
 # it includes, and the build script that holds the compiler flags)
@@ -84,7 +92,7 @@ def algorithmic_bytes():
     b["moe_i8k10"] = (E * K + 2 * K + 4 * E + 2 * K + 11 * (2 * int4_bytes(inter, K) + int4_bytes(K, inter))
                       + 2 * K + 2 * K + 8 * 10)
     b["lmhead1"] = int4_bytes(V, K) + 2 * K + 4 * V + 4
-    b["lmhead8"] = int4_bytes(V, K) + 2 * 8 * K + 4 * 8 * V + 4 * 8
+    b["lmhead8"] = b["lmhead8_mc"] = int4_bytes(V, K) + 2 * 8 * K + 4 * 8 * V + 4 * 8
     # entry replication, the attn and mlp reads (with inject weights) and injects, the stand-in
     # sublayer GEMV, the MoE layer, and the final mixer's read
     read = int4_bytes(R, C * H) + int4_bytes(C * H, R) + int4_bytes(C, C * H) + 4 * C * H + 2 * H + 4 * C
@@ -104,8 +112,10 @@ STEP_CALLS = ("gemv", "hc", "moe", "prefill", "lmhead1", "lmhead8")
 # layer with the INT8 scaled router at top-10, an inject fused in front of the next
 # hyper-connection read (decodehp_hc_inject_read), the hyper-connection read and inject of a
 # 128-token chunk, and one token through a whole decoder layer plus the final mixer, as a
-# launch sequence and as a graph.
-EXTRA_CALLS = ("moe_prefill", "moe_i8k10", "hc_inject_read", "hc_chunk", "layer_eager", "layer_graph")
+# launch sequence and as a graph; and the M=8 LM head on the matrix-core arm (an explicit option:
+# fp16-rounded weights, another summation order).
+EXTRA_CALLS = ("moe_prefill", "moe_i8k10", "hc_inject_read", "hc_chunk", "layer_eager", "layer_graph",
+               "lmhead8_mc")
 CALLS = STEP_CALLS + EXTRA_CALLS
 MOE_CHUNK = 128
 
@@ -178,7 +188,7 @@ def build_workload(torch, hca, synth, ring: int, only=None):
                         mixed=torch.empty((MOE_CHUNK, 2560), dtype=torch.float16, device=dev),
                         iw=torch.empty((MOE_CHUNK, 4), dtype=torch.float32, device=dev))
 
-    if want("lmhead1", "lmhead8"):
+    if want("lmhead1", "lmhead8", "lmhead8_mc"):
         l1 = synth.lmhead_workload(0, m=1)
         lw = up_int4(l1["w"])
         W["lm_w"] = [lw, clone(lw)]
@@ -287,6 +297,8 @@ def prepare_calls(hca, W, ring: int, only=None):
                                                W["layer"]["mg"]).launch],
         "lmhead1": lambda: [hca.prepare_gemv(W["lm_w"][0], W["lm_x1"], W["lm_y1"], argmax=W["lm_a1"])],
         "lmhead8": lambda: [hca.prepare_gemv(W["lm_w"][1], W["lm_x8"], W["lm_y8"], argmax=W["lm_a8"])],
+        "lmhead8_mc": lambda: [hca.prepare_gemv(W["lm_w"][1], W["lm_x8"], W["lm_y8"], argmax=W["lm_a8"],
+                                                matrix_cores=True)],
     }
     return {name: f() for name, f in make.items() if only is None or name == only}
 
@@ -309,14 +321,20 @@ def run_call(c):
 def step(calls, i, ev=None, stream=None):
     run_call(calls["gemv"][i % len(calls["gemv"])])
     run_call(calls["hc"][i % len(calls["hc"])])
-    run_call(calls["moe"][i % len(calls["moe"])])
-    run_call(calls["prefill"][i % len(calls["prefill"])])
     if ev is not None:
         ev[0].record(stream)
-    run_call(calls["lmhead1"][0])
+    run_call(calls["moe"][i % len(calls["moe"])])
     if ev is not None:
         ev[1].record(stream)
+    run_call(calls["prefill"][i % len(calls["prefill"])])
+    if ev is not None:
+        ev[2].record(stream)
+    run_call(calls["lmhead1"][0])
+    if ev is not None:
+        ev[3].record(stream)
     run_call(calls["lmhead8"][0])
+    if ev is not None:
+        ev[4].record(stream)
 
 
 class HipEvent:
@@ -373,8 +391,9 @@ def per_call_pass(torch, calls, nbytes, iters: int, exact: bool = False):
     stream = torch.cuda.current_stream()
     for name in calls:
         seq = calls[name]
-        n = iters if exact else (max(iters, len(seq)) if name not in ("lmhead1", "lmhead8") else max(8, iters // 4))
-        batch = max(1, min(n, 4 if name in ("lmhead1", "lmhead8") else 16))
+        big = name.startswith("lmhead")
+        n = iters if exact else (max(iters, len(seq)) if not big else max(8, iters // 4))
+        batch = max(1, min(n, 4 if big else 16))
         nb = max(1, n // batch)
         for i in range(3):
             run_call(seq[i % len(seq)])
@@ -777,7 +796,7 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
+    ev = [tuple(HipEvent() for _ in range(5)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -786,8 +805,11 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
-    dom_us = float(np.mean([a.us_until(b) for a, b in ev]))
-    print(f"[bench] {args.steps} steps, {ms_per_step:.3f} ms/step, {value:.1f} GB/s; lmhead1 {dom_us:.2f} us",
+    moe_us = float(np.mean([e[0].us_until(e[1]) for e in ev]))
+    dom_us = float(np.mean([e[2].us_until(e[3]) for e in ev]))
+    m8_us = float(np.mean([e[3].us_until(e[4]) for e in ev]))
+    print(f"[bench] {args.steps} steps, {ms_per_step:.3f} ms/step, {value:.1f} GB/s; lmhead1 {dom_us:.2f} us, "
+          f"lmhead8 {m8_us:.2f} us",
           file=sys.stderr, flush=True)
 
     dom_ach = nbytes["lmhead1"] / dom_us / 1e3
@@ -795,6 +817,18 @@ def main():
                 "frac": round(dom_ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
                 "kernel": "k_gemv_m1_reg<5,f32,argmax> + k_argmax_final (LM head 151936 x 2560, M=1)",
                 "algorithmic_bytes_per_launch": nbytes["lmhead1"], "avg_launch_us": round(dom_us, 2)}
+    dot2_ops = 8 * 151936 * 2560 // 2
+    m8_ach = dot2_ops / m8_us / 1e6                     # T lane-ops/s
+    roofline_m8 = {"bound": "alu", "achieved": round(m8_ach, 2), "peak": ALU_PEAK_TOPS, "unit": "T v_dot2 lane-op/s",
+                   "frac": round(m8_ach / ALU_PEAK_TOPS, 4), "traffic": None,
+                   "kernel": "k_gemv_rows<8,f32,argmax,full> + k_argmax_final (LM head 151936 x 2560, M=8)",
+                   "algorithmic_ops_per_launch": dot2_ops, "avg_launch_us": round(m8_us, 2),
+                   "hbm_GBps": round(nbytes["lmhead8"] / m8_us / 1e3, 1)}
+    moe_ach = nbytes["moe"] / moe_us / 1e3
+    roofline_moe = {"bound": "hbm", "achieved": round(moe_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(moe_ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "MoE decode (router + top-8, phase 1, phase 2: three launches), E=256, top-8",
+                    "algorithmic_bytes_per_launch": nbytes["moe"], "avg_call_us": round(moe_us, 2)}
 
     per_call = None if args.no_per_call else per_call_pass(torch, calls, nbytes, iters=100)
     if per_call is not None:
@@ -824,6 +858,8 @@ def main():
                    "step_bytes": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
                    "parallelism": "1 GPU"},
         "roofline": roofline,
+        "roofline_m8": roofline_m8,
+        "roofline_moe": roofline_moe,
         "cpu_baseline": cpu,
         "calls": per_call,
     }

@@ -10,16 +10,20 @@
 // eights, sixteens); the row is scaled by 1/16. Here the same operations run in the same order,
 // only spread differently:
 //
-//  * A lane owns one weight row and runs all 16 virtual lanes' chains for it, for up to MR
-//    activation rows at once: each chunk's codes are unpacked once and feed every activation
-//    row, whose chains stay in registers (16 * MR accumulators).
-//  * A lane reads its row a 128-byte line (8 chunks) at a time, the next line in flight while
-//    the current one computes; a line is one cache line, so each is fetched once.
-//  * The activations are the same for every lane. Each block stages them once in LDS, in the
+//  * Four lanes own one weight row. Of each 16 chunks (one per virtual lane) the lane in quarter
+//    p = 0..3 of its wave (lane bits 4 and 5) runs chunks 4p .. 4p+3, i.e. virtual lanes
+//    4p .. 4p+3, for up to MR activation rows at once: each chunk's codes are unpacked once and
+//    feed every activation row, whose chains stay in registers (4 * MR accumulators).
+//  * The 16 rows of a wave read their 64-byte quarters of each 256-byte segment in one load
+//    instruction, the next segment in flight while the current one computes.
+//  * The activations are the same for every row. Each block stages them once in LDS, in the
 //    form the M=1 kernels compute per chunk (x32_off_from: the permuted pairs, 16 * sum and
-//    -1024 * sum), for as many chunks as fit (all of K = 2560 at 8 rows); every lane then
-//    reads them at the same LDS addresses.
-//  * After the last chunk each lane sums its 16 chains in the butterfly's order.
+//    -1024 * sum), for as many chunks as fit (all of K = 2560 at 8 rows). The four lanes of a
+//    quad run the same chunk for four rows; each reads a quarter of the chunk's activations
+//    and the dots take the rest from the quad by DPP.
+//  * At the end each lane sums its four chains (the butterfly's quad of virtual lanes), and two
+//    exchanges across the quarters (lane XOR 16, then XOR 32) add the quads in the butterfly's
+//    order; floating-point addition is commutative, so every quarter ends with the same bits.
 // The arithmetic is the M=1 kernels' for every K they take, so the two agree bit for bit
 // wherever both run. The matrix-core kernels (gemv_mfma.hip, gemm.hip) round each dequantized
 // weight to fp16 and sum in another order; they remain as an explicit option.
@@ -31,29 +35,24 @@
 namespace {
 
 constexpr int SEG = 16;          // chunks per segment: one per virtual lane
+constexpr int QCH = 4;           // chunks of a segment per lane (virtual lanes 4p .. 4p+3)
 constexpr int XW = 20;           // dwords per staged (chunk, activation row): 16 pair words, 16 sum, -1024 sum, pad
-constexpr int ROWS_BLOCK = 256;  // weight rows per block (one per thread)
+// dwords per staged chunk (its MR rows): 4 dwords of padding put the chunks that the four quarters of
+// a wave read at once (4 chunks apart) 16 banks apart
+constexpr int cstride(int MR) { return MR * XW + 4; }
+constexpr int THREADS = 256;     // 4 waves
+constexpr int ROWS_BLOCK = THREADS / 4;   // weight rows per block (16 per wave)
 constexpr size_t STAGE_BYTES = 64 * 1024;   // LDS for the staged activations
 
-// The 16 chains of one row summed in the order of group_sum<16>'s DPP butterfly (XOR 1, XOR 2,
-// half-row mirror, row mirror): pairs, then quads, eights, sixteens.
-DHP_DEV float butterfly16(const float (&a)[SEG]) {
-    const float q0 = (a[0] + a[1]) + (a[2] + a[3]);
-    const float q1 = (a[4] + a[5]) + (a[6] + a[7]);
-    const float q2 = (a[8] + a[9]) + (a[10] + a[11]);
-    const float q3 = (a[12] + a[13]) + (a[14] + a[15]);
-    return (q0 + q1) + (q2 + q3);
-}
-
 // Chunks per staging window for MR activation rows: a multiple of 16, at most STAGE_BYTES.
-constexpr int window_chunks(int MR) { return (int)(STAGE_BYTES / (MR * XW * 4)) / SEG * SEG; }
+constexpr int window_chunks(int MR) { return (int)(STAGE_BYTES / (cstride(MR) * 4)) / SEG * SEG; }
 
 // Stage chunks w0 .. w0+W-1 (those below CH) of activation rows m0 .. m0+MR-1 (rows past mr
 // repeat row mr - 1, so the compute loop needs no check per row; their results are never stored).
 template <int MR>
 DHP_DEV void stage_window(uint32_t* xs, const _Float16* __restrict__ x, int m0, int mr, int K, int CH, int w0, int W) {
     __syncthreads();                          // the previous window's reads are done
-    for (int it = threadIdx.x; it < W * MR; it += ROWS_BLOCK) {
+    for (int it = threadIdx.x; it < W * MR; it += THREADS) {
         const int j = it / MR, r = it - j * MR;
         const int c = w0 + j;
         if (c < CH) {
@@ -63,7 +62,7 @@ DHP_DEV void stage_window(uint32_t* xs, const _Float16* __restrict__ x, int m0, 
             h2 xp[16];
             float nc;
             const float s16 = x32_off_from(v, xp, nc);
-            uint32_t* dst = xs + (size_t)it * XW;
+            uint32_t* dst = xs + (size_t)j * cstride(MR) + r * XW;
 #pragma unroll
             for (int l = 0; l < 4; ++l)                 // lane l of a quad reads words l, l+4, l+8, l+12
                 *reinterpret_cast<u32x4*>(dst + 4 * l) =
@@ -75,26 +74,32 @@ DHP_DEV void stage_window(uint32_t* xs, const _Float16* __restrict__ x, int m0, 
     __syncthreads();
 }
 
-// One 128-byte line of this lane's row: 8 chunks of codes and the 4 groups' scales and biases.
-// Chunks past the row are clamped to its last chunk (loaded, never used).
-struct LineRegs {
-    u32x4 c[8];
-    uint32_t s[4], b[4];
+// One lane's quarter of a segment of its row: 4 chunks of codes and the scales and biases of
+// their 2 groups, packed as two bf16 per word. Chunks past the row are clamped to its last chunk
+// (loaded, never used). With FULL (K % 512 == 0) the row's scales start 16-byte aligned and a
+// quarter's pair of groups is one 4-byte load.
+struct QuarterRegs {
+    u32x4 c[QCH];
+    uint32_t s, b;
 };
-DHP_DEV void load_line(LineRegs& l, const u32x4* __restrict__ cr, const uint16_t* __restrict__ sr,
-                       const uint16_t* __restrict__ br, int c0, int CH) {
+template <bool FULL>
+DHP_DEV void load_quarter(QuarterRegs& l, const u32x4* __restrict__ cr, const uint16_t* __restrict__ sr,
+                          const uint16_t* __restrict__ br, int cb, int CH) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) l.c[i] = __builtin_nontemporal_load(cr + min(c0 + i, CH - 1));
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int cc = min(c0 + 2 * g, CH - 1);
-        l.s[g] = sr[cc >> 1];
-        l.b[g] = br[cc >> 1];
+    for (int i = 0; i < QCH; ++i) l.c[i] = __builtin_nontemporal_load(cr + min(cb + i, CH - 1));
+    if constexpr (FULL) {
+        const int g0 = min(cb, CH - QCH) >> 1;          // even: 4-byte aligned
+        l.s = *reinterpret_cast<const uint32_t*>(sr + g0);
+        l.b = *reinterpret_cast<const uint32_t*>(br + g0);
+    } else {
+        const int g0 = min(cb, CH - 1) >> 1, g1 = min(cb + 2, CH - 1) >> 1;
+        l.s = (uint32_t)sr[g0] | ((uint32_t)sr[g1] << 16);
+        l.b = (uint32_t)br[g0] | ((uint32_t)br[g1] << 16);
     }
 }
+// group h (0, 1) of a quarter: its scale or bias as fp32
+DHP_DEV float half_bf16(uint32_t w, int h) { return __builtin_bit_cast(float, h ? (w & 0xFFFF0000u) : (w << 16)); }
 
-// The chains of chunks c0 .. c0+7 (chunk c0 + i extends virtual lane J0 + i's chain) for every
-// activation row; xw: the staged blocks of chunk c0 (its MR rows), then the next chunk's.
 // Eight pair dots (pairs 8h .. 8h+7 of a chunk, dot32_off's order) for NC activation rows at once,
 // each row's activation word e taken from lane e & 3 of the quad by a DPP quad broadcast inside
 // v_dot2c (every lane of a quad holds 16 bytes of the chunk's 64, so LDS delivers a quarter of
@@ -143,17 +148,19 @@ DHP_DEV void dots_chunk(float (&d)[NC], const uint32_t (&t)[16], const u32x4 (&x
 // compiler hoists every LDS read of a line to the top and runs out of registers).
 DHP_DEV void mem_fence_compiler() { asm volatile("" ::: "memory"); }
 
-template <int MR, int J0, bool TAIL>
-DHP_DEV void run_line(const LineRegs& l, const uint32_t* xw, float (&acc)[MR][SEG], int c0, int CH,
-                      const NibConsts& nk, int q) {
+// The chains of chunks cb .. cb+3 (chunk cb + i extends this lane's chain i) for every activation
+// row; xw: the staged blocks of chunk cb (its MR rows), then the next chunk's.
+template <int MR, bool TAIL>
+DHP_DEV void run_quarter(const QuarterRegs& l, const uint32_t* xw, float (&acc)[MR][QCH], int cb, int CH,
+                         const NibConsts& nk, int q) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < QCH; ++i) {
         mem_fence_compiler();                 // one chunk's activations read at a time
         // in a partial segment, chunks past the row run on clamped codes and stale LDS and are
-        // discarded by a select (a branch here had the compiler hoist the whole line's reads)
-        const bool live = !TAIL || c0 + i < CH;
-        const float s = bf16_to_f32(l.s[i >> 1]);
-        const float b = bf16_to_f32(l.b[i >> 1]);
+        // discarded by a select (a branch here had the compiler hoist the whole segment's reads)
+        const bool live = !TAIL || cb + i < CH;
+        const float s = half_bf16(l.s, i >> 1);
+        const float b = half_bf16(l.b, i >> 1);
         h2 tp[16];
         unpack8_off(l.c[i].x, tp, nk);
         unpack8_off(l.c[i].y, tp + 4, nk);
@@ -170,7 +177,7 @@ DHP_DEV void run_line(const LineRegs& l, const uint32_t* xw, float (&acc)[MR][SE
             float d[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const uint32_t* blk = xw + (size_t)(i * MR + r0 + c) * XW;
+                const uint32_t* blk = xw + (size_t)i * cstride(MR) + (r0 + c) * XW;
                 xq[c] = *reinterpret_cast<const u32x4*>(blk + 4 * q);
                 sn[c] = *reinterpret_cast<const float2*>(blk + 16);
                 d[c] = sn[c].y;
@@ -178,9 +185,9 @@ DHP_DEV void run_line(const LineRegs& l, const uint32_t* xw, float (&acc)[MR][SE
             dots_chunk<NC>(d, t, xq);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const float a0 = acc[r0 + c][J0 + i];
+                const float a0 = acc[r0 + c][i];
                 const float a1 = __builtin_fmaf(b, sn[c].x, __builtin_fmaf(s, d[c], a0));
-                acc[r0 + c][J0 + i] = live ? a1 : a0;
+                acc[r0 + c][i] = live ? a1 : a0;
             }
             mem_fence_compiler();                 // one block of rows' activations in registers at a time
         }
@@ -188,56 +195,66 @@ DHP_DEV void run_line(const LineRegs& l, const uint32_t* xw, float (&acc)[MR][SE
 }
 
 template <int MR, bool F32OUT, bool ARGMAX, bool FULL>
-__global__ __launch_bounds__(ROWS_BLOCK, 2) void k_gemv_rows(
+__global__ __launch_bounds__(THREADS, 3) void k_gemv_rows(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const _Float16* __restrict__ x, int m0, int mr, int N, int K, void* __restrict__ y,
     float* __restrict__ part_v, int* __restrict__ part_i) {
-    extern __shared__ __align__(16) uint32_t xs[];     // [window chunks][MR][XW]
+    extern __shared__ __align__(16) uint32_t xs[];     // [window chunks][cstride(MR)]: [MR][XW], pad
     constexpr int WMAX = window_chunks(MR);
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int q = lane & 3;                  // quad lane: which 16 bytes of a staged chunk it reads
-    const int row = blockIdx.x * ROWS_BLOCK + t;
+    const int p = lane >> 4;                 // quarter: virtual lanes 4p .. 4p+3
+    const int row = blockIdx.x * ROWS_BLOCK + wave * 16 + (lane & 15);
     const int rr = min(row, N - 1);          // rows past N compute the last row again, unstored
     const int CH = K >> 5, G = K >> 6;
     const u32x4* cr = codes + (size_t)rr * CH;
     const uint16_t* sr = scales + (size_t)rr * G;
     const uint16_t* br = biases + (size_t)rr * G;
     const int W = min(WMAX, (CH + SEG - 1) / SEG * SEG);
+    const int pc = QCH * p;                  // this lane's first chunk in a segment
 
-    float acc[MR][SEG];
+    float acc[MR][QCH];
 #pragma unroll
     for (int r = 0; r < MR; ++r)
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) acc[r][j] = 0.0f;
+        for (int j = 0; j < QCH; ++j) acc[r][j] = 0.0f;
     const NibConsts nk = nib_consts();
 
-    // segments of two lines (16 chunks: virtual lanes 0..7, then 8..15); one line in flight ahead
-    LineRegs la, lb;
-    load_line(la, cr, sr, br, 0, CH);
+    // one segment computes while the next is in flight; segments alternate between two register sets
+    QuarterRegs la, lb;
+    load_quarter<FULL>(la, cr, sr, br, pc, CH);
     int w0 = -WMAX;
 #pragma unroll 1
-    for (int c0 = 0; c0 < CH; c0 += SEG) {
-        if (c0 >= w0 + WMAX) {               // the next staging window (once, at K <= 3264 for 8 rows)
+    for (int c0 = 0; c0 < CH; c0 += 2 * SEG) {
+        if (c0 >= w0 + WMAX) {               // the next staging window (once, at K <= 3072 for 8 rows)
             w0 = c0;
             stage_window<MR>(xs, x, m0, mr, K, CH, w0, W);
         }
-        const uint32_t* xw = xs + (size_t)(c0 - w0) * MR * XW;
-        load_line(lb, cr, sr, br, c0 + 8, CH);
-        // every segment whole when FULL; otherwise each chunk's update goes through a select
-        run_line<MR, 0, !FULL>(la, xw, acc, c0, CH, nk, q);
-        load_line(la, cr, sr, br, c0 + SEG, CH);
-        run_line<MR, 8, !FULL>(lb, xw + (size_t)8 * MR * XW, acc, c0 + 8, CH, nk, q);
+        load_quarter<FULL>(lb, cr, sr, br, c0 + SEG + pc, CH);
+        run_quarter<MR, !FULL>(la, xs + (size_t)(c0 - w0 + pc) * cstride(MR), acc, c0 + pc, CH, nk, q);
+        const int c1 = c0 + SEG;
+        if (c1 < CH) {                       // uniform over the block
+            if (c1 >= w0 + WMAX) {
+                w0 = c1;
+                stage_window<MR>(xs, x, m0, mr, K, CH, w0, W);
+            }
+            load_quarter<FULL>(la, cr, sr, br, c1 + SEG + pc, CH);
+            run_quarter<MR, !FULL>(lb, xs + (size_t)(c1 - w0 + pc) * cstride(MR), acc, c1 + pc, CH, nk, q);
+        }
     }
 
-    __shared__ float bv_s[MR][ROWS_BLOCK / 64];
-    __shared__ int bi_s[MR][ROWS_BLOCK / 64];
+    __shared__ float bv_s[MR][THREADS / 64];
+    __shared__ int bi_s[MR][THREADS / 64];
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
         if (r < mr) {
-            const float v = butterfly16(acc[r]) * 0.0625f;
+            // this lane's quad of virtual lanes, then the quads in the butterfly's order
+            const float qv = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
+            const float h = qv + __shfl_xor(qv, 16);
+            const float v = (h + __shfl_xor(h, 32)) * 0.0625f;
             const size_t o = (size_t)(m0 + r) * N + row;
-            if (row < N) {
+            if (row < N && (r & 3) == p) {   // the quarters hold the same bits; one stores each row
                 if constexpr (F32OUT) reinterpret_cast<float*>(y)[o] = v;
                 else reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
             }
@@ -254,7 +271,7 @@ __global__ __launch_bounds__(ROWS_BLOCK, 2) void k_gemv_rows(
         if (t < mr) {
             float bv = bv_s[t][0];
             int bi = bi_s[t][0];
-            for (int w = 1; w < ROWS_BLOCK / 64; ++w)
+            for (int w = 1; w < THREADS / 64; ++w)
                 if (better(bv_s[t][w], bi_s[t][w], bv, bi)) { bv = bv_s[t][w]; bi = bi_s[t][w]; }
             part_v[(size_t)(m0 + t) * gridDim.x + blockIdx.x] = bv;     // [act row][block], as the
             part_i[(size_t)(m0 + t) * gridDim.x + blockIdx.x] = bi;     // final reduction reads them
@@ -266,7 +283,7 @@ template <int MR, bool FULL>
 hipError_t launch_rows_full(bool f32, bool am, dim3 g, size_t lds, hipStream_t s, const u32x4* c, const uint16_t* sc,
                             const uint16_t* bi, const _Float16* x, int m0, int mr, int N, int K, void* y, float* pv,
                             int* pi) {
-    const dim3 b(ROWS_BLOCK);
+    const dim3 b(THREADS);
     if (f32 && am) hipLaunchKernelGGL((k_gemv_rows<MR, true, true, FULL>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
     else if (f32) hipLaunchKernelGGL((k_gemv_rows<MR, true, false, FULL>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
     else if (am) hipLaunchKernelGGL((k_gemv_rows<MR, false, true, FULL>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
@@ -280,7 +297,7 @@ hipError_t launch_rows_mr(bool f32, bool am, dim3 g, hipStream_t s, const u32x4*
                           int* pi) {
     const int CH = K >> 5;
     const int W = min(window_chunks(MR), (CH + SEG - 1) / SEG * SEG);
-    const size_t lds = (size_t)W * MR * XW * 4;
+    const size_t lds = (size_t)W * cstride(MR) * 4;
     if (CH % SEG == 0) return launch_rows_full<MR, true>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
     return launch_rows_full<MR, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
 }
