@@ -30,7 +30,9 @@ Also printed in the same JSON line:
   calls         per-call microseconds and GB/s from a separate pass: batches of back-to-back
                 launches between fence-free HIP events (median over batches);
   diagnostics   each call with a cold last-level cache (a 1 GiB read before every timed call;
-                median, p10, p90 of 50), the empty-kernel launch floor, the HBM read ceiling of
+                median, p10, p90 of 50), the empty-kernel launch floor, the cost of one grid-wide
+                barrier inside a launch (what fusing dependent kernels would pay instead of a
+                launch), the HBM read ceiling of
                 a plain streaming-read kernel, and the M=1 GEMV's GB/s against its row count.
 
 `--oracle-timing` instead times the fp64 oracle per workload on all cores and on one core.
@@ -502,6 +504,34 @@ def launch_floor(torch, hca, n: int = 200, reps: int = 30):
             "single_idle_us": round(float(np.median(single)), 2)}
 
 
+def grid_barrier_cost(torch, hca, reps: int = 10):
+    """Microseconds per grid-wide barrier inside one launch (the slope between launches with 1 and
+    21 barriers), for 64 and 256 blocks, ordered (release/acquire, as data hand-over between blocks
+    needs) and relaxed, next to the kernel boundary it would replace (launch_floor)."""
+    state = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    out = {}
+    for blocks in (64, cus):
+        for ordered in (True, False):
+            t = {}
+            for n in (1, 21):
+                hca.probe_grid_barrier(blocks, n, ordered, state, sink)
+                torch.cuda.synchronize()
+                a, b = HipEvent(), HipEvent()
+                a.record(stream)
+                for _ in range(reps):
+                    hca.probe_grid_barrier(blocks, n, ordered, state, sink)
+                b.record(stream)
+                t[n] = a.us_until(b) / reps
+            out[f"{'ordered' if ordered else 'relaxed'}_{blocks}_blocks_us"] = round((t[21] - t[1]) / 20, 2)
+    torch.cuda.synchronize()
+    st = state.cpu().tolist()
+    out["all_waits_ended"] = bool(st[0] == 0 and st[2] == 0)
+    return out
+
+
 def read_ceiling(torch, hca, flush, sink, target_bytes: int = 219400704, reps: int = 5):
     """The read probe over a 1 GiB buffer (larger than the last-level cache, so every pass reads
     HBM) for a grid of (blocks per CU, loads in flight per lane), and the best arrangement over a
@@ -840,6 +870,7 @@ def main():
         sink = torch.empty(16 * 1024, dtype=torch.int32, device="cuda")
         diag = {"calls_cold": cold_call_pass(torch, hca, calls, nbytes, flush, sink),
                 "launch_floor": launch_floor(torch, hca),
+                "grid_barrier": grid_barrier_cost(torch, hca),
                 "read_ceiling": read_ceiling(torch, hca, flush, sink),
                 "gemv_rows_sweep_cold": rows_sweep(torch, hca, W, flush, sink)}
         del flush

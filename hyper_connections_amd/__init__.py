@@ -110,6 +110,7 @@ def lib() -> ctypes.CDLL:
                                               sz, vp]
         L.decodehp_probe_empty.argtypes = [i32, vp]
         L.decodehp_probe_read.argtypes = [vp, sz, i32, i32, vp, i32, vp]
+        L.decodehp_probe_grid_barrier.argtypes = [i32, i32, i32, vp, vp, vp]
         L.decodehp_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.decodehp_workspace_bytes.restype = sz
         L.decodehp_last_error.restype = ctypes.c_char_p
@@ -478,6 +479,14 @@ def hc_inject_read(prev, out, inject_w, hc_norm, C: int, H: int, down: Int4Weigh
 def probe_empty(count: int = 1, stream=None):
     """Launch `count` kernels that do nothing, back to back (the per-launch floor)."""
     _check(lib().decodehp_probe_empty(count, _stream(stream)))
+
+
+def probe_grid_barrier(blocks: int, n: int, ordered: bool, state, sink, stream=None):
+    """One launch of `blocks` blocks passing n grid-wide barriers. state: int32 [4] zeroed device
+    tensor (kept between calls); sink: int32 [>= blocks] device tensor (1 per block that never ran
+    out of polls)."""
+    _check(lib().decodehp_probe_grid_barrier(blocks, n, int(bool(ordered)), state.data_ptr(), sink.data_ptr(),
+                                             _stream(stream)))
 
 
 def probe_read(buf, blocks_per_cu: int = 2, loads_in_flight: int = 4, sink=None, stream=None):

@@ -6,6 +6,15 @@
 //  k_probe_read  : streams a buffer once with 16-byte nontemporal loads, U loads in flight per
 //                  lane and a grid stride over the buffer; every block writes one word (the XOR
 //                  of what its lanes read) so that no load can be dropped.
+//  k_probe_barrier: n grid-wide barriers in a grid small enough to be resident at once: the cost
+//                  of joining all blocks inside one launch, against the cost of a kernel boundary
+//                  (k_probe_empty). Thread 0 of each block adds one to a device-scope arrival
+//                  counter; the last arrival resets it and advances a generation word that the
+//                  others poll (sleeping between polls). ORDERED: the arrival is a release and the
+//                  wait ends with an acquire (what a barrier that hands data between blocks needs:
+//                  the caches are written back and invalidated), else both are relaxed (the
+//                  atomics alone). Every wait is bounded; a wait that runs out sets the third
+//                  state word and ends the kernel.
 #include "dhp_internal.hpp"
 
 namespace {
@@ -32,6 +41,41 @@ __global__ __launch_bounds__(256) void k_probe_read(const u32x4* __restrict__ bu
     if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) sink[blockIdx.x] = (w[0] ^ w[1]) ^ (w[2] ^ w[3]);
+}
+
+template <bool ORDERED>
+__global__ __launch_bounds__(256) void k_probe_barrier(uint32_t* __restrict__ state, int n, uint32_t* __restrict__ sink) {
+    __shared__ uint32_t ok_s;
+    for (int i = 0; i < n; ++i) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t ok = 1;
+            const uint32_t gen = __hip_atomic_load(state + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t a = ORDERED
+                ? __hip_atomic_fetch_add(state, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT)
+                : __hip_atomic_fetch_add(state, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (a == gridDim.x - 1) {
+                __hip_atomic_store(state, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (ORDERED) __hip_atomic_fetch_add(state + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                else __hip_atomic_fetch_add(state + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                uint32_t polls = 0;
+                while (__hip_atomic_load(state + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+                    if (++polls > (1u << 18)) {
+                        ok = 0;
+                        __hip_atomic_store(state + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                if (ORDERED) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            ok_s = ok;
+        }
+        __syncthreads();
+        if (!ok_s) break;
+    }
+    if (threadIdx.x == 0) sink[blockIdx.x] = ok_s;
 }
 
 int launch_status(const char* what) {
@@ -75,6 +119,22 @@ int decodehp_probe_read(const void* buf, size_t bytes, int32_t blocks_per_cu, in
         default: hipLaunchKernelGGL(k_probe_read<8>, dim3(blocks), dim3(256), 0, s, p, n16, sink); break;
     }
     return launch_status("read probe");
+}
+
+// n barriers in one launch of `blocks` blocks of 256 threads (at most one per CU, so all are
+// resident). state: 4 zeroed 32-bit words of device memory, left with a zero count (word 2 is
+// set if a wait ran out); sink: `blocks` words.
+int decodehp_probe_grid_barrier(int32_t blocks, int32_t n, int32_t ordered, uint32_t* state, uint32_t* sink,
+                                void* stream) {
+    if (!state || !sink) return dhp_fail(DHP_ERR_INVALID, "null state or sink");
+    if (n < 0 || n > 10000) return dhp_fail(DHP_ERR_UNSUPPORTED, "n=%d (0..10000)", n);
+    DeviceFacts dev;
+    if (!dhp_current_device(&dev)) return DHP_ERR_NO_DEVICE;
+    if (blocks < 1 || blocks > dev.cus) return dhp_fail(DHP_ERR_UNSUPPORTED, "blocks=%d (1..%d)", blocks, dev.cus);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (ordered) hipLaunchKernelGGL(k_probe_barrier<true>, dim3(blocks), dim3(256), 0, s, state, n, sink);
+    else hipLaunchKernelGGL(k_probe_barrier<false>, dim3(blocks), dim3(256), 0, s, state, n, sink);
+    return launch_status("grid barrier probe");
 }
 
 }  // extern "C"

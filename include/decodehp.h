@@ -408,8 +408,8 @@ int decodehp_graph_launch(const dhp_graph* graph, void* stream);
 void decodehp_graph_destroy(dhp_graph* graph);
 
 /*
- * Measurement probes (not steps of the decode path): the launch floor and the HBM read
- * ceiling the decode kernels are measured against.
+ * Measurement probes (not steps of the decode path): the launch floor, the cost of a grid-wide
+ * barrier and the HBM read ceiling the decode kernels are measured against.
  *
  * decodehp_probe_empty -- launches `count` (1..100000) kernels that do nothing, back to back
  * on the stream. Errors: -2 count, -5, -6.
@@ -422,8 +422,20 @@ void decodehp_graph_destroy(dhp_graph* graph);
  *   at least blocks_per_cu * compute units words.
  * Errors: -1 null buf/sink or zero bytes, -2 blocks_per_cu outside 1..16 or loads_in_flight,
  *         -3 alignment, -4 sink too small, -5, -6.
+ *
+ * decodehp_probe_grid_barrier -- one launch of `blocks` (1..compute units) blocks of 256 threads
+ * that pass n (0..10000) grid-wide barriers: the cost of joining all blocks inside a launch, to
+ * set against a kernel boundary. ordered != 0: each arrival is a device-scope release and each
+ * wait ends with an acquire (the caches are written back and invalidated, as a barrier that
+ * hands data between blocks needs); 0: relaxed atomics only. Every wait is bounded (2^18 polls);
+ * one that runs out sets state[2] and ends the launch.
+ *   state : uint32 [4] device memory, zero before the first call (left with state[0] = 0).
+ *   sink  : uint32 [blocks]; block b writes 1 if all its waits ended normally.
+ * Errors: -1 null state/sink, -2 blocks or n out of range, -5, -6.
  */
 int decodehp_probe_empty(int32_t count, void* stream);
+int decodehp_probe_grid_barrier(int32_t blocks, int32_t n, int32_t ordered, uint32_t* state, uint32_t* sink,
+                                void* stream);
 int decodehp_probe_read(const void* buf, size_t bytes, int32_t blocks_per_cu, int32_t loads_in_flight,
                         uint32_t* sink, int32_t sink_words, void* stream);
 

@@ -284,6 +284,14 @@ def test_hc_batched_rejects_bad_calls():
     assert g(m=0) == -2 and g(wide=None) == -1 and g(wide=FAKE + 8) == -3
 
 
+def test_probe_grid_barrier_rejects_bad_calls():
+    L = hca.lib()
+    assert L.decodehp_probe_grid_barrier(64, 1, 1, None, FAKE, None) == -1
+    assert L.decodehp_probe_grid_barrier(64, 1, 1, FAKE, None, None) == -1
+    assert L.decodehp_probe_grid_barrier(64, -1, 1, FAKE, FAKE, None) == -2
+    assert L.decodehp_probe_grid_barrier(64, 10001, 0, FAKE, FAKE, None) == -2
+
+
 def test_probe_read_rejects_bad_calls():
     L = hca.lib()
     assert L.decodehp_probe_read(0, 1 << 20, 2, 4, FAKE, 4096, None) == -1
