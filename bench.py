@@ -60,12 +60,38 @@ DOMINANT_SRCS = ("hyper_connections_amd/csrc/gemv.hip", "hyper_connections_amd/c
                  "include/decodehp.h", "hyper_connections_amd/build.py")
 
 
-def dominant_sources_sha256() -> str:
+# the same for the other calls whose HBM traffic the counters measured (profiles/traffic_counters.json)
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+CALL_SRCS = {
+    "lmhead8": ("hyper_connections_amd/csrc/gemv_rows.hip", "hyper_connections_amd/csrc/gemv.hip",
+                "hyper_connections_amd/csrc/dhp_internal.hpp", "include/decodehp.h", "hyper_connections_amd/build.py"),
+    "moe": ("hyper_connections_amd/csrc/moe.hip", "hyper_connections_amd/csrc/dhp_internal.hpp", "include/decodehp.h",
+            "hyper_connections_amd/build.py"),
+}
+
+
+def sources_sha256(paths) -> str:
     h = hashlib.sha256()
-    for rel in DOMINANT_SRCS:
+    for rel in paths:
         h.update(rel.encode() + b"\0")
         h.update(open(os.path.join(ROOT, rel), "rb").read())
     return h.hexdigest()
+
+
+def dominant_sources_sha256() -> str:
+    return sources_sha256(DOMINANT_SRCS)
+
+
+def call_traffic(call: str):
+    """HBM bytes per call from the committed counter runs, if taken on the current sources of
+    every kernel of the call; else None."""
+    try:
+        d = json.load(open(TRAFFIC_PROFILE))["calls"][call]
+        if d.get("sources_sha256") != sources_sha256(CALL_SRCS[call]):
+            return None
+        return d.get("hbm_bytes_per_call")
+    except Exception:
+        return None
 
 
 def int4_bytes(rows, cols):
@@ -850,13 +876,13 @@ def main():
     dot2_ops = 8 * 151936 * 2560 // 2
     m8_ach = dot2_ops / m8_us / 1e6                     # T lane-ops/s
     roofline_m8 = {"bound": "alu", "achieved": round(m8_ach, 2), "peak": ALU_PEAK_TOPS, "unit": "T v_dot2 lane-op/s",
-                   "frac": round(m8_ach / ALU_PEAK_TOPS, 4), "traffic": None,
+                   "frac": round(m8_ach / ALU_PEAK_TOPS, 4), "traffic": call_traffic("lmhead8"),
                    "kernel": "k_gemv_rows<8,f32,argmax,full> + k_argmax_final (LM head 151936 x 2560, M=8)",
                    "algorithmic_ops_per_launch": dot2_ops, "avg_launch_us": round(m8_us, 2),
                    "hbm_GBps": round(nbytes["lmhead8"] / m8_us / 1e3, 1)}
     moe_ach = nbytes["moe"] / moe_us / 1e3
     roofline_moe = {"bound": "hbm", "achieved": round(moe_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(moe_ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(moe_ach / HBM_PEAK_GBS, 4), "traffic": call_traffic("moe"),
                     "kernel": "MoE decode (router + top-8, phase 1, phase 2: three launches), E=256, top-8",
                     "algorithmic_bytes_per_launch": nbytes["moe"], "avg_call_us": round(moe_us, 2)}
 

@@ -160,7 +160,12 @@ __global__ __launch_bounds__(UP_THREADS) void k_hc_up(
     const int lane16 = threadIdx.x & 15;
     const int c = lane16 / LPRU;
     const int sub = lane16 % LPRU;
-    const int h = blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4);
+    // Blocks go to the 8 XCDs round-robin by index. Neighbouring blocks share the cache lines of
+    // their rows' scales and biases (a row's are 2 R / 64 bytes), so consecutive runs of
+    // positions are given to the blocks of one XCD, whose L2 then fetches each line once.
+    const int nb = gridDim.x, x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    const int lb = x * (nb >> 3) + min(x, nb & 7) + i;
+    const int h = lb * (blockDim.x >> 4) + (threadIdx.x >> 4);
     const bool live = h < H;              // whole 16-lane groups share h; no early exit before the DPP sums
     const size_t urow = (size_t)c * H + (live ? h : 0);
     const u32x4* cr = ucodes + urow * CHR;
