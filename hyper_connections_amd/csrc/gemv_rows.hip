@@ -22,7 +22,7 @@
 //    quad run the same chunk for four rows; each reads a quarter of the chunk's activations
 //    and the dots take the rest from the quad by DPP.
 //  * At the end each lane sums its four chains (the butterfly's quad of virtual lanes), and two
-//    exchanges across the quarters (lane XOR 16, then XOR 32) add the quads in the butterfly's
+//    exchanges across the quarters (the 16- and 32-lane swaps) add the quads in the butterfly's
 //    order; floating-point addition is commutative, so every quarter ends with the same bits.
 // The arithmetic is the M=1 kernels' for every K they take, so the two agree bit for bit
 // wherever both run. The matrix-core kernels (gemv_mfma.hip, gemm.hip) round each dequantized
@@ -246,24 +246,45 @@ __global__ __launch_bounds__(THREADS, 3) void k_gemv_rows(
 
     __shared__ float bv_s[MR][THREADS / 64];
     __shared__ int bi_s[MR][THREADS / 64];
+    float vals[MR];
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
-        if (r < mr) {
-            // this lane's quad of virtual lanes, then the quads in the butterfly's order
-            const float qv = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
-            const float h = qv + __shfl_xor(qv, 16);
-            const float v = (h + __shfl_xor(h, 32)) * 0.0625f;
-            const size_t o = (size_t)(m0 + r) * N + row;
-            if (row < N && (r & 3) == p) {   // the quarters hold the same bits; one stores each row
-                if constexpr (F32OUT) reinterpret_cast<float*>(y)[o] = v;
-                else reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
-            }
-            if constexpr (ARGMAX) {
-                float bv = (row < N) ? v : -INFINITY;
-                int bi = (row < N) ? row : INT_MAX;
-                wave_best(bv, bi);
-                if (lane == 0) { bv_s[r][wave] = bv; bi_s[r][wave] = bi; }
-            }
+        // this lane's quad of virtual lanes, then the quads in the butterfly's order: the
+        // 16-lane row swap adds quarters 0+1 and 2+3, the 32-lane swap the two halves (each
+        // swap hands both operands to every lane; addition is commutative, so all quarters end
+        // with the same bits)
+        const float qv = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
+        const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, qv), __builtin_bit_cast(uint32_t, qv),
+                                                        false, false);
+        const float h = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+        const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, h),
+                                                        false, false);
+        const float v = (__builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1])) * 0.0625f;
+        vals[r] = v;
+        const size_t o = (size_t)(m0 + r) * N + row;
+        if (r < mr && row < N && (r & 3) == p) {   // one quarter stores each row
+            if constexpr (F32OUT) reinterpret_cast<float*>(y)[o] = v;
+            else reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
+        }
+    }
+    if constexpr (ARGMAX) {
+        // the wave's best weight row for activation rows r0 .. r0+3 at once: quarter p ranks
+        // row r0 + p over its 16 lanes (the wave's 16 weight rows)
+#pragma unroll
+        for (int r0 = 0; r0 < MR; r0 += 4) {
+            float mine = vals[r0];
+#pragma unroll
+            for (int q = 1; q < 4; ++q)
+                if (r0 + q < MR && p == q) mine = vals[r0 + q];
+            const int ar = r0 + p;
+            const bool ok = row < N && ar < mr;
+            float bv = ok ? mine : -INFINITY;
+            int bi = ok ? row : INT_MAX;
+            best_step<DPP_XOR1>(bv, bi);
+            best_step<DPP_XOR2>(bv, bi);
+            best_step<DPP_HALF_MIRROR>(bv, bi);
+            best_step<DPP_MIRROR>(bv, bi);
+            if ((lane & 15) == 0 && ar < mr) { bv_s[ar][wave] = bv; bi_s[ar][wave] = bi; }
         }
     }
     if constexpr (ARGMAX) {
