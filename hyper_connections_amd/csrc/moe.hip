@@ -63,9 +63,9 @@ struct MoeArgs {
     int32_t* route;    // ws [M][top_k + 1] (batched only): (token << 4 | slot), grouped by expert
     int32_t* items;    // ws [max items][4] (batched only): (expert, first route entry, count, 0)
     int32_t* nitems;   // ws [1] (batched only): work items in use
-    u32x4* xraw;       // ws [M][4][hidden / 32] (batched only): each token's activations in the form of
+    u32x4* xraw;       // ws [M][4][hidden / 32] (decode: M = 1): each token's activations in the form of
                        // x32_off_from (16 permuted pairs per 32-value chunk, as 4 u32x4 planes)
-    float2* xrsum;     // ws [M][hidden / 32] (batched only): per chunk, (16 * sum, -1024 * sum)
+    float2* xrsum;     // ws [M][hidden / 32] (decode: M = 1): per chunk, (16 * sum, -1024 * sum)
     _Float16* out;     // [M][hidden]
     int32_t* ids;      // [M][top_k]
     float* weights;    // [M][top_k]
@@ -261,11 +261,32 @@ DHP_DEV void load_x_regs(const _Float16* x, int j, h2 (*xp)[16], float* xs, floa
     for (int i = 0; i < CPL; ++i) xs[i] = load_x32_off(x + (size_t)(j + LPR * i) * 32, xp[i], nc[i]);
 }
 
-// Blocks [0, E): router rows. Block E: shared gate logit. Blocks after: 4 shared pairs each.
+// Blocks [0, E): router rows. Block E: shared gate logit. Then 4 shared pairs per block; the last
+// ceil(hidden / 2048) blocks write the token's activations in the offset form pair_act multiplies
+// (x32_off_from: the permuted pairs, 16 * sum and -1024 * sum per 32-value chunk) to the workspace,
+// once per token, for phase 1 to load instead of converting them again in every wave.
 template <int CPL>
 __global__ __launch_bounds__(64) void k_moe_router(MoeArgs a) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
+    const int xb0 = a.E + 1 + (a.inter + 3) / 4;
+    if (b >= xb0) {
+        const int CH32 = a.hidden >> 5;
+        const int c = (b - xb0) * 64 + lane;
+        if (c < CH32) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(a.x + 32 * c);
+            const u32x4 v[4] = {src[0], src[1], src[2], src[3]};
+            h2 xp[16];
+            float nc;
+            const float xs = x32_off_from(v, xp, nc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                a.xraw[(size_t)q * CH32 + c] = u32x4{h2_bits(xp[4 * q]), h2_bits(xp[4 * q + 1]),
+                                                     h2_bits(xp[4 * q + 2]), h2_bits(xp[4 * q + 3])};
+            a.xrsum[c] = float2{xs, nc};
+        }
+        return;
+    }
     if (b < a.E) {
         const size_t rb = router_row_bytes(a.router_kind, a.hidden);
         const float v = wave_row_dot<CPL>(static_cast<const uint8_t*>(a.router) + rb * b, a.router_kind, a.x,
@@ -436,7 +457,24 @@ __global__ __launch_bounds__(64) void k_moe_phase1(MoeArgs a) {
     topk_load<PER>(tin, a.logits, a.E);    // the routing decision waits on these: issue first
     h2 xp[CPL][16];
     float xs[CPL], nc[CPL];
-    load_x_regs<CPL>(a.x, j, xp, xs, nc);  // independent of routing
+    {   // the activations in offset form, written by the router kernel; independent of routing
+        const int CH32 = a.hidden >> 5;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = j + LPR * i;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 u = a.xraw[(size_t)q * CH32 + c];
+                xp[i][4 * q] = as_h2(u.x);
+                xp[i][4 * q + 1] = as_h2(u.y);
+                xp[i][4 * q + 2] = as_h2(u.z);
+                xp[i][4 * q + 3] = as_h2(u.w);
+            }
+            const float2 sn = a.xrsum[c];
+            xs[i] = sn.x;
+            nc[i] = sn.y;
+        }
+    }
 
     // a block only needs the ranks up to its last (slot, row) pair; block 0 also needs all
     // top_k of them for the softmax weights
@@ -1024,7 +1062,8 @@ hipError_t launch_prefill_all(const MoeArgs& a, hipStream_t s) {
 template <int CPL>
 hipError_t launch_all(const MoeArgs& a, hipStream_t s) {
     const int shared_blocks = (a.inter + 3) / 4;
-    hipLaunchKernelGGL(k_moe_router<CPL>, dim3(a.E + 1 + shared_blocks), dim3(64), 0, s, a);
+    const int x_blocks = (a.hidden / 32 + 63) / 64;
+    hipLaunchKernelGGL(k_moe_router<CPL>, dim3(a.E + 1 + shared_blocks + x_blocks), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int pairs = a.top_k * a.inter;
@@ -1041,9 +1080,17 @@ hipError_t launch_all(const MoeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t dhp_moe_ws(int32_t n_experts, int32_t top_k, int32_t inter) {
+// Decode workspace: logits fp32 [E], the gate logit, pad to 16 bytes, act fp32 [top_k + 1][inter];
+// at the next 256-byte boundary the token's offset-form activations, sized for the largest hidden
+// (4096: 128 chunks): 4 planes of u32x4 [128], then (16 sum, -1024 sum) float2 [128].
+constexpr size_t MOE_XRAW_BYTES = 4 * 128 * sizeof(u32x4);
+constexpr size_t MOE_XRSUM_BYTES = 128 * sizeof(float2);
+static size_t moe_x_offset(int32_t n_experts, int32_t top_k, int32_t inter) {
     const size_t floats = (size_t)((n_experts + 4) & ~3) + (size_t)(top_k + 1) * inter;
     return (floats * sizeof(float) + 255) & ~(size_t)255;
+}
+size_t dhp_moe_ws(int32_t n_experts, int32_t top_k, int32_t inter) {
+    return moe_x_offset(n_experts, top_k, inter) + MOE_XRAW_BYTES + MOE_XRSUM_BYTES;
 }
 
 namespace {
@@ -1132,8 +1179,9 @@ int launch_moe(const void* x, const dhp_router* router, const void* sgate_row,
     a.act = w + ((a.E + 4) & ~3);        // 16-byte aligned
     a.dsum = nullptr;
     a.route = a.items = a.nitems = nullptr;
-    a.xraw = nullptr;
-    a.xrsum = nullptr;
+    char* xbase = static_cast<char*>(ws) + moe_x_offset(a.E, top_k, a.inter);
+    a.xraw = reinterpret_cast<u32x4*>(xbase);
+    a.xrsum = reinterpret_cast<float2*>(xbase + MOE_XRAW_BYTES);
 
     hipError_t e;
     switch (a.hidden / 512) {

@@ -179,19 +179,19 @@ int decodehp_moe_decode(const void* x, const void* router, int32_t router_dtype,
  * that cannot allocate device memory (code recorded under graph capture, tight serving loops,
  * harnesses that forbid allocation). The call allocates nothing: its scratch (router logits,
  * gate logit, fp32 activations) lives in a fixed array inside the library, one per GPU,
- * DHP_NOALLOC_SCRATCH_BYTES (32 KiB) long and held until the process ends.
+ * DHP_NOALLOC_SCRATCH_BYTES (48 KiB) long and held until the process ends.
  *   Arguments, results and the kernels run: as decodehp_moe_decode, minus ws and ws_bytes.
  *   Limit: decodehp_workspace_bytes(DHP_OP_MOE_DECODE, n_experts, top_k, inter), about
- *   4 * (n_experts + (top_k + 1) * inter) bytes, must not exceed DHP_NOALLOC_SCRATCH_BYTES: every
+ *   4 * (n_experts + (top_k + 1) * inter) + 9216 bytes, must not exceed DHP_NOALLOC_SCRATCH_BYTES: every
  *   top_k <= 10 fits up to n_experts 1024 with inter 640 (the 256-expert top-8 layer with inter
- *   512 takes 19,712 bytes); larger layers get -4 and must use decodehp_moe_decode.
+ *   512 takes 28,928 bytes); larger layers get -4 and must use decodehp_moe_decode.
  *   Concurrency: every call on one GPU uses the same array, so calls that overlap in time on
  *   one GPU (different streams, or different threads' streams) race; calls on one stream are
  *   ordered and safe. Nothing in the array has to start at zero: each call writes what it reads.
  * Errors: as decodehp_moe_decode (-4: the layer needs more than the fixed scratch; -6 also when
  *         the scratch's device address cannot be obtained).
  */
-#define DHP_NOALLOC_SCRATCH_BYTES 32768
+#define DHP_NOALLOC_SCRATCH_BYTES 49152
 int decodehp_moe_decode_noalloc(const void* x, const void* router, int32_t router_dtype,
                                 const void* shared_gate_row, const dhp_int4_experts* gate,
                                 const dhp_int4_experts* up, const dhp_int4_experts* down,

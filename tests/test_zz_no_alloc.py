@@ -90,7 +90,7 @@ def test_noalloc_rejects_a_layer_beyond_its_scratch():
     out = torch.empty(512, dtype=torch.float16, device="cuda")
     ids = torch.empty(10, dtype=torch.int32, device="cuda")
     w = torch.empty(10, dtype=torch.float32, device="cuda")
-    # (16 + 11 * 1024) * 4 bytes > 32 KiB
+    # (20 + 11 * 1024) * 4 bytes, rounded up to 256, + 9216 > 48 KiB
     with pytest.raises(hca.DecodeHPError) as e:
         hca.moe_decode_noalloc(xd, *layer.args(), out, ids, w)
     assert e.value.code == -4
