@@ -40,7 +40,7 @@ constexpr int XW = 20;           // dwords per staged (chunk, activation row): 1
 // dwords per staged chunk (its MR rows): 4 dwords of padding put the chunks that the four quarters of
 // a wave read at once (4 chunks apart) 16 banks apart
 constexpr int cstride(int MR) { return MR * XW + 4; }
-constexpr int THREADS = 256;     // 4 waves
+constexpr int THREADS = 512;     // 8 waves
 constexpr int ROWS_BLOCK = THREADS / 4;   // weight rows per block (16 per wave)
 constexpr size_t STAGE_BYTES = 64 * 1024;   // LDS for the staged activations
 
@@ -195,7 +195,9 @@ DHP_DEV void run_quarter(const QuarterRegs& l, const uint32_t* xw, float (&acc)[
 }
 
 template <int MR, bool F32OUT, bool ARGMAX, bool FULL>
-__global__ __launch_bounds__(THREADS, 3) void k_gemv_rows(
+// 128 VGPRs, four waves per SIMD: two blocks of eight waves per CU (their staged activations
+// fit the LDS twice)
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gemv_rows(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const _Float16* __restrict__ x, int m0, int mr, int N, int K, void* __restrict__ y,
     float* __restrict__ part_v, int* __restrict__ part_i) {
