@@ -195,9 +195,10 @@ DHP_DEV void run_quarter(const QuarterRegs& l, const uint32_t* xw, float (&acc)[
 }
 
 template <int MR, bool F32OUT, bool ARGMAX, bool FULL>
-// 128 VGPRs, four waves per SIMD: two blocks of eight waves per CU (their staged activations
-// fit the LDS twice)
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_gemv_rows(
+// Whole segments (K % 512 == 0): 128 VGPRs, four waves per SIMD, two blocks of eight waves per CU
+// (their staged activations fit the LDS twice). With a partial last segment the selects need more
+// registers: one block per CU, no spills.
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? 4 : 2, FULL ? 4 : 2))) void k_gemv_rows(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const _Float16* __restrict__ x, int m0, int mr, int N, int K, void* __restrict__ y,
     float* __restrict__ part_v, int* __restrict__ part_i) {
