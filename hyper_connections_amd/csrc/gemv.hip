@@ -277,6 +277,13 @@ int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t
     const long cap = (block == MAX_BLOCK) ? 2L * dev.cus : 16L * dev.cus;
     if (blocks > cap) blocks = cap;
     if (blocks > GEMV_MAX_BLOCKS) blocks = GEMV_MAX_BLOCKS;
+    // the fewest blocks that still take the same number of grid-stride steps: every block then
+    // works in every step, and the last step has no idle half of the grid
+    {
+        const long groups = (N + rpb - 1) / rpb;
+        const long steps = (groups + blocks - 1) / blocks;
+        blocks = (groups + steps - 1) / steps;
+    }
     const int nparts = (int)blocks;
 
     float* pv = am ? static_cast<float*>(ws) : nullptr;
