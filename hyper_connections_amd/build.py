@@ -31,9 +31,17 @@ CFLAGS = [
 ]
 
 
+# Extra device-code flags per source: the multi-row GEMV reads every matrix-instruction result
+# with vector instructions right away, so its results go to ordinary VGPRs rather than the
+# accumulation registers (one v_accvgpr_read per result word otherwise).
+DEVICE_FLAGS = {
+    "gemv_rows.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *DEVICE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -147,7 +147,7 @@ int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, 
     if (m == 1)
         return launch_gemv_m1(w, x, y, y_dtype == DHP_F32, argmax, ws, static_cast<hipStream_t>(stream), dev);
     return launch_gemv_rows(w, x, m, y, y_dtype == DHP_F32, argmax, ws, dhp_argmax_part_stride(w->rows, m),
-                            static_cast<hipStream_t>(stream));
+                            static_cast<hipStream_t>(stream), dev.cus);
 }
 
 int decodehp_dequant_gemv_mc(const dhp_int4* w, const void* x, int32_t m, void* y, int32_t y_dtype,

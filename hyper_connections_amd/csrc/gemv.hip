@@ -9,17 +9,18 @@
 //  * 16 lanes own one weight row. Lane j reads 16-byte code chunks j, j+16, j+32, ... of
 //    the row, so one load instruction of a 16-lane group covers 256 contiguous bytes and a
 //    wave streams four rows at once.
-//  * The activation slice a lane needs is the same for every row it visits, so it is
-//    loaded once, rearranged into the pair order of the nibble unpack, and kept in
-//    registers (K = 2560: 80 VGPRs). A block walks rows with a grid stride and keeps the
-//    next row group's codes in flight while it computes the current one.
-//  * Per 64-weight group the affine form is factored: s * sum(q*x) + b * sum(x); the
-//    inner sum runs on v_dot2_f32_f16 over the codes in their offset fp16 form (see
-//    unpack8_off), which carries a factor 16 through both halves; the finished row is
-//    scaled by 1/16 (exact).
-//  * The 16 partial sums of a row meet in a fixed butterfly, so a row's value does not
-//    depend on which block, wave or lane group computed it: duplicated rows give equal
-//    bits, which is what the argmax tie rule needs.
+//  * Per 64-weight group the affine form is factored: s * sum(q*x) + b * sum(x). Each 32-code
+//    chunk's sum(q*x) is formed exactly on integers (the activations as three int8 pieces
+//    relative to the chunk's largest magnitude, v_dot4_i32_i8 over the codes; see
+//    xq_stage_quad), so its value does not depend on the order of the products.
+//  * The activations' pieces are the same for every row: each block converts them once into
+//    LDS (four lanes per chunk) and, where K = 16 * CPL * 32 with CPL <= 5, every lane keeps
+//    the pieces of its own chunks in registers. A block walks rows with a grid stride and
+//    keeps the next row group's codes in flight while it computes the current one.
+//  * Lane j's chunks form chain j, one fp32 step per chunk; the 16 chains of a row meet in a
+//    fixed butterfly, so a row's value does not depend on which block, wave or lane group
+//    computed it: duplicated rows give equal bits, which is what the argmax tie rule needs, and
+//    the multi-row kernel (gemv_rows.hip) reproduces every row bit for bit.
 #include "dhp_internal.hpp"
 
 #include <math.h>
@@ -76,12 +77,20 @@ DHP_DEV void block_argmax_write(float bv, int bi, bool leader, float* part_v, in
     }
 }
 
-// Register-resident activations: K = 16 * CPL * 32.
+// Stage the activations' chunk pieces (XQ_DW words per chunk) into LDS, four lanes per chunk.
+DHP_DEV void stage_x(const _Float16* __restrict__ x, int CH, uint32_t* __restrict__ xs) {
+    for (int it = threadIdx.x; it < 4 * CH; it += blockDim.x)
+        xq_stage_quad(x + (size_t)(it >> 2) * 32, it & 3, xs + (size_t)(it >> 2) * XQ_DW);
+    __syncthreads();
+}
+
+// Register-resident activation pieces: K = 16 * CPL * 32.
 template <int CPL, bool F32OUT, bool ARGMAX>
 __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ x, void* __restrict__ y,
     int N, float* __restrict__ part_v, int* __restrict__ part_i) {
+    __shared__ __align__(16) uint32_t xs[LPR * CPL * XQ_DW];
     const int t = threadIdx.x;
     const int j = t % LPR;
     const int rpb = blockDim.x / LPR;
@@ -98,24 +107,33 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     RowRegs r[CPL];
     load_row<CPL>(codes, scales, biases, min(base + rw, N - 1), j, r);
 
-    h2 xp[CPL][16];
-    float xs[CPL], nc[CPL];
+    // the first codes are in flight while the block converts the activations
+    stage_x(x, LPR * CPL, xs);
+    uint32_t xq[CPL][24];
+    float sx[CPL], pe[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) xs[i] = load_x32_off(x + (size_t)(j + LPR * i) * 32, xp[i], nc[i]);
+    for (int i = 0; i < CPL; ++i) {
+        const uint32_t* src = xs + (size_t)(j + LPR * i) * XQ_DW;
+#pragma unroll
+        for (int w = 0; w < 24; w += 2) {
+            const uint2 v = *reinterpret_cast<const uint2*>(src + w);
+            xq[i][w] = v.x;
+            xq[i][w + 1] = v.y;
+        }
+        const float2 sp = *reinterpret_cast<const float2*>(src + 24);
+        sx[i] = sp.x;
+        pe[i] = sp.y;
+    }
 
-    const NibConsts nk = nib_consts();
     float best_v = -INFINITY;
     int best_i = INT_MAX;
     for (; base < N; base += stride) {
         const int row = base + rw;
         float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const float d = dot32_off(r[i].c, xp[i], nc[i], nk);
-            acc = __builtin_fmaf(bf16_to_f32(r[i].s), d, acc);
-            acc = __builtin_fmaf(bf16_to_f32(r[i].b), xs[i], acc);
-        }
-        acc = group_sum<LPR>(acc) * 0.0625f;
+        for (int i = 0; i < CPL; ++i)
+            acc = xq_chunk_acc(acc, dot32_i8(r[i].c, xq[i]), bf16_to_f32(r[i].s), bf16_to_f32(r[i].b), sx[i], pe[i]);
+        acc = group_sum<LPR>(acc);
         if (j == 0 && row < N) {
             if constexpr (F32OUT) reinterpret_cast<float*>(y)[row] = acc;
             else reinterpret_cast<_Float16*>(y)[row] = (_Float16)acc;
@@ -127,35 +145,21 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     block_argmax_write<ARGMAX>(best_v, best_i, j == 0, part_v, part_i);
 }
 
-// Any K (multiple of 64, <= 16384): activations staged once per block in LDS as permuted
-// pairs plus per-chunk (16 sum, -1024 sum); lane j walks chunks j, j+16, ... of each row with
-// the same operations, in the same order, as k_gemv_m1_reg.
+// Any K (multiple of 64, <= 16384): the activations' pieces stay in LDS; lane j walks chunks
+// j, j+16, ... of each row with the same operations, in the same order, as k_gemv_m1_reg.
 template <bool F32OUT, bool ARGMAX>
 __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ x, void* __restrict__ y,
     int N, int K, float* __restrict__ part_v, int* __restrict__ part_i) {
-    extern __shared__ u32x4 lds_x[];            // [CH][4] u32x4 = 16 permuted pairs per chunk
+    extern __shared__ __align__(16) uint32_t xs_dyn[];      // [CH][XQ_DW]
     const int CH = K / 32;
     const int G = K / 64;
-    float2* lds_sum = reinterpret_cast<float2*>(lds_x + (size_t)CH * 4);
-    for (int ch = threadIdx.x; ch < CH; ch += blockDim.x) {
-        h2 p[16];
-        float nc;
-        const float xs = load_x32_off(x + (size_t)ch * 32, p, nc);
-        lds_sum[ch] = float2{xs, nc};
-        u32x4* dst = lds_x + (size_t)ch * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dst[i] = u32x4{h2_bits(p[4 * i]), h2_bits(p[4 * i + 1]), h2_bits(p[4 * i + 2]),
-                           h2_bits(p[4 * i + 3])};
-    }
-    __syncthreads();
+    stage_x(x, CH, xs_dyn);
 
     const int t = threadIdx.x;
     const int j = t % LPR;
     const int rpb = blockDim.x / LPR;
-    const NibConsts nk = nib_consts();
     float best_v = -INFINITY;
     int best_i = INT_MAX;
     // whole 16-lane groups share a row, so the DPP sum below sees only live lanes
@@ -166,20 +170,18 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
         float acc = 0.0f;
         for (int ch = j; ch < CH; ch += LPR) {
             const u32x4 c = __builtin_nontemporal_load(cr + ch);
-            h2 p[16];
-            const u32x4* src = lds_x + (size_t)ch * 4;
+            const uint32_t* src = xs_dyn + (size_t)ch * XQ_DW;
+            uint32_t xq[24];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 u = src[i];
-                p[4 * i] = as_h2(u.x); p[4 * i + 1] = as_h2(u.y);
-                p[4 * i + 2] = as_h2(u.z); p[4 * i + 3] = as_h2(u.w);
+            for (int w = 0; w < 24; w += 2) {
+                const uint2 v = *reinterpret_cast<const uint2*>(src + w);
+                xq[w] = v.x;
+                xq[w + 1] = v.y;
             }
-            const float2 sn = lds_sum[ch];
-            const float d = dot32_off(c, p, sn.y, nk);
-            acc = __builtin_fmaf(bf16_to_f32(sr[ch >> 1]), d, acc);
-            acc = __builtin_fmaf(bf16_to_f32(br[ch >> 1]), sn.x, acc);
+            const float2 sp = *reinterpret_cast<const float2*>(src + 24);
+            acc = xq_chunk_acc(acc, dot32_i8(c, xq), bf16_to_f32(sr[ch >> 1]), bf16_to_f32(br[ch >> 1]), sp.x, sp.y);
         }
-        acc = group_sum<LPR>(acc) * 0.0625f;
+        acc = group_sum<LPR>(acc);
         if (j == 0) {
             if constexpr (F32OUT) reinterpret_cast<float*>(y)[row] = acc;
             else reinterpret_cast<_Float16*>(y)[row] = (_Float16)acc;
@@ -269,12 +271,12 @@ int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t
 
     // Small problems spread over more, narrower blocks; large ones run a grid stride over
     // a few resident blocks per compute unit.
-    const int rows_per_wave = 64 / LPR;
-    const long waves = (N + rows_per_wave - 1) / rows_per_wave;
-    int block = (waves < 4L * dev.cus) ? 64 : MAX_BLOCK;
+    // Blocks of four waves (every block converts the activations once, so one-wave blocks
+    // would repeat that work for every four rows); at most two resident per compute unit.
+    const int block = MAX_BLOCK;
     const int rpb = block / LPR;
     long blocks = (N + rpb - 1) / rpb;
-    const long cap = (block == MAX_BLOCK) ? 2L * dev.cus : 16L * dev.cus;
+    const long cap = 2L * dev.cus;
     if (blocks > cap) blocks = cap;
     if (blocks > GEMV_MAX_BLOCKS) blocks = GEMV_MAX_BLOCKS;
     // the fewest blocks that still take the same number of grid-stride steps: every block then
@@ -298,10 +300,8 @@ int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t
         case 3: e = launch_reg<3>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
         case 4: e = launch_reg<4>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
         case 5: e = launch_reg<5>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
-        case 6: e = launch_reg<6>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
-        case 8: e = launch_reg<8>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
         default: {
-            const size_t lds = (size_t)CH * 64 + (size_t)CH * 8;
+            const size_t lds = (size_t)CH * XQ_DW * 4;
             if (y_f32 && am) hipLaunchKernelGGL((k_gemv_m1_lds<true, true>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);
             else if (y_f32) hipLaunchKernelGGL((k_gemv_m1_lds<true, false>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);
             else if (am) hipLaunchKernelGGL((k_gemv_m1_lds<false, true>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);

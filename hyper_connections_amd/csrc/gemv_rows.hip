@@ -1,301 +1,287 @@
-// Multi-row INT4-affine GEMV (2 <= m <= 16 rows of activations) that gives every output exactly
-// the bits the M=1 GEMV gives for that row alone.
+// Multi-row INT4-affine GEMV (2 <= m <= 16 rows of activations) on the matrix cores that gives
+// every output exactly the bits the M=1 GEMV gives for that row alone.
 //
 // "src/real_forward.rs" (turbospark-runtime 0.3.0), field batched_gemv_prefill: the batched
 // GEMV kernel and the per-row GEMV agree bit for bit (only the matrix-instruction variant, a
-// separate option, differs). The M=1 kernels (gemv.hip) fix each output's arithmetic: 16 lanes
-// ("virtual lanes" j = 0..15) each run a chain over the 32-code chunks j, j+16, j+32, ... of the
-// row, d = -1024 sum(x) then sixteen v_dot2 over the offset-form codes, acc = fma(s, d, acc),
-// acc = fma(b, 16 sum(x), acc); the 16 chains meet in the DPP butterfly (pairs, then quads,
-// eights, sixteens); the row is scaled by 1/16. Here the same operations run in the same order,
-// only spread differently:
+// separate option, differs). The M=1 kernels (gemv.hip) fix each output's arithmetic: chain j
+// (j = 0..15) takes the 32-code chunks j, j+16, j+32, ... of the row, one fp32 step per chunk on
+// the chunk's exact integer sum (xq_chunk_acc over dot32_i8); the 16 chains meet in the
+// butterfly (pairs, quads, eights, sixteens). The integer sum is exact whatever the order of its
+// products, so the matrix cores may form it:
 //
-//  * Four lanes own one weight row. Of each 16 chunks (one per virtual lane) the lane in quarter
-//    p = 0..3 of its wave (lane bits 4 and 5) runs chunks 4p .. 4p+3, i.e. virtual lanes
-//    4p .. 4p+3, for up to MR activation rows at once: each chunk's codes are unpacked once and
-//    feed every activation row, whose chains stay in registers (4 * MR accumulators).
-//  * The 16 rows of a wave read their 64-byte quarters of each 256-byte segment in one load
-//    instruction, the next segment in flight while the current one computes.
-//  * The activations are the same for every row. Each block stages them once in LDS, in the
-//    form the M=1 kernels compute per chunk (x32_off_from: the permuted pairs, 16 * sum and
-//    -1024 * sum), for as many chunks as fit (all of K = 2560 at 8 rows). The four lanes of a
-//    quad run the same chunk for four rows; each reads a quarter of the chunk's activations
-//    and the dots take the rest from the quad by DPP.
-//  * At the end each lane sums its four chains (the butterfly's quad of virtual lanes), and two
-//    exchanges across the quarters (the 16- and 32-lane swaps) add the quads in the butterfly's
-//    order; floating-point addition is commutative, so every quarter ends with the same bits.
-// The arithmetic is the M=1 kernels' for every K they take, so the two agree bit for bit
-// wherever both run. The matrix-core kernels (gemv_mfma.hip, gemm.hip) round each dequantized
-// weight to fp16 and sum in another order; they remain as an explicit option.
+//  * A wave owns a tile of 16 weight rows over all of K. v_mfma_i32_16x16x32_i8 takes one chunk
+//    per instruction: B is the chunk's codes (lane (n, g) = weight row n, code word g, unpacked to
+//    int8 in unpack_i8's order), A holds four activation rows' three int8 pieces (fragment row
+//    4a + p = activation row a, piece p; the fourth slot repeats piece 2 and its result is
+//    unused), so lane (n, a) receives row a's three piece sums for weight row n and joins them
+//    (D = P2 * 2^14 + P1 * 2^7 + P0, exact). Eight activation rows take two instructions.
+//  * Codes stream as 16-byte loads: lane (n, g) loads chunk c0 + 4u + g of its row (four lanes
+//    read 64 contiguous bytes), and two swaps across the wave halves (v_permlane32_swap) and two
+//    across neighbouring 16-lane rows (v_permlane16_swap) transpose each 4 x 4 block so that lane
+//    (n, g) holds code word g of the four chunks. A super-step is 16 chunks (one per chain); the
+//    next super-step's codes, scales and biases are in flight while one computes.
+//  * The activations' pieces (xq_stage_quad, the same conversion as the M=1 kernels) are staged
+//    once per block in LDS; blocks stay resident and walk groups of tiles with a grid stride.
+//  * Each chain's steps run in chunk order, and the final butterfly adds the chains in the M=1
+//    kernels' order (addition is commutative, so each pair gives the same bits either way round).
 #include "dhp_internal.hpp"
 
 #include <math.h>
 #include <limits.h>
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 namespace {
 
-constexpr int SEG = 16;          // chunks per segment: one per virtual lane
-constexpr int QCH = 4;           // chunks of a segment per lane (virtual lanes 4p .. 4p+3)
-constexpr int XW = 20;           // dwords per staged (chunk, activation row): 16 pair words, 16 sum, -1024 sum, pad
-// dwords per staged chunk (its MR rows): 4 dwords of padding put the chunks that the four quarters of
-// a wave read at once (4 chunks apart) 16 banks apart
-constexpr int cstride(int MR) { return MR * XW + 4; }
-constexpr int THREADS = 512;     // 8 waves
-constexpr int ROWS_BLOCK = THREADS / 4;   // weight rows per block (16 per wave)
-constexpr size_t STAGE_BYTES = 64 * 1024;   // LDS for the staged activations
+constexpr int WPB = 4;                   // waves per block
+constexpr int THREADS = 64 * WPB;
+constexpr int SUP = 16;                  // chunks per super-step: one per chain
+constexpr size_t STAGE_MAX = 80 * 1024;  // LDS for the staged activations of one block
 
-// Chunks per staging window for MR activation rows: a multiple of 16, at most STAGE_BYTES.
-constexpr int window_chunks(int MR) { return (int)(STAGE_BYTES / (cstride(MR) * 4)) / SEG * SEG; }
+// LDS of one block: the staged pieces [W chunks][MR rows][XQ_DW] (row stride 26 words keeps the
+// four rows and three pieces an A-fragment read touches on distinct banks), then each row's
+// (sum, power of two) pairs [MR][W] so that a lane reads four chunks' pairs with two 16-byte reads.
+#define DHP_DEV_HOST_INLINE __host__ __device__ __forceinline__
 
-// Stage chunks w0 .. w0+W-1 (those below CH) of activation rows m0 .. m0+MR-1 (rows past mr
-// repeat row mr - 1, so the compute loop needs no check per row; their results are never stored).
+constexpr size_t stage_bytes_per_chunk(int MR) { return (size_t)MR * (XQ_DW * 4 + 8); }
+
+// Chunks per staging window for MR activation rows: all of K rounded up to 16 chunks when that fits
+// (all of K = 2560 at 8 rows), else a multiple of 32, so that windows start where a pair of
+// super-steps does.
 template <int MR>
-DHP_DEV void stage_window(uint32_t* xs, const _Float16* __restrict__ x, int m0, int mr, int K, int CH, int w0, int W) {
+DHP_DEV_HOST_INLINE int window_chunks(int CH) {
+    const int fit = (int)(STAGE_MAX / stage_bytes_per_chunk(MR));
+    const int all = (CH + SUP - 1) / SUP * SUP;
+    return all <= fit ? all : fit / (2 * SUP) * (2 * SUP);
+}
+
+// Stage chunks w0 .. w0+W-1 (those below CH) of activation rows m0 .. m0+MR-1 (rows past mr repeat
+// row mr - 1; their results are never stored).
+template <int MR>
+DHP_DEV void stage_window(uint32_t* xs, float2* sps, const _Float16* __restrict__ x, int m0, int mr, int K, int CH,
+                          int w0, int W) {
     __syncthreads();                          // the previous window's reads are done
-    for (int it = threadIdx.x; it < W * MR; it += THREADS) {
-        const int j = it / MR, r = it - j * MR;
-        const int c = w0 + j;
-        if (c < CH) {
-            const int rs = r < mr ? r : mr - 1;
-            const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)(m0 + rs) * K + 32 * c);
-            const u32x4 v[4] = {src[0], src[1], src[2], src[3]};
-            h2 xp[16];
-            float nc;
-            const float s16 = x32_off_from(v, xp, nc);
-            uint32_t* dst = xs + (size_t)j * cstride(MR) + r * XW;
-#pragma unroll
-            for (int l = 0; l < 4; ++l)                 // lane l of a quad reads words l, l+4, l+8, l+12
-                *reinterpret_cast<u32x4*>(dst + 4 * l) =
-                    u32x4{h2_bits(xp[l]), h2_bits(xp[4 + l]), h2_bits(xp[8 + l]), h2_bits(xp[12 + l])};
-            dst[16] = __builtin_bit_cast(uint32_t, s16);
-            dst[17] = __builtin_bit_cast(uint32_t, nc);
-        }
+    const int n = 4 * min(W, CH - w0) * MR;   // four lanes per (chunk, row)
+    for (int it = threadIdx.x; it < n; it += THREADS) {
+        const int item = it >> 2;
+        const int j = item / MR, r = item - j * MR;
+        const int rs = r < mr ? r : mr - 1;
+        const float2 sp = xq_stage_quad(x + (size_t)(m0 + rs) * K + 32 * (w0 + j), it & 3, xs + (size_t)item * XQ_DW);
+        if ((it & 3) == 0) sps[r * W + j] = sp;
     }
     __syncthreads();
 }
 
-// One lane's quarter of a segment of its row: 4 chunks of codes and the scales and biases of
-// their 2 groups, packed as two bf16 per word. Chunks past the row are clamped to its last chunk
-// (loaded, never used). With FULL (K % 512 == 0) the row's scales start 16-byte aligned and a
-// quarter's pair of groups is one 4-byte load.
-struct QuarterRegs {
-    u32x4 c[QCH];
-    uint32_t s, b;
+// One super-step of one lane: 16 chunks' codes (lane g of row n holds chunk c0 + 4u + g in c[u])
+// and the scales and biases of their 8 groups, two bf16 per word. Chunks past the row are clamped
+// to its last chunk (loaded, never used). With FULL (K % 512 == 0 and 16-byte aligned scale and
+// bias arrays) the 8 groups are one 16-byte load each.
+struct SupRegs {
+    u32x4 c[4];
+    u32x4 s, b;
 };
+// cb, sb, bb: the tile's first row (uniform over the wave); lc, lg: this lane's row offset from it
+// in chunks and in groups (32-bit lane offsets keep one register per address).
 template <bool FULL>
-DHP_DEV void load_quarter(QuarterRegs& l, const u32x4* __restrict__ cr, const uint16_t* __restrict__ sr,
-                          const uint16_t* __restrict__ br, int cb, int CH) {
+DHP_DEV void load_sup(SupRegs& l, const u32x4* __restrict__ cb, const uint16_t* __restrict__ sb,
+                      const uint16_t* __restrict__ bb, int lc, int lg, int c0, int g, int CH, int G) {
 #pragma unroll
-    for (int i = 0; i < QCH; ++i) l.c[i] = __builtin_nontemporal_load(cr + min(cb + i, CH - 1));
+    for (int u = 0; u < 4; ++u) l.c[u] = __builtin_nontemporal_load(cb + (lc + min(c0 + 4 * u + g, CH - 1)));
     if constexpr (FULL) {
-        const int g0 = min(cb, CH - QCH) >> 1;          // even: 4-byte aligned
-        l.s = *reinterpret_cast<const uint32_t*>(sr + g0);
-        l.b = *reinterpret_cast<const uint32_t*>(br + g0);
+        const int g0 = min(c0 >> 1, G - 8);       // the last super-step's loads (never used) stay in the row
+        l.s = *reinterpret_cast<const u32x4*>(sb + (lg + g0));
+        l.b = *reinterpret_cast<const u32x4*>(bb + (lg + g0));
     } else {
-        const int g0 = min(cb, CH - 1) >> 1, g1 = min(cb + 2, CH - 1) >> 1;
-        l.s = (uint32_t)sr[g0] | ((uint32_t)sr[g1] << 16);
-        l.b = (uint32_t)br[g0] | ((uint32_t)br[g1] << 16);
+        uint32_t sw[4], bw[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int g0 = min((c0 >> 1) + 2 * h, G - 1), g1 = min((c0 >> 1) + 2 * h + 1, G - 1);
+            sw[h] = (uint32_t)sb[lg + g0] | ((uint32_t)sb[lg + g1] << 16);
+            bw[h] = (uint32_t)bb[lg + g0] | ((uint32_t)bb[lg + g1] << 16);
+        }
+        l.s = u32x4{sw[0], sw[1], sw[2], sw[3]};
+        l.b = u32x4{bw[0], bw[1], bw[2], bw[3]};
     }
 }
-// group h (0, 1) of a quarter: its scale or bias as fp32
+
+// group h (0, 1) of a word: its scale or bias as fp32
 DHP_DEV float half_bf16(uint32_t w, int h) { return __builtin_bit_cast(float, h ? (w & 0xFFFF0000u) : (w << 16)); }
 
-// Eight pair dots (pairs 8h .. 8h+7 of a chunk, dot32_off's order) for NC activation rows at once,
-// each row's activation word e taken from lane e & 3 of the quad by a DPP quad broadcast inside
-// v_dot2c (every lane of a quad holds 16 bytes of the chunk's 64, so LDS delivers a quarter of
-// what reading every word in every lane would). The compiler cannot see the instructions in the
-// block, so the block keeps its own wait states: three on entry (a DPP instruction must not read a
-// VGPR a VALU instruction wrote in the two cycles before), three on exit (a VALU instruction other
-// than the same dot must not read a dot's result within three), and inside it a row's accumulator
-// is written at least two instructions before it is read again (four rows: three other dots in
-// between; two rows: one dot and a nop).
-//   d[c]: row c's chain; t8: the 8 code pairs; xw2[c]: row c's words from component 2h, 2h+1.
-DHP_DEV void dots_half4(float (&d)[4], const uint32_t (&t8)[8], const uint32_t (&xw2)[4][2]) {
-    asm("s_nop 2\n\tv_dot2c_f32_f16_dpp %0, %12, %4 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %14, %4 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %2, %16, %4 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %3, %18, %4 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %0, %12, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %14, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %2, %16, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %3, %18, %5 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %0, %12, %6 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %14, %6 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %2, %16, %6 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %3, %18, %6 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %0, %12, %7 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %14, %7 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %2, %16, %7 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %3, %18, %7 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %0, %13, %8 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %15, %8 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %2, %17, %8 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %3, %19, %8 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %0, %13, %9 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %15, %9 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %2, %17, %9 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %3, %19, %9 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %0, %13, %10 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %15, %10 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %2, %17, %10 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %3, %19, %10 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %0, %13, %11 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %15, %11 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %2, %17, %11 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %3, %19, %11 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\ts_nop 2"
-        : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3])
-        : "v"(t8[0]), "v"(t8[1]), "v"(t8[2]), "v"(t8[3]), "v"(t8[4]), "v"(t8[5]), "v"(t8[6]), "v"(t8[7]),
-          "v"(xw2[0][0]), "v"(xw2[0][1]), "v"(xw2[1][0]), "v"(xw2[1][1]), "v"(xw2[2][0]), "v"(xw2[2][1]),
-          "v"(xw2[3][0]), "v"(xw2[3][1]));
+// v_permlane32_swap: a's upper 32 lanes trade places with b's lower 32 lanes.
+DHP_DEV void swap32(uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
 }
-DHP_DEV void dots_half2(float (&d)[2], const uint32_t (&t8)[8], const uint32_t (&xw2)[2][2]) {
-    asm("s_nop 2\n\tv_dot2c_f32_f16_dpp %0, %10, %2 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %12, %2 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\ts_nop 0\n\tv_dot2c_f32_f16_dpp %0, %10, %3 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %12, %3 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\ts_nop 0\n\tv_dot2c_f32_f16_dpp %0, %10, %4 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %12, %4 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\ts_nop 0\n\tv_dot2c_f32_f16_dpp %0, %10, %5 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %12, %5 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\ts_nop 0\n\tv_dot2c_f32_f16_dpp %0, %11, %6 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %13, %6 quad_perm:[0,0,0,0] row_mask:0xf bank_mask:0xf\n\ts_nop 0\n\tv_dot2c_f32_f16_dpp %0, %11, %7 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %13, %7 quad_perm:[1,1,1,1] row_mask:0xf bank_mask:0xf\n\ts_nop 0\n\tv_dot2c_f32_f16_dpp %0, %11, %8 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %13, %8 quad_perm:[2,2,2,2] row_mask:0xf bank_mask:0xf\n\ts_nop 0\n\tv_dot2c_f32_f16_dpp %0, %11, %9 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\tv_dot2c_f32_f16_dpp %1, %13, %9 quad_perm:[3,3,3,3] row_mask:0xf bank_mask:0xf\n\ts_nop 0\n\ts_nop 2"
-        : "+v"(d[0]), "+v"(d[1])
-        : "v"(t8[0]), "v"(t8[1]), "v"(t8[2]), "v"(t8[3]), "v"(t8[4]), "v"(t8[5]), "v"(t8[6]), "v"(t8[7]),
-          "v"(xw2[0][0]), "v"(xw2[0][1]), "v"(xw2[1][0]), "v"(xw2[1][1]));
+// v_permlane16_swap: a's odd 16-lane rows trade places with b's even rows.
+DHP_DEV void swap16(uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
 }
 
-// The 16 pair dots of one chunk for NC rows: d[c] starts at row c's -1024 sum and ends at
-// 16 q.x; xw[c] is row c's 16 bytes (components 0..3 = words q, q+4, q+8, q+12 of quad lane q).
-template <int NC>
-DHP_DEV void dots_chunk(float (&d)[NC], const uint32_t (&t)[16], const u32x4 (&xw)[NC]) {
+// The chains' steps for the 16 chunks of one super-step (chunk c0 + ci extends chain ci) for
+// MI groups of four activation rows; xw: the staged pieces of chunk c0, spw: row 0's pair of
+// chunk c0 (row r's at spw + r * W). Each quad of chunks reads all its LDS operands first, then
+// runs its 4 * MI matrix instructions, then their chain steps.
+template <int MI, bool TAIL>
+DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, int W, float (&acc)[MI][SUP], int c0,
+                     int CH, int lane) {
+    constexpr int MR = 4 * MI;
+    const int g = lane >> 4;                          // code word of a chunk; activation row of a result
+    const int a_off = ((lane & 15) >> 2) * XQ_DW + min(lane & 3, 2) * 8 + 2 * g;   // A fragment words
+    const uint32_t sv[4] = {l.s.x, l.s.y, l.s.z, l.s.w};
+    const uint32_t bv[4] = {l.b.x, l.b.y, l.b.z, l.b.w};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t t8[8];
+    for (int u = 0; u < 4; ++u) {
+        // one quad in registers at a time (the scheduler would interleave all of them)
+        __builtin_amdgcn_sched_barrier(0);
+        long aq[4][MI];
+        float2 sp[4][MI];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t8[e] = t[8 * h + e];
-        uint32_t x2[NC][2];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            x2[c][0] = h ? xw[c].z : xw[c].x;
-            x2[c][1] = h ? xw[c].w : xw[c].y;
+            for (int mi = 0; mi < MI; ++mi)
+                aq[i][mi] = *reinterpret_cast<const long*>(xw + (size_t)((4 * u + i) * MR + 4 * mi) * XQ_DW + a_off);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const float4* q = reinterpret_cast<const float4*>(spw + (4 * mi + g) * W + 4 * u);
+            const float4 v0 = q[0], v1 = q[1];
+            sp[0][mi] = float2{v0.x, v0.y};
+            sp[1][mi] = float2{v0.z, v0.w};
+            sp[2][mi] = float2{v1.x, v1.y};
+            sp[3][mi] = float2{v1.z, v1.w};
         }
-        if constexpr (NC == 4) dots_half4(d, t8, x2);
-        else dots_half2(d, t8, x2);
-    }
-}
-
-// A compiler barrier for memory operations: LDS reads are not moved across it (without it the
-// compiler hoists every LDS read of a line to the top and runs out of registers).
-DHP_DEV void mem_fence_compiler() { asm volatile("" ::: "memory"); }
-
-// The chains of chunks cb .. cb+3 (chunk cb + i extends this lane's chain i) for every activation
-// row; xw: the staged blocks of chunk cb (its MR rows), then the next chunk's.
-template <int MR, bool TAIL>
-DHP_DEV void run_quarter(const QuarterRegs& l, const uint32_t* xw, float (&acc)[MR][QCH], int cb, int CH,
-                         const NibConsts& nk, int q) {
+        // lane (n, g) holds the four words of chunk c0 + 4u + g; afterwards word g of chunks
+        // c0 + 4u .. c0 + 4u + 3
+        uint32_t r0 = l.c[u].x, r1 = l.c[u].y, r2 = l.c[u].z, r3 = l.c[u].w;
+        swap32(r0, r2);
+        swap32(r1, r3);
+        swap16(r0, r1);
+        swap16(r2, r3);
+        const uint32_t wv[4] = {r0, r1, r2, r3};
 #pragma unroll
-    for (int i = 0; i < QCH; ++i) {
-        mem_fence_compiler();                 // one chunk's activations read at a time
-        // in a partial segment, chunks past the row run on clamped codes and stale LDS and are
-        // discarded by a select (a branch here had the compiler hoist the whole segment's reads)
-        const bool live = !TAIL || cb + i < CH;
-        const float s = half_bf16(l.s, i >> 1);
-        const float b = half_bf16(l.b, i >> 1);
-        h2 tp[16];
-        unpack8_off(l.c[i].x, tp, nk);
-        unpack8_off(l.c[i].y, tp + 4, nk);
-        unpack8_off(l.c[i].z, tp + 8, nk);
-        unpack8_off(l.c[i].w, tp + 12, nk);
-        uint32_t t[16];
+        for (int i = 0; i < 4; ++i) {
+            const int ci = 4 * u + i;
+            if (TAIL && c0 + ci >= CH) break;         // uniform: the row's last super-step is partial
+            uint32_t lo, hi;
+            unpack_i8(wv[i], lo, hi);
+            const long bq = (long)(((uint64_t)hi << 32) | lo);
+            const float s = half_bf16(sv[u], i >> 1);   // chunk ci is in group ci / 2 = 2u + i / 2
+            const float b = half_bf16(bv[u], i >> 1);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) t[e] = h2_bits(tp[e]);
-        constexpr int NC = MR >= 4 ? 4 : 2;       // rows per dot block
-#pragma unroll
-        for (int r0 = 0; r0 < MR; r0 += NC) {
-            u32x4 xq[NC];
-            float2 sn[NC];
-            float d[NC];
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const uint32_t* blk = xw + (size_t)i * cstride(MR) + (r0 + c) * XW;
-                xq[c] = *reinterpret_cast<const u32x4*>(blk + 4 * q);
-                sn[c] = *reinterpret_cast<const float2*>(blk + 16);
-                d[c] = sn[c].y;
+            for (int mi = 0; mi < MI; ++mi) {
+                const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(aq[i][mi], bq, i32x4{0, 0, 0, 0}, 0, 0, 0);
+                acc[mi][ci] = xq_chunk_acc(acc[mi][ci], d[2] * 16384 + d[1] * 128 + d[0], s, b, sp[i][mi].x, sp[i][mi].y);
             }
-            dots_chunk<NC>(d, t, xq);
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const float a0 = acc[r0 + c][i];
-                const float a1 = __builtin_fmaf(b, sn[c].x, __builtin_fmaf(s, d[c], a0));
-                acc[r0 + c][i] = live ? a1 : a0;
-            }
-            mem_fence_compiler();                 // one block of rows' activations in registers at a time
         }
     }
 }
 
-template <int MR, bool F32OUT, bool ARGMAX, bool FULL>
-// Whole segments (K % 512 == 0): 128 VGPRs, four waves per SIMD, two blocks of eight waves per CU
-// (their staged activations fit the LDS twice). With a partial last segment the selects need more
-// registers: one block per CU, no spills.
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? 4 : 2, FULL ? 4 : 2))) void k_gemv_rows(
+// Two waves per SIMD (two resident blocks per compute unit, which their LDS allows). ONE: all of
+// K fits one staging window, staged once per block before the first tile.
+template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemv_rows(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const _Float16* __restrict__ x, int m0, int mr, int N, int K, void* __restrict__ y,
     float* __restrict__ part_v, int* __restrict__ part_i) {
-    extern __shared__ __align__(16) uint32_t xs[];     // [window chunks][cstride(MR)]: [MR][XW], pad
-    constexpr int WMAX = window_chunks(MR);
+    constexpr int MR = 4 * MI;
+    extern __shared__ __align__(16) uint32_t xs[];     // [W][MR][XQ_DW], then the pairs [MR][W]
     const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int q = lane & 3;                  // quad lane: which 16 bytes of a staged chunk it reads
-    const int p = lane >> 4;                 // quarter: virtual lanes 4p .. 4p+3
-    const int row = blockIdx.x * ROWS_BLOCK + wave * 16 + (lane & 15);
-    const int rr = min(row, N - 1);          // rows past N compute the last row again, unstored
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int n = lane & 15, g = lane >> 4;
     const int CH = K >> 5, G = K >> 6;
-    const u32x4* cr = codes + (size_t)rr * CH;
-    const uint16_t* sr = scales + (size_t)rr * G;
-    const uint16_t* br = biases + (size_t)rr * G;
-    const int W = min(WMAX, (CH + SEG - 1) / SEG * SEG);
-    const int pc = QCH * p;                  // this lane's first chunk in a segment
+    const int W = window_chunks<MR>(CH);
+    float2* sps = reinterpret_cast<float2*>(xs + (size_t)W * MR * XQ_DW);
+    const int ngroups = ((N + 15) / 16 + WPB - 1) / WPB;
+    if constexpr (ONE) stage_window<MR>(xs, sps, x, m0, mr, K, CH, 0, W);
 
-    float acc[MR][QCH];
+    float best_v[MI];
+    int best_i[MI];
 #pragma unroll
-    for (int r = 0; r < MR; ++r)
-#pragma unroll
-        for (int j = 0; j < QCH; ++j) acc[r][j] = 0.0f;
-    const NibConsts nk = nib_consts();
+    for (int mi = 0; mi < MI; ++mi) {
+        best_v[mi] = -INFINITY;
+        best_i[mi] = INT_MAX;
+    }
+    for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {      // uniform over the block
+        const int r0 = (grp * WPB + wave) * 16;  // the tile's first row, uniform over the wave
+        const int row = r0 + n;
+        const int ro = min(n, max(N - 1 - r0, 0));   // rows past N compute the last row again, unstored
+        const u32x4* cb = codes + (size_t)min(r0, N - 1) * CH;
+        const uint16_t* sb = scales + (size_t)min(r0, N - 1) * G;
+        const uint16_t* bb = biases + (size_t)min(r0, N - 1) * G;
+        const int lc = ro * CH, lg = ro * G;
 
-    // one segment computes while the next is in flight; segments alternate between two register sets
-    QuarterRegs la, lb;
-    load_quarter<FULL>(la, cr, sr, br, pc, CH);
-    int w0 = -WMAX;
+        float acc[MI][SUP];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int j = 0; j < SUP; ++j) acc[mi][j] = 0.0f;
+
+        SupRegs la, lb;
+        load_sup<FULL>(la, cb, sb, bb, lc, lg, 0, g, CH, G);
+        int w0 = ONE ? 0 : -W;
 #pragma unroll 1
-    for (int c0 = 0; c0 < CH; c0 += 2 * SEG) {
-        if (c0 >= w0 + WMAX) {               // the next staging window (once, at K <= 3072 for 8 rows)
-            w0 = c0;
-            stage_window<MR>(xs, x, m0, mr, K, CH, w0, W);
-        }
-        load_quarter<FULL>(lb, cr, sr, br, c0 + SEG + pc, CH);
-        run_quarter<MR, !FULL>(la, xs + (size_t)(c0 - w0 + pc) * cstride(MR), acc, c0 + pc, CH, nk, q);
-        const int c1 = c0 + SEG;
-        if (c1 < CH) {                       // uniform over the block
-            if (c1 >= w0 + WMAX) {
-                w0 = c1;
-                stage_window<MR>(xs, x, m0, mr, K, CH, w0, W);
+        for (int c0 = 0; c0 < CH; c0 += 2 * SUP) {
+            if (!ONE && c0 >= w0 + W) {          // the next staging window (only when K does not fit)
+                w0 = c0;
+                stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
-            load_quarter<FULL>(la, cr, sr, br, c1 + SEG + pc, CH);
-            run_quarter<MR, !FULL>(lb, xs + (size_t)(c1 - w0 + pc) * cstride(MR), acc, c1 + pc, CH, nk, q);
+            load_sup<FULL>(lb, cb, sb, bb, lc, lg, c0 + SUP, g, CH, G);
+            run_sup<MI, !FULL>(la, xs + (size_t)(c0 - w0) * MR * XQ_DW, sps + (c0 - w0), W, acc, c0, CH, lane);
+            const int c1 = c0 + SUP;
+            if (c1 < CH) {                       // uniform over the block
+                load_sup<FULL>(la, cb, sb, bb, lc, lg, c1 + SUP, g, CH, G);
+                run_sup<MI, !FULL>(lb, xs + (size_t)(c1 - w0) * MR * XQ_DW, sps + (c1 - w0), W, acc, c1, CH, lane);
+            }
+        }
+
+        // the chains meet in the M=1 kernels' butterfly order; lane (n, g) holds activation row
+        // 4 mi + g of weight row n
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            float p[8], q4[4];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) p[k] = acc[mi][2 * k] + acc[mi][2 * k + 1];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q4[k] = p[2 * k] + p[2 * k + 1];
+            const float v = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+            const int ar = 4 * mi + g;
+            if (ar < mr && row < N) {
+                const size_t o = (size_t)(m0 + ar) * N + row;
+                if constexpr (F32OUT) reinterpret_cast<float*>(y)[o] = v;
+                else reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
+            }
+            if constexpr (ARGMAX)
+                if (row < N && better(v, row, best_v[mi], best_i[mi])) {
+                    best_v[mi] = v;
+                    best_i[mi] = row;
+                }
         }
     }
 
-    __shared__ float bv_s[MR][THREADS / 64];
-    __shared__ int bi_s[MR][THREADS / 64];
-    float vals[MR];
-#pragma unroll
-    for (int r = 0; r < MR; ++r) {
-        // this lane's quad of virtual lanes, then the quads in the butterfly's order: the
-        // 16-lane row swap adds quarters 0+1 and 2+3, the 32-lane swap the two halves (each
-        // swap hands both operands to every lane; addition is commutative, so all quarters end
-        // with the same bits)
-        const float qv = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
-        const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, qv), __builtin_bit_cast(uint32_t, qv),
-                                                        false, false);
-        const float h = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
-        const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, h),
-                                                        false, false);
-        const float v = (__builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1])) * 0.0625f;
-        vals[r] = v;
-        const size_t o = (size_t)(m0 + r) * N + row;
-        if (r < mr && row < N && (r & 3) == p) {   // one quarter stores each row
-            if constexpr (F32OUT) reinterpret_cast<float*>(y)[o] = v;
-            else reinterpret_cast<_Float16*>(y)[o] = (_Float16)v;
-        }
-    }
     if constexpr (ARGMAX) {
-        // the wave's best weight row for activation rows r0 .. r0+3 at once: quarter p ranks
-        // row r0 + p over its 16 lanes (the wave's 16 weight rows)
+        __shared__ float bv_s[MR][WPB];
+        __shared__ int bi_s[MR][WPB];
 #pragma unroll
-        for (int r0 = 0; r0 < MR; r0 += 4) {
-            float mine = vals[r0];
-#pragma unroll
-            for (int q = 1; q < 4; ++q)
-                if (r0 + q < MR && p == q) mine = vals[r0 + q];
-            const int ar = r0 + p;
-            const bool ok = row < N && ar < mr;
-            float bv = ok ? mine : -INFINITY;
-            int bi = ok ? row : INT_MAX;
-            best_step<DPP_XOR1>(bv, bi);
+        for (int mi = 0; mi < MI; ++mi) {
+            float bv = best_v[mi];
+            int bi = best_i[mi];
+            best_step<DPP_XOR1>(bv, bi);          // over the 16 weight rows of the 16-lane row
             best_step<DPP_XOR2>(bv, bi);
             best_step<DPP_HALF_MIRROR>(bv, bi);
             best_step<DPP_MIRROR>(bv, bi);
-            if ((lane & 15) == 0 && ar < mr) { bv_s[ar][wave] = bv; bi_s[ar][wave] = bi; }
+            if (n == 0) {
+                bv_s[4 * mi + g][wave] = bv;
+                bi_s[4 * mi + g][wave] = bi;
+            }
         }
-    }
-    if constexpr (ARGMAX) {
         __syncthreads();
         if (t < mr) {
             float bv = bv_s[t][0];
             int bi = bi_s[t][0];
-            for (int w = 1; w < THREADS / 64; ++w)
+            for (int w = 1; w < WPB; ++w)
                 if (better(bv_s[t][w], bi_s[t][w], bv, bi)) { bv = bv_s[t][w]; bi = bi_s[t][w]; }
             part_v[(size_t)(m0 + t) * gridDim.x + blockIdx.x] = bv;     // [act row][block], as the
             part_i[(size_t)(m0 + t) * gridDim.x + blockIdx.x] = bi;     // final reduction reads them
@@ -303,38 +289,48 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? 
     }
 }
 
-template <int MR, bool FULL>
+template <int MI, bool FULL, bool ONE>
 hipError_t launch_rows_full(bool f32, bool am, dim3 g, size_t lds, hipStream_t s, const u32x4* c, const uint16_t* sc,
                             const uint16_t* bi, const _Float16* x, int m0, int mr, int N, int K, void* y, float* pv,
                             int* pi) {
     const dim3 b(THREADS);
-    if (f32 && am) hipLaunchKernelGGL((k_gemv_rows<MR, true, true, FULL>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    else if (f32) hipLaunchKernelGGL((k_gemv_rows<MR, true, false, FULL>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    else if (am) hipLaunchKernelGGL((k_gemv_rows<MR, false, true, FULL>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    else hipLaunchKernelGGL((k_gemv_rows<MR, false, false, FULL>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    if (f32 && am) hipLaunchKernelGGL((k_gemv_rows<MI, true, true, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    else if (f32) hipLaunchKernelGGL((k_gemv_rows<MI, true, false, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    else if (am) hipLaunchKernelGGL((k_gemv_rows<MI, false, true, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    else hipLaunchKernelGGL((k_gemv_rows<MI, false, false, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
     return hipGetLastError();
 }
 
-template <int MR>
-hipError_t launch_rows_mr(bool f32, bool am, dim3 g, hipStream_t s, const u32x4* c, const uint16_t* sc,
+template <int MI>
+hipError_t launch_rows_mi(bool f32, bool am, dim3 g, bool full, hipStream_t s, const u32x4* c, const uint16_t* sc,
                           const uint16_t* bi, const _Float16* x, int m0, int mr, int N, int K, void* y, float* pv,
                           int* pi) {
     const int CH = K >> 5;
-    const int W = min(window_chunks(MR), (CH + SEG - 1) / SEG * SEG);
-    const size_t lds = (size_t)W * cstride(MR) * 4;
-    if (CH % SEG == 0) return launch_rows_full<MR, true>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    return launch_rows_full<MR, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    const int W = window_chunks<4 * MI>(CH);
+    const size_t lds = (size_t)W * stage_bytes_per_chunk(4 * MI);
+    const bool one = CH <= W;
+    if (full && one) return launch_rows_full<MI, true, true>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    if (full) return launch_rows_full<MI, true, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    if (one) return launch_rows_full<MI, false, true>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    return launch_rows_full<MI, false, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
 }
 
 }  // namespace
 
-// Blocks of the multi-row GEMV for N weight rows (the argmax partials per activation row).
-int dhp_gemv_rows_blocks(int N) { return (N + ROWS_BLOCK - 1) / ROWS_BLOCK; }
+// Blocks of the multi-row GEMV for N weight rows (also the argmax partials per activation row):
+// at most two resident blocks per compute unit, each taking the same number of tile groups.
+int dhp_gemv_rows_blocks(int N, int cus) {
+    const long groups = ((N + 15) / 16 + WPB - 1) / WPB;
+    long blocks = groups < 2L * cus ? groups : 2L * cus;
+    const long steps = (groups + blocks - 1) / blocks;
+    blocks = (groups + steps - 1) / steps;
+    return (int)blocks;
+}
 
 int launch_gemv_rows(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
-                     size_t ws_part_stride, hipStream_t s) {
+                     size_t ws_part_stride, hipStream_t s, int cus) {
     const int N = w->rows, K = w->cols;
-    const int nb = dhp_gemv_rows_blocks(N);
+    const int nb = dhp_gemv_rows_blocks(N, cus);
     // the partials [M][nb] fit the workspace's half of ws_part_stride bytes
     if (argmax && (size_t)nb * M * sizeof(float) > ws_part_stride)
         return dhp_fail(DHP_ERR_UNSUPPORTED, "N=%d needs %d argmax partials per row", N, nb);
@@ -345,14 +341,14 @@ int launch_gemv_rows(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     const auto* bi = static_cast<const uint16_t*>(w->biases);
     const auto* xh = static_cast<const _Float16*>(x);
     const bool am = argmax != nullptr;
+    const bool full = K % 512 == 0 && ((uintptr_t)sc % 16) == 0 && ((uintptr_t)bi % 16) == 0;
     const dim3 g((unsigned)nb);
     // activation rows in passes of up to 8 (each pass streams the weights once)
     for (int m0 = 0; m0 < M; m0 += 8) {
         const int mr = M - m0 < 8 ? M - m0 : 8;
         hipError_t e;
-        if (mr <= 2) e = launch_rows_mr<2>(y_f32, am, g, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
-        else if (mr <= 4) e = launch_rows_mr<4>(y_f32, am, g, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
-        else e = launch_rows_mr<8>(y_f32, am, g, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
+        if (mr <= 4) e = launch_rows_mi<1>(y_f32, am, g, full, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
+        else e = launch_rows_mi<2>(y_f32, am, g, full, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
         if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemv rows launch: %s", hipGetErrorString(e));
     }
     if (argmax) {
