@@ -137,22 +137,22 @@ DHP_DEV float dot32_f32(const u32x4 c, const float* x) {
     return d;
 }
 
-// ------------------------------------------------------------------ exact chunk sums (the GEMV)
+// ------------------------------------------------------------------ exact group sums (the GEMV)
 //
-// The GEMV forms each 32-code chunk's dot on integers, so the chunk's value is exact and does
+// The GEMV forms each 64-code group's dot on integers, so the group's value is exact and does
 // not depend on the order of its products: the vector-ALU kernels (v_dot4_i32_i8) and the
-// matrix-core multi-row kernel (v_mfma_i32_16x16x32_i8) produce the same bits. For one
-// activation row and one chunk of 32 activations:
-//   e    = exponent of the chunk's largest |x| (0 for an all-zero chunk),
+// matrix-core multi-row kernel (v_mfma_i32_16x16x64_i8) produce the same bits. For one
+// activation row and one group of 64 activations (the group of one scale and one bias):
+//   e    = exponent of the group's largest |x| (0 for an all-zero group),
 //   X_k  = rint(x_k * 2^(20 - e)); |X_k| < 2^21, exact for every x_k within 2^10 of the largest,
 //   X_k  = P2 * 2^14 + P1 * 2^7 + P0 with P0, P1 in 0..127 and P2 in -128..127 (int8 pieces),
-//   D    = sum_k q_k X_k over the chunk's 4-bit codes (|D| < 2^30, so int32 holds it exactly),
-//   the chunk's step of its chain: acc = fma(fma(s, float(D), b * float(sum_k X_k)), 2^(e-20), acc)
-// with s, b the group's scale and bias. A staged chunk is XQ_DW words: word 8p + 2i + h holds the
-// bytes of X_p at k = 8i + h, 8i + 2 + h, 8i + 4 + h, 8i + 6 + h (piece p, code word i, parity h:
-// the order in which unpack_i8 lays out the codes of word i), word 24 float(sum_k X_k), word 25
-// 2^(e-20).
-constexpr int XQ_DW = 26;
+//   D    = sum_k q_k X_k over the group's 4-bit codes (|D| < 64 * 15 * 2^21 < 2^31: int32, exact),
+//   the group's step of its chain: acc = fma(fma(s, float(D), b * float(sum_k X_k)), 2^(e-20), acc).
+// A staged group is XG_DW words: word 16p + 4w + 2h + r holds the bytes of X_p at
+// k = 32h + 8w + r + {0, 2, 4, 6} (piece p, chunk h of the group, code word w of the chunk,
+// parity r: the order in which unpack_i8 lays out the codes of word w), word 48 float(sum_k X_k),
+// word 49 2^(e-20), two words of padding (16-byte aligned groups).
+constexpr int XG_DW = 52;
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
@@ -160,23 +160,24 @@ DHP_DEV uint32_t pack_bytes(int a, int b, int c, int d) {
     return ((uint32_t)a & 0xFFu) | (((uint32_t)b & 0xFFu) << 8) | (((uint32_t)c & 0xFFu) << 16) | ((uint32_t)d << 24);
 }
 
-// Lanes 4t .. 4t+3 (all active, quad-aligned) convert one chunk: lane i = 0..3 reads k = 8i .. 8i+7
-// of xc (the chunk's 32 fp16 activations, 16-byte aligned) and writes its six piece words of dst
-// (8-byte aligned); lane 0 also writes the sum and the power of two, which every lane of the quad
+// Lanes 8t .. 8t+7 (all active, aligned to 8) convert one group: lane i = 0..7 reads k = 8i .. 8i+7
+// of xg (the group's 64 fp16 activations, 16-byte aligned) and writes its six piece words of dst
+// (8-byte aligned); lane 0 also writes the sum and the power of two, which every lane of the eight
 // returns. The activations must be finite.
-DHP_DEV float2 xq_stage_quad(const _Float16* __restrict__ xc, int i, uint32_t* __restrict__ dst) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xc + 8 * i);
+DHP_DEV float2 xg_stage_octet(const _Float16* __restrict__ xg, int i, uint32_t* __restrict__ dst) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xg + 8 * i);
     // largest magnitude: fp16 magnitude bits order like the magnitudes
     const u16x2 m2 = __builtin_elementwise_max(
         __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu), __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu)),
         __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu), __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu)));
     int m = max((int)m2.x, (int)m2.y);
-    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0xB1, 0xF, 0xF, false));   // quad lanes 1,0,3,2
-    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x4E, 0xF, 0xF, false));   // quad lanes 2,3,0,1
+    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0xB1, 0xF, 0xF, false));    // quad lanes 1,0,3,2
+    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x4E, 0xF, 0xF, false));    // quad lanes 2,3,0,1
+    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x141, 0xF, 0xF, false));   // reversed within 8 lanes
     const float mf = (float)__builtin_bit_cast(_Float16, (uint16_t)m);
-    const int eb = (int)(__builtin_bit_cast(uint32_t, mf) >> 23);           // biased; 0 only for mf = 0
+    const int eb = (int)(__builtin_bit_cast(uint32_t, mf) >> 23);            // biased; 0 only for mf = 0
     const int e = eb ? eb - 127 : 0;
-    const float sc = __builtin_bit_cast(float, (uint32_t)(147 - e) << 23);   // 2^(20 - e)
+    const float sc = __builtin_bit_cast(float, (uint32_t)(147 - e) << 23);    // 2^(20 - e)
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
     int X[8];
     int sx = 0;
@@ -189,30 +190,29 @@ DHP_DEV float2 xq_stage_quad(const _Float16* __restrict__ xc, int i, uint32_t* _
     }
     sx += __builtin_amdgcn_update_dpp(0, sx, 0xB1, 0xF, 0xF, false);
     sx += __builtin_amdgcn_update_dpp(0, sx, 0x4E, 0xF, 0xF, false);
-    uint32_t w[3][2];
+    sx += __builtin_amdgcn_update_dpp(0, sx, 0x141, 0xF, 0xF, false);
+    uint32_t* d = dst + 4 * (i & 3) + 2 * (i >> 2);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int a = X[h], b = X[2 + h], c = X[4 + h], d = X[6 + h];
-        w[0][h] = pack_bytes(a & 127, b & 127, c & 127, d & 127);
-        w[1][h] = pack_bytes((a >> 7) & 127, (b >> 7) & 127, (c >> 7) & 127, (d >> 7) & 127);
-        w[2][h] = pack_bytes(a >> 14, b >> 14, c >> 14, d >> 14);
+    for (int r = 0; r < 2; ++r) {
+        const int a = X[r], b = X[2 + r], c = X[4 + r], e8 = X[6 + r];
+        d[r] = pack_bytes(a & 127, b & 127, c & 127, e8 & 127);
+        d[16 + r] = pack_bytes((a >> 7) & 127, (b >> 7) & 127, (c >> 7) & 127, (e8 >> 7) & 127);
+        d[32 + r] = pack_bytes(a >> 14, b >> 14, c >> 14, e8 >> 14);
     }
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-        *reinterpret_cast<uint2*>(dst + 8 * p + 2 * i) = uint2{w[p][0], w[p][1]};
     const float2 sp = {(float)sx, __builtin_bit_cast(float, (uint32_t)(107 + e) << 23)};   // 2^(e - 20)
-    if (i == 0) *reinterpret_cast<float2*>(dst + 24) = sp;
+    if (i == 0) *reinterpret_cast<float2*>(dst + 48) = sp;
     return sp;
 }
 
-// The codes of one code word (k = 8i .. 8i+7, byte j: k = 2j low nibble, 2j + 1 high) as int8:
-// lo = k 0, 2, 4, 6 and hi = k 1, 3, 5, 7 of the word.
+// The codes of one code word (k = 8w .. 8w+7 of a chunk, byte j: k = 2j low nibble, 2j + 1 high)
+// as int8: lo = k 0, 2, 4, 6 and hi = k 1, 3, 5, 7 of the word.
 DHP_DEV void unpack_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
     lo = w & 0x0F0F0F0Fu;
     hi = (w >> 4) & 0x0F0F0F0Fu;
 }
 
-// sum_k q_k X_k over one chunk, exact: c the chunk's four code words, xq its 24 piece words.
+// One chunk's share of its group's exact sum: c the chunk's four code words, xq its 24 piece words
+// (word 8p + 2w + r = staged word 16p + 4w + 2h + r of the chunk's group).
 DHP_DEV int dot32_i8(const u32x4 c, const uint32_t* xq) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     int s0 = 0, s1 = 0, s2 = 0;
@@ -230,9 +230,9 @@ DHP_DEV int dot32_i8(const u32x4 c, const uint32_t* xq) {
     return s2 * 16384 + s1 * 128 + s0;
 }
 
-// One chunk's step of its chain (the same operations in every kernel; the empty asm keeps the
+// One group's step of its chain (the same operations in every kernel; the empty asm keeps the
 // bias product rounded on its own, so no kernel contracts it into a fused operation).
-DHP_DEV float xq_chunk_acc(float acc, int d, float s, float b, float sx, float pe) {
+DHP_DEV float xg_group_acc(float acc, int d, float s, float b, float sx, float pe) {
     float bs = b * sx;
     asm volatile("" : "+v"(bs));
     return __builtin_fmaf(__builtin_fmaf(s, (float)d, bs), pe, acc);

@@ -9,18 +9,20 @@
 //  * 16 lanes own one weight row. Lane j reads 16-byte code chunks j, j+16, j+32, ... of
 //    the row, so one load instruction of a 16-lane group covers 256 contiguous bytes and a
 //    wave streams four rows at once.
-//  * Per 64-weight group the affine form is factored: s * sum(q*x) + b * sum(x). Each 32-code
-//    chunk's sum(q*x) is formed exactly on integers (the activations as three int8 pieces
-//    relative to the chunk's largest magnitude, v_dot4_i32_i8 over the codes; see
-//    xq_stage_quad), so its value does not depend on the order of the products.
+//  * Per 64-weight group the affine form is factored: s * sum(q*x) + b * sum(x). The group's
+//    sum(q*x) is formed exactly on integers (the activations as three int8 pieces relative to
+//    the group's largest magnitude, v_dot4_i32_i8 over the codes; see xg_stage_octet), so its
+//    value does not depend on the order of the products. Lane j holds one of the group's two
+//    chunks; the neighbouring lane holds the other, and one DPP exchange adds the halves.
 //  * The activations' pieces are the same for every row: each block converts them once into
-//    LDS (four lanes per chunk) and, where K = 16 * CPL * 32 with CPL <= 5, every lane keeps
+//    LDS (eight lanes per group) and, where K = 16 * CPL * 32 with CPL <= 5, every lane keeps
 //    the pieces of its own chunks in registers. A block walks rows with a grid stride and
 //    keeps the next row group's codes in flight while it computes the current one.
-//  * Lane j's chunks form chain j, one fp32 step per chunk; the 16 chains of a row meet in a
-//    fixed butterfly, so a row's value does not depend on which block, wave or lane group
-//    computed it: duplicated rows give equal bits, which is what the argmax tie rule needs, and
-//    the multi-row kernel (gemv_rows.hip) reproduces every row bit for bit.
+//  * Lanes 2j' and 2j'+1 run chain j' (j' = 0..7) over the groups j', j'+8, j'+16, ..., one fp32
+//    step per group; the 8 chains of a row meet in a fixed butterfly, so a row's value does not
+//    depend on which block, wave or lane group computed it: duplicated rows give equal bits,
+//    which is what the argmax tie rule needs, and the multi-row kernel (gemv_rows.hip)
+//    reproduces every row bit for bit.
 #include "dhp_internal.hpp"
 
 #include <math.h>
@@ -77,11 +79,32 @@ DHP_DEV void block_argmax_write(float bv, int bi, bool leader, float* part_v, in
     }
 }
 
-// Stage the activations' chunk pieces (XQ_DW words per chunk) into LDS, four lanes per chunk.
-DHP_DEV void stage_x(const _Float16* __restrict__ x, int CH, uint32_t* __restrict__ xs) {
-    for (int it = threadIdx.x; it < 4 * CH; it += blockDim.x)
-        xq_stage_quad(x + (size_t)(it >> 2) * 32, it & 3, xs + (size_t)(it >> 2) * XQ_DW);
+// Stage the activations' group pieces (XG_DW words per group) into LDS, eight lanes per group.
+DHP_DEV void stage_x(const _Float16* __restrict__ x, int G, uint32_t* __restrict__ xs) {
+    for (int it = threadIdx.x; it < 8 * G; it += blockDim.x)
+        xg_stage_octet(x + (size_t)(it >> 3) * 64, it & 7, xs + (size_t)(it >> 3) * XG_DW);
     __syncthreads();
+}
+
+// The 24 piece words and the (sum, power of two) pair of chunk ch from the staged groups.
+DHP_DEV void load_chunk_pieces(const uint32_t* __restrict__ xs, int ch, uint32_t (&xq)[24], float2& sp) {
+    const uint32_t* src = xs + (size_t)(ch >> 1) * XG_DW + 2 * (ch & 1);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint2 v = *reinterpret_cast<const uint2*>(src + 16 * p + 4 * w);
+            xq[8 * p + 2 * w] = v.x;
+            xq[8 * p + 2 * w + 1] = v.y;
+        }
+    sp = *reinterpret_cast<const float2*>(xs + (size_t)(ch >> 1) * XG_DW + 48);
+}
+
+// The group's exact sum from this lane's chunk and its neighbour's (lanes 2j', 2j'+1 hold the
+// group's two chunks), then the group's chain step; both lanes of the pair end with equal bits.
+DHP_DEV float group_step(float acc, int d_chunk, uint32_t s16, uint32_t b16, float2 sp) {
+    const int d = d_chunk + dpp_i<DPP_XOR1>(d_chunk);
+    return xg_group_acc(acc, d, bf16_to_f32(s16), bf16_to_f32(b16), sp.x, sp.y);
 }
 
 // Register-resident activation pieces: K = 16 * CPL * 32.
@@ -90,7 +113,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ x, void* __restrict__ y,
     int N, float* __restrict__ part_v, int* __restrict__ part_i) {
-    __shared__ __align__(16) uint32_t xs[LPR * CPL * XQ_DW];
+    __shared__ __align__(16) uint32_t xs[LPR * CPL / 2 * XG_DW];
     const int t = threadIdx.x;
     const int j = t % LPR;
     const int rpb = blockDim.x / LPR;
@@ -108,22 +131,11 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
     load_row<CPL>(codes, scales, biases, min(base + rw, N - 1), j, r);
 
     // the first codes are in flight while the block converts the activations
-    stage_x(x, LPR * CPL, xs);
+    stage_x(x, LPR * CPL / 2, xs);
     uint32_t xq[CPL][24];
-    float sx[CPL], pe[CPL];
+    float2 sp[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const uint32_t* src = xs + (size_t)(j + LPR * i) * XQ_DW;
-#pragma unroll
-        for (int w = 0; w < 24; w += 2) {
-            const uint2 v = *reinterpret_cast<const uint2*>(src + w);
-            xq[i][w] = v.x;
-            xq[i][w + 1] = v.y;
-        }
-        const float2 sp = *reinterpret_cast<const float2*>(src + 24);
-        sx[i] = sp.x;
-        pe[i] = sp.y;
-    }
+    for (int i = 0; i < CPL; ++i) load_chunk_pieces(xs, j + LPR * i, xq[i], sp[i]);
 
     float best_v = -INFINITY;
     int best_i = INT_MAX;
@@ -131,9 +143,8 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
         const int row = base + rw;
         float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            acc = xq_chunk_acc(acc, dot32_i8(r[i].c, xq[i]), bf16_to_f32(r[i].s), bf16_to_f32(r[i].b), sx[i], pe[i]);
-        acc = group_sum<LPR>(acc);
+        for (int i = 0; i < CPL; ++i) acc = group_step(acc, dot32_i8(r[i].c, xq[i]), r[i].s, r[i].b, sp[i]);
+        acc = group_sum<LPR, 2>(acc);
         if (j == 0 && row < N) {
             if constexpr (F32OUT) reinterpret_cast<float*>(y)[row] = acc;
             else reinterpret_cast<_Float16*>(y)[row] = (_Float16)acc;
@@ -146,23 +157,24 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_reg(
 }
 
 // Any K (multiple of 64, <= 16384): the activations' pieces stay in LDS; lane j walks chunks
-// j, j+16, ... of each row with the same operations, in the same order, as k_gemv_m1_reg.
+// j, j+16, ... of each row with the same operations, in the same order, as k_gemv_m1_reg (the
+// two lanes of a pair always hold the two chunks of one group: K is a multiple of 64).
 template <bool F32OUT, bool ARGMAX>
 __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const _Float16* __restrict__ x, void* __restrict__ y,
     int N, int K, float* __restrict__ part_v, int* __restrict__ part_i) {
-    extern __shared__ __align__(16) uint32_t xs_dyn[];      // [CH][XQ_DW]
+    extern __shared__ __align__(16) uint32_t xs_dyn[];      // [G][XG_DW]
     const int CH = K / 32;
     const int G = K / 64;
-    stage_x(x, CH, xs_dyn);
+    stage_x(x, G, xs_dyn);
 
     const int t = threadIdx.x;
     const int j = t % LPR;
     const int rpb = blockDim.x / LPR;
     float best_v = -INFINITY;
     int best_i = INT_MAX;
-    // whole 16-lane groups share a row, so the DPP sum below sees only live lanes
+    // whole 16-lane groups share a row, so the DPP sums below see only live lanes
     for (int row = blockIdx.x * rpb + t / LPR; row < N; row += gridDim.x * rpb) {
         const u32x4* cr = codes + (size_t)row * CH;
         const uint16_t* sr = scales + (size_t)row * G;
@@ -170,18 +182,12 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
         float acc = 0.0f;
         for (int ch = j; ch < CH; ch += LPR) {
             const u32x4 c = __builtin_nontemporal_load(cr + ch);
-            const uint32_t* src = xs_dyn + (size_t)ch * XQ_DW;
             uint32_t xq[24];
-#pragma unroll
-            for (int w = 0; w < 24; w += 2) {
-                const uint2 v = *reinterpret_cast<const uint2*>(src + w);
-                xq[w] = v.x;
-                xq[w + 1] = v.y;
-            }
-            const float2 sp = *reinterpret_cast<const float2*>(src + 24);
-            acc = xq_chunk_acc(acc, dot32_i8(c, xq), bf16_to_f32(sr[ch >> 1]), bf16_to_f32(br[ch >> 1]), sp.x, sp.y);
+            float2 sp;
+            load_chunk_pieces(xs_dyn, ch, xq, sp);
+            acc = group_step(acc, dot32_i8(c, xq), sr[ch >> 1], br[ch >> 1], sp);
         }
-        acc = group_sum<LPR>(acc);
+        acc = group_sum<LPR, 2>(acc);
         if (j == 0) {
             if constexpr (F32OUT) reinterpret_cast<float*>(y)[row] = acc;
             else reinterpret_cast<_Float16*>(y)[row] = (_Float16)acc;
@@ -301,7 +307,7 @@ int launch_gemv_m1(const dhp_int4* w, const void* x, void* y, int y_f32, int32_t
         case 4: e = launch_reg<4>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
         case 5: e = launch_reg<5>(y_f32, am, g, b, s, c, sc, bi, xh, y, N, pv, pi); break;
         default: {
-            const size_t lds = (size_t)CH * XQ_DW * 4;
+            const size_t lds = (size_t)(CH / 2) * XG_DW * 4;
             if (y_f32 && am) hipLaunchKernelGGL((k_gemv_m1_lds<true, true>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);
             else if (y_f32) hipLaunchKernelGGL((k_gemv_m1_lds<true, false>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);
             else if (am) hipLaunchKernelGGL((k_gemv_m1_lds<false, true>), g, b, lds, s, c, sc, bi, xh, y, N, K, pv, pi);

@@ -4,25 +4,26 @@
 // "src/real_forward.rs" (turbospark-runtime 0.3.0), field batched_gemv_prefill: the batched
 // GEMV kernel and the per-row GEMV agree bit for bit (only the matrix-instruction variant, a
 // separate option, differs). The M=1 kernels (gemv.hip) fix each output's arithmetic: chain j
-// (j = 0..15) takes the 32-code chunks j, j+16, j+32, ... of the row, one fp32 step per chunk on
-// the chunk's exact integer sum (xq_chunk_acc over dot32_i8); the 16 chains meet in the
-// butterfly (pairs, quads, eights, sixteens). The integer sum is exact whatever the order of its
-// products, so the matrix cores may form it:
+// (j = 0..7) takes the 64-code groups j, j+8, j+16, ... of the row, one fp32 step per group on
+// the group's exact integer sum (xg_group_acc); the 8 chains meet in the butterfly (pairs,
+// quads, eights). The integer sum is exact whatever the order of its products, so the matrix
+// cores may form it:
 //
-//  * A wave owns a tile of 16 weight rows over all of K. v_mfma_i32_16x16x32_i8 takes one chunk
-//    per instruction: B is the chunk's codes (lane (n, g) = weight row n, code word g, unpacked to
-//    int8 in unpack_i8's order), A holds four activation rows' three int8 pieces (fragment row
-//    4a + p = activation row a, piece p; the fourth slot repeats piece 2 and its result is
-//    unused), so lane (n, a) receives row a's three piece sums for weight row n and joins them
-//    (D = P2 * 2^14 + P1 * 2^7 + P0, exact). Eight activation rows take two instructions.
-//  * Codes stream as 16-byte loads: lane (n, g) loads chunk c0 + 4u + g of its row (four lanes
+//  * A wave owns a tile of 16 weight rows over all of K. v_mfma_i32_16x16x64_i8 takes one group
+//    per instruction: B is the group's codes (lane (n, w) = weight row n, code word w of both
+//    chunks, unpacked to int8 in unpack_i8's order), A holds four activation rows' three int8
+//    pieces (fragment row 4a + p = activation row a, piece p; the fourth slot repeats piece 2 and
+//    its result is unused), so lane (n, a) receives row a's three piece sums for weight row n and
+//    joins them (D = P2 * 2^14 + P1 * 2^7 + P0, exact). Eight activation rows take two
+//    instructions.
+//  * Codes stream as 16-byte loads: lane (n, w) loads chunk c0 + 4u + w of its row (four lanes
 //    read 64 contiguous bytes), and two swaps across the wave halves (v_permlane32_swap) and two
 //    across neighbouring 16-lane rows (v_permlane16_swap) transpose each 4 x 4 block so that lane
-//    (n, g) holds code word g of the four chunks. A super-step is 16 chunks (one per chain); the
-//    next super-step's codes, scales and biases are in flight while one computes.
-//  * The activations' pieces (xq_stage_quad, the same conversion as the M=1 kernels) are staged
+//    (n, w) holds code word w of the four chunks. A super-step is 16 chunks (8 groups, one per
+//    chain); the next super-step's codes, scales and biases are in flight while one computes.
+//  * The activations' pieces (xg_stage_octet, the same conversion as the M=1 kernels) are staged
 //    once per block in LDS; blocks stay resident and walk groups of tiles with a grid stride.
-//  * Each chain's steps run in chunk order, and the final butterfly adds the chains in the M=1
+//  * Each chain's steps run in group order, and the final butterfly adds the chains in the M=1
 //    kernels' order (addition is commutative, so each pair gives the same bits either way round).
 #include "dhp_internal.hpp"
 
@@ -33,17 +34,19 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int WPB = 4;                   // waves per block
+#ifndef DHP_ROWS_WPB
+#define DHP_ROWS_WPB 8
+#endif
+constexpr int WPB = DHP_ROWS_WPB;        // waves per block
 constexpr int THREADS = 64 * WPB;
 constexpr int SUP = 16;                  // chunks per super-step: one per chain
 constexpr size_t STAGE_MAX = 80 * 1024;  // LDS for the staged activations of one block
 
-// LDS of one block: the staged pieces [W chunks][MR rows][XQ_DW] (row stride 26 words keeps the
-// four rows and three pieces an A-fragment read touches on distinct banks), then each row's
-// (sum, power of two) pairs [MR][W] so that a lane reads four chunks' pairs with two 16-byte reads.
 #define DHP_DEV_HOST_INLINE __host__ __device__ __forceinline__
 
-constexpr size_t stage_bytes_per_chunk(int MR) { return (size_t)MR * (XQ_DW * 4 + 8); }
+// LDS of one block: the staged groups [W/2 groups][MR rows][XG_DW], then each row's (sum, power
+// of two) pairs [MR][W/2] so that a lane reads two groups' pairs with one 16-byte read.
+constexpr size_t stage_bytes_per_chunk(int MR) { return (size_t)MR * (XG_DW * 4 + 8) / 2; }
 
 // Chunks per staging window for MR activation rows: all of K rounded up to 16 chunks when that fits
 // (all of K = 2560 at 8 rows), else a multiple of 32, so that windows start where a pair of
@@ -55,19 +58,20 @@ DHP_DEV_HOST_INLINE int window_chunks(int CH) {
     return all <= fit ? all : fit / (2 * SUP) * (2 * SUP);
 }
 
-// Stage chunks w0 .. w0+W-1 (those below CH) of activation rows m0 .. m0+MR-1 (rows past mr repeat
-// row mr - 1; their results are never stored).
+// Stage chunks w0 .. w0+W-1 (those below CH; W and w0 even) of activation rows m0 .. m0+MR-1 (rows
+// past mr repeat row mr - 1; their results are never stored).
 template <int MR>
 DHP_DEV void stage_window(uint32_t* xs, float2* sps, const _Float16* __restrict__ x, int m0, int mr, int K, int CH,
                           int w0, int W) {
     __syncthreads();                          // the previous window's reads are done
-    const int n = 4 * min(W, CH - w0) * MR;   // four lanes per (chunk, row)
+    const int WG = W / 2;
+    const int n = 8 * min(WG, (CH - w0) / 2) * MR;   // eight lanes per (group, row)
     for (int it = threadIdx.x; it < n; it += THREADS) {
-        const int item = it >> 2;
+        const int item = it >> 3;
         const int j = item / MR, r = item - j * MR;
         const int rs = r < mr ? r : mr - 1;
-        const float2 sp = xq_stage_quad(x + (size_t)(m0 + rs) * K + 32 * (w0 + j), it & 3, xs + (size_t)item * XQ_DW);
-        if ((it & 3) == 0) sps[r * W + j] = sp;
+        const float2 sp = xg_stage_octet(x + (size_t)(m0 + rs) * K + 32 * w0 + 64 * j, it & 7, xs + (size_t)item * XG_DW);
+        if ((it & 7) == 0) sps[r * WG + j] = sp;
     }
     __syncthreads();
 }
@@ -120,40 +124,37 @@ DHP_DEV void swap16(uint32_t& a, uint32_t& b) {
     b = r[1];
 }
 
-// The chains' steps for the 16 chunks of one super-step (chunk c0 + ci extends chain ci) for
-// MI groups of four activation rows; xw: the staged pieces of chunk c0, spw: row 0's pair of
-// chunk c0 (row r's at spw + r * W). Each quad of chunks reads all its LDS operands first, then
-// runs its 4 * MI matrix instructions, then their chain steps.
+// The chains' steps for the 8 groups of one super-step (group gi extends chain gi) for MI groups of
+// four activation rows; xw: the staged pieces of the super-step's first group, spw: row 0's pair
+// of that group (row r's at spw + r * WG). Each quad of chunks (two groups) reads its LDS operands
+// first, then runs its 2 * MI matrix instructions and their chain steps.
 template <int MI, bool TAIL>
-DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, int W, float (&acc)[MI][SUP], int c0,
-                     int CH, int lane) {
+DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, int WG, float (&acc)[MI][SUP / 2],
+                     int c0, int CH, int lane) {
     constexpr int MR = 4 * MI;
-    const int g = lane >> 4;                          // code word of a chunk; activation row of a result
-    const int a_off = ((lane & 15) >> 2) * XQ_DW + min(lane & 3, 2) * 8 + 2 * g;   // A fragment words
+    const int w = lane >> 4;                          // code word of a chunk; activation row of a result
+    const int a_off = ((lane & 15) >> 2) * XG_DW + min(lane & 3, 2) * 16 + 4 * w;   // A fragment words
     const uint32_t sv[4] = {l.s.x, l.s.y, l.s.z, l.s.w};
     const uint32_t bv[4] = {l.b.x, l.b.y, l.b.z, l.b.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         // one quad in registers at a time (the scheduler would interleave all of them)
         __builtin_amdgcn_sched_barrier(0);
-        long aq[4][MI];
-        float2 sp[4][MI];
+        i32x4 aq[2][MI];
+        float2 sp[2][MI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int e = 0; e < 2; ++e)
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
-                aq[i][mi] = *reinterpret_cast<const long*>(xw + (size_t)((4 * u + i) * MR + 4 * mi) * XQ_DW + a_off);
+                aq[e][mi] = *reinterpret_cast<const i32x4*>(xw + (size_t)((2 * u + e) * MR + 4 * mi) * XG_DW + a_off);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-            const float4* q = reinterpret_cast<const float4*>(spw + (4 * mi + g) * W + 4 * u);
-            const float4 v0 = q[0], v1 = q[1];
-            sp[0][mi] = float2{v0.x, v0.y};
-            sp[1][mi] = float2{v0.z, v0.w};
-            sp[2][mi] = float2{v1.x, v1.y};
-            sp[3][mi] = float2{v1.z, v1.w};
+            const float4 v = *reinterpret_cast<const float4*>(spw + (4 * mi + w) * WG + 2 * u);
+            sp[0][mi] = float2{v.x, v.y};
+            sp[1][mi] = float2{v.z, v.w};
         }
-        // lane (n, g) holds the four words of chunk c0 + 4u + g; afterwards word g of chunks
-        // c0 + 4u .. c0 + 4u + 3
+        // lane (n, w) holds the four words of chunk c0 + 4u + w; afterwards word w of chunks
+        // c0 + 4u .. c0 + 4u + 3 (groups 2u and 2u + 1 of the super-step)
         uint32_t r0 = l.c[u].x, r1 = l.c[u].y, r2 = l.c[u].z, r3 = l.c[u].w;
         swap32(r0, r2);
         swap32(r1, r3);
@@ -161,39 +162,41 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
         swap16(r2, r3);
         const uint32_t wv[4] = {r0, r1, r2, r3};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ci = 4 * u + i;
-            if (TAIL && c0 + ci >= CH) break;         // uniform: the row's last super-step is partial
-            uint32_t lo, hi;
-            unpack_i8(wv[i], lo, hi);
-            const long bq = (long)(((uint64_t)hi << 32) | lo);
-            const float s = half_bf16(sv[u], i >> 1);   // chunk ci is in group ci / 2 = 2u + i / 2
-            const float b = half_bf16(bv[u], i >> 1);
+        for (int e = 0; e < 2; ++e) {
+            const int gi = 2 * u + e;
+            if (TAIL && c0 + 2 * gi >= CH) break;     // uniform: the row's last super-step is partial
+            uint32_t lo0, hi0, lo1, hi1;
+            unpack_i8(wv[2 * e], lo0, hi0);
+            unpack_i8(wv[2 * e + 1], lo1, hi1);
+            const i32x4 bq = {(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+            const float s = half_bf16(sv[u], e);      // group gi = 2u + e: half e of word u
+            const float b = half_bf16(bv[u], e);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(aq[i][mi], bq, i32x4{0, 0, 0, 0}, 0, 0, 0);
-                acc[mi][ci] = xq_chunk_acc(acc[mi][ci], d[2] * 16384 + d[1] * 128 + d[0], s, b, sp[i][mi].x, sp[i][mi].y);
+                const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[e][mi], bq, i32x4{0, 0, 0, 0}, 0, 0, 0);
+                acc[mi][gi] = xg_group_acc(acc[mi][gi], d[2] * 16384 + d[1] * 128 + d[0], s, b, sp[e][mi].x, sp[e][mi].y);
             }
         }
     }
 }
 
-// Two waves per SIMD (two resident blocks per compute unit, which their LDS allows). ONE: all of
-// K fits one staging window, staged once per block before the first tile.
+// Two resident blocks per compute unit (their LDS allows two). ONE: all of K fits one staging
+// window, staged once per block before the first tile.
 template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemv_rows(
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 2, WPB / 2))) void k_gemv_rows(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const _Float16* __restrict__ x, int m0, int mr, int N, int K, void* __restrict__ y,
     float* __restrict__ part_v, int* __restrict__ part_i) {
     constexpr int MR = 4 * MI;
-    extern __shared__ __align__(16) uint32_t xs[];     // [W][MR][XQ_DW], then the pairs [MR][W]
+    extern __shared__ __align__(16) uint32_t xs[];     // [W/2][MR][XG_DW], then the pairs [MR][W/2]
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int CH = K >> 5, G = K >> 6;
     const int W = window_chunks<MR>(CH);
-    float2* sps = reinterpret_cast<float2*>(xs + (size_t)W * MR * XQ_DW);
+    const int WG = W / 2;
+    float2* sps = reinterpret_cast<float2*>(xs + (size_t)WG * MR * XG_DW);
     const int ngroups = ((N + 15) / 16 + WPB - 1) / WPB;
     if constexpr (ONE) stage_window<MR>(xs, sps, x, m0, mr, K, CH, 0, W);
 
@@ -204,8 +207,14 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
         best_v[mi] = -INFINITY;
         best_i[mi] = INT_MAX;
     }
-    for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {      // uniform over the block
-        const int r0 = (grp * WPB + wave) * 16;  // the tile's first row, uniform over the wave
+    // With all of K staged once, every wave walks its own tiles (wave-major over the grid, so the
+    // waves that take one tile more are spread over all blocks); otherwise the waves of a block
+    // walk groups of WPB tiles together, restaging at each window.
+    const int first = ONE ? wave * (int)gridDim.x + (int)blockIdx.x : (int)blockIdx.x;
+    const int lim = ONE ? (N + 15) / 16 : ngroups;
+    const int step = ONE ? WPB * (int)gridDim.x : (int)gridDim.x;
+    for (int it = first; it < lim; it += step) {
+        const int r0 = (ONE ? it : it * WPB + wave) * 16;   // the tile's first row, uniform over the wave
         const int row = r0 + n;
         const int ro = min(n, max(N - 1 - r0, 0));   // rows past N compute the last row again, unstored
         const u32x4* cb = codes + (size_t)min(r0, N - 1) * CH;
@@ -213,40 +222,47 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const uint16_t* bb = biases + (size_t)min(r0, N - 1) * G;
         const int lc = ro * CH, lg = ro * G;
 
-        float acc[MI][SUP];
+        float acc[MI][SUP / 2];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-            for (int j = 0; j < SUP; ++j) acc[mi][j] = 0.0f;
+            for (int j = 0; j < SUP / 2; ++j) acc[mi][j] = 0.0f;
 
+        // Super-steps in pairs, each loading the next while it computes; both loads of a pair are
+        // unconditional (a load used only under a branch is sunk into it and then waited for at
+        // once). A pair runs while its second super-step exists (the first is then whole; the
+        // second may be partial), and an odd last super-step runs after the loop on the set
+        // already loaded.
         SupRegs la, lb;
         load_sup<FULL>(la, cb, sb, bb, lc, lg, 0, g, CH, G);
         int w0 = ONE ? 0 : -W;
+        int c0 = 0;
 #pragma unroll 1
-        for (int c0 = 0; c0 < CH; c0 += 2 * SUP) {
+        for (; c0 + SUP < CH; c0 += 2 * SUP) {
             if (!ONE && c0 >= w0 + W) {          // the next staging window (only when K does not fit)
                 w0 = c0;
                 stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
             load_sup<FULL>(lb, cb, sb, bb, lc, lg, c0 + SUP, g, CH, G);
-            run_sup<MI, !FULL>(la, xs + (size_t)(c0 - w0) * MR * XQ_DW, sps + (c0 - w0), W, acc, c0, CH, lane);
-            const int c1 = c0 + SUP;
-            if (c1 < CH) {                       // uniform over the block
-                load_sup<FULL>(la, cb, sb, bb, lc, lg, c1 + SUP, g, CH, G);
-                run_sup<MI, !FULL>(lb, xs + (size_t)(c1 - w0) * MR * XQ_DW, sps + (c1 - w0), W, acc, c1, CH, lane);
+            run_sup<MI, false>(la, xs + (size_t)(c0 - w0) / 2 * MR * XG_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane);
+            load_sup<FULL>(la, cb, sb, bb, lc, lg, c0 + 2 * SUP, g, CH, G);
+            run_sup<MI, !FULL>(lb, xs + (size_t)(c0 + SUP - w0) / 2 * MR * XG_DW, sps + (c0 + SUP - w0) / 2, WG, acc,
+                               c0 + SUP, CH, lane);
+        }
+        if (c0 < CH) {                           // uniform: one (possibly partial) super-step left
+            if (!ONE && c0 >= w0 + W) {
+                w0 = c0;
+                stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
+            run_sup<MI, !FULL>(la, xs + (size_t)(c0 - w0) / 2 * MR * XG_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane);
         }
 
         // the chains meet in the M=1 kernels' butterfly order; lane (n, g) holds activation row
         // 4 mi + g of weight row n
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-            float p[8], q4[4];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) p[k] = acc[mi][2 * k] + acc[mi][2 * k + 1];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) q4[k] = p[2 * k] + p[2 * k + 1];
-            const float v = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+            const float v = ((acc[mi][0] + acc[mi][1]) + (acc[mi][2] + acc[mi][3])) +
+                            ((acc[mi][4] + acc[mi][5]) + (acc[mi][6] + acc[mi][7]));
             const int ar = 4 * mi + g;
             if (ar < mr && row < N) {
                 const size_t o = (size_t)(m0 + ar) * N + row;
@@ -318,13 +334,10 @@ hipError_t launch_rows_mi(bool f32, bool am, dim3 g, bool full, hipStream_t s, c
 }  // namespace
 
 // Blocks of the multi-row GEMV for N weight rows (also the argmax partials per activation row):
-// at most two resident blocks per compute unit, each taking the same number of tile groups.
+// at most two resident blocks per compute unit.
 int dhp_gemv_rows_blocks(int N, int cus) {
     const long groups = ((N + 15) / 16 + WPB - 1) / WPB;
-    long blocks = groups < 2L * cus ? groups : 2L * cus;
-    const long steps = (groups + blocks - 1) / blocks;
-    blocks = (groups + steps - 1) / steps;
-    return (int)blocks;
+    return (int)(groups < 2L * cus ? groups : 2L * cus);
 }
 
 int launch_gemv_rows(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
