@@ -148,10 +148,10 @@ DHP_DEV float dot32_f32(const u32x4 c, const float* x) {
 //   X_k  = P2 * 2^14 + P1 * 2^7 + P0 with P0, P1 in 0..127 and P2 in -128..127 (int8 pieces),
 //   D    = sum_k q_k X_k over the group's 4-bit codes (|D| < 64 * 15 * 2^21 < 2^31: int32, exact),
 //   the group's step of its chain: acc = fma(fma(s, float(D), b * float(sum_k X_k)), 2^(e-20), acc).
-// A staged group is XG_DW words: word 16p + 4w + 2h + r holds the bytes of X_p at
-// k = 32h + 8w + r + {0, 2, 4, 6} (piece p, chunk h of the group, code word w of the chunk,
-// parity r: the order in which unpack_i8 lays out the codes of word w), word 48 float(sum_k X_k),
-// word 49 2^(e-20), two words of padding (16-byte aligned groups).
+// The piece word (p, h, w, r) holds the bytes of X_p at k = 32h + 8w + r + {0, 2, 4, 6} (piece p,
+// chunk h of the group, code word w of the chunk, parity r: the order in which unpack_i8 lays out
+// the codes of word w). The M=1 kernels stage a group as XG_DW words: (p, h, w, r) at
+// 16p + 4w + 2h + r, then float(sum_k X_k) and 2^(e-20) at words 48 and 49, two words of padding.
 constexpr int XG_DW = 52;
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
@@ -161,10 +161,10 @@ DHP_DEV uint32_t pack_bytes(int a, int b, int c, int d) {
 }
 
 // Lanes 8t .. 8t+7 (all active, aligned to 8) convert one group: lane i = 0..7 reads k = 8i .. 8i+7
-// of xg (the group's 64 fp16 activations, 16-byte aligned) and writes its six piece words of dst
-// (8-byte aligned); lane 0 also writes the sum and the power of two, which every lane of the eight
-// returns. The activations must be finite.
-DHP_DEV float2 xg_stage_octet(const _Float16* __restrict__ xg, int i, uint32_t* __restrict__ dst) {
+// of xg (the group's 64 fp16 activations, 16-byte aligned), i.e. chunk h = i / 4, code word
+// w = i % 4, and writes its six piece words (p, h, w, r) at d[p * pstride + r] (d 8-byte aligned).
+// Every lane of the eight returns (float(sum_k X_k), 2^(e-20)). The activations must be finite.
+DHP_DEV float2 xg_stage_octet(const _Float16* __restrict__ xg, int i, uint32_t* __restrict__ d, int pstride) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(xg + 8 * i);
     // largest magnitude: fp16 magnitude bits order like the magnitudes
     const u16x2 m2 = __builtin_elementwise_max(
@@ -191,17 +191,17 @@ DHP_DEV float2 xg_stage_octet(const _Float16* __restrict__ xg, int i, uint32_t* 
     sx += __builtin_amdgcn_update_dpp(0, sx, 0xB1, 0xF, 0xF, false);
     sx += __builtin_amdgcn_update_dpp(0, sx, 0x4E, 0xF, 0xF, false);
     sx += __builtin_amdgcn_update_dpp(0, sx, 0x141, 0xF, 0xF, false);
-    uint32_t* d = dst + 4 * (i & 3) + 2 * (i >> 2);
+    uint32_t w[3][2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int a = X[r], b = X[2 + r], c = X[4 + r], e8 = X[6 + r];
-        d[r] = pack_bytes(a & 127, b & 127, c & 127, e8 & 127);
-        d[16 + r] = pack_bytes((a >> 7) & 127, (b >> 7) & 127, (c >> 7) & 127, (e8 >> 7) & 127);
-        d[32 + r] = pack_bytes(a >> 14, b >> 14, c >> 14, e8 >> 14);
+        w[0][r] = pack_bytes(a & 127, b & 127, c & 127, e8 & 127);
+        w[1][r] = pack_bytes((a >> 7) & 127, (b >> 7) & 127, (c >> 7) & 127, (e8 >> 7) & 127);
+        w[2][r] = pack_bytes(a >> 14, b >> 14, c >> 14, e8 >> 14);
     }
-    const float2 sp = {(float)sx, __builtin_bit_cast(float, (uint32_t)(107 + e) << 23)};   // 2^(e - 20)
-    if (i == 0) *reinterpret_cast<float2*>(dst + 48) = sp;
-    return sp;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) *reinterpret_cast<uint2*>(d + p * pstride) = uint2{w[p][0], w[p][1]};
+    return float2{(float)sx, __builtin_bit_cast(float, (uint32_t)(107 + e) << 23)};   // 2^(e - 20)
 }
 
 // The codes of one code word (k = 8w .. 8w+7 of a chunk, byte j: k = 2j low nibble, 2j + 1 high)
@@ -212,7 +212,7 @@ DHP_DEV void unpack_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
 }
 
 // One chunk's share of its group's exact sum: c the chunk's four code words, xq its 24 piece words
-// (word 8p + 2w + r = staged word 16p + 4w + 2h + r of the chunk's group).
+// (word 8p + 2w + r = piece word (p, h, w, r) of the chunk's group).
 DHP_DEV int dot32_i8(const u32x4 c, const uint32_t* xq) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     int s0 = 0, s1 = 0, s2 = 0;

@@ -8,7 +8,8 @@
 //
 //  * 16 lanes own one weight row. Lane j reads 16-byte code chunks j, j+16, j+32, ... of
 //    the row, so one load instruction of a 16-lane group covers 256 contiguous bytes and a
-//    wave streams four rows at once.
+//    wave streams four rows at once (ordinary loads: the streaming hint measured ~1 us slower
+//    on the LM head).
 //  * Per 64-weight group the affine form is factored: s * sum(q*x) + b * sum(x). The group's
 //    sum(q*x) is formed exactly on integers (the activations as three int8 pieces relative to
 //    the group's largest magnitude, v_dot4_i32_i8 over the codes; see xg_stage_octet), so its
@@ -50,7 +51,7 @@ DHP_DEV void load_row(const u32x4* __restrict__ codes, const uint16_t* __restric
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = j + LPR * i;
-        r[i].c = __builtin_nontemporal_load(cr + ch);
+        r[i].c = cr[ch];
         r[i].s = sr[ch >> 1];
         r[i].b = br[ch >> 1];
     }
@@ -81,8 +82,12 @@ DHP_DEV void block_argmax_write(float bv, int bi, bool leader, float* part_v, in
 
 // Stage the activations' group pieces (XG_DW words per group) into LDS, eight lanes per group.
 DHP_DEV void stage_x(const _Float16* __restrict__ x, int G, uint32_t* __restrict__ xs) {
-    for (int it = threadIdx.x; it < 8 * G; it += blockDim.x)
-        xg_stage_octet(x + (size_t)(it >> 3) * 64, it & 7, xs + (size_t)(it >> 3) * XG_DW);
+    for (int it = threadIdx.x; it < 8 * G; it += blockDim.x) {
+        const int i = it & 7;
+        uint32_t* dst = xs + (size_t)(it >> 3) * XG_DW;
+        const float2 sp = xg_stage_octet(x + (size_t)(it >> 3) * 64, i, dst + 4 * (i & 3) + 2 * (i >> 2), 16);
+        if (i == 0) *reinterpret_cast<float2*>(dst + 48) = sp;
+    }
     __syncthreads();
 }
 
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(MAX_BLOCK) void k_gemv_m1_lds(
         const uint16_t* br = biases + (size_t)row * G;
         float acc = 0.0f;
         for (int ch = j; ch < CH; ch += LPR) {
-            const u32x4 c = __builtin_nontemporal_load(cr + ch);
+            const u32x4 c = cr[ch];
             uint32_t xq[24];
             float2 sp;
             load_chunk_pieces(xs_dyn, ch, xq, sp);

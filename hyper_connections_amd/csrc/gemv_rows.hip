@@ -44,9 +44,13 @@ constexpr size_t STAGE_MAX = 80 * 1024;  // LDS for the staged activations of on
 
 #define DHP_DEV_HOST_INLINE __host__ __device__ __forceinline__
 
-// LDS of one block: the staged groups [W/2 groups][MR rows][XG_DW], then each row's (sum, power
-// of two) pairs [MR][W/2] so that a lane reads two groups' pairs with one 16-byte read.
-constexpr size_t stage_bytes_per_chunk(int MR) { return (size_t)MR * (XG_DW * 4 + 8) / 2; }
+// LDS of one block: the staged groups, then each row's (sum, power of two) pairs [MR][W/2] so that
+// a lane reads two groups' pairs with one 16-byte read. Group g of activation rows 4mi .. 4mi+3 is
+// one A operand block of AB_DW words laid out in lane order: the 16 bytes of piece word
+// (p, 0..1, w, 0..1) of row 4mi + a at word 4 (12w + 3a + p), so the lanes of one fragment read
+// consecutive 16-byte slots (slot p = 3 of a row repeats p = 2) without bank conflicts.
+constexpr int AB_DW = 4 * 4 * 3 * 4;
+constexpr size_t stage_bytes_per_chunk(int MR) { return (size_t)(MR / 4) * AB_DW * 4 / 2 + (size_t)MR * 4; }
 
 // Chunks per staging window for MR activation rows: all of K rounded up to 16 chunks when that fits
 // (all of K = 2560 at 8 rows), else a multiple of 32, so that windows start where a pair of
@@ -67,11 +71,12 @@ DHP_DEV void stage_window(uint32_t* xs, float2* sps, const _Float16* __restrict_
     const int WG = W / 2;
     const int n = 8 * min(WG, (CH - w0) / 2) * MR;   // eight lanes per (group, row)
     for (int it = threadIdx.x; it < n; it += THREADS) {
-        const int item = it >> 3;
+        const int item = it >> 3, i = it & 7;
         const int j = item / MR, r = item - j * MR;
         const int rs = r < mr ? r : mr - 1;
-        const float2 sp = xg_stage_octet(x + (size_t)(m0 + rs) * K + 32 * w0 + 64 * j, it & 7, xs + (size_t)item * XG_DW);
-        if ((it & 7) == 0) sps[r * WG + j] = sp;
+        uint32_t* d = xs + ((size_t)j * (MR / 4) + (r >> 2)) * AB_DW + 4 * (12 * (i & 3) + 3 * (r & 3)) + 2 * (i >> 2);
+        const float2 sp = xg_stage_octet(x + (size_t)(m0 + rs) * K + 32 * w0 + 64 * j, i, d, 4);
+        if (i == 0) sps[r * WG + j] = sp;
     }
     __syncthreads();
 }
@@ -88,18 +93,21 @@ struct SupRegs {
 // in chunks and in groups (32-bit lane offsets keep one register per address).
 template <bool FULL>
 DHP_DEV void load_sup(SupRegs& l, const u32x4* __restrict__ cb, const uint16_t* __restrict__ sb,
-                      const uint16_t* __restrict__ bb, int lc, int lg, int c0, int g, int CH, int G) {
+                      const uint16_t* __restrict__ bb, uint32_t lc, uint32_t lg, int c0, int g, int CH, int G) {
+    // Ordinary (not streaming) loads: one instruction reads 64 bytes of each of 16 rows, half a
+    // cache line, and the next instruction the other half, which then comes from the L1 instead
+    // of a second L2 request (streaming loads here took the M=8 LM head from 46 to 62 us).
 #pragma unroll
-    for (int u = 0; u < 4; ++u) l.c[u] = __builtin_nontemporal_load(cb + (lc + min(c0 + 4 * u + g, CH - 1)));
+    for (int u = 0; u < 4; ++u) l.c[u] = cb[lc + (uint32_t)min(c0 + 4 * u + g, CH - 1)];
     if constexpr (FULL) {
-        const int g0 = min(c0 >> 1, G - 8);       // the last super-step's loads (never used) stay in the row
+        const uint32_t g0 = (uint32_t)min(c0 >> 1, G - 8);   // the last super-step's loads (never used) stay in the row
         l.s = *reinterpret_cast<const u32x4*>(sb + (lg + g0));
         l.b = *reinterpret_cast<const u32x4*>(bb + (lg + g0));
     } else {
         uint32_t sw[4], bw[4];
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            const int g0 = min((c0 >> 1) + 2 * h, G - 1), g1 = min((c0 >> 1) + 2 * h + 1, G - 1);
+            const uint32_t g0 = (uint32_t)min((c0 >> 1) + 2 * h, G - 1), g1 = (uint32_t)min((c0 >> 1) + 2 * h + 1, G - 1);
             sw[h] = (uint32_t)sb[lg + g0] | ((uint32_t)sb[lg + g1] << 16);
             bw[h] = (uint32_t)bb[lg + g0] | ((uint32_t)bb[lg + g1] << 16);
         }
@@ -131,9 +139,8 @@ DHP_DEV void swap16(uint32_t& a, uint32_t& b) {
 template <int MI, bool TAIL>
 DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, int WG, float (&acc)[MI][SUP / 2],
                      int c0, int CH, int lane) {
-    constexpr int MR = 4 * MI;
     const int w = lane >> 4;                          // code word of a chunk; activation row of a result
-    const int a_off = ((lane & 15) >> 2) * XG_DW + min(lane & 3, 2) * 16 + 4 * w;   // A fragment words
+    const int a_off = 4 * (12 * w + 3 * ((lane & 15) >> 2) + min(lane & 3, 2));   // A fragment words
     const uint32_t sv[4] = {l.s.x, l.s.y, l.s.z, l.s.w};
     const uint32_t bv[4] = {l.b.x, l.b.y, l.b.z, l.b.w};
 #pragma unroll
@@ -146,7 +153,7 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
         for (int e = 0; e < 2; ++e)
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
-                aq[e][mi] = *reinterpret_cast<const i32x4*>(xw + (size_t)((2 * u + e) * MR + 4 * mi) * XG_DW + a_off);
+                aq[e][mi] = *reinterpret_cast<const i32x4*>(xw + (size_t)((2 * u + e) * MI + mi) * AB_DW + a_off);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
             const float4 v = *reinterpret_cast<const float4*>(spw + (4 * mi + w) * WG + 2 * u);
@@ -180,15 +187,16 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
     }
 }
 
-// Two resident blocks per compute unit (their LDS allows two). ONE: all of K fits one staging
-// window, staged once per block before the first tile.
+// Two resident blocks per compute unit (their LDS allows two); with a partial last super-step the
+// selects need more registers, so one block. ONE: all of K fits one staging window, staged once
+// per block before the first tile.
 template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 2, WPB / 2))) void k_gemv_rows(
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? WPB / 2 : WPB / 4, FULL ? WPB / 2 : WPB / 4))) void k_gemv_rows(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const _Float16* __restrict__ x, int m0, int mr, int N, int K, void* __restrict__ y,
     float* __restrict__ part_v, int* __restrict__ part_i) {
     constexpr int MR = 4 * MI;
-    extern __shared__ __align__(16) uint32_t xs[];     // [W/2][MR][XG_DW], then the pairs [MR][W/2]
+    extern __shared__ __align__(16) uint32_t xs[];     // [W/2][MI][AB_DW], then the pairs [MR][W/2]
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 2
     const int CH = K >> 5, G = K >> 6;
     const int W = window_chunks<MR>(CH);
     const int WG = W / 2;
-    float2* sps = reinterpret_cast<float2*>(xs + (size_t)WG * MR * XG_DW);
+    float2* sps = reinterpret_cast<float2*>(xs + (size_t)WG * MI * AB_DW);
     const int ngroups = ((N + 15) / 16 + WPB - 1) / WPB;
     if constexpr (ONE) stage_window<MR>(xs, sps, x, m0, mr, K, CH, 0, W);
 
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 2
         const u32x4* cb = codes + (size_t)min(r0, N - 1) * CH;
         const uint16_t* sb = scales + (size_t)min(r0, N - 1) * G;
         const uint16_t* bb = biases + (size_t)min(r0, N - 1) * G;
-        const int lc = ro * CH, lg = ro * G;
+        const uint32_t lc = (uint32_t)(ro * CH), lg = (uint32_t)(ro * G);
 
         float acc[MI][SUP / 2];
 #pragma unroll
@@ -244,9 +252,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 2
                 stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
             load_sup<FULL>(lb, cb, sb, bb, lc, lg, c0 + SUP, g, CH, G);
-            run_sup<MI, false>(la, xs + (size_t)(c0 - w0) / 2 * MR * XG_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane);
+            run_sup<MI, false>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane);
             load_sup<FULL>(la, cb, sb, bb, lc, lg, c0 + 2 * SUP, g, CH, G);
-            run_sup<MI, !FULL>(lb, xs + (size_t)(c0 + SUP - w0) / 2 * MR * XG_DW, sps + (c0 + SUP - w0) / 2, WG, acc,
+            run_sup<MI, !FULL>(lb, xs + (size_t)(c0 + SUP - w0) / 2 * MI * AB_DW, sps + (c0 + SUP - w0) / 2, WG, acc,
                                c0 + SUP, CH, lane);
         }
         if (c0 < CH) {                           // uniform: one (possibly partial) super-step left
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 2
                 w0 = c0;
                 stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
-            run_sup<MI, !FULL>(la, xs + (size_t)(c0 - w0) / 2 * MR * XG_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane);
+            run_sup<MI, !FULL>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane);
         }
 
         // the chains meet in the M=1 kernels' butterfly order; lane (n, g) holds activation row
