@@ -98,8 +98,10 @@ typedef struct dhp_int4_experts {
  * call over the vocabulary, with argmax.
  * Every row r of an m-row call gives exactly the bits (y and argmax) of an m = 1 call on row r
  * alone, for any weights and biases: both run each output as s * (q . x) + b * sum(x) per
- * 64-weight group in fp32, in one fixed operation order (see decodehp_dequant_gemv_mc for the
- * matrix-core arm, which does not).
+ * 64-weight group, with q . x an exact integer sum (the group's activations taken to 21 bits
+ * of its largest magnitude; every activation within 2^10 of it exactly) and the groups joined
+ * in fp32 in one fixed operation order (see decodehp_dequant_gemv_mc for the fp16
+ * matrix-core arm, which does not). The activations must be finite.
  *   w       : weight [N x K].
  *   x       : fp16 [m][K], row-major, 16-byte aligned.
  *   y       : [m][N] row-major, fp16 (y_dtype DHP_F16) or fp32 (DHP_F32); fp32 accumulate.

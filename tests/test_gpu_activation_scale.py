@@ -1,6 +1,7 @@
-"""GPU parity at large activations: every call whose dot products run on the offset code form
-(t = 1024 + 16 q, the accumulator started at -1024 sum(x)) against the fp64 oracle with the
-activations scaled up, where that form's rounding (proportional to |x|) is largest.
+"""GPU parity at large activations against the fp64 oracle: the GEMV calls (exact integer group
+sums of the codes with the activations taken to 21 bits of their group's largest magnitude) and
+the MoE calls (whose dots run on the offset code form t = 1024 + 16 q with the accumulator
+started at -1024 sum(x), a rounding proportional to |x|), with the activations scaled up.
 
 Bar: |gpu - oracle| <= 1e-3 + 1e-2 |oracle| elementwise, argmax and expert ids exact. Scales:
 activation standard deviation 8 and 32, and N(0, 1) activations with sixteen channels set to
