@@ -87,8 +87,8 @@ DHP_DEV void load_pair(PairRegs<CPL>& p, const u32x4* gc, const uint16_t* gs, co
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int ch = j + LPR * i;
-        p.cg[i] = gc[(size_t)row * CH + ch];
-        p.cu[i] = uc[(size_t)row * CH + ch];
+        p.cg[i] = __builtin_nontemporal_load(gc + (size_t)row * CH + ch);
+        p.cu[i] = __builtin_nontemporal_load(uc + (size_t)row * CH + ch);
         p.sg[i] = gs[(size_t)row * G + (ch >> 1)];
         p.bg[i] = gb[(size_t)row * G + (ch >> 1)];
         p.su[i] = us[(size_t)row * G + (ch >> 1)];
@@ -137,13 +137,13 @@ DHP_DEV void router_row_load(RouterRow<CPL, KIND>& r, const void* row) {
     if constexpr (KIND != RK_I8) {
         const u32x4* p = static_cast<const u32x4*>(row);
 #pragma unroll
-        for (int i = 0; i < (KIND == RK_F32 ? 2 * CPL : CPL); ++i) r.w[i] = p[lane + 64 * i];
+        for (int i = 0; i < (KIND == RK_F32 ? 2 * CPL : CPL); ++i) r.w[i] = __builtin_nontemporal_load(p + lane + 64 * i);
     } else {
         typedef uint32_t u32x2n __attribute__((ext_vector_type(2)));
         const u32x2n* p = static_cast<const u32x2n*>(row);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const u32x2n q = p[lane + 64 * i];
+            const u32x2n q = __builtin_nontemporal_load(p + lane + 64 * i);
             r.w[i] = u32x4{q.x, q.y, 0u, 0u};
         }
     }
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(64 * P2W) void k_moe_phase2(MoeArgs a) {
 #pragma unroll
                 for (int i = 0; i < CPLD; ++i) {
                     const int ch = min(j + LPR * i, CH - 1);
-                    c[t][r][i] = dc[(size_t)h * CH + ch];
+                    c[t][r][i] = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
                     sv[t][r][i] = ds[(size_t)h * G + (ch >> 1)];
                     bv[t][r][i] = db[(size_t)h * G + (ch >> 1)];
                 }
@@ -966,7 +966,7 @@ __global__ __launch_bounds__(256) void k_moep_phase2(MoeArgs a) {
 #pragma unroll
             for (int i = 0; i < CPLD; ++i) {
                 const int ch = min(j + LPR * i, CH - 1);
-                c[q][r][i] = dc[(size_t)h * CH + ch];
+                c[q][r][i] = __builtin_nontemporal_load(dc + (size_t)h * CH + ch);
                 sv[q][r][i] = ds[(size_t)h * G + (ch >> 1)];
                 bv[q][r][i] = db[(size_t)h * G + (ch >> 1)];
             }
