@@ -789,6 +789,8 @@ def main():
     ap.add_argument("--ring", type=int, default=8, help="rotating copies of each small weight set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-call", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="with --only: evict the last-level cache before every launch (median over launches)")
     ap.add_argument("--copy-probe", action="store_true", help="also time a plain 1 GiB copy (counter scaling)")
     ap.add_argument("--only", choices=CALLS + ("copy",),
                     help="launch just this call (or the plain 1 GiB copy) --steps times after --warmup, and "
@@ -842,7 +844,12 @@ def main():
             nbytes["moe_prefill"] = chunk_bytes(torch, W, calls)
         for i in range(args.warmup):
             run_call(calls[args.only][i % len(calls[args.only])])
-        r = per_call_pass(torch, calls, nbytes, iters=args.steps, exact=True)[args.only]
+        if args.cold:
+            flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+            r = cold_call_pass(torch, hca, calls, nbytes, flush, None, reps=args.steps)[args.only]
+            r["cold"] = True
+        else:
+            r = per_call_pass(torch, calls, nbytes, iters=args.steps, exact=True)[args.only]
         print(json.dumps({"only": args.only, "algorithmic_bytes": nbytes[args.only], **r}), flush=True)
         return
 
