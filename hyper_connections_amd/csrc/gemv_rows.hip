@@ -16,13 +16,15 @@
 //    its result is unused), so lane (n, a) receives row a's three piece sums for weight row n and
 //    joins them (D = P2 * 2^14 + P1 * 2^7 + P0, exact). Eight activation rows take two
 //    instructions.
-//  * Codes stream as 16-byte loads: lane (n, w) loads chunk c0 + 4u + w of its row (four lanes
-//    read 64 contiguous bytes), and two swaps across the wave halves (v_permlane32_swap) and two
-//    across neighbouring 16-lane rows (v_permlane16_swap) transpose each 4 x 4 block so that lane
-//    (n, w) holds code word w of the four chunks. A super-step is 16 chunks (8 groups, one per
-//    chain); the next super-step's codes, scales and biases are in flight while one computes.
+//  * Codes stream as in the M=1 kernels: 16 lanes read 256 contiguous bytes of one row (16-byte
+//    nontemporal loads, four rows per instruction), each lane with the scale and bias of its own
+//    chunk. A super-step is 16 chunks of the tile's 16 rows (8 groups, one per chain); the next
+//    one is in flight while one computes. A small LDS region per wave turns it around: lane
+//    (n, w) reads back chunk c0 + 4u + w of row n, and two swaps across the wave halves
+//    (v_permlane32_swap) and two across neighbouring 16-lane rows (v_permlane16_swap) transpose
+//    each 4 x 4 block so that lane (n, w) holds code word w of the four chunks.
 //  * The activations' pieces (xg_stage_octet, the same conversion as the M=1 kernels) are staged
-//    once per block in LDS; blocks stay resident and walk groups of tiles with a grid stride.
+//    once per block in LDS; one block of twelve waves per compute unit, walking tiles.
 //  * Each chain's steps run in group order, and the final butterfly adds the chains in the M=1
 //    kernels' order (addition is commutative, so each pair gives the same bits either way round).
 #include "dhp_internal.hpp"
@@ -35,12 +37,18 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 namespace {
 
 #ifndef DHP_ROWS_WPB
-#define DHP_ROWS_WPB 8
+#define DHP_ROWS_WPB 12
 #endif
 constexpr int WPB = DHP_ROWS_WPB;        // waves per block
 constexpr int THREADS = 64 * WPB;
 constexpr int SUP = 16;                  // chunks per super-step: one per chain
 constexpr size_t STAGE_MAX = 80 * 1024;  // LDS for the staged activations of one block
+// One wave's turnaround region in LDS: the super-step's codes (16 rows of 16 chunks, rows padded
+// by 16 bytes so that the 16-byte reads of eight rows hit distinct banks) and the scale and bias
+// words (16 rows of 8 groups; a 40-byte row pitch keeps 16 rows' 8-byte reads on distinct banks).
+constexpr int TR_PITCH = 272;
+constexpr int SB_PITCH = 40;
+constexpr int TR_BYTES = 16 * TR_PITCH + 16 * SB_PITCH;
 
 #define DHP_DEV_HOST_INLINE __host__ __device__ __forceinline__
 
@@ -51,6 +59,8 @@ constexpr size_t STAGE_MAX = 80 * 1024;  // LDS for the staged activations of on
 // consecutive 16-byte slots (slot p = 3 of a row repeats p = 2) without bank conflicts.
 constexpr int AB_DW = 4 * 4 * 3 * 4;
 constexpr size_t stage_bytes_per_chunk(int MR) { return (size_t)(MR / 4) * AB_DW * 4 / 2 + (size_t)MR * 4; }
+// Bytes of a staging window of W chunks, rounded up to 16 (the turnaround regions follow).
+DHP_DEV_HOST_INLINE size_t stage_bytes(int MR, int W) { return ((size_t)W * stage_bytes_per_chunk(MR) + 15) / 16 * 16; }
 
 // Chunks per staging window for MR activation rows: all of K rounded up to 16 chunks when that fits
 // (all of K = 2560 at 8 rows), else a multiple of 32, so that windows start where a pair of
@@ -78,46 +88,36 @@ DHP_DEV void stage_window(uint32_t* xs, float2* sps, const _Float16* __restrict_
         const float2 sp = xg_stage_octet(x + (size_t)(m0 + rs) * K + 32 * w0 + 64 * j, i, d, 4);
         if (i == 0) sps[r * WG + j] = sp;
     }
+    // groups past the row (the padding of a last, partial super-step): zero pieces and pairs, so
+    // that their products are exact zeros
+    const int jr = min(WG, (CH - w0) / 2);
+    const int nz = (WG - jr) * (MR / 4) * AB_DW;
+    for (int it = threadIdx.x; it < nz; it += THREADS) xs[(size_t)jr * (MR / 4) * AB_DW + it] = 0u;
+    for (int it = threadIdx.x; it < (WG - jr) * MR; it += THREADS)
+        sps[(it / (WG - jr)) * WG + jr + it % (WG - jr)] = float2{0.0f, 0.0f};
     __syncthreads();
 }
 
-// One super-step of one lane: 16 chunks' codes (lane g of row n holds chunk c0 + 4u + g in c[u])
-// and the scales and biases of their 8 groups, two bf16 per word. Chunks past the row are clamped
-// to its last chunk (loaded, never used). With FULL (K % 512 == 0 and 16-byte aligned scale and
-// bias arrays) the 8 groups are one 16-byte load each.
+// One super-step of one lane as loaded: lane (g, j) holds chunk c0 + j of tile row 4u + g in c[u],
+// and that chunk's group scale (low half) and bias (high half) in sb[u]. Rows past N are clamped
+// to the last row (computed again, never stored); chunks past the row to its last chunk.
+typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
 struct SupRegs {
     u32x4 c[4];
-    u32x4 s, b;
+    u16x2v sb[4];
 };
-// cb, sb, bb: the tile's first row (uniform over the wave); lc, lg: this lane's row offset from it
-// in chunks and in groups (32-bit lane offsets keep one register per address).
-template <bool FULL>
+// cb, sb, bb: the tile's first row (uniform over the wave); rmax: the tile's last real row.
 DHP_DEV void load_sup(SupRegs& l, const u32x4* __restrict__ cb, const uint16_t* __restrict__ sb,
-                      const uint16_t* __restrict__ bb, uint32_t lc, uint32_t lg, int c0, int g, int CH, int G) {
-    // Ordinary (not streaming) loads: one instruction reads 64 bytes of each of 16 rows, half a
-    // cache line, and the next instruction the other half, which then comes from the L1 instead
-    // of a second L2 request (streaming loads here took the M=8 LM head from 46 to 62 us).
+                      const uint16_t* __restrict__ bb, int rmax, int c0, int g, int j, int CH, int G) {
+    const int ch = min(c0 + j, CH - 1);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) l.c[u] = cb[lc + (uint32_t)min(c0 + 4 * u + g, CH - 1)];
-    if constexpr (FULL) {
-        const uint32_t g0 = (uint32_t)min(c0 >> 1, G - 8);   // the last super-step's loads (never used) stay in the row
-        l.s = *reinterpret_cast<const u32x4*>(sb + (lg + g0));
-        l.b = *reinterpret_cast<const u32x4*>(bb + (lg + g0));
-    } else {
-        uint32_t sw[4], bw[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const uint32_t g0 = (uint32_t)min((c0 >> 1) + 2 * h, G - 1), g1 = (uint32_t)min((c0 >> 1) + 2 * h + 1, G - 1);
-            sw[h] = (uint32_t)sb[lg + g0] | ((uint32_t)sb[lg + g1] << 16);
-            bw[h] = (uint32_t)bb[lg + g0] | ((uint32_t)bb[lg + g1] << 16);
-        }
-        l.s = u32x4{sw[0], sw[1], sw[2], sw[3]};
-        l.b = u32x4{bw[0], bw[1], bw[2], bw[3]};
+    for (int u = 0; u < 4; ++u) {
+        const int r = min(4 * u + g, rmax);
+        l.c[u] = __builtin_nontemporal_load(cb + (uint32_t)(r * CH + ch));
+        const uint32_t o = (uint32_t)(r * G + (ch >> 1));
+        l.sb[u] = u16x2v{sb[o], bb[o]};
     }
 }
-
-// group h (0, 1) of a word: its scale or bias as fp32
-DHP_DEV float half_bf16(uint32_t w, int h) { return __builtin_bit_cast(float, h ? (w & 0xFFFF0000u) : (w << 16)); }
 
 // v_permlane32_swap: a's upper 32 lanes trade places with b's lower 32 lanes.
 DHP_DEV void swap32(uint32_t& a, uint32_t& b) {
@@ -134,15 +134,45 @@ DHP_DEV void swap16(uint32_t& a, uint32_t& b) {
 
 // The chains' steps for the 8 groups of one super-step (group gi extends chain gi) for MI groups of
 // four activation rows; xw: the staged pieces of the super-step's first group, spw: row 0's pair
-// of that group (row r's at spw + r * WG). Each quad of chunks (two groups) reads its LDS operands
-// first, then runs its 2 * MI matrix instructions and their chain steps.
-template <int MI, bool TAIL>
+// of that group (row r's at spw + r * WG); tw: the wave's turnaround region. Each quad of chunks
+// (two groups) reads its LDS operands first, then runs its 2 * MI matrix instructions and their
+// chain steps.
+//
+// PAD (K % 512 != 0): the row's last super-step runs past the row. Its padding groups have zero
+// staged pieces and pairs (so D = 0, sum 0, power of two 0) and get -0 as scale and bias, so each
+// of their steps is fma(fma(-0, 0, -0 * 0), 0, acc) = acc + (-0), which is acc for every acc,
+// zeros of either sign included: the chains take the same values as in the M=1 kernels.
+template <int MI, bool PAD>
 DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, int WG, float (&acc)[MI][SUP / 2],
-                     int c0, int CH, int lane) {
+                     int c0, int CH, int lane, uint8_t* tw) {
     const int w = lane >> 4;                          // code word of a chunk; activation row of a result
-    const int a_off = 4 * (12 * w + 3 * ((lane & 15) >> 2) + min(lane & 3, 2));   // A fragment words
-    const uint32_t sv[4] = {l.s.x, l.s.y, l.s.z, l.s.w};
-    const uint32_t bv[4] = {l.b.x, l.b.y, l.b.z, l.b.w};
+    const int j = lane & 15;
+    const int a_off = 4 * (12 * w + 3 * (j >> 2) + min(lane & 3, 2));   // A fragment words
+    // turnaround: lane (w, j) wrote chunk c0 + j of tile rows 4u + w; lane (n = j, w) reads back
+    // chunk c0 + 4u + w of row n, and the scale and bias words of groups 2u, 2u + 1 of row n
+    u32x4 cq[4];
+    uint2 sbq[4];
+    uint8_t* tsb = tw + 16 * TR_PITCH;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(tw + (4 * u + w) * TR_PITCH + 16 * j) = l.c[u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        uint32_t pk = __builtin_bit_cast(uint32_t, l.sb[u]);
+        if (PAD && c0 + j >= CH) pk = 0x80008000u;    // -0 scale and bias for a padding group
+        // both lanes of a group write the same word
+        *reinterpret_cast<uint32_t*>(tsb + (4 * u + w) * SB_PITCH + 4 * (j >> 1)) = pk;
+    }
+    // the region is the wave's own: its LDS operations complete in order, so only the compiler
+    // must not move the reads above the writes
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cq[u] = *reinterpret_cast<const u32x4*>(tw + j * TR_PITCH + 16 * (4 * u + w));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sbq[u] = *reinterpret_cast<const uint2*>(tsb + j * SB_PITCH + 8 * u);
+    // and the next super-step's writes must not move above these reads
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         // one quad in registers at a time (the scheduler would interleave all of them)
@@ -162,7 +192,7 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
         }
         // lane (n, w) holds the four words of chunk c0 + 4u + w; afterwards word w of chunks
         // c0 + 4u .. c0 + 4u + 3 (groups 2u and 2u + 1 of the super-step)
-        uint32_t r0 = l.c[u].x, r1 = l.c[u].y, r2 = l.c[u].z, r3 = l.c[u].w;
+        uint32_t r0 = cq[u].x, r1 = cq[u].y, r2 = cq[u].z, r3 = cq[u].w;
         swap32(r0, r2);
         swap32(r1, r3);
         swap16(r0, r1);
@@ -171,13 +201,13 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int gi = 2 * u + e;
-            if (TAIL && c0 + 2 * gi >= CH) break;     // uniform: the row's last super-step is partial
             uint32_t lo0, hi0, lo1, hi1;
             unpack_i8(wv[2 * e], lo0, hi0);
             unpack_i8(wv[2 * e + 1], lo1, hi1);
             const i32x4 bq = {(int)lo0, (int)hi0, (int)lo1, (int)hi1};
-            const float s = half_bf16(sv[u], e);      // group gi = 2u + e: half e of word u
-            const float b = half_bf16(bv[u], e);
+            const uint32_t sbw = e ? sbq[u].y : sbq[u].x;   // group gi: scale low, bias high (bf16)
+            const float s = __builtin_bit_cast(float, sbw << 16);
+            const float b = __builtin_bit_cast(float, sbw & 0xFFFF0000u);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[e][mi], bq, i32x4{0, 0, 0, 0}, 0, 0, 0);
@@ -187,11 +217,11 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
     }
 }
 
-// Two resident blocks per compute unit (their LDS allows two); with a partial last super-step the
-// selects need more registers, so one block. ONE: all of K fits one staging window, staged once
-// per block before the first tile.
+// One resident block per compute unit (the staged activations and the waves' turnaround regions
+// need more than half its LDS). FULL: K % 512 == 0, no padding groups. ONE: all of K fits one
+// staging window, staged once per block before the first tile.
 template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? WPB / 2 : WPB / 4, FULL ? WPB / 2 : WPB / 4))) void k_gemv_rows(
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 4, WPB / 4))) void k_gemv_rows(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const _Float16* __restrict__ x, int m0, int mr, int N, int K, void* __restrict__ y,
     float* __restrict__ part_v, int* __restrict__ part_i) {
@@ -205,6 +235,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? 
     const int W = window_chunks<MR>(CH);
     const int WG = W / 2;
     float2* sps = reinterpret_cast<float2*>(xs + (size_t)WG * MI * AB_DW);
+    uint8_t* tw = reinterpret_cast<uint8_t*>(xs) + stage_bytes(MR, W) + (size_t)wave * TR_BYTES;
     const int ngroups = ((N + 15) / 16 + WPB - 1) / WPB;
     if constexpr (ONE) stage_window<MR>(xs, sps, x, m0, mr, K, CH, 0, W);
 
@@ -224,11 +255,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? 
     for (int it = first; it < lim; it += step) {
         const int r0 = (ONE ? it : it * WPB + wave) * 16;   // the tile's first row, uniform over the wave
         const int row = r0 + n;
-        const int ro = min(n, max(N - 1 - r0, 0));   // rows past N compute the last row again, unstored
-        const u32x4* cb = codes + (size_t)min(r0, N - 1) * CH;
-        const uint16_t* sb = scales + (size_t)min(r0, N - 1) * G;
-        const uint16_t* bb = biases + (size_t)min(r0, N - 1) * G;
-        const uint32_t lc = (uint32_t)(ro * CH), lg = (uint32_t)(ro * G);
+        // the tile's rows past N repeat row N - 1 (a block's last group of tiles may start past N)
+        const int rb = min(r0, N - 1), rmax = max(N - 1 - r0, 0);
+        const u32x4* cb = codes + (size_t)rb * CH;
+        const uint16_t* sb = scales + (size_t)rb * G;
+        const uint16_t* bb = biases + (size_t)rb * G;
 
         float acc[MI][SUP / 2];
 #pragma unroll
@@ -242,7 +273,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? 
         // second may be partial), and an odd last super-step runs after the loop on the set
         // already loaded.
         SupRegs la, lb;
-        load_sup<FULL>(la, cb, sb, bb, lc, lg, 0, g, CH, G);
+        load_sup(la, cb, sb, bb, rmax, 0, g, n, CH, G);
         int w0 = ONE ? 0 : -W;
         int c0 = 0;
 #pragma unroll 1
@@ -251,18 +282,18 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? 
                 w0 = c0;
                 stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
-            load_sup<FULL>(lb, cb, sb, bb, lc, lg, c0 + SUP, g, CH, G);
-            run_sup<MI, false>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane);
-            load_sup<FULL>(la, cb, sb, bb, lc, lg, c0 + 2 * SUP, g, CH, G);
+            load_sup(lb, cb, sb, bb, rmax, c0 + SUP, g, n, CH, G);
+            run_sup<MI, false>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane, tw);
+            load_sup(la, cb, sb, bb, rmax, c0 + 2 * SUP, g, n, CH, G);
             run_sup<MI, !FULL>(lb, xs + (size_t)(c0 + SUP - w0) / 2 * MI * AB_DW, sps + (c0 + SUP - w0) / 2, WG, acc,
-                               c0 + SUP, CH, lane);
+                               c0 + SUP, CH, lane, tw);
         }
         if (c0 < CH) {                           // uniform: one (possibly partial) super-step left
             if (!ONE && c0 >= w0 + W) {
                 w0 = c0;
                 stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
-            run_sup<MI, !FULL>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane);
+            run_sup<MI, !FULL>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane, tw);
         }
 
         // the chains meet in the M=1 kernels' butterfly order; lane (n, g) holds activation row
@@ -313,11 +344,30 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FULL ? 
     }
 }
 
+// Dynamic LDS above 64 KiB must be allowed once per kernel and device.
+template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE>
+hipError_t allow_lds(size_t lds) {
+    static unsigned long long configured = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & bit) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_rows<MI, F32OUT, ARGMAX, FULL, ONE>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess) __atomic_fetch_or(&configured, bit, __ATOMIC_RELEASE);
+    return e;
+}
+
 template <int MI, bool FULL, bool ONE>
 hipError_t launch_rows_full(bool f32, bool am, dim3 g, size_t lds, hipStream_t s, const u32x4* c, const uint16_t* sc,
                             const uint16_t* bi, const _Float16* x, int m0, int mr, int N, int K, void* y, float* pv,
                             int* pi) {
     const dim3 b(THREADS);
+    const hipError_t e = f32 && am ? allow_lds<MI, true, true, FULL, ONE>(lds)
+                         : f32     ? allow_lds<MI, true, false, FULL, ONE>(lds)
+                         : am      ? allow_lds<MI, false, true, FULL, ONE>(lds)
+                                   : allow_lds<MI, false, false, FULL, ONE>(lds);
+    if (e != hipSuccess) return e;
     if (f32 && am) hipLaunchKernelGGL((k_gemv_rows<MI, true, true, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
     else if (f32) hipLaunchKernelGGL((k_gemv_rows<MI, true, false, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
     else if (am) hipLaunchKernelGGL((k_gemv_rows<MI, false, true, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
@@ -331,7 +381,7 @@ hipError_t launch_rows_mi(bool f32, bool am, dim3 g, bool full, hipStream_t s, c
                           int* pi) {
     const int CH = K >> 5;
     const int W = window_chunks<4 * MI>(CH);
-    const size_t lds = (size_t)W * stage_bytes_per_chunk(4 * MI);
+    const size_t lds = stage_bytes(4 * MI, W) + (size_t)WPB * TR_BYTES;
     const bool one = CH <= W;
     if (full && one) return launch_rows_full<MI, true, true>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
     if (full) return launch_rows_full<MI, true, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
@@ -342,10 +392,10 @@ hipError_t launch_rows_mi(bool f32, bool am, dim3 g, bool full, hipStream_t s, c
 }  // namespace
 
 // Blocks of the multi-row GEMV for N weight rows (also the argmax partials per activation row):
-// at most two resident blocks per compute unit.
+// one resident block per compute unit.
 int dhp_gemv_rows_blocks(int N, int cus) {
     const long groups = ((N + 15) / 16 + WPB - 1) / WPB;
-    return (int)(groups < 2L * cus ? groups : 2L * cus);
+    return (int)(groups < (long)cus ? groups : (long)cus);
 }
 
 int launch_gemv_rows(const dhp_int4* w, const void* x, int M, void* y, int y_f32, int32_t* argmax, void* ws,
@@ -362,7 +412,7 @@ int launch_gemv_rows(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     const auto* bi = static_cast<const uint16_t*>(w->biases);
     const auto* xh = static_cast<const _Float16*>(x);
     const bool am = argmax != nullptr;
-    const bool full = K % 512 == 0 && ((uintptr_t)sc % 16) == 0 && ((uintptr_t)bi % 16) == 0;
+    const bool full = K % 512 == 0;              // whole super-steps only
     const dim3 g((unsigned)nb);
     // activation rows in passes of up to 8 (each pass streams the weights once)
     for (int m0 = 0; m0 < M; m0 += 8) {
