@@ -43,12 +43,17 @@ constexpr int WPB = DHP_ROWS_WPB;        // waves per block
 constexpr int THREADS = 64 * WPB;
 constexpr int SUP = 16;                  // chunks per super-step: one per chain
 constexpr size_t STAGE_MAX = 80 * 1024;  // LDS for the staged activations of one block
-// One wave's turnaround region in LDS: the super-step's codes (16 rows of 16 chunks, rows padded
-// by 16 bytes so that the 16-byte reads of eight rows hit distinct banks) and the scale and bias
-// words (16 rows of 8 groups; a 40-byte row pitch keeps 16 rows' 8-byte reads on distinct banks).
+// One wave's region in LDS: the super-step's codes (16 rows of 16 chunks, rows padded by 16 bytes
+// so that the 16-byte reads of eight rows hit distinct banks), then either
+//  * the tile's scales and biases as one block (SBT: [scales 16 rows x G][biases 16 rows x G],
+//    bf16, at most SBT_MAX bytes), written once per tile, or
+//  * the super-step's scale and bias words (16 rows of 8 groups; a 40-byte row pitch keeps 16
+//    rows' 8-byte reads on distinct banks), written every super-step.
 constexpr int TR_PITCH = 272;
 constexpr int SB_PITCH = 40;
-constexpr int TR_BYTES = 16 * TR_PITCH + 16 * SB_PITCH;
+constexpr int TR_CODES = 16 * TR_PITCH;
+constexpr int SBT_MAX = 3072;
+template <bool SBT> constexpr int region_bytes() { return TR_CODES + (SBT ? SBT_MAX : 16 * SB_PITCH); }
 
 #define DHP_DEV_HOST_INLINE __host__ __device__ __forceinline__
 
@@ -106,7 +111,9 @@ struct SupRegs {
     u32x4 c[4];
     u16x2v sb[4];
 };
-// cb, sb, bb: the tile's first row (uniform over the wave); rmax: the tile's last real row.
+// cb, sb, bb: the tile's first row (uniform over the wave); rmax: the tile's last real row. With
+// SBT the scales and biases come from the tile block instead.
+template <bool SBT>
 DHP_DEV void load_sup(SupRegs& l, const u32x4* __restrict__ cb, const uint16_t* __restrict__ sb,
                       const uint16_t* __restrict__ bb, int rmax, int c0, int g, int j, int CH, int G) {
     const int ch = min(c0 + j, CH - 1);
@@ -114,8 +121,31 @@ DHP_DEV void load_sup(SupRegs& l, const u32x4* __restrict__ cb, const uint16_t* 
     for (int u = 0; u < 4; ++u) {
         const int r = min(4 * u + g, rmax);
         l.c[u] = __builtin_nontemporal_load(cb + (uint32_t)(r * CH + ch));
-        const uint32_t o = (uint32_t)(r * G + (ch >> 1));
-        l.sb[u] = u16x2v{sb[o], bb[o]};
+        if constexpr (!SBT) {
+            const uint32_t o = (uint32_t)(r * G + (ch >> 1));
+            l.sb[u] = u16x2v{sb[o], bb[o]};
+        }
+    }
+}
+
+// The tile block (SBT, every tile whole: N % 16 == 0): the 16 rows' scales, then their biases
+// (32 G bytes each, contiguous in memory, 16-byte aligned), as 16-byte pieces p = lane + 64 i,
+// i < 3 (64 G <= 3072). Pieces past 4 G read the last piece again and are not written.
+DHP_DEV void load_tile_sb(u32x4 (&q)[3], const uint16_t* __restrict__ sb, const uint16_t* __restrict__ bb,
+                          int G, int lane) {
+    const int half = 32 * G;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int off = min(16 * (lane + 64 * i), 64 * G - 16);
+        const bool isb = off >= half;
+        q[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(isb ? bb : sb) + (isb ? off - half : off));
+    }
+}
+DHP_DEV void store_tile_sb(const u32x4 (&q)[3], uint8_t* blk, int G, int lane) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int off = 16 * (lane + 64 * i);
+        if (off < 64 * G) *reinterpret_cast<u32x4*>(blk + off) = q[i];
     }
 }
 
@@ -142,25 +172,32 @@ DHP_DEV void swap16(uint32_t& a, uint32_t& b) {
 // staged pieces and pairs (so D = 0, sum 0, power of two 0) and get -0 as scale and bias, so each
 // of their steps is fma(fma(-0, 0, -0 * 0), 0, acc) = acc + (-0), which is acc for every acc,
 // zeros of either sign included: the chains take the same values as in the M=1 kernels.
-template <int MI, bool PAD>
+//
+// sbq[u]: groups 2u, 2u + 1 of the super-step for row n. SBT: their two scales (x) and two biases
+// (y) from the tile block, group 2u in the low halves (G even, so a padding group's pair is padding
+// as a whole). Otherwise the per-super-step words: group 2u's (scale, bias) in x, group 2u + 1's
+// in y.
+template <int MI, bool PAD, bool SBT>
 DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, int WG, float (&acc)[MI][SUP / 2],
-                     int c0, int CH, int lane, uint8_t* tw) {
+                     int c0, int CH, int G, int lane, uint8_t* tw) {
     const int w = lane >> 4;                          // code word of a chunk; activation row of a result
     const int j = lane & 15;
     const int a_off = 4 * (12 * w + 3 * (j >> 2) + min(lane & 3, 2));   // A fragment words
     // turnaround: lane (w, j) wrote chunk c0 + j of tile rows 4u + w; lane (n = j, w) reads back
-    // chunk c0 + 4u + w of row n, and the scale and bias words of groups 2u, 2u + 1 of row n
+    // chunk c0 + 4u + w of row n (and, per super-step, the scale and bias words of row n)
     u32x4 cq[4];
     uint2 sbq[4];
-    uint8_t* tsb = tw + 16 * TR_PITCH;
+    uint8_t* tsb = tw + TR_CODES;
 #pragma unroll
     for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(tw + (4 * u + w) * TR_PITCH + 16 * j) = l.c[u];
+    if constexpr (!SBT) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        uint32_t pk = __builtin_bit_cast(uint32_t, l.sb[u]);
-        if (PAD && c0 + j >= CH) pk = 0x80008000u;    // -0 scale and bias for a padding group
-        // both lanes of a group write the same word
-        *reinterpret_cast<uint32_t*>(tsb + (4 * u + w) * SB_PITCH + 4 * (j >> 1)) = pk;
+        for (int u = 0; u < 4; ++u) {
+            uint32_t pk = __builtin_bit_cast(uint32_t, l.sb[u]);
+            if (PAD && c0 + j >= CH) pk = 0x80008000u;    // -0 scale and bias for a padding group
+            // both lanes of a group write the same word
+            *reinterpret_cast<uint32_t*>(tsb + (4 * u + w) * SB_PITCH + 4 * (j >> 1)) = pk;
+        }
     }
     // the region is the wave's own: its LDS operations complete in order, so only the compiler
     // must not move the reads above the writes
@@ -168,8 +205,18 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int u = 0; u < 4; ++u) cq[u] = *reinterpret_cast<const u32x4*>(tw + j * TR_PITCH + 16 * (4 * u + w));
+    if constexpr (SBT) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sbq[u] = *reinterpret_cast<const uint2*>(tsb + j * SB_PITCH + 8 * u);
+        for (int u = 0; u < 4; ++u) {
+            const int ga = (c0 >> 1) + 2 * u;
+            const int o = j * 2 * G + 2 * min(ga, G - 2);
+            sbq[u] = uint2{*reinterpret_cast<const uint32_t*>(tsb + o), *reinterpret_cast<const uint32_t*>(tsb + 32 * G + o)};
+            if (PAD && ga >= G) sbq[u] = uint2{0x80008000u, 0x80008000u};   // -0 for a padding pair
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sbq[u] = *reinterpret_cast<const uint2*>(tsb + j * SB_PITCH + 8 * u);
+    }
     // and the next super-step's writes must not move above these reads
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
@@ -205,9 +252,15 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
             unpack_i8(wv[2 * e], lo0, hi0);
             unpack_i8(wv[2 * e + 1], lo1, hi1);
             const i32x4 bq = {(int)lo0, (int)hi0, (int)lo1, (int)hi1};
-            const uint32_t sbw = e ? sbq[u].y : sbq[u].x;   // group gi: scale low, bias high (bf16)
-            const float s = __builtin_bit_cast(float, sbw << 16);
-            const float b = __builtin_bit_cast(float, sbw & 0xFFFF0000u);
+            float s, b;                                // group gi = 2u + e as fp32
+            if constexpr (SBT) {
+                s = __builtin_bit_cast(float, e ? (sbq[u].x & 0xFFFF0000u) : (sbq[u].x << 16));
+                b = __builtin_bit_cast(float, e ? (sbq[u].y & 0xFFFF0000u) : (sbq[u].y << 16));
+            } else {
+                const uint32_t sbw = e ? sbq[u].y : sbq[u].x;
+                s = __builtin_bit_cast(float, sbw << 16);
+                b = __builtin_bit_cast(float, sbw & 0xFFFF0000u);
+            }
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[e][mi], bq, i32x4{0, 0, 0, 0}, 0, 0, 0);
@@ -217,10 +270,12 @@ DHP_DEV void run_sup(const SupRegs& l, const uint32_t* xw, const float2* spw, in
     }
 }
 
-// One resident block per compute unit (the staged activations and the waves' turnaround regions
-// need more than half its LDS). FULL: K % 512 == 0, no padding groups. ONE: all of K fits one
-// staging window, staged once per block before the first tile.
-template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE>
+// One resident block per compute unit (the staged activations and the waves' regions need more
+// than half its LDS). FULL: K % 512 == 0, no padding groups. ONE: all of K fits one staging
+// window, staged once per block before the first tile. SBT (only with ONE): each tile's scales
+// and biases arrive as one coalesced block (2.5 KB at K = 2560) instead of 2-byte loads per chunk;
+// with a cold last-level cache the loads alone of the M=8 LM head took 44.7 against 47.4 us.
+template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE, bool SBT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 4, WPB / 4))) void k_gemv_rows(
     const u32x4* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const _Float16* __restrict__ x, int m0, int mr, int N, int K, void* __restrict__ y,
@@ -235,7 +290,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 4
     const int W = window_chunks<MR>(CH);
     const int WG = W / 2;
     float2* sps = reinterpret_cast<float2*>(xs + (size_t)WG * MI * AB_DW);
-    uint8_t* tw = reinterpret_cast<uint8_t*>(xs) + stage_bytes(MR, W) + (size_t)wave * TR_BYTES;
+    uint8_t* tw = reinterpret_cast<uint8_t*>(xs) + stage_bytes(MR, W) + (size_t)wave * region_bytes<SBT>();
     const int ngroups = ((N + 15) / 16 + WPB - 1) / WPB;
     if constexpr (ONE) stage_window<MR>(xs, sps, x, m0, mr, K, CH, 0, W);
 
@@ -273,7 +328,16 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 4
         // second may be partial), and an odd last super-step runs after the loop on the set
         // already loaded.
         SupRegs la, lb;
-        load_sup(la, cb, sb, bb, rmax, 0, g, n, CH, G);
+        u32x4 tq[3];
+        if constexpr (SBT) load_tile_sb(tq, sb, bb, G, lane);
+        load_sup<SBT>(la, cb, sb, bb, rmax, 0, g, n, CH, G);
+        if constexpr (SBT) {
+            // the previous tile's reads of the block come first in the wave's LDS order
+            asm volatile("" ::: "memory");
+            store_tile_sb(tq, tw + TR_CODES, G, lane);
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");
+        }
         int w0 = ONE ? 0 : -W;
         int c0 = 0;
 #pragma unroll 1
@@ -282,18 +346,20 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 4
                 w0 = c0;
                 stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
-            load_sup(lb, cb, sb, bb, rmax, c0 + SUP, g, n, CH, G);
-            run_sup<MI, false>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane, tw);
-            load_sup(la, cb, sb, bb, rmax, c0 + 2 * SUP, g, n, CH, G);
-            run_sup<MI, !FULL>(lb, xs + (size_t)(c0 + SUP - w0) / 2 * MI * AB_DW, sps + (c0 + SUP - w0) / 2, WG, acc,
-                               c0 + SUP, CH, lane, tw);
+            load_sup<SBT>(lb, cb, sb, bb, rmax, c0 + SUP, g, n, CH, G);
+            run_sup<MI, false, SBT>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, G,
+                                    lane, tw);
+            load_sup<SBT>(la, cb, sb, bb, rmax, c0 + 2 * SUP, g, n, CH, G);
+            run_sup<MI, !FULL, SBT>(lb, xs + (size_t)(c0 + SUP - w0) / 2 * MI * AB_DW, sps + (c0 + SUP - w0) / 2, WG,
+                                    acc, c0 + SUP, CH, G, lane, tw);
         }
         if (c0 < CH) {                           // uniform: one (possibly partial) super-step left
             if (!ONE && c0 >= w0 + W) {
                 w0 = c0;
                 stage_window<MR>(xs, sps, x, m0, mr, K, CH, w0, W);
             }
-            run_sup<MI, !FULL>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, lane, tw);
+            run_sup<MI, !FULL, SBT>(la, xs + (size_t)(c0 - w0) / 2 * MI * AB_DW, sps + (c0 - w0) / 2, WG, acc, c0, CH, G,
+                                    lane, tw);
         }
 
         // the chains meet in the M=1 kernels' butterfly order; lane (n, g) holds activation row
@@ -345,48 +411,62 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPB / 4
 }
 
 // Dynamic LDS above 64 KiB must be allowed once per kernel and device.
-template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE>
+template <int MI, bool F32OUT, bool ARGMAX, bool FULL, bool ONE, bool SBT>
 hipError_t allow_lds(size_t lds) {
     static unsigned long long configured = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
     const unsigned long long bit = 1ull << (dev & 63);
     if (__atomic_load_n(&configured, __ATOMIC_ACQUIRE) & bit) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_rows<MI, F32OUT, ARGMAX, FULL, ONE>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_gemv_rows<MI, F32OUT, ARGMAX, FULL, ONE, SBT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e == hipSuccess) __atomic_fetch_or(&configured, bit, __ATOMIC_RELEASE);
     return e;
 }
 
-template <int MI, bool FULL, bool ONE>
+template <int MI, bool FULL, bool ONE, bool SBT>
 hipError_t launch_rows_full(bool f32, bool am, dim3 g, size_t lds, hipStream_t s, const u32x4* c, const uint16_t* sc,
                             const uint16_t* bi, const _Float16* x, int m0, int mr, int N, int K, void* y, float* pv,
                             int* pi) {
     const dim3 b(THREADS);
-    const hipError_t e = f32 && am ? allow_lds<MI, true, true, FULL, ONE>(lds)
-                         : f32     ? allow_lds<MI, true, false, FULL, ONE>(lds)
-                         : am      ? allow_lds<MI, false, true, FULL, ONE>(lds)
-                                   : allow_lds<MI, false, false, FULL, ONE>(lds);
+    const hipError_t e = f32 && am ? allow_lds<MI, true, true, FULL, ONE, SBT>(lds)
+                         : f32     ? allow_lds<MI, true, false, FULL, ONE, SBT>(lds)
+                         : am      ? allow_lds<MI, false, true, FULL, ONE, SBT>(lds)
+                                   : allow_lds<MI, false, false, FULL, ONE, SBT>(lds);
     if (e != hipSuccess) return e;
-    if (f32 && am) hipLaunchKernelGGL((k_gemv_rows<MI, true, true, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    else if (f32) hipLaunchKernelGGL((k_gemv_rows<MI, true, false, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    else if (am) hipLaunchKernelGGL((k_gemv_rows<MI, false, true, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    else hipLaunchKernelGGL((k_gemv_rows<MI, false, false, FULL, ONE>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    if (f32 && am)
+        hipLaunchKernelGGL((k_gemv_rows<MI, true, true, FULL, ONE, SBT>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    else if (f32)
+        hipLaunchKernelGGL((k_gemv_rows<MI, true, false, FULL, ONE, SBT>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    else if (am)
+        hipLaunchKernelGGL((k_gemv_rows<MI, false, true, FULL, ONE, SBT>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    else
+        hipLaunchKernelGGL((k_gemv_rows<MI, false, false, FULL, ONE, SBT>), g, b, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
     return hipGetLastError();
 }
 
+// Dynamic LDS a launch may take: the compute unit's 160 KiB less room for the static arrays.
+constexpr size_t LDS_DYN_MAX = 160 * 1024 - 1024;
+
 template <int MI>
-hipError_t launch_rows_mi(bool f32, bool am, dim3 g, bool full, hipStream_t s, const u32x4* c, const uint16_t* sc,
-                          const uint16_t* bi, const _Float16* x, int m0, int mr, int N, int K, void* y, float* pv,
-                          int* pi) {
-    const int CH = K >> 5;
+hipError_t launch_rows_mi(bool f32, bool am, dim3 g, bool full, bool sb_aligned, hipStream_t s, const u32x4* c,
+                          const uint16_t* sc, const uint16_t* bi, const _Float16* x, int m0, int mr, int N, int K,
+                          void* y, float* pv, int* pi) {
+    const int CH = K >> 5, G = K >> 6;
     const int W = window_chunks<4 * MI>(CH);
-    const size_t lds = stage_bytes(4 * MI, W) + (size_t)WPB * TR_BYTES;
     const bool one = CH <= W;
-    if (full && one) return launch_rows_full<MI, true, true>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    if (full) return launch_rows_full<MI, true, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    if (one) return launch_rows_full<MI, false, true>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
-    return launch_rows_full<MI, false, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    // the tile block: all of K in one window, whole tiles (N % 16 == 0), G even, 64 G bytes within
+    // the region, 16-byte aligned scale and bias arrays, and the larger regions within the LDS
+    const size_t lds_sbt = stage_bytes(4 * MI, W) + (size_t)WPB * region_bytes<true>();
+    const bool sbt = one && N % 16 == 0 && G % 2 == 0 && 64 * G <= SBT_MAX && sb_aligned && lds_sbt <= LDS_DYN_MAX;
+    if (sbt && full) return launch_rows_full<MI, true, true, true>(f32, am, g, lds_sbt, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    if (sbt) return launch_rows_full<MI, false, true, true>(f32, am, g, lds_sbt, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    const size_t lds = stage_bytes(4 * MI, W) + (size_t)WPB * region_bytes<false>();
+    if (full && one) return launch_rows_full<MI, true, true, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    if (full) return launch_rows_full<MI, true, false, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    if (one) return launch_rows_full<MI, false, true, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
+    return launch_rows_full<MI, false, false, false>(f32, am, g, lds, s, c, sc, bi, x, m0, mr, N, K, y, pv, pi);
 }
 
 }  // namespace
@@ -413,13 +493,14 @@ int launch_gemv_rows(const dhp_int4* w, const void* x, int M, void* y, int y_f32
     const auto* xh = static_cast<const _Float16*>(x);
     const bool am = argmax != nullptr;
     const bool full = K % 512 == 0;              // whole super-steps only
+    const bool sb_aligned = ((uintptr_t)sc % 16) == 0 && ((uintptr_t)bi % 16) == 0;
     const dim3 g((unsigned)nb);
     // activation rows in passes of up to 8 (each pass streams the weights once)
     for (int m0 = 0; m0 < M; m0 += 8) {
         const int mr = M - m0 < 8 ? M - m0 : 8;
         hipError_t e;
-        if (mr <= 4) e = launch_rows_mi<1>(y_f32, am, g, full, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
-        else e = launch_rows_mi<2>(y_f32, am, g, full, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
+        if (mr <= 4) e = launch_rows_mi<1>(y_f32, am, g, full, sb_aligned, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
+        else e = launch_rows_mi<2>(y_f32, am, g, full, sb_aligned, s, c, sc, bi, xh, m0, mr, N, K, y, pv, pi);
         if (e != hipSuccess) return dhp_fail(DHP_ERR_LAUNCH, "gemv rows launch: %s", hipGetErrorString(e));
     }
     if (argmax) {

@@ -5,7 +5,9 @@ bit for bit. Bar: every row's fp32 logits bit for bit equal to the m = 1 call on
 its argmax equal, and the rows within |d| <= 1e-3 + 1e-2 |oracle| of the fp64 oracle. Shapes
 cover ragged row counts (not a multiple of the 256-row block), K with a partial last segment of
 16 chunks (K % 512 != 0, where the m = 1 call takes its LDS kernel), activation rows in two
-passes (m > 8), and biases other than -8 * scale.
+passes (m > 8), and biases other than -8 * scale. Row counts that are multiples of 16 with an even
+number of groups (at most 48) take each tile's scales and biases as one coalesced block; the
+others take them per chunk.
 """
 import numpy as np
 import pytest
@@ -69,6 +71,21 @@ def test_rows_bitwise_shapes(n, k):
     y, am, ys, ams = rows_and_singles(dev(t), X)
     assert_bitwise(y, am, ys, ams, f"n={n} k={k}")
     assert_within_tol(y.numpy(), oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, X), f"rows n={n} k={k}")
+
+
+@pytest.mark.parametrize("n,k,m", [(4096, 2560, 8), (1024, 640, 4), (512, 1152, 6), (2048, 1536, 12)])
+def test_rows_bitwise_tile_block(n, k, m):
+    """Whole tiles, G even: the tile-block path, with whole and partial last super-steps, one and
+    two groups of activation rows, and two passes."""
+    say(f"gemv rows tile block m={m} n={n} k={k}")
+    rng = np.random.default_rng([95, n, k, m])
+    t = general_bias(rng, synth.int4_tensor(rng, n, k))
+    X = synth.normal_f16(rng, (m, k))
+    y, am, ys, ams = rows_and_singles(dev(t), X)
+    assert_bitwise(y, am, ys, ams, f"tile block n={n} k={k} m={m}")
+    ref = oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, X)
+    assert_within_tol(y.numpy(), ref, f"rows tile block n={n} k={k} m={m}")
+    assert am.numpy().tolist() == oracle.argmax_lowest(ref).tolist()
 
 
 def test_rows_bitwise_general_biases():
