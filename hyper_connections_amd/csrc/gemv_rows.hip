@@ -17,12 +17,15 @@
 //    joins them (D = P2 * 2^14 + P1 * 2^7 + P0, exact). Eight activation rows take two
 //    instructions.
 //  * Codes stream as in the M=1 kernels: 16 lanes read 256 contiguous bytes of one row (16-byte
-//    nontemporal loads, four rows per instruction), each lane with the scale and bias of its own
-//    chunk. A super-step is 16 chunks of the tile's 16 rows (8 groups, one per chain); the next
-//    one is in flight while one computes. A small LDS region per wave turns it around: lane
-//    (n, w) reads back chunk c0 + 4u + w of row n, and two swaps across the wave halves
-//    (v_permlane32_swap) and two across neighbouring 16-lane rows (v_permlane16_swap) transpose
-//    each 4 x 4 block so that lane (n, w) holds code word w of the four chunks.
+//    nontemporal loads, four rows per instruction). A super-step is 16 chunks of the tile's 16
+//    rows (8 groups, one per chain); the next one is in flight while one computes. A small LDS
+//    region per wave turns it around: lane (n, w) reads back chunk c0 + 4u + w of row n, and two
+//    swaps across the wave halves (v_permlane32_swap) and two across neighbouring 16-lane rows
+//    (v_permlane16_swap) transpose each 4 x 4 block so that lane (n, w) holds code word w of the
+//    four chunks.
+//  * Scales and biases: where the tile's rows are whole and few enough groups (SBT), the tile's
+//    16 rows of scales and biases arrive as one coalesced block into the wave's region; otherwise
+//    each lane loads the scale and bias of its own chunk and they take the same turnaround.
 //  * The activations' pieces (xg_stage_octet, the same conversion as the M=1 kernels) are staged
 //    once per block in LDS; one block of twelve waves per compute unit, walking tiles.
 //  * Each chain's steps run in group order, and the final butterfly adds the chains in the M=1
@@ -104,8 +107,9 @@ DHP_DEV void stage_window(uint32_t* xs, float2* sps, const _Float16* __restrict_
 }
 
 // One super-step of one lane as loaded: lane (g, j) holds chunk c0 + j of tile row 4u + g in c[u],
-// and that chunk's group scale (low half) and bias (high half) in sb[u]. Rows past N are clamped
-// to the last row (computed again, never stored); chunks past the row to its last chunk.
+// and (per-chunk path only) that chunk's group scale (low half) and bias (high half) in sb[u].
+// Rows past N are clamped to the last row (computed again, never stored); chunks past the row to
+// its last chunk.
 typedef unsigned short u16x2v __attribute__((ext_vector_type(2)));
 struct SupRegs {
     u32x4 c[4];
