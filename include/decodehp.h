@@ -117,9 +117,10 @@ int decodehp_dequant_gemv(const dhp_int4* w, const void* x, int32_t m, void* y, 
                           int32_t* argmax, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * decodehp_dequant_gemv_mc -- decodehp_dequant_gemv on the matrix cores (the pages' separate
- * matrix-instruction variant, "src/real_forward.rs", field batched_gemv_prefill): faster for
- * m >= 8 (the LM head over 8 rows), but NOT bit-equal to the m = 1 call. Each weight is
+ * decodehp_dequant_gemv_mc -- decodehp_dequant_gemv on the fp16 matrix cores (the pages' separate
+ * matrix-instruction variant, "src/real_forward.rs", field batched_gemv_prefill). It is NOT
+ * bit-equal to the m = 1 call, and at the LM head's size over 8 rows it is no faster than
+ * decodehp_dequant_gemv (about 52 against 49 us per call from HBM). Each weight is
  * dequantized once into an fp16 operand, q*s+b rounded to fp16 (exact when the bias is
  * -8*scale and the scale is a bf16 value in fp16's normal range; otherwise off by up to half
  * an fp16 ulp per weight, which can put outputs near zero past the 1e-3 + 1e-2|y| bar), and
