@@ -73,10 +73,12 @@ def test_rows_bitwise_shapes(n, k):
     assert_within_tol(y.numpy(), oracle.dequant_gemv(t.q, t.s_bits, t.b_bits, X), f"rows n={n} k={k}")
 
 
-@pytest.mark.parametrize("n,k,m", [(4096, 2560, 8), (1024, 640, 4), (512, 1152, 6), (2048, 1536, 12)])
+@pytest.mark.parametrize("n,k,m", [(4096, 2560, 8), (1024, 640, 4), (512, 1152, 6), (2048, 1536, 12),
+                                   (256, 128, 3), (64, 3072, 4)])
 def test_rows_bitwise_tile_block(n, k, m):
     """Whole tiles, G even: the tile-block path, with whole and partial last super-steps, one and
-    two groups of activation rows, and two passes."""
+    two groups of activation rows, and two passes; the smallest block (K = 128, a super-step
+    mostly padding) and the largest (K = 3072, 64 G = 3072 bytes, which fits the LDS at m <= 4)."""
     say(f"gemv rows tile block m={m} n={n} k={k}")
     rng = np.random.default_rng([95, n, k, m])
     t = general_bias(rng, synth.int4_tensor(rng, n, k))
